@@ -1,0 +1,211 @@
+"""fp64 CPU oracle for the Gated Delta Rule-2 layer -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py`` may import
+this module.  The product library (``gated_delta_rule_gdr_amd``) never imports it, and it imports
+nothing from the product library: the two share no code.
+
+What lives here:
+  * a ctypes wrapper around ``gdr2_oracle.c`` (token-by-token fp64 recurrence, its hand-derived
+    reverse mode, one decode step, and the KDA / Gated DeltaNet reduced rules written as explicit
+    transition-matrix products);
+  * ``la_closed_form``: causal linear attention written as masked matrix products (the textbook
+    definition), which is what GDR-2 must reduce to at alpha = 1, b = 0, w = 1;
+  * ``gla_closed_form``: the b = 0 case as an explicit double sum over (query token, key token)
+    with cumulative decay products, i.e. channel-wise gated linear attention.
+
+Citations (page title, section):
+  * update rule and the KDA / Gated DeltaNet reductions -- forum summary "Gated DeltaNet-2:
+    Decoupling Erase and Write Gates in Linear Attention for Better Memory Editing"
+    (zhichai.net, English), section "Gated Delta Rule-2";
+  * decay before the edit, erase gate on the key side, write gate on the value side -- the
+    ainews.random.gg article on NVIDIA's Gated DeltaNet-2, section "Gated Delta Rule-2: two gates
+    instead of one";
+  * "basic linear attention only adds" -- forum summary, section "The Memory Dilemma".
+
+Every function takes and returns float64 numpy arrays in the layouts of ``gdr2_oracle.c``:
+q, k, log_alpha, b: [B,T,H,dk]; v, w, o, dO: [B,T,H,dv]; states [B,H,dk,dv].
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gdr2_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libgdr2_oracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the C oracle (gcc, -O2, OpenMP) next to its source and return the path."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.check_call(
+            ["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c99", "-Wall", "-o", tmp, _SRC,
+             "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB_PATH)
+        L, P = ctypes.c_long, ctypes.c_void_p
+        lib.gdr2o_forward.argtypes = [L] * 5 + [P] * 9
+        lib.gdr2o_forward.restype = None
+        lib.gdr2o_backward.argtypes = [L] * 5 + [P] * 16
+        lib.gdr2o_backward.restype = None
+        lib.gdr2o_decode_step.argtypes = [L] * 4 + [P] * 9
+        lib.gdr2o_decode_step.restype = None
+        lib.gdr2o_kda_forward.argtypes = [L] * 5 + [ctypes.c_int] + [P] * 8
+        lib.gdr2o_kda_forward.restype = None
+        lib.gdr2o_num_threads.argtypes = []
+        lib.gdr2o_num_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _f64(x):
+    return None if x is None else np.ascontiguousarray(x, dtype=np.float64)
+
+
+def _ptr(x):
+    return None if x is None else x.ctypes.data_as(ctypes.c_void_p)
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle runs on."""
+    return int(_load().gdr2o_num_threads())
+
+
+def forward(q, k, v, log_alpha, b, w, S0=None):
+    """Token-by-token GDR-2 forward.  Returns (o [B,T,H,dv], S_T [B,H,dk,dv])."""
+    q, k, v, la, b, w, S0 = map(_f64, (q, k, v, log_alpha, b, w, S0))
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    o = np.zeros((B, T, H, dv))
+    ST = np.zeros((B, H, dk, dv))
+    _load().gdr2o_forward(B, T, H, dk, dv, *map(_ptr, (q, k, v, la, b, w, S0, o, ST)))
+    return o, ST
+
+
+def backward(q, k, v, log_alpha, b, w, dO, S0=None, dST=None):
+    """Reverse mode of ``forward``.
+
+    Returns a dict with dq, dk, dv, dlog_alpha, db, dw (token layouts) and dS0 [B,H,dk,dv].
+    ``dST`` is the cotangent of the final state (None = 0)."""
+    q, k, v, la, b, w, dO, S0, dST = map(_f64, (q, k, v, log_alpha, b, w, dO, S0, dST))
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    out = {n: np.zeros(q.shape) for n in ("dq", "dk", "dlog_alpha", "db")}
+    out.update({n: np.zeros(v.shape) for n in ("dv", "dw")})
+    out["dS0"] = np.zeros((B, H, dk, dv))
+    _load().gdr2o_backward(
+        B, T, H, dk, dv, *map(_ptr, (q, k, v, la, b, w, S0, dO, dST, out["dq"], out["dk"],
+                                      out["dv"], out["dlog_alpha"], out["db"], out["dw"],
+                                      out["dS0"])))
+    return out
+
+
+def decode_step(q, k, v, log_alpha, b, w, S_in=None):
+    """One recurrent token for N sequences x H heads.
+
+    q, k, log_alpha, b: [N,H,dk]; v, w: [N,H,dv]; S_in: [N,H,dk,dv] or None (= 0).
+    Returns (o [N,H,dv], S_out [N,H,dk,dv])."""
+    q, k, v, la, b, w, S_in = map(_f64, (q, k, v, log_alpha, b, w, S_in))
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    S_out = np.zeros((N, H, dk, dv))
+    o = np.zeros((N, H, dv))
+    _load().gdr2o_decode_step(N, H, dk, dv, *map(_ptr, (q, k, v, la, b, w, S_in, S_out, o)))
+    return o, S_out
+
+
+def kda_forward(q, k, v, log_alpha, beta, S0=None, scalar_decay=False):
+    """Reduced rules: KDA (channel-wise decay, one scalar edit strength beta per token and head)
+    and, with ``scalar_decay``, Gated DeltaNet (alpha is log_alpha[..., 0] per token and head).
+
+    beta: [B,T,H].  Returns (o, S_T)."""
+    q, k, v, la, beta, S0 = map(_f64, (q, k, v, log_alpha, beta, S0))
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    o = np.zeros((B, T, H, dv))
+    ST = np.zeros((B, H, dk, dv))
+    _load().gdr2o_kda_forward(B, T, H, dk, dv, 1 if scalar_decay else 0,
+                              *map(_ptr, (q, k, v, la, beta, S0, o, ST)))
+    return o, ST
+
+
+def la_closed_form(q, k, v, S0=None):
+    """Causal linear attention (the rule that "only adds"), per (batch, head):
+    O = tril(Q K^T) V + Q S0,   S_T = S0 + K^T V.   Returns (o, S_T)."""
+    q, k, v, S0 = map(_f64, (q, k, v, S0))
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    o = np.zeros((B, T, H, dv))
+    ST = np.zeros((B, H, dk, dv))
+    mask = np.tril(np.ones((T, T)))
+    for bb in range(B):
+        for h in range(H):
+            Q, K, V = q[bb, :, h], k[bb, :, h], v[bb, :, h]
+            s0 = np.zeros((dk, dv)) if S0 is None else S0[bb, h]
+            o[bb, :, h] = ((Q @ K.T) * mask) @ V + Q @ s0
+            ST[bb, h] = s0 + K.T @ V
+    return o, ST
+
+
+def la_backward_closed_form(q, k, v, dO, S0=None, dST=None):
+    """Gradients of ``la_closed_form`` written out as matrix products:
+    with M = tril mask, P = (Q K^T) * M, dP = (dO V^T) * M:
+      dQ = dP K + dO S0^T;  dK = dP^T Q + V dST^T;  dV = P^T dO + K dST;  dS0 = Q^T dO + dST."""
+    q, k, v, dO, S0, dST = map(_f64, (q, k, v, dO, S0, dST))
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    g = {n: np.zeros(q.shape) for n in ("dq", "dk")}
+    g["dv"] = np.zeros(v.shape)
+    g["dS0"] = np.zeros((B, H, dk, dv))
+    mask = np.tril(np.ones((T, T)))
+    for bb in range(B):
+        for h in range(H):
+            Q, K, V, D = q[bb, :, h], k[bb, :, h], v[bb, :, h], dO[bb, :, h]
+            s0 = np.zeros((dk, dv)) if S0 is None else S0[bb, h]
+            ds = np.zeros((dk, dv)) if dST is None else dST[bb, h]
+            P = (Q @ K.T) * mask
+            dP = (D @ V.T) * mask
+            g["dq"][bb, :, h] = dP @ K + D @ s0.T
+            g["dk"][bb, :, h] = dP.T @ Q + V @ ds.T
+            g["dv"][bb, :, h] = P.T @ D + K @ ds
+            g["dS0"][bb, h] = Q.T @ D + ds
+    return g
+
+
+def gla_closed_form(q, k, v, log_alpha, w, S0=None):
+    """GDR-2 with b = 0 (no erase): channel-wise gated linear attention as an explicit sum,
+        o_t[j] = sum_i q_t[i] * A(0,t)[i] * S0[i,j]
+               + sum_{s<=t} sum_i q_t[i] k_s[i] A(s,t)[i] * w_s[j] v_s[j],
+    with A(s,t)[i] = prod_{u=s+1..t} alpha_u[i] (and A(0,t) including alpha_1..alpha_t).
+    O(T^2 d^2) -- tiny inputs only.  Returns o."""
+    q, k, v, la, w, S0 = map(_f64, (q, k, v, log_alpha, w, S0))
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    o = np.zeros((B, T, H, dv))
+    for bb in range(B):
+        for h in range(H):
+            alpha = np.exp(la[bb, :, h])  # [T, dk]
+            for t in range(T):
+                acc = np.zeros(dv)
+                if S0 is not None:
+                    dec = np.prod(alpha[: t + 1], axis=0)
+                    acc += (q[bb, t, h] * dec) @ S0[bb, h]
+                for s in range(t + 1):
+                    dec = np.prod(alpha[s + 1: t + 1], axis=0) if s < t else np.ones(dk)
+                    coef = float(np.sum(q[bb, t, h] * k[bb, s, h] * dec))
+                    acc += coef * w[bb, s, h] * v[bb, s, h]
+                o[bb, t, h] = acc
+    return o
