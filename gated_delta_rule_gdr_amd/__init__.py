@@ -1,0 +1,164 @@
+"""gated_delta_rule_gdr_amd -- Gated Delta Rule-2 layer on MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libgdr2.so`` (see ``include/gdr2.h``).  It only marshals
+arguments: every step of the computation runs in the library's HIP kernels.  PyTorch provides
+device memory and the current HIP stream.  There is no fallback: if the library is missing or
+fails to load, every call raises.
+
+Entry points (same names as the C ABI):
+  gdr2_fwd_chunked(q, k, v, log_alpha, b, w, S0=None, want_final_state=True, want_chunk_states=False)
+  gdr2_bwd_chunked(q, k, v, log_alpha, b, w, dO, S0=None, dS_T=None, chunk_states=None, want_dS0=True)
+  gdr2_decode_step(q, k, v, log_alpha, b, w, S_in=None, S_out=None)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["gdr2_fwd_chunked", "gdr2_bwd_chunked", "gdr2_decode_step", "library_path",
+           "load_library", "Gdr2Error", "CHUNK"]
+
+CHUNK = 64
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libgdr2.so")
+_lib = None
+
+_STATUS = {0: "ok", 1: "GDR2_E_NULL", 2: "GDR2_E_SHAPE", 3: "GDR2_E_DTYPE",
+           4: "GDR2_E_UNSUPPORTED", 5: "GDR2_E_ALIGN", 6: "GDR2_E_ALIAS", 7: "GDR2_E_WORKSPACE",
+           8: "GDR2_E_HIP"}
+_DT = {torch.float32: 0, torch.bfloat16: 1}
+
+
+class Gdr2Error(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn} failed: {_STATUS.get(status, status)}")
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libgdr2.so (built in-tree by ``gated_delta_rule_gdr_amd/build.py``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"HIP library not built: {_LIB_PATH} is missing "
+                           "(run python gated_delta_rule_gdr_amd/build.py)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    I64, P, SZ = ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+    lib.gdr2_fwd_chunked.argtypes = [I64] * 5 + [ctypes.c_int] + [P] * 11
+    lib.gdr2_fwd_chunked.restype = ctypes.c_int
+    lib.gdr2_bwd_chunked.argtypes = [I64] * 5 + [ctypes.c_int] + [P] * 18 + [SZ, P]
+    lib.gdr2_bwd_chunked.restype = ctypes.c_int
+    lib.gdr2_decode_step.argtypes = [I64] * 4 + [ctypes.c_int] + [P] * 10
+    lib.gdr2_decode_step.restype = ctypes.c_int
+    lib.gdr2_bwd_workspace_bytes.argtypes = [I64] * 5 + [ctypes.c_int, ctypes.c_int]
+    lib.gdr2_bwd_workspace_bytes.restype = SZ
+    lib.gdr2_chunk_states_bytes.argtypes = [I64] * 5 + [ctypes.c_int]
+    lib.gdr2_chunk_states_bytes.restype = SZ
+    lib.gdr2_num_chunks.argtypes = [I64]
+    lib.gdr2_num_chunks.restype = I64
+    lib.gdr2_status_string.argtypes = [ctypes.c_int]
+    lib.gdr2_status_string.restype = ctypes.c_char_p
+    lib.gdr2_abi_version.argtypes = []
+    lib.gdr2_abi_version.restype = ctypes.c_int
+    lib.gdr2_dtype_size.argtypes = [ctypes.c_int]
+    lib.gdr2_dtype_size.restype = SZ
+    _lib = lib
+    return lib
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _check(fn, st):
+    if st != 0:
+        raise Gdr2Error(fn, st)
+
+
+def _shapes(q, v):
+    B, T, H, dk = q.shape
+    return B, T, H, dk, v.shape[-1]
+
+
+def _dtype(q):
+    if q.dtype not in _DT:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    return _DT[q.dtype]
+
+
+def _contig(*ts):
+    for t in ts:
+        if t is not None and not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+
+
+def gdr2_fwd_chunked(q, k, v, log_alpha, b, w, S0=None, want_final_state=True,
+                     want_chunk_states=False):
+    """Chunked forward.  Returns (o, S_T or None, chunk_states or None)."""
+    lib = load_library()
+    _contig(q, k, v, log_alpha, b, w, S0)
+    B, T, H, dk, dv = _shapes(q, v)
+    dt = _dtype(q)
+    o = torch.empty((B, T, H, dv), dtype=q.dtype, device=q.device)
+    ST = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device) if want_final_state else None
+    cs = None
+    if want_chunk_states:
+        nbytes = lib.gdr2_chunk_states_bytes(B, T, H, dk, dv, dt)
+        cs = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    st = lib.gdr2_fwd_chunked(B, T, H, dk, dv, dt, _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
+                              _ptr(b), _ptr(w), _ptr(S0), _ptr(o), _ptr(ST), _ptr(cs), _stream())
+    _check("gdr2_fwd_chunked", st)
+    return o, ST, cs
+
+
+def gdr2_bwd_chunked(q, k, v, log_alpha, b, w, dO, S0=None, dS_T=None, chunk_states=None,
+                     want_dS0=True):
+    """Gate-aware backward.  Returns a dict dq, dk, dv, dlog_alpha, db, dw, dS0 (None if not
+    wanted)."""
+    lib = load_library()
+    _contig(q, k, v, log_alpha, b, w, dO, S0, dS_T)
+    B, T, H, dk, dv = _shapes(q, v)
+    dt = _dtype(q)
+    dev = q.device
+    g = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
+             dlog_alpha=torch.empty_like(log_alpha), db=torch.empty_like(b),
+             dw=torch.empty_like(w),
+             dS0=torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev) if want_dS0 else None)
+    wsb = lib.gdr2_bwd_workspace_bytes(B, T, H, dk, dv, dt, 1 if chunk_states is not None else 0)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    st = lib.gdr2_bwd_chunked(B, T, H, dk, dv, dt, _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
+                              _ptr(b), _ptr(w), _ptr(S0), _ptr(chunk_states), _ptr(dO),
+                              _ptr(dS_T), _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]),
+                              _ptr(g["dlog_alpha"]), _ptr(g["db"]), _ptr(g["dw"]),
+                              _ptr(g["dS0"]), _ptr(ws), wsb, _stream())
+    _check("gdr2_bwd_chunked", st)
+    return g
+
+
+def gdr2_decode_step(q, k, v, log_alpha, b, w, S_in=None, S_out=None):
+    """One decode token for [N, H] sequences-heads.  S_out defaults to S_in (in place) or a new
+    buffer.  Returns (o, S_out)."""
+    lib = load_library()
+    _contig(q, k, v, log_alpha, b, w, S_in, S_out)
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = _dtype(q)
+    if S_out is None:
+        S_out = S_in if S_in is not None else torch.empty((N, H, dk, dv), dtype=torch.float32,
+                                                          device=q.device)
+    o = torch.empty((N, H, dv), dtype=q.dtype, device=q.device)
+    st = lib.gdr2_decode_step(N, H, dk, dv, dt, _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
+                              _ptr(b), _ptr(w), _ptr(S_in), _ptr(S_out), _ptr(o), _stream())
+    _check("gdr2_decode_step", st)
+    return o, S_out

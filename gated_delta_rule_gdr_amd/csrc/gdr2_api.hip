@@ -1,0 +1,225 @@
+// gdr2_api.hip -- the C ABI declared in include/gdr2.h: host-side validation, then kernel launch.
+// Nothing here touches device memory before every check has passed.
+#include "gdr2.h"
+
+#include <hip/hip_runtime.h>
+
+#include "gdr2_kernels.hpp"
+
+namespace {
+
+struct Range {
+    const void* p;
+    size_t n;
+};
+
+bool overlap(const Range& a, const Range& b) {
+    if (!a.p || !b.p || a.n == 0 || b.n == 0) return false;
+    const uintptr_t a0 = (uintptr_t)a.p, b0 = (uintptr_t)b.p;
+    return a0 < b0 + b.n && b0 < a0 + a.n;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool dims_ok(int64_t d) { return d == 64 || d == 128; }
+
+// Any output overlapping any input or another output?
+bool any_alias(const Range* outs, int no, const Range* ins, int ni) {
+    for (int i = 0; i < no; ++i) {
+        for (int j = 0; j < ni; ++j)
+            if (overlap(outs[i], ins[j])) return true;
+        for (int j = i + 1; j < no; ++j)
+            if (overlap(outs[i], outs[j])) return true;
+    }
+    return false;
+}
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace
+
+extern "C" {
+
+size_t gdr2_dtype_size(gdr2_dtype dt) {
+    return dt == GDR2_F32 ? 4 : dt == GDR2_BF16 ? 2 : 0;
+}
+
+int64_t gdr2_num_chunks(int64_t T) { return T <= 0 ? 0 : (T + GDR2_CHUNK - 1) / GDR2_CHUNK; }
+
+const char* gdr2_status_string(gdr2_status s) {
+    switch (s) {
+        case GDR2_OK: return "ok";
+        case GDR2_E_NULL: return "required pointer is NULL";
+        case GDR2_E_SHAPE: return "invalid size";
+        case GDR2_E_DTYPE: return "unknown dtype";
+        case GDR2_E_UNSUPPORTED: return "unsupported head size / dtype combination";
+        case GDR2_E_ALIGN: return "pointer not 16-byte aligned";
+        case GDR2_E_ALIAS: return "output overlaps an input or another output";
+        case GDR2_E_WORKSPACE: return "workspace missing or too small";
+        case GDR2_E_HIP: return "HIP launch failed";
+    }
+    return "unknown status";
+}
+
+int gdr2_abi_version(void) { return GDR2_ABI_VERSION; }
+
+size_t gdr2_chunk_states_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                               gdr2_dtype dt) {
+    if (B < 0 || T < 0 || H < 0 || dk < 0 || dv < 0) return 0;
+    return (size_t)B * H * gdr2_num_chunks(T) * dk * dv * gdr2_dtype_size(dt);
+}
+
+size_t gdr2_bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                                gdr2_dtype dt, int have_chunk_states) {
+    const size_t one = round_up(gdr2_chunk_states_bytes(B, T, H, dk, dv, dt), 256);
+    return have_chunk_states ? one : 2 * one;
+}
+
+// Shared shape / dtype checks of the two chunked passes.
+static gdr2_status check_chunked(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                                 gdr2_dtype dt) {
+    if (dt != GDR2_F32 && dt != GDR2_BF16) return GDR2_E_DTYPE;
+    if (B < 0 || T < 0 || H < 0 || dk < 0 || dv < 0) return GDR2_E_SHAPE;
+    if (!dims_ok(dk) || !dims_ok(dv)) return GDR2_E_UNSUPPORTED;
+    if (dt == GDR2_F32 && dk != 64) return GDR2_E_UNSUPPORTED;
+    if (B * H * (dv / 16) > (int64_t)1 << 30) return GDR2_E_SHAPE;
+    if (B * H * gdr2_num_chunks(T) > (int64_t)1 << 30) return GDR2_E_SHAPE;
+    if (T > ((int64_t)1 << 40) || B * T * H > ((int64_t)1 << 50)) return GDR2_E_SHAPE;
+    return GDR2_OK;
+}
+
+gdr2_status gdr2_fwd_chunked(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                             gdr2_dtype dt, const void* q, const void* k, const void* v,
+                             const float* log_alpha, const void* b, const void* w,
+                             const float* S0, void* o, float* S_T, void* chunk_states,
+                             void* stream) {
+    gdr2_status st = check_chunked(B, T, H, dk, dv, dt);
+    if (st != GDR2_OK) return st;
+    if (B == 0 || H == 0) return GDR2_OK;
+    const bool have_tokens = T > 0;
+    if (have_tokens && (!q || !k || !v || !log_alpha || !b || !w || !o)) return GDR2_E_NULL;
+    const void* ptrs[] = {q, k, v, log_alpha, b, w, S0, o, S_T, chunk_states};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return GDR2_E_ALIGN;
+    const size_t es = gdr2_dtype_size(dt);
+    const size_t nk = (size_t)B * T * H * dk, nv = (size_t)B * T * H * dv;
+    const size_t ns = (size_t)B * H * dk * dv;
+    const Range ins[] = {{q, nk * es}, {k, nk * es}, {v, nv * es}, {log_alpha, nk * 4},
+                         {b, nk * es}, {w, nv * es}, {S0, ns * 4}};
+    const Range outs[] = {{o, nv * es}, {S_T, ns * 4},
+                          {chunk_states, gdr2_chunk_states_bytes(B, T, H, dk, dv, dt)}};
+    if (any_alias(outs, 3, ins, 7)) return GDR2_E_ALIAS;
+
+    const int bf = dt == GDR2_BF16;
+    const int dvs = gdr2::fwd_slice_width(bf, (int)dk, (int)dv, B * H);
+    gdr2::FwdParams p;
+    p.B = (int)B;
+    p.H = (int)H;
+    p.NS = (int)(dv / dvs);
+    p.NC = (int)gdr2_num_chunks(T);
+    p.T = T;
+    p.DV = dv;
+    p.q = q; p.k = k; p.v = v; p.b = b; p.w = w;
+    p.la = log_alpha;
+    p.S0 = S0;
+    p.o = o;
+    p.ST = S_T;
+    p.states = chunk_states;
+    hipError_t e = gdr2::fwd_dispatch(bf, (int)dk, dvs, p, (hipStream_t)stream);
+    return e == hipSuccess ? GDR2_OK : GDR2_E_HIP;
+}
+
+gdr2_status gdr2_bwd_chunked(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                             gdr2_dtype dt, const void* q, const void* k, const void* v,
+                             const float* log_alpha, const void* b, const void* w,
+                             const float* S0, const void* chunk_states, const void* dO,
+                             const float* dS_T, void* dq, void* dk_, void* dv_,
+                             float* dlog_alpha, void* db, void* dw, float* dS0,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+    gdr2_status st = check_chunked(B, T, H, dk, dv, dt);
+    if (st != GDR2_OK) return st;
+    if (B == 0 || H == 0) return GDR2_OK;
+    const bool have_tokens = T > 0;
+    if (have_tokens && (!q || !k || !v || !log_alpha || !b || !w || !dO || !dq || !dk_ ||
+                        !dv_ || !dlog_alpha || !db || !dw))
+        return GDR2_E_NULL;
+    const void* ptrs[] = {q, k, v, log_alpha, b, w, S0, chunk_states, dO, dS_T, dq, dk_, dv_,
+                          dlog_alpha, db, dw, dS0, workspace};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return GDR2_E_ALIGN;
+    const size_t need = gdr2_bwd_workspace_bytes(B, T, H, dk, dv, dt, chunk_states != nullptr);
+    if (have_tokens && (!workspace || workspace_bytes < need)) return GDR2_E_WORKSPACE;
+    const size_t es = gdr2_dtype_size(dt);
+    const size_t nk = (size_t)B * T * H * dk, nv = (size_t)B * T * H * dv;
+    const size_t ns = (size_t)B * H * dk * dv;
+    const size_t csb = gdr2_chunk_states_bytes(B, T, H, dk, dv, dt);
+    const Range ins[] = {{q, nk * es},     {k, nk * es},  {v, nv * es},
+                         {log_alpha, nk * 4}, {b, nk * es}, {w, nv * es},
+                         {S0, ns * 4},     {chunk_states, csb}, {dO, nv * es},
+                         {dS_T, ns * 4}};
+    const Range outs[] = {{dq, nk * es},  {dk_, nk * es}, {dv_, nv * es}, {dlog_alpha, nk * 4},
+                          {db, nk * es},  {dw, nv * es},  {dS0, ns * 4},
+                          {workspace, have_tokens ? need : 0}};
+    if (any_alias(outs, 8, ins, 10)) return GDR2_E_ALIAS;
+
+    const int bf = dt == GDR2_BF16;
+    const int NC = (int)gdr2_num_chunks(T);
+    char* ws = (char*)workspace;
+    void* dSx = ws;
+    const void* states = chunk_states;
+    if (!states && have_tokens) {
+        void* rec = ws + round_up(csb, 256);
+        gdr2::FwdParams fp;
+        const int dvs = gdr2::fwd_slice_width(bf, (int)dk, (int)dv, B * H);
+        fp.B = (int)B; fp.H = (int)H; fp.NS = (int)(dv / dvs); fp.NC = NC;
+        fp.T = T; fp.DV = dv;
+        fp.q = q; fp.k = k; fp.v = v; fp.b = b; fp.w = w; fp.la = log_alpha; fp.S0 = S0;
+        fp.o = nullptr; fp.ST = nullptr; fp.states = rec;
+        hipError_t e = gdr2::fwd_dispatch(bf, (int)dk, dvs, fp, (hipStream_t)stream);
+        if (e != hipSuccess) return GDR2_E_HIP;
+        states = rec;
+    }
+    gdr2::BwdParams p;
+    p.B = (int)B; p.H = (int)H; p.NC = NC; p.T = T; p.DV = dv;
+    const int dvs = gdr2::bwd_slice_width(bf, (int)dk, (int)dv, B * H);
+    p.NS = (int)(dv / dvs);
+    p.q = q; p.k = k; p.v = v; p.b = b; p.w = w; p.la = log_alpha;
+    p.states = states; p.dO = dO; p.dST = dS_T; p.dSx = dSx; p.dS0 = dS0;
+    p.dq = dq; p.dk = dk_; p.dv = dv_; p.db = db; p.dw = dw; p.dla = dlog_alpha;
+    hipError_t e = gdr2::bwd_dispatch(bf, (int)dk, dvs, p, (hipStream_t)stream);
+    if (e == hipErrorNotSupported) return GDR2_E_UNSUPPORTED;
+    return e == hipSuccess ? GDR2_OK : GDR2_E_HIP;
+}
+
+gdr2_status gdr2_decode_step(int64_t N, int64_t H, int64_t dk, int64_t dv, gdr2_dtype dt,
+                             const void* q, const void* k, const void* v,
+                             const float* log_alpha, const void* b, const void* w,
+                             const float* S_in, float* S_out, void* o, void* stream) {
+    if (dt != GDR2_F32 && dt != GDR2_BF16) return GDR2_E_DTYPE;
+    if (N < 0 || H < 0 || dk < 0 || dv < 0) return GDR2_E_SHAPE;
+    if (!dims_ok(dk) || !dims_ok(dv)) return GDR2_E_UNSUPPORTED;
+    if (N * H > ((int64_t)1 << 31) - 1) return GDR2_E_SHAPE;
+    if (N == 0 || H == 0) return GDR2_OK;
+    if (!q || !k || !v || !log_alpha || !b || !w || !S_out || !o) return GDR2_E_NULL;
+    const void* ptrs[] = {q, k, v, log_alpha, b, w, S_in, S_out, o};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return GDR2_E_ALIGN;
+    const size_t es = gdr2_dtype_size(dt);
+    const size_t nk = (size_t)N * H * dk, nv = (size_t)N * H * dv, ns = (size_t)N * H * dk * dv;
+    const Range ins[] = {{q, nk * es}, {k, nk * es}, {v, nv * es}, {log_alpha, nk * 4},
+                         {b, nk * es}, {w, nv * es}};
+    const Range outs[] = {{S_out, ns * 4}, {o, nv * es}};
+    if (any_alias(outs, 2, ins, 6)) return GDR2_E_ALIAS;
+    // S_in may be S_out exactly; any other overlap with an output is an error
+    if (S_in && S_in != S_out && (overlap({S_in, ns * 4}, outs[0]) || overlap({S_in, ns * 4}, outs[1])))
+        return GDR2_E_ALIAS;
+    if (S_in && S_in == S_out && overlap({S_in, ns * 4}, outs[1])) return GDR2_E_ALIAS;
+    gdr2::DecodeParams p;
+    p.N = N; p.H = H;
+    p.q = q; p.k = k; p.v = v; p.b = b; p.w = w; p.la = log_alpha;
+    p.S_in = S_in; p.S_out = S_out; p.o = o;
+    hipError_t e = gdr2::decode_dispatch(dt == GDR2_BF16, (int)dk, (int)dv, p, (hipStream_t)stream);
+    return e == hipSuccess ? GDR2_OK : GDR2_E_HIP;
+}
+
+}  // extern "C"

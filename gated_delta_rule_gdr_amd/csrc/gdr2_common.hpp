@@ -1,0 +1,157 @@
+// gdr2_common.hpp -- device building blocks shared by the GDR-2 kernels (gfx950 only).
+//
+// Matrix-core tiles: every contraction uses the 16x16 MFMA family with fp32 accumulation,
+//   bf16 operands: v_mfma_f32_16x16x32_bf16 (K step 32, 8 operand values per lane),
+//   fp32 operands: v_mfma_f32_16x16x4_f32  (K step 4, 1 operand value per lane).
+// Lane layout (wave64, l = lane):
+//   A operand  : row  l%16, k = kbase + KPL*(l/16) + j   (j < KPL)
+//   B operand  : col  l%16, k = kbase + KPL*(l/16) + j
+//   accumulator: col  l%16, rows 4*(l/16) + i            (i < 4)
+// Every operand tile in LDS is therefore stored "k-contiguous": A as [m][k], B as [n][k], with a
+// 16-byte row pad so that the 16 rows a fragment load touches fall in different banks.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdr2 {
+
+constexpr int kChunk = 64;  // tokens per chunk
+constexpr int kThreads = 256;
+constexpr int kWaves = 4;
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+
+// ------------------------------------------------------------------ element conversions
+__device__ __forceinline__ float to_f(float x) { return x; }
+__device__ __forceinline__ float to_f(bf16 x) { return (float)x; }
+template <typename T> __device__ __forceinline__ T from_f(float x);
+template <> __device__ __forceinline__ float from_f<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f<bf16>(float x) { return (bf16)x; }  // RNE
+
+// Four consecutive elements from global memory, widened to fp32 (8-byte or 16-byte load).
+__device__ __forceinline__ f32x4 load4(const float* p) { return *(const f32x4*)p; }
+__device__ __forceinline__ f32x4 load4(const bf16* p) {
+    bf16x4 v = *(const bf16x4*)p;
+    return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+__device__ __forceinline__ void store4(float* p, f32x4 v) { *(f32x4*)p = v; }
+__device__ __forceinline__ void store4(bf16* p, f32x4 v) {
+    *(bf16x4*)p = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+}
+
+// ------------------------------------------------------------------ MFMA wrappers
+template <typename OT> struct Mfma;
+
+template <> struct Mfma<bf16> {
+    static constexpr int KS = 32;   // K per instruction
+    static constexpr int KPL = 8;   // K values per lane
+    typedef bf16x8 frag;
+    // fragment of a k-contiguous tile: row (m0 + l%16), k = k0 + 8*(l/16) .. +7
+    static __device__ __forceinline__ frag load(const bf16* t, int pitch, int m0, int k0) {
+        int l = lane_id();
+        return *(const bf16x8*)(t + (m0 + (l & 15)) * pitch + k0 + 8 * (l >> 4));
+    }
+    // same, each value multiplied by s[k] (fp32) before rounding back to bf16
+    static __device__ __forceinline__ frag load_scaled(const bf16* t, int pitch, int m0, int k0,
+                                                        const float* s) {
+        int l = lane_id();
+        int kk = k0 + 8 * (l >> 4);
+        bf16x8 v = *(const bf16x8*)(t + (m0 + (l & 15)) * pitch + kk);
+        f32x4 s0 = *(const f32x4*)(s + kk), s1 = *(const f32x4*)(s + kk + 4);
+        bf16x8 r;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            r[j] = (bf16)((float)v[j] * s0[j]);
+            r[j + 4] = (bf16)((float)v[j + 4] * s1[j]);
+        }
+        return r;
+    }
+    static __device__ __forceinline__ void mma(f32x4& c, const frag& a, const frag& b) {
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+};
+
+template <> struct Mfma<float> {
+    static constexpr int KS = 4;
+    static constexpr int KPL = 1;
+    typedef float frag;
+    static __device__ __forceinline__ frag load(const float* t, int pitch, int m0, int k0) {
+        int l = lane_id();
+        return t[(m0 + (l & 15)) * pitch + k0 + (l >> 4)];
+    }
+    static __device__ __forceinline__ frag load_scaled(const float* t, int pitch, int m0, int k0,
+                                                        const float* s) {
+        int l = lane_id();
+        int kk = k0 + (l >> 4);
+        return t[(m0 + (l & 15)) * pitch + kk] * s[kk];
+    }
+    static __device__ __forceinline__ void mma(f32x4& c, const frag& a, const frag& b) {
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    }
+};
+
+// fp32 16x16x4 fragment loads from a row-major fp32 tile, used by the triangular solve:
+//   A operand from X[m][k] (pitch p), B operand from Y[k][n] (pitch p).
+__device__ __forceinline__ float fa32(const float* X, int p, int m0, int k0) {
+    int l = lane_id();
+    return X[(m0 + (l & 15)) * p + k0 + (l >> 4)];
+}
+__device__ __forceinline__ float fb32(const float* Y, int p, int k0, int n0) {
+    int l = lane_id();
+    return Y[(k0 + (l >> 4)) * p + n0 + (l & 15)];
+}
+__device__ __forceinline__ void mma32(f32x4& c, float a, float b) {
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Accumulator element (i) of the calling lane: row and column inside its 16x16 block.
+__device__ __forceinline__ int acc_row(int i) { return 4 * (lane_id() >> 4) + i; }
+__device__ __forceinline__ int acc_col() { return lane_id() & 15; }
+
+// Write a 16x16 accumulator block transposed into a k-contiguous tile: dst[n][m] (n = column of
+// the block, m = row); the four rows of a lane are contiguous in dst, one 8/16-byte store.
+template <typename OT>
+__device__ __forceinline__ void store_acc_T(OT* dst, int pitch, int n0, int m0, const f32x4& c) {
+    int l = lane_id();
+    OT* p = dst + (n0 + (l & 15)) * pitch + m0 + 4 * (l >> 4);
+    if constexpr (sizeof(OT) == 2) {
+        *(bf16x4*)p = bf16x4{(bf16)c[0], (bf16)c[1], (bf16)c[2], (bf16)c[3]};
+    } else {
+        *(f32x4*)p = c;
+    }
+}
+
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Map a linear workgroup index so that the `group` consecutive work items that share key-side
+// data land on the same XCD (workgroups are dispatched round-robin over the 8 XCDs; each XCD
+// has its own L2).  Identity when the grid does not split evenly.
+__device__ __forceinline__ int xcd_swizzle(int bid, int nblocks) {
+    if (nblocks % 8 != 0) return bid;
+    int per = nblocks / 8;
+    return (bid % 8) * per + bid / 8;
+}
+
+}  // namespace gdr2
+
+namespace gdr2 {
+// Workgroup barrier that waits only for this wave's LDS traffic (lgkmcnt(0)) and leaves global
+// loads in flight, so that next-chunk prefetches survive it.  The empty asm with a memory clobber
+// keeps the compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // vmcnt = max, expcnt = max, lgkmcnt = 0
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+}  // namespace gdr2

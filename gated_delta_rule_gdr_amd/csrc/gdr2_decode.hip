@@ -1,0 +1,117 @@
+// gdr2_decode.hip -- one recurrent Gated Delta Rule-2 token for many independent sequences.
+//
+// Decoding runs the recurrence one token at a time in constant memory (forum summary "Gated
+// DeltaNet-2: Decoupling Erase and Write Gates in Linear Attention for Better Memory Editing",
+// section "The Memory Dilemma"; abstract on thelatestinai.com).  Per (sequence, head), with the
+// decay applied before the edit (ainews.random.gg article, section "Gated Delta Rule-2: two gates
+// instead of one"):
+//     Sbar = Diag(alpha) S;  r = Sbar^T (b . k);  S <- Sbar + k (w . v - r)^T;  o = S^T q.
+// Value column j of the new state depends only on column j of the old one, through two length-d_k
+// reductions r_j = sum_i alpha_i e_i S_ij and p_j = sum_i alpha_i q_i S_ij; then
+//     S_ij <- alpha_i S_ij + k_i (z_j - r_j),   o_j = p_j + (q . k)(z_j - r_j).
+// The kernel is a pure stream over the fp32 state: every element is read once and written once
+// (in place when S_in == S_out), from registers, with 16-byte coalesced accesses.
+#include "gdr2_common.hpp"
+#include "gdr2_kernels.hpp"
+
+namespace gdr2 {
+
+template <typename IT, int DK, int DV>
+__global__ __launch_bounds__(kThreads) void gdr2_decode_kernel(DecodeParams p) {
+    constexpr int CGR = DV / 4;           // 4-column groups
+    constexpr int RGR = kThreads / CGR;   // row groups
+    constexpr int RPT = DK / RGR;         // rows per thread
+    static_assert(RPT * RGR == DK, "mapping");
+    __shared__ float red_r[RGR][DV];
+    __shared__ float red_p[RGR][DV];
+    __shared__ float red_qk[RGR];
+
+    const long nh = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int jg = tid % CGR, ig = tid / CGR;
+    const int j0 = 4 * jg, ibase = ig * RPT;
+    const IT* q = (const IT*)p.q + nh * DK;
+    const IT* k = (const IT*)p.k + nh * DK;
+    const IT* b = (const IT*)p.b + nh * DK;
+    const float* la = p.la + nh * DK;
+    const IT* v = (const IT*)p.v + nh * DV;
+    const IT* w = (const IT*)p.w + nh * DV;
+    const float* Sin = p.S_in ? p.S_in + nh * DK * DV : nullptr;
+    float* Sout = p.S_out + nh * DK * DV;
+
+    f32x4 s[RPT];
+    if (Sin) {
+#pragma unroll
+        for (int u = 0; u < RPT; ++u) s[u] = *(const f32x4*)(Sin + (ibase + u) * DV + j0);
+    }
+    float kk[RPT];
+    f32x4 pr = {0.f, 0.f, 0.f, 0.f}, pp = {0.f, 0.f, 0.f, 0.f};
+    float pqk = 0.f;
+#pragma unroll
+    for (int u = 0; u < RPT; ++u) {
+        const int i = ibase + u;
+        const float a = __expf(la[i]);
+        const float ki = to_f(k[i]), qi = to_f(q[i]);
+        const float e = to_f(b[i]) * ki;
+        kk[u] = ki;
+        pqk += qi * ki;
+        if (!Sin) s[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            s[u][j] *= a;  // decay first
+            pr[j] += e * s[u][j];
+            pp[j] += qi * s[u][j];
+        }
+    }
+    *(f32x4*)&red_r[ig][j0] = pr;
+    *(f32x4*)&red_p[ig][j0] = pp;
+    if (jg == 0) red_qk[ig] = pqk;
+    __syncthreads();
+    f32x4 r = {0.f, 0.f, 0.f, 0.f}, pq = {0.f, 0.f, 0.f, 0.f};
+    float qk = 0.f;
+#pragma unroll
+    for (int g = 0; g < RGR; ++g) {
+        r += *(const f32x4*)&red_r[g][j0];
+        pq += *(const f32x4*)&red_p[g][j0];
+        qk += red_qk[g];
+    }
+    f32x4 u4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) u4[j] = to_f(w[j0 + j]) * to_f(v[j0 + j]) - r[j];
+#pragma unroll
+    for (int u = 0; u < RPT; ++u) {
+        f32x4 x;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[j] = s[u][j] + kk[u] * u4[j];
+        *(f32x4*)(Sout + (ibase + u) * DV + j0) = x;
+    }
+    if (ig == 0) {
+        f32x4 ov;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ov[j] = pq[j] + qk * u4[j];
+        store4((IT*)p.o + nh * DV + j0, ov);
+    }
+}
+
+template <typename IT, int DK, int DV>
+static hipError_t launch_decode(const DecodeParams& p, hipStream_t s) {
+    hipLaunchKernelGGL((gdr2_decode_kernel<IT, DK, DV>), dim3(p.N * p.H), dim3(kThreads), 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t decode_dispatch(int bf, int dk, int dv, const DecodeParams& p, hipStream_t s) {
+    if (bf) {
+        if (dk == 128 && dv == 128) return launch_decode<bf16, 128, 128>(p, s);
+        if (dk == 128 && dv == 64) return launch_decode<bf16, 128, 64>(p, s);
+        if (dk == 64 && dv == 128) return launch_decode<bf16, 64, 128>(p, s);
+        if (dk == 64 && dv == 64) return launch_decode<bf16, 64, 64>(p, s);
+    } else {
+        if (dk == 128 && dv == 128) return launch_decode<float, 128, 128>(p, s);
+        if (dk == 128 && dv == 64) return launch_decode<float, 128, 64>(p, s);
+        if (dk == 64 && dv == 128) return launch_decode<float, 64, 128>(p, s);
+        if (dk == 64 && dv == 64) return launch_decode<float, 64, 64>(p, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace gdr2

@@ -1,0 +1,149 @@
+/*
+ * gdr2.h -- C ABI of the MI355X (gfx950) Gated Delta Rule-2 library (libgdr2.so).
+ *
+ * The operation (per batch b, head h, with state S in R^{d_k x d_v}) is the Gated Delta Rule-2
+ * update printed in the forum summary "Gated DeltaNet-2: Decoupling Erase and Write Gates in
+ * Linear Attention for Better Memory Editing" (zhichai.net, English), section "Gated Delta Rule-2":
+ *
+ *     S_t = (I - k_t (b_t . k_t)^T) Diag(alpha_t) S_{t-1} + k_t (w_t . v_t)^T
+ *
+ * with the channel-wise decay applied before the edit, the erase gate b_t in [0,1]^{d_k} on the
+ * key side and the write gate w_t in [0,1]^{d_v} on the value side (ainews.random.gg article on
+ * Gated DeltaNet-2, section "Gated Delta Rule-2: two gates instead of one"), and the read-out
+ * o_t = S_t^T q_t on the updated state (no query scale; callers pre-scale q if they want one).
+ * The decay is passed as log(alpha_t), natural log, one value per key channel.
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are dense, row-major, and live in DEVICE memory owned by the caller.  The library
+ *     allocates nothing, keeps no state between calls and never frees caller memory.
+ *   - Token tensors: q, k, log_alpha, b : [B][T][H][d_k];  v, w, o, dO : [B][T][H][d_v].
+ *     States: [B][H][d_k][d_v], fp32.
+ *   - dtype selects the element type of q, k, v, b, w, o and of dq, dk, dv, db, dw:
+ *     GDR2_BF16 (bfloat16) or GDR2_F32.  log_alpha, dlog_alpha and every state are fp32.
+ *   - Every pointer must be 16-byte aligned.  Outputs must not overlap inputs or each other
+ *     (decode's S_in == S_out is the one allowed, exact, alias).
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null stream).  All
+ *     validation happens on the host before any launch: on any error nothing is launched and
+ *     no output is written.  Launch failures return GDR2_E_HIP; faults during execution
+ *     surface at the caller's next synchronisation.  No C++ exception crosses this ABI.
+ *   - Results are bitwise deterministic run to run (no floating-point atomics).
+ *   - Supported sizes: d_k, d_v in {64, 128}; the chunked passes in GDR2_F32 need d_k = 64.
+ *     B, H >= 1 and T >= 0 (T = 0 produces no tokens; S_T then equals S0).
+ */
+#ifndef GDR2_H
+#define GDR2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDR2_ABI_VERSION 1
+#define GDR2_CHUNK 64 /* tokens per chunk of the chunked passes */
+
+typedef enum gdr2_status {
+    GDR2_OK = 0,
+    GDR2_E_NULL = 1,        /* a required pointer is NULL */
+    GDR2_E_SHAPE = 2,       /* a size is negative, or too large for 32-bit launch indexing */
+    GDR2_E_DTYPE = 3,       /* dtype is not GDR2_F32 / GDR2_BF16 */
+    GDR2_E_UNSUPPORTED = 4, /* head sizes / dtype combination not built */
+    GDR2_E_ALIGN = 5,       /* a pointer is not 16-byte aligned */
+    GDR2_E_ALIAS = 6,       /* an output overlaps an input or another output */
+    GDR2_E_WORKSPACE = 7,   /* workspace missing or smaller than gdr2_bwd_workspace_bytes() */
+    GDR2_E_HIP = 8          /* the HIP runtime refused the launch */
+} gdr2_status;
+
+typedef enum gdr2_dtype { GDR2_F32 = 0, GDR2_BF16 = 1 } gdr2_dtype;
+
+/* Bytes of one element of `dtype` (4 or 2), 0 for an unknown dtype. */
+size_t gdr2_dtype_size(gdr2_dtype dtype);
+
+/* Number of chunks, ceil(T / GDR2_CHUNK). */
+int64_t gdr2_num_chunks(int64_t T);
+
+/*
+ * Chunked forward: o_t = S_t^T q_t for all tokens, optionally the final state and the
+ * chunk-entry states that the backward consumes.  Implements the chunkwise WY form in which the
+ * cumulative channel-wise decay of a chunk is absorbed into the two factors of each rank-one
+ * erase (ainews.random.gg article, section "Chunkwise training and gate-aware backward").
+ *
+ *   q, k, b         [B][T][H][dk]  dtype          (inputs)
+ *   v, w            [B][T][H][dv]  dtype          (inputs)
+ *   log_alpha       [B][T][H][dk]  fp32           (input, natural log of the decay)
+ *   S0              [B][H][dk][dv] fp32 or NULL   (input, initial state; NULL = zero)
+ *   o               [B][T][H][dv]  dtype          (output)
+ *   S_T             [B][H][dk][dv] fp32 or NULL   (output, final state; NULL = not wanted)
+ *   chunk_states    NULL, or an opaque checkpoint of gdr2_chunk_states_bytes() bytes that
+ *                   receives the state entering every chunk, in dtype, laid out
+ *                   [B][H][num_chunks][dv][dk] (each state transposed).  Pass it to
+ *                   gdr2_bwd_chunked to skip the state recompute there.
+ */
+gdr2_status gdr2_fwd_chunked(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                             gdr2_dtype dtype, const void* q, const void* k, const void* v,
+                             const float* log_alpha, const void* b, const void* w,
+                             const float* S0, void* o, float* S_T, void* chunk_states,
+                             void* stream);
+
+/* Size in bytes of the chunk_states checkpoint for these sizes (B*H*num_chunks*dv*dk elements). */
+size_t gdr2_chunk_states_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                               gdr2_dtype dtype);
+
+/* Bytes of device workspace gdr2_bwd_chunked needs: the per-chunk state gradients, plus the
+ * chunk-entry states when the caller does not pass them (have_chunk_states == 0). */
+size_t gdr2_bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                                gdr2_dtype dtype, int have_chunk_states);
+
+/*
+ * Gate-aware backward (vector-Jacobian product) of gdr2_fwd_chunked for the loss
+ * L = <dO, o> + <dS_T, S_T>.  The erase gate b and the write gate w enter the gradient dot
+ * products themselves rather than as one scalar factor (ainews.random.gg article, section
+ * "Chunkwise training and gate-aware backward").
+ *
+ *   q, k, v, log_alpha, b, w, S0   as in gdr2_fwd_chunked (same values)
+ *   chunk_states    the checkpoint written by gdr2_fwd_chunked for these inputs, or NULL
+ *                   (then the states are recomputed into the workspace)
+ *   dO              [B][T][H][dv]  dtype           (input)
+ *   dS_T            [B][H][dk][dv] fp32 or NULL    (input; NULL = zero)
+ *   dq, dk_, db     [B][T][H][dk]  dtype           (outputs)
+ *   dv_, dw         [B][T][H][dv]  dtype           (outputs)
+ *   dlog_alpha      [B][T][H][dk]  fp32            (output)
+ *   dS0             [B][H][dk][dv] fp32 or NULL    (output; NULL = not wanted)
+ *   workspace       device memory of at least gdr2_bwd_workspace_bytes(..., chunk_states != NULL)
+ */
+gdr2_status gdr2_bwd_chunked(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                             gdr2_dtype dtype, const void* q, const void* k, const void* v,
+                             const float* log_alpha, const void* b, const void* w,
+                             const float* S0, const void* chunk_states, const void* dO,
+                             const float* dS_T, void* dq, void* dk_, void* dv_,
+                             float* dlog_alpha, void* db, void* dw, float* dS0,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One recurrent token for N independent sequences x H heads (constant-memory decoding; forum
+ * summary, section "The Memory Dilemma").  The state stays in HBM and is updated in place when
+ * S_in == S_out.
+ *
+ *   q, k, b         [N][H][dk]  dtype
+ *   v, w            [N][H][dv]  dtype
+ *   log_alpha       [N][H][dk]  fp32
+ *   S_in            [N][H][dk][dv] fp32 or NULL (= zero state); may equal S_out
+ *   S_out           [N][H][dk][dv] fp32 (required)
+ *   o               [N][H][dv]  dtype (output)
+ */
+gdr2_status gdr2_decode_step(int64_t N, int64_t H, int64_t dk, int64_t dv, gdr2_dtype dtype,
+                             const void* q, const void* k, const void* v,
+                             const float* log_alpha, const void* b, const void* w,
+                             const float* S_in, float* S_out, void* o, void* stream);
+
+/* Static description of a status code. */
+const char* gdr2_status_string(gdr2_status s);
+
+/* GDR2_ABI_VERSION of the loaded library. */
+int gdr2_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GDR2_H */

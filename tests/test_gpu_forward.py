@@ -1,0 +1,140 @@
+"""GPU parity of the chunked forward and of decode against the fp64 oracle (through the C ABI)."""
+import numpy as np
+import pytest
+import torch
+
+from gated_delta_rule_gdr_amd import gdr2_decode_step, gdr2_fwd_chunked
+from gated_delta_rule_gdr_amd.inputs import (config_inputs, decode_inputs, layer_inputs,
+                                             strong_decay_inputs, to_f64)
+from oracle import oracle as orc
+from tests._util import TOL, announce, assert_close, to_np
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _gpu(x):
+    return {n: (None if t is None else t.to(DEV)) for n, t in x.items()}
+
+
+def _run_fwd(x, chunk_states=False):
+    g = _gpu(x)
+    o, ST, cs = gdr2_fwd_chunked(g["q"], g["k"], g["v"], g["log_alpha"], g["b"], g["w"],
+                                 S0=g["S0"], want_chunk_states=chunk_states)
+    torch.cuda.synchronize()
+    return o, ST, cs
+
+
+def _check_fwd(x, tol, tag):
+    announce(tag)
+    o, ST, _ = _run_fwd(x)
+    f = to_f64(x)
+    ro, rS = orc.forward(f["q"], f["k"], f["v"], f["log_alpha"], f["b"], f["w"], f["S0"])
+    eo = assert_close(f"{tag} o", to_np(o), ro, tol)
+    eS = assert_close(f"{tag} S_T", to_np(ST), rS, tol)
+    print(f"  {tag}: o {eo:.2e}  S_T {eS:.2e}")
+
+
+def test_fwd_pr1_fp32():
+    """The fp32 reference workload: B=1, H=1, T=256, d=64."""
+    _check_fwd(config_inputs("pr1_fp32"), TOL["f32"], "pr1_fp32")
+
+
+@pytest.mark.parametrize("T", [1, 37, 64, 65, 200])
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 128), (128, 64), (64, 64)])
+def test_fwd_bf16_shapes(T, dk, dv):
+    x = layer_inputs(2, T, 3, dk, dv, dtype="bf16", seed=10 + T + dk + dv, s0_std=0.05, grads=False)
+    _check_fwd(x, TOL["bf16"], f"bf16 T={T} dk={dk} dv={dv}")
+
+
+@pytest.mark.parametrize("T,dv", [(1, 64), (130, 64), (130, 128), (256, 128)])
+def test_fwd_fp32_shapes(T, dv):
+    x = layer_inputs(2, T, 2, 64, dv, dtype="f32", seed=20 + T + dv, s0_std=0.05, grads=False)
+    _check_fwd(x, TOL["f32"], f"f32 T={T} dk=64 dv={dv}")
+
+
+def test_fwd_many_chains_slice_paths():
+    """Enough (b, h) chains that the wider value slices (fewer workgroups per chain) are used."""
+    x = layer_inputs(4, 130, 64, 128, 128, dtype="bf16", seed=5, grads=False)
+    _check_fwd(x, TOL["bf16"], "bf16 B=4 H=64 (wide slices)")
+    x = layer_inputs(4, 130, 64, 64, 128, dtype="bf16", seed=6, grads=False)
+    _check_fwd(x, TOL["bf16"], "bf16 B=4 H=64 dk=64")
+
+
+def test_fwd_strong_decay():
+    """Channels decaying by up to e^-6 per token: far outside the naive e^{+-G} factor range of a
+    whole chunk (|G| up to 384), inside the per-16-token-block range the kernel guarantees."""
+    x = strong_decay_inputs(1, 256, 2, 128, 128, dtype="bf16", seed=3, floor=-5.0)
+    _check_fwd(x, TOL["bf16"], "bf16 strong decay")
+    x = strong_decay_inputs(1, 256, 2, 64, 64, dtype="f32", seed=4, floor=-5.0)
+    _check_fwd(x, TOL["f32"], "f32 strong decay")
+
+
+def test_fwd_chunk_states_checkpoint():
+    """The chunk-entry checkpoint equals the oracle state after 64*c tokens (rounded to dtype)."""
+    x = layer_inputs(1, 150, 2, 128, 64, dtype="bf16", seed=9, s0_std=0.05, grads=False)
+    announce("chunk states")
+    o, ST, cs = _run_fwd(x, chunk_states=True)
+    NC = 3
+    st = cs.view(torch.bfloat16).view(1, 2, NC, 64, 128).float().cpu().numpy()  # [B,H,NC,dv,dk]
+    f = to_f64(x)
+    for c in range(NC):
+        if c == 0:
+            ref = f["S0"]
+        else:
+            sub = {n: (a[:, :64 * c] if a is not None and n != "S0" else a) for n, a in f.items()}
+            _, ref = orc.forward(sub["q"], sub["k"], sub["v"], sub["log_alpha"], sub["b"],
+                                 sub["w"], sub["S0"])
+        got = np.swapaxes(st[:, :, c], -1, -2)
+        assert_close(f"state entering chunk {c}", got, ref, TOL["bf16"])
+
+
+def test_fwd_layer_1p3b_sampled_chains():
+    """Full model-shaped layer (B=4, T=4096, H=16, d=128) in the launch configuration the bench
+    times; the oracle recomputes two whole (b, h) chains."""
+    x = config_inputs("layer_1p3b")
+    announce("layer_1p3b forward, full size")
+    o, ST, _ = _run_fwd(x)
+    f = to_f64(x)
+    for (b, h) in [(0, 0), (3, 15)]:
+        sub = {n: (None if a is None else a[b:b + 1, :, h:h + 1]) for n, a in f.items()
+               if n in ("q", "k", "v", "log_alpha", "b", "w")}
+        ro, rS = orc.forward(sub["q"], sub["k"], sub["v"], sub["log_alpha"], sub["b"], sub["w"])
+        assert_close(f"o chain ({b},{h})", to_np(o[b:b + 1, :, h:h + 1]), ro, TOL["bf16"])
+        assert_close(f"S_T chain ({b},{h})", to_np(ST[b:b + 1, h:h + 1]), rS, TOL["bf16"])
+
+
+@pytest.mark.parametrize("dt,dk,dv", [("bf16", 128, 128), ("f32", 64, 128), ("bf16", 64, 64),
+                                      ("f32", 128, 64)])
+def test_decode_steps_vs_oracle(dt, dk, dv):
+    N, H, steps = 5, 3, 6
+    announce(f"decode {dt} dk={dk} dv={dv}")
+    S = None
+    Sref = None
+    for s in range(steps):
+        x = decode_inputs(s, N=N, H=H, dk=dk, dv=dv, dtype=dt)
+        g = _gpu(x)
+        o, S = gdr2_decode_step(g["q"], g["k"], g["v"], g["log_alpha"], g["b"], g["w"], S_in=S)
+        torch.cuda.synchronize()
+        f = to_f64(x)
+        ro, Sref = orc.decode_step(f["q"], f["k"], f["v"], f["log_alpha"], f["b"], f["w"], Sref)
+        assert_close(f"decode o step {s}", to_np(o), ro, TOL[dt])
+        assert_close(f"decode S step {s}", to_np(S), Sref, TOL[dt])
+
+
+def test_decode_equals_chunked_forward():
+    """T decode steps from S0 reproduce the chunked forward's outputs and final state."""
+    x = layer_inputs(3, 70, 2, 128, 128, dtype="bf16", seed=77, s0_std=0.05, grads=False)
+    announce("decode == chunked")
+    o, ST, _ = _run_fwd(x)
+    g = _gpu(x)
+    S = g["S0"].clone()
+    outs = []
+    for t in range(70):
+        ot, S = gdr2_decode_step(*(g[n][:, t].contiguous() for n in ("q", "k", "v", "log_alpha", "b", "w")),
+                                 S_in=S, S_out=S)
+        outs.append(ot)
+    torch.cuda.synchronize()
+    od = torch.stack(outs, dim=1)
+    assert_close("decode vs chunked o", to_np(od), to_np(o), TOL["bf16"])
+    assert_close("decode vs chunked S_T", to_np(S), to_np(ST), TOL["bf16"])
