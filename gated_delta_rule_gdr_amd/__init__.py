@@ -6,8 +6,8 @@ device memory and the current HIP stream.  There is no fallback: if the library 
 fails to load, every call raises.
 
 Entry points (same names as the C ABI):
-  gdr2_fwd_chunked(q, k, v, log_alpha, b, w, S0=None, want_final_state=True, want_chunk_states=False)
-  gdr2_bwd_chunked(q, k, v, log_alpha, b, w, dO, S0=None, dS_T=None, chunk_states=None, want_dS0=True)
+  gdr2_fwd_chunked(q, k, v, log_alpha, b, w, S0=None, want_final_state=True) -> (o, S_T, fwd_ws)
+  gdr2_bwd_chunked(q, k, v, log_alpha, b, w, dO, fwd_ws, dS_T=None, want_dS0=True) -> grads
   gdr2_decode_step(q, k, v, log_alpha, b, w, S_in=None, S_out=None)
 """
 from __future__ import annotations
@@ -51,16 +51,17 @@ def load_library():
                            "(run python gated_delta_rule_gdr_amd/build.py)")
     lib = ctypes.CDLL(_LIB_PATH)
     I64, P, SZ = ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
-    lib.gdr2_fwd_chunked.argtypes = [I64] * 5 + [ctypes.c_int] + [P] * 11
+    lib.gdr2_fwd_chunked.argtypes = [I64] * 5 + [ctypes.c_int] + [P] * 10 + [SZ, P]
     lib.gdr2_fwd_chunked.restype = ctypes.c_int
-    lib.gdr2_bwd_chunked.argtypes = [I64] * 5 + [ctypes.c_int] + [P] * 18 + [SZ, P]
+    lib.gdr2_bwd_chunked.argtypes = ([I64] * 5 + [ctypes.c_int] + [P] * 7 + [SZ] + [P] * 10
+                                     + [SZ, P])
     lib.gdr2_bwd_chunked.restype = ctypes.c_int
     lib.gdr2_decode_step.argtypes = [I64] * 4 + [ctypes.c_int] + [P] * 10
     lib.gdr2_decode_step.restype = ctypes.c_int
-    lib.gdr2_bwd_workspace_bytes.argtypes = [I64] * 5 + [ctypes.c_int, ctypes.c_int]
+    lib.gdr2_fwd_workspace_bytes.argtypes = [I64] * 5 + [ctypes.c_int]
+    lib.gdr2_fwd_workspace_bytes.restype = SZ
+    lib.gdr2_bwd_workspace_bytes.argtypes = [I64] * 5 + [ctypes.c_int]
     lib.gdr2_bwd_workspace_bytes.restype = SZ
-    lib.gdr2_chunk_states_bytes.argtypes = [I64] * 5 + [ctypes.c_int]
-    lib.gdr2_chunk_states_bytes.restype = SZ
     lib.gdr2_num_chunks.argtypes = [I64]
     lib.gdr2_num_chunks.restype = I64
     lib.gdr2_status_string.argtypes = [ctypes.c_int]
@@ -103,31 +104,32 @@ def _contig(*ts):
             raise ValueError("all tensors must be contiguous")
 
 
-def gdr2_fwd_chunked(q, k, v, log_alpha, b, w, S0=None, want_final_state=True,
-                     want_chunk_states=False):
-    """Chunked forward.  Returns (o, S_T or None, chunk_states or None)."""
+def gdr2_fwd_chunked(q, k, v, log_alpha, b, w, S0=None, want_final_state=True, workspace=None):
+    """Chunked forward.  Returns (o, S_T or None, fwd_ws); fwd_ws holds the per-chunk factors and
+    chunk-entry states that gdr2_bwd_chunked needs.  ``workspace`` may pass a preallocated uint8
+    device tensor of at least the required size."""
     lib = load_library()
     _contig(q, k, v, log_alpha, b, w, S0)
     B, T, H, dk, dv = _shapes(q, v)
     dt = _dtype(q)
     o = torch.empty((B, T, H, dv), dtype=q.dtype, device=q.device)
     ST = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device) if want_final_state else None
-    cs = None
-    if want_chunk_states:
-        nbytes = lib.gdr2_chunk_states_bytes(B, T, H, dk, dv, dt)
-        cs = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    need = lib.gdr2_fwd_workspace_bytes(B, T, H, dk, dv, dt)
+    ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8,
+                                                             device=q.device)
     st = lib.gdr2_fwd_chunked(B, T, H, dk, dv, dt, _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
-                              _ptr(b), _ptr(w), _ptr(S0), _ptr(o), _ptr(ST), _ptr(cs), _stream())
+                              _ptr(b), _ptr(w), _ptr(S0), _ptr(o), _ptr(ST), _ptr(ws),
+                              ws.numel(), _stream())
     _check("gdr2_fwd_chunked", st)
-    return o, ST, cs
+    return o, ST, ws
 
 
-def gdr2_bwd_chunked(q, k, v, log_alpha, b, w, dO, S0=None, dS_T=None, chunk_states=None,
-                     want_dS0=True):
-    """Gate-aware backward.  Returns a dict dq, dk, dv, dlog_alpha, db, dw, dS0 (None if not
-    wanted)."""
+def gdr2_bwd_chunked(q, k, v, log_alpha, b, w, dO, fwd_ws, dS_T=None, want_dS0=True,
+                     workspace=None):
+    """Gate-aware backward.  ``fwd_ws`` is the third result of gdr2_fwd_chunked on the same inputs.
+    Returns a dict dq, dk, dv, dlog_alpha, db, dw, dS0 (None if not wanted)."""
     lib = load_library()
-    _contig(q, k, v, log_alpha, b, w, dO, S0, dS_T)
+    _contig(q, k, v, log_alpha, b, w, dO, dS_T)
     B, T, H, dk, dv = _shapes(q, v)
     dt = _dtype(q)
     dev = q.device
@@ -135,13 +137,14 @@ def gdr2_bwd_chunked(q, k, v, log_alpha, b, w, dO, S0=None, dS_T=None, chunk_sta
              dlog_alpha=torch.empty_like(log_alpha), db=torch.empty_like(b),
              dw=torch.empty_like(w),
              dS0=torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev) if want_dS0 else None)
-    wsb = lib.gdr2_bwd_workspace_bytes(B, T, H, dk, dv, dt, 1 if chunk_states is not None else 0)
-    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    need = lib.gdr2_bwd_workspace_bytes(B, T, H, dk, dv, dt)
+    ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8,
+                                                             device=dev)
     st = lib.gdr2_bwd_chunked(B, T, H, dk, dv, dt, _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
-                              _ptr(b), _ptr(w), _ptr(S0), _ptr(chunk_states), _ptr(dO),
+                              _ptr(b), _ptr(w), _ptr(fwd_ws), fwd_ws.numel(), _ptr(dO),
                               _ptr(dS_T), _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]),
                               _ptr(g["dlog_alpha"]), _ptr(g["db"]), _ptr(g["dw"]),
-                              _ptr(g["dS0"]), _ptr(ws), wsb, _stream())
+                              _ptr(g["dS0"]), _ptr(ws), ws.numel(), _stream())
     _check("gdr2_bwd_chunked", st)
     return g
 

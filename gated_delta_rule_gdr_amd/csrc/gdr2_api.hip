@@ -63,16 +63,52 @@ const char* gdr2_status_string(gdr2_status s) {
 
 int gdr2_abi_version(void) { return GDR2_ABI_VERSION; }
 
-size_t gdr2_chunk_states_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
-                               gdr2_dtype dt) {
-    if (B < 0 || T < 0 || H < 0 || dk < 0 || dv < 0) return 0;
-    return (size_t)B * H * gdr2_num_chunks(T) * dk * dv * gdr2_dtype_size(dt);
+// Layout of the forward workspace: per-chunk WY factors, then the chunk-entry states.
+struct FwdWs {
+    size_t yh, qg, kt, p, tm, u, gam, states, total;
+};
+static FwdWs fwd_ws_layout(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, gdr2_dtype dt) {
+    const size_t es = gdr2_dtype_size(dt);
+    const size_t ncc = (size_t)B * H * gdr2_num_chunks(T);
+    const size_t C = GDR2_CHUNK;
+    FwdWs w;
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off += round_up(bytes, 256); return o; };
+    w.yh = take(ncc * C * dk * es);
+    w.qg = take(ncc * C * dk * es);
+    w.kt = take(ncc * C * dk * es);
+    w.p = take(ncc * C * C * es);
+    w.tm = take(ncc * C * C * es);
+    w.u = take(ncc * C * dv * es);
+    w.gam = take(ncc * dk * 4);
+    w.states = take(ncc * dv * dk * es);
+    w.total = off;
+    return w;
+}
+
+static gdr2::WyBufs wy_bufs(const FwdWs& L, void* base) {
+    char* b = (char*)base;
+    gdr2::WyBufs w;
+    w.Yh = b + L.yh;
+    w.Qg = b + L.qg;
+    w.Kt = b + L.kt;
+    w.P = b + L.p;
+    w.Tm = b + L.tm;
+    w.U = b + L.u;
+    w.gam = (float*)(b + L.gam);
+    return w;
+}
+
+size_t gdr2_fwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                                gdr2_dtype dt) {
+    if (B < 0 || T < 0 || H < 0 || dk < 0 || dv < 0 || gdr2_dtype_size(dt) == 0) return 0;
+    return fwd_ws_layout(B, T, H, dk, dv, dt).total;
 }
 
 size_t gdr2_bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
-                                gdr2_dtype dt, int have_chunk_states) {
-    const size_t one = round_up(gdr2_chunk_states_bytes(B, T, H, dk, dv, dt), 256);
-    return have_chunk_states ? one : 2 * one;
+                                gdr2_dtype dt) {
+    if (B < 0 || T < 0 || H < 0 || dk < 0 || dv < 0 || gdr2_dtype_size(dt) == 0) return 0;
+    return round_up((size_t)B * H * gdr2_num_chunks(T) * dk * dv * gdr2_dtype_size(dt), 256);
 }
 
 // Shared shape / dtype checks of the two chunked passes.
@@ -81,37 +117,16 @@ static gdr2_status check_chunked(int64_t B, int64_t T, int64_t H, int64_t dk, in
     if (dt != GDR2_F32 && dt != GDR2_BF16) return GDR2_E_DTYPE;
     if (B < 0 || T < 0 || H < 0 || dk < 0 || dv < 0) return GDR2_E_SHAPE;
     if (!dims_ok(dk) || !dims_ok(dv)) return GDR2_E_UNSUPPORTED;
-    if (dt == GDR2_F32 && dk != 64) return GDR2_E_UNSUPPORTED;
     if (B * H * (dv / 16) > (int64_t)1 << 30) return GDR2_E_SHAPE;
     if (B * H * gdr2_num_chunks(T) > (int64_t)1 << 30) return GDR2_E_SHAPE;
     if (T > ((int64_t)1 << 40) || B * T * H > ((int64_t)1 << 50)) return GDR2_E_SHAPE;
     return GDR2_OK;
 }
 
-gdr2_status gdr2_fwd_chunked(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
-                             gdr2_dtype dt, const void* q, const void* k, const void* v,
-                             const float* log_alpha, const void* b, const void* w,
-                             const float* S0, void* o, float* S_T, void* chunk_states,
-                             void* stream) {
-    gdr2_status st = check_chunked(B, T, H, dk, dv, dt);
-    if (st != GDR2_OK) return st;
-    if (B == 0 || H == 0) return GDR2_OK;
-    const bool have_tokens = T > 0;
-    if (have_tokens && (!q || !k || !v || !log_alpha || !b || !w || !o)) return GDR2_E_NULL;
-    const void* ptrs[] = {q, k, v, log_alpha, b, w, S0, o, S_T, chunk_states};
-    for (const void* p : ptrs)
-        if (p && !aligned16(p)) return GDR2_E_ALIGN;
-    const size_t es = gdr2_dtype_size(dt);
-    const size_t nk = (size_t)B * T * H * dk, nv = (size_t)B * T * H * dv;
-    const size_t ns = (size_t)B * H * dk * dv;
-    const Range ins[] = {{q, nk * es}, {k, nk * es}, {v, nv * es}, {log_alpha, nk * 4},
-                         {b, nk * es}, {w, nv * es}, {S0, ns * 4}};
-    const Range outs[] = {{o, nv * es}, {S_T, ns * 4},
-                          {chunk_states, gdr2_chunk_states_bytes(B, T, H, dk, dv, dt)}};
-    if (any_alias(outs, 3, ins, 7)) return GDR2_E_ALIAS;
-
-    const int bf = dt == GDR2_BF16;
-    const int dvs = gdr2::fwd_slice_width(bf, (int)dk, (int)dv, B * H);
+static gdr2::FwdParams fwd_params(int64_t B, int64_t T, int64_t H, int64_t dv, const void* q,
+                                  const void* k, const void* v, const float* la, const void* b,
+                                  const void* w, const float* S0, void* o, float* S_T,
+                                  const FwdWs& L, void* ws, int dvs) {
     gdr2::FwdParams p;
     p.B = (int)B;
     p.H = (int)H;
@@ -120,20 +135,53 @@ gdr2_status gdr2_fwd_chunked(int64_t B, int64_t T, int64_t H, int64_t dk, int64_
     p.T = T;
     p.DV = dv;
     p.q = q; p.k = k; p.v = v; p.b = b; p.w = w;
-    p.la = log_alpha;
+    p.la = la;
     p.S0 = S0;
     p.o = o;
     p.ST = S_T;
-    p.states = chunk_states;
-    hipError_t e = gdr2::fwd_dispatch(bf, (int)dk, dvs, p, (hipStream_t)stream);
+    p.states = ws ? (char*)ws + L.states : nullptr;
+    p.wy = wy_bufs(L, ws);
+    return p;
+}
+
+gdr2_status gdr2_fwd_chunked(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                             gdr2_dtype dt, const void* q, const void* k, const void* v,
+                             const float* log_alpha, const void* b, const void* w,
+                             const float* S0, void* o, float* S_T, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+    gdr2_status st = check_chunked(B, T, H, dk, dv, dt);
+    if (st != GDR2_OK) return st;
+    if (B == 0 || H == 0) return GDR2_OK;
+    const bool have_tokens = T > 0;
+    if (have_tokens && (!q || !k || !v || !log_alpha || !b || !w || !o)) return GDR2_E_NULL;
+    const void* ptrs[] = {q, k, v, log_alpha, b, w, S0, o, S_T, workspace};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return GDR2_E_ALIGN;
+    const FwdWs L = fwd_ws_layout(B, T, H, dk, dv, dt);
+    if (have_tokens && (!workspace || workspace_bytes < L.total)) return GDR2_E_WORKSPACE;
+    const size_t es = gdr2_dtype_size(dt);
+    const size_t nk = (size_t)B * T * H * dk, nv = (size_t)B * T * H * dv;
+    const size_t ns = (size_t)B * H * dk * dv;
+    const Range ins[] = {{q, nk * es}, {k, nk * es}, {v, nv * es}, {log_alpha, nk * 4},
+                         {b, nk * es}, {w, nv * es}, {S0, ns * 4}};
+    const Range outs[] = {{o, nv * es}, {S_T, ns * 4}, {workspace, have_tokens ? L.total : 0}};
+    if (any_alias(outs, 3, ins, 7)) return GDR2_E_ALIAS;
+
+    const int bf = dt == GDR2_BF16;
+    const int dvs = gdr2::carry_slice_width(bf, (int)dk, (int)dv, B * H);
+    gdr2::FwdParams p = fwd_params(B, T, H, dv, q, k, v, log_alpha, b, w, S0, o, S_T, L,
+                                   have_tokens ? workspace : nullptr, dvs);
+    hipError_t e = hipSuccess;
+    if (have_tokens) e = gdr2::wy_dispatch(bf, (int)dk, (int)dv, p, (hipStream_t)stream);
+    if (e == hipSuccess) e = gdr2::carry_fwd_dispatch(bf, (int)dk, dvs, p, (hipStream_t)stream);
     return e == hipSuccess ? GDR2_OK : GDR2_E_HIP;
 }
 
 gdr2_status gdr2_bwd_chunked(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
                              gdr2_dtype dt, const void* q, const void* k, const void* v,
                              const float* log_alpha, const void* b, const void* w,
-                             const float* S0, const void* chunk_states, const void* dO,
-                             const float* dS_T, void* dq, void* dk_, void* dv_,
+                             const void* fwd_workspace, size_t fwd_workspace_bytes,
+                             const void* dO, const float* dS_T, void* dq, void* dk_, void* dv_,
                              float* dlog_alpha, void* db, void* dw, float* dS0,
                              void* workspace, size_t workspace_bytes, void* stream) {
     gdr2_status st = check_chunked(B, T, H, dk, dv, dt);
@@ -141,52 +189,39 @@ gdr2_status gdr2_bwd_chunked(int64_t B, int64_t T, int64_t H, int64_t dk, int64_
     if (B == 0 || H == 0) return GDR2_OK;
     const bool have_tokens = T > 0;
     if (have_tokens && (!q || !k || !v || !log_alpha || !b || !w || !dO || !dq || !dk_ ||
-                        !dv_ || !dlog_alpha || !db || !dw))
+                        !dv_ || !dlog_alpha || !db || !dw || !fwd_workspace))
         return GDR2_E_NULL;
-    const void* ptrs[] = {q, k, v, log_alpha, b, w, S0, chunk_states, dO, dS_T, dq, dk_, dv_,
+    const void* ptrs[] = {q, k, v, log_alpha, b, w, fwd_workspace, dO, dS_T, dq, dk_, dv_,
                           dlog_alpha, db, dw, dS0, workspace};
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return GDR2_E_ALIGN;
-    const size_t need = gdr2_bwd_workspace_bytes(B, T, H, dk, dv, dt, chunk_states != nullptr);
-    if (have_tokens && (!workspace || workspace_bytes < need)) return GDR2_E_WORKSPACE;
+    const FwdWs L = fwd_ws_layout(B, T, H, dk, dv, dt);
+    const size_t need = gdr2_bwd_workspace_bytes(B, T, H, dk, dv, dt);
+    if (have_tokens && (fwd_workspace_bytes < L.total || !workspace || workspace_bytes < need))
+        return GDR2_E_WORKSPACE;
     const size_t es = gdr2_dtype_size(dt);
     const size_t nk = (size_t)B * T * H * dk, nv = (size_t)B * T * H * dv;
     const size_t ns = (size_t)B * H * dk * dv;
-    const size_t csb = gdr2_chunk_states_bytes(B, T, H, dk, dv, dt);
     const Range ins[] = {{q, nk * es},     {k, nk * es},  {v, nv * es},
                          {log_alpha, nk * 4}, {b, nk * es}, {w, nv * es},
-                         {S0, ns * 4},     {chunk_states, csb}, {dO, nv * es},
+                         {fwd_workspace, have_tokens ? L.total : 0}, {dO, nv * es},
                          {dS_T, ns * 4}};
     const Range outs[] = {{dq, nk * es},  {dk_, nk * es}, {dv_, nv * es}, {dlog_alpha, nk * 4},
                           {db, nk * es},  {dw, nv * es},  {dS0, ns * 4},
                           {workspace, have_tokens ? need : 0}};
-    if (any_alias(outs, 8, ins, 10)) return GDR2_E_ALIAS;
+    if (any_alias(outs, 8, ins, 9)) return GDR2_E_ALIAS;
 
     const int bf = dt == GDR2_BF16;
-    const int NC = (int)gdr2_num_chunks(T);
-    char* ws = (char*)workspace;
-    void* dSx = ws;
-    const void* states = chunk_states;
-    if (!states && have_tokens) {
-        void* rec = ws + round_up(csb, 256);
-        gdr2::FwdParams fp;
-        const int dvs = gdr2::fwd_slice_width(bf, (int)dk, (int)dv, B * H);
-        fp.B = (int)B; fp.H = (int)H; fp.NS = (int)(dv / dvs); fp.NC = NC;
-        fp.T = T; fp.DV = dv;
-        fp.q = q; fp.k = k; fp.v = v; fp.b = b; fp.w = w; fp.la = log_alpha; fp.S0 = S0;
-        fp.o = nullptr; fp.ST = nullptr; fp.states = rec;
-        hipError_t e = gdr2::fwd_dispatch(bf, (int)dk, dvs, fp, (hipStream_t)stream);
-        if (e != hipSuccess) return GDR2_E_HIP;
-        states = rec;
-    }
     gdr2::BwdParams p;
-    p.B = (int)B; p.H = (int)H; p.NC = NC; p.T = T; p.DV = dv;
-    const int dvs = gdr2::bwd_slice_width(bf, (int)dk, (int)dv, B * H);
-    p.NS = (int)(dv / dvs);
+    p.B = (int)B; p.H = (int)H; p.NC = (int)gdr2_num_chunks(T); p.T = T; p.DV = dv;
+    p.NS = (int)(dv / gdr2::carry_slice_width(bf, (int)dk, (int)dv, B * H));
     p.q = q; p.k = k; p.v = v; p.b = b; p.w = w; p.la = log_alpha;
-    p.states = states; p.dO = dO; p.dST = dS_T; p.dSx = dSx; p.dS0 = dS0;
+    void* fws = const_cast<void*>(fwd_workspace);
+    p.states = fws ? (const char*)fws + L.states : nullptr;
+    p.wy = wy_bufs(L, fws);
+    p.dO = dO; p.dST = dS_T; p.dSx = workspace; p.dS0 = dS0;
     p.dq = dq; p.dk = dk_; p.dv = dv_; p.db = db; p.dw = dw; p.dla = dlog_alpha;
-    hipError_t e = gdr2::bwd_dispatch(bf, (int)dk, dvs, p, (hipStream_t)stream);
+    hipError_t e = gdr2::bwd_dispatch(bf, (int)dk, (int)dv, p, (hipStream_t)stream);
     if (e == hipErrorNotSupported) return GDR2_E_UNSUPPORTED;
     return e == hipSuccess ? GDR2_OK : GDR2_E_HIP;
 }

@@ -3,6 +3,5 @@
 #include "gdr2_kernels.hpp"
 
 namespace gdr2 {
-int bwd_slice_width(int, int, int, long) { return 16; }
 hipError_t bwd_dispatch(int, int, int, const BwdParams&, hipStream_t) { return hipErrorNotSupported; }
 }  // namespace gdr2

@@ -23,6 +23,7 @@ typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));  // 16 raw bytes
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
@@ -41,6 +42,18 @@ __device__ __forceinline__ f32x4 load4(const bf16* p) {
     return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
 }
 __device__ __forceinline__ void store4(float* p, f32x4 v) { *(f32x4*)p = v; }
+// Four raw elements kept undecoded in registers (a prefetch must not be widened before use).
+template <typename OT> struct Raw4;
+template <> struct Raw4<float> {
+    typedef f32x4 t;
+    static __device__ __forceinline__ f32x4 widen(const t& x) { return x; }
+};
+template <> struct Raw4<bf16> {
+    typedef bf16x4 t;
+    static __device__ __forceinline__ f32x4 widen(const t& x) {
+        return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+    }
+};
 __device__ __forceinline__ void store4(bf16* p, f32x4 v) {
     *(bf16x4*)p = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
 }
@@ -153,5 +166,84 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_s_waitcnt(0xc07f);  // vmcnt = max, expcnt = max, lgkmcnt = 0
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
+}
+}  // namespace gdr2
+
+namespace gdr2 {
+// ------------------------------------------------------------------ operand fragments
+// Two kinds of LDS tiles feed MFMA operands (for A and B alike: index = l%16, k = KPL*(l/16)+j):
+//   kc: "k-contiguous" tile X[idx][k]  -> one 16-byte read per lane (bf16) / one scalar (fp32)
+//   tr: "k-major"      tile X[k][idx]  -> two ds_read_b64_tr_b16 per lane (bf16) / one scalar.
+// ds_read_b64_tr_b16 works on groups of 16 lanes: lane p of a group supplies the address of four
+// 16-bit elements M[p][0..3]; lane i of the group receives M[4j + i/4][i%4] for j = 0..3.  With
+// lane p pointing at X[kb + p/4][c0 + 4*(p%4)], lane i receives X[kb .. kb+3][c0 + i].
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+__device__ __forceinline__ bf16x4 ds_read_tr4(const bf16* p) {
+    s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+    return __builtin_bit_cast(bf16x4, v);
+}
+
+template <typename OT> struct Frag;
+template <> struct Frag<bf16> {
+    typedef bf16x8 t;
+    static __device__ __forceinline__ t kc(const bf16* X, int pitch, int i0, int k0) {
+        const int l = lane_id();
+        return *(const bf16x8*)(X + (i0 + (l & 15)) * pitch + k0 + 8 * (l >> 4));
+    }
+    static __device__ __forceinline__ t tr(const bf16* X, int pitch, int k0, int i0) {
+        const int l = lane_id(), p = l & 15, kb = k0 + 8 * (l >> 4) + (p >> 2);
+        const bf16* a = X + kb * pitch + i0 + 4 * (p & 3);
+        bf16x4 lo = ds_read_tr4(a), hi = ds_read_tr4(a + 4 * pitch);
+        return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+    // fragment straight from global memory, row-major [idx][k] with the given pitch
+    static __device__ __forceinline__ t gkc(const bf16* X, long pitch, int i0, int k0) {
+        const int l = lane_id();
+        return *(const bf16x8*)(X + (long)(i0 + (l & 15)) * pitch + k0 + 8 * (l >> 4));
+    }
+    // fragment from 8 fp32 values, multiplied by 8 fp32 scales
+    static __device__ __forceinline__ t from_f32(const float* v) {
+        return bf16x8{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3],
+                      (bf16)v[4], (bf16)v[5], (bf16)v[6], (bf16)v[7]};
+    }
+    static __device__ __forceinline__ t scale(const t& x, const float* s) {
+        t r;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) r[j] = (bf16)((float)x[j] * s[j]);
+        return r;
+    }
+};
+template <> struct Frag<float> {
+    typedef float t;
+    static __device__ __forceinline__ t kc(const float* X, int pitch, int i0, int k0) {
+        const int l = lane_id();
+        return X[(i0 + (l & 15)) * pitch + k0 + (l >> 4)];
+    }
+    static __device__ __forceinline__ t tr(const float* X, int pitch, int k0, int i0) {
+        const int l = lane_id();
+        return X[(k0 + (l >> 4)) * pitch + i0 + (l & 15)];
+    }
+    static __device__ __forceinline__ t gkc(const float* X, long pitch, int i0, int k0) {
+        const int l = lane_id();
+        return X[(long)(i0 + (l & 15)) * pitch + k0 + (l >> 4)];
+    }
+    static __device__ __forceinline__ t from_f32(const float* v) { return v[0]; }
+    static __device__ __forceinline__ t scale(const t& x, const float* s) { return x * s[0]; }
+};
+
+// Inclusive prefix sum over the 16 lanes of each DPP row (lanes 16g .. 16g+15).
+__device__ __forceinline__ float row_scan16(float x) {
+    int v = __builtin_bit_cast(int, x);
+    float y;
+    y = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false));
+    x += y; v = __builtin_bit_cast(int, x);
+    y = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false));
+    x += y; v = __builtin_bit_cast(int, x);
+    y = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false));
+    x += y; v = __builtin_bit_cast(int, x);
+    y = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false));
+    return x + y;
 }
 }  // namespace gdr2

@@ -4,15 +4,29 @@
 
 namespace gdr2 {
 
+// Per-chunk WY factors written by the chunk-parallel factor kernel and read by the state-carry
+// kernels (forward and backward) and the chunk-gradient kernel.  Element type = input dtype
+// except gam.  Every array is indexed [chain = b*H + h][chunk][...].
+struct WyBufs {
+    void* Yh;    // -Y = -(T Ebar),                          [C][DK] row-major
+    void* Qg;    // Qbar = Q . exp(G),                        [C][DK]
+    void* Kt;    // Ktilde = K . exp(G_C - G),                [C][DK]
+    void* P;     // P = lower(Qbar Kbar^T),                   [C][C]
+    void* Tm;    // T = (I + A)^-1,                           [C][C]
+    void* U;     // U = T Z in MFMA accumulator order,        [4][DV/16][64 lanes][4]
+    float* gam;  // gamma = exp(G_C),                         [DK] fp32
+};
+
 struct FwdParams {
     int B, H, NS, NC;   // batch, heads, value slices per chain, chunks
     long T, DV;         // tokens, value width (DK is a template parameter)
     const void *q, *k, *v, *b, *w;  // input dtype
     const float* la;    // log decay, fp32
     const float* S0;    // [B,H,DK,DV] fp32 or null
-    void* o;            // [B,T,H,DV] input dtype
+    void* o;            // [B,T,H,DV] input dtype or null
     float* ST;          // [B,H,DK,DV] fp32 or null
-    void* states;       // [B*H][NC][DV][DK] input dtype or null (chunk-entry states, transposed)
+    void* states;       // [B*H][NC][DV][DK] input dtype (chunk-entry states, transposed)
+    WyBufs wy;
 };
 
 struct DecodeParams {
@@ -30,6 +44,7 @@ struct BwdParams {
     const void *q, *k, *v, *b, *w;
     const float* la;
     const void* states;   // chunk-entry states [B*H][NC][DV][DK] (input dtype)
+    WyBufs wy;            // factors of the forward
     const void* dO;       // [B,T,H,DV]
     const float* dST;     // [B,H,DK,DV] fp32 or null
     void* dSx;            // per-chunk exit-state gradients [B*H][NC][DV][DK] (input dtype)
@@ -38,10 +53,11 @@ struct BwdParams {
     float* dla;
 };
 
-int fwd_slice_width(int dtype_bf16, int dk, int dv, long chains);
-hipError_t fwd_dispatch(int dtype_bf16, int dk, int dvs, const FwdParams& p, hipStream_t s);
+// forward: factor kernel (chunk-parallel) + state carry (sequential over chunks)
+hipError_t wy_dispatch(int dtype_bf16, int dk, int dv, const FwdParams& p, hipStream_t s);
+int carry_slice_width(int dtype_bf16, int dk, int dv, long chains);
+hipError_t carry_fwd_dispatch(int dtype_bf16, int dk, int dvs, const FwdParams& p, hipStream_t s);
 hipError_t decode_dispatch(int dtype_bf16, int dk, int dv, const DecodeParams& p, hipStream_t s);
-int bwd_slice_width(int dtype_bf16, int dk, int dv, long chains);
-hipError_t bwd_dispatch(int dtype_bf16, int dk, int dvs, const BwdParams& p, hipStream_t s);
+hipError_t bwd_dispatch(int dtype_bf16, int dk, int dv, const BwdParams& p, hipStream_t s);
 
 }  // namespace gdr2

@@ -1,0 +1,361 @@
+// gdr2_wy.hpp -- per-chunk WY factors of the Gated Delta Rule-2 chunk form (device code).
+//
+// One workgroup (4 waves) handles one chunk of C = 64 tokens of one (batch, head) chain.  Wave R
+// owns token rows 16R .. 16R+15; lane l owns row 16R + l%16 and, of every channel vector, the
+// channels ks*KS + KPL*(l/16) + j -- exactly the MFMA operand layout, so the gate prep feeds the
+// Gram products straight from registers.
+//
+// Chunk algebra (per chunk; G_r = inclusive cumsum of log alpha inside the chunk, e = b . k,
+// z = w . v): the cumulative channel-wise decay is absorbed into the two factors of each rank-one
+// erase (ainews.random.gg article on Gated DeltaNet-2, section "Chunkwise training and gate-aware
+// backward"):
+//     A_rs = sum_i e_ri exp(G_ri - G_si) k_si   (r > s)      T = (I + A)^-1
+//     P_rs = sum_i q_ri exp(G_ri - G_si) k_si   (r >= s)
+//     Y = T (E . e^G),   U = T Z,   Qbar = Q . e^G,   Ktilde = K . e^{G_C - G},   gamma = e^{G_C}.
+#pragma once
+#include "gdr2_common.hpp"
+#include "gdr2_kernels.hpp"
+
+namespace gdr2 {
+
+template <typename OT, int DK, int DV>
+struct WyCfg {
+    static constexpr int C = kChunk;
+    static constexpr int KS = Mfma<OT>::KS, KPL = Mfma<OT>::KPL;
+    static constexpr int PAD = 16 / (int)sizeof(OT);
+    static constexpr int PK = DK + PAD, PV = DV + PAD, PC = C + PAD;
+    static constexpr int PAF = C + 4;                      // fp32 A / T pitch, 16-byte rows
+    static constexpr int NKS = DK / KS, NVS = DV / KS;     // k-steps over key / value channels
+    static constexpr int NCH = NKS * KPL, NCV = NVS * KPL; // channels per lane (DK/4, DV/4)
+};
+
+template <typename OT, int DK, int DV>
+struct alignas(16) WySmem {
+    using Cf = WyCfg<OT, DK, DV>;
+    union {
+        OT Kb[kChunk * Cf::PK];  // phase 1: k . exp(ref_S - G)          [s][i]
+        struct {
+            OT Eg[kChunk * Cf::PK];  // phase 2: e . exp(G)              [s][i]
+            OT Z[kChunk * Cf::PV];   // phase 2: z = w . v               [s][j]
+        } e;
+    } u;
+    float Af[kChunk * Cf::PAF];  // A (strict lower), then T in fp32 (see tblk)
+    OT Tm[kChunk * Cf::PC];      // T in operand precision           [r][s]
+    float Mf[kWaves][16 * 17];   // per-wave scratch of the solve
+    float tot[4][DK];            // per-block log-decay totals
+    float ctab[6][DK];           // exp(ref_R - ref_S), R > S
+    float gRt[4][DK];            // exp(ref_R)
+    float hRt[4][DK];            // exp(G_C - ref_R)
+};
+
+// Location of block T_RS of the inverse inside Af: diagonal blocks overwrite A_RR, off-diagonal
+// blocks live in the (unused) strictly upper block (S, R) so that A_RK stays readable.
+template <int PAF>
+__device__ __forceinline__ float* tblk(float* Af, int R, int S) {
+    return R == S ? Af + 16 * R * PAF + 16 * R : Af + 16 * S * PAF + 16 * R;
+}
+
+// T = (I + A)^-1 for the strictly lower 64 x 64 A held in Af (fp32), 16 x 16 blocked:
+// diagonal blocks by forward substitution (wave R, lane = column), then
+// T_RS = -T_RR sum_{S <= K < R} A_RK T_KS level by level with fp32 MFMA.  T is also written, in
+// operand precision, to Tm (row-major, zero above the diagonal).  Ends with a barrier.
+template <typename OT, int PAF, int PC>
+__device__ void solve_unit_lower_64(float* Af, float (*Mf)[16 * 17], OT* Tm) {
+    const int w = wave_id(), l = lane_id();
+    for (int x = threadIdx.x; x < 6 * 256; x += kThreads) {
+        const int blk = x >> 8, e = x & 255;
+        const int R = blk < 3 ? 0 : blk < 5 ? 1 : 2;
+        const int S = blk < 3 ? blk + 1 : blk < 5 ? blk - 1 : 3;
+        Tm[(16 * R + (e >> 4)) * PC + 16 * S + (e & 15)] = from_f<OT>(0.f);
+    }
+    {
+        float* Ab = Af + 16 * w * PAF + 16 * w;
+        const int c = l & 15;
+        float x[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float acc = (r == c) ? 1.f : 0.f;
+#pragma unroll
+            for (int s = 0; s < r; ++s) acc -= Ab[r * PAF + s] * x[s];
+            x[r] = acc;
+        }
+        wave_sync();
+        if (l < 16) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                Ab[r * PAF + c] = x[r];
+                Tm[(16 * w + r) * PC + 16 * w + c] = from_f<OT>(x[r]);
+            }
+        }
+    }
+    lds_barrier();
+#pragma unroll
+    for (int d = 1; d <= 3; ++d) {
+        if (w < 4 - d) {
+            const int S = w, R = w + d;
+            f32x4 m = {0.f, 0.f, 0.f, 0.f};
+            for (int K = S; K < R; ++K) {
+                const float* tks = tblk<PAF>(Af, K, S);
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk)
+                    mma32(m, fa32(Af, PAF, 16 * R, 16 * K + 4 * kk), fb32(tks, PAF, 4 * kk, 0));
+            }
+            float* M = Mf[w];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) M[acc_row(e) * 17 + acc_col()] = m[e];
+            wave_sync();
+            f32x4 n = {0.f, 0.f, 0.f, 0.f};
+            const float* trr = tblk<PAF>(Af, R, R);
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) mma32(n, fa32(trr, PAF, 0, 4 * kk), fb32(M, 17, 4 * kk, 0));
+            float* trs = tblk<PAF>(Af, R, S);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                trs[acc_row(e) * PAF + acc_col()] = -n[e];
+                Tm[(16 * R + acc_row(e)) * PC + 16 * S + acc_col()] = from_f<OT>(-n[e]);
+            }
+        }
+        lds_barrier();
+    }
+}
+
+// The KPL values of k-step ks that lane group g owns in a row: channels ks*KS + KPL*g + j.
+template <typename OT>
+__device__ __forceinline__ void load_lane(const OT* row, int ks, int g, float* out) {
+    if constexpr (sizeof(OT) == 2) {
+        bf16x8 x = *(const bf16x8*)(row + ks * 32 + 8 * g);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) out[j] = (float)x[j];
+    } else {
+        out[0] = row[ks * 4 + g];
+    }
+}
+template <typename OT>
+__device__ __forceinline__ void load_lane_f32(const float* row, int ks, int g, float* out) {
+    if constexpr (sizeof(OT) == 2) {
+        f32x4 a = *(const f32x4*)(row + ks * 32 + 8 * g), b = *(const f32x4*)(row + ks * 32 + 8 * g + 4);
+        out[0] = a[0]; out[1] = a[1]; out[2] = a[2]; out[3] = a[3];
+        out[4] = b[0]; out[5] = b[1]; out[6] = b[2]; out[7] = b[3];
+    } else {
+        out[0] = row[ks * 4 + g];
+    }
+}
+template <typename OT>
+__device__ __forceinline__ void store_lane(OT* row, int ks, int g, const float* v) {
+    if constexpr (sizeof(OT) == 2) {
+        *(bf16x8*)(row + ks * 32 + 8 * g) = Frag<bf16>::from_f32(v);
+    } else {
+        row[ks * 4 + g] = v[0];
+    }
+}
+__device__ __forceinline__ void store_lane_f32(float* row, int ks, int g, const float* v, int kpl) {
+    if (kpl == 8) {
+        *(f32x4*)(row + ks * 32 + 8 * g) = f32x4{v[0], v[1], v[2], v[3]};
+        *(f32x4*)(row + ks * 32 + 8 * g + 4) = f32x4{v[4], v[5], v[6], v[7]};
+    } else {
+        row[ks * 4 + g] = v[0];
+    }
+}
+
+// Where one workgroup's chunk lives.
+template <typename OT, int DK, int DV>
+struct WyChunk {
+    int chain, c, R, l, rl, g, r;
+    long T, H, DVl, row, cix;
+    bool valid;
+    const OT *q, *k, *b, *v, *w;
+    const float* la;
+    __device__ WyChunk(int B, int H_, long T_, long DV_, int NC, int bid, const void* q_,
+                       const void* k_, const void* b_, const float* la_, const void* v_,
+                       const void* w_) {
+        (void)B;
+        chain = bid / NC;
+        c = bid % NC;
+        const int bb = chain / H_, h = chain % H_;
+        R = wave_id();
+        l = lane_id();
+        rl = l & 15;
+        g = l >> 4;
+        T = T_;
+        H = H_;
+        DVl = DV_;
+        r = 16 * R + rl;
+        const long t = (long)c * kChunk + r;
+        valid = t < T;
+        const long tt = valid ? t : T - 1;
+        row = ((long)bb * T + tt) * H + h;
+        cix = (long)chain * NC + c;
+        q = (const OT*)q_ + row * DK;
+        k = (const OT*)k_ + row * DK;
+        b = (const OT*)b_ + row * DK;
+        la = la_ + row * DK;
+        v = (const OT*)v_ + row * DV_;
+        w = (const OT*)w_ + row * DV_;
+    }
+};
+
+// Compute and store the WY factors of one chunk (see the file comment); every thread of the
+// workgroup calls it.
+template <typename OT, int DK, int DV>
+__device__ void wy_factors(WySmem<OT, DK, DV>& sm, const WyChunk<OT, DK, DV>& ch, const WyBufs& wy) {
+    using Cf = WyCfg<OT, DK, DV>;
+    using MM = Mfma<OT>;
+    using FR = Frag<OT>;
+    constexpr int C = kChunk, KS = Cf::KS, KPL = Cf::KPL, PK = Cf::PK, PV = Cf::PV;
+    constexpr int PC = Cf::PC, PAF = Cf::PAF, NKS = Cf::NKS, NVS = Cf::NVS, NCH = Cf::NCH;
+    constexpr int NCV = Cf::NCV;
+    const int R = ch.R, l = ch.l, rl = ch.rl, g = ch.g, r = ch.r;
+    const long cix = ch.cix, DVl = ch.DVl;
+
+    float qv[NCH], kv[NCH], bv[NCH], lv[NCH], zv[NCV];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+        load_lane<OT>(ch.q, ks, g, qv + ks * KPL);
+        load_lane<OT>(ch.k, ks, g, kv + ks * KPL);
+        load_lane<OT>(ch.b, ks, g, bv + ks * KPL);
+        load_lane_f32<OT>(ch.la, ks, g, lv + ks * KPL);
+    }
+#pragma unroll
+    for (int ks = 0; ks < NVS; ++ks) {
+        float vv[KPL], wv[KPL];
+        load_lane<OT>(ch.v, ks, g, vv);
+        load_lane<OT>(ch.w, ks, g, wv);
+#pragma unroll
+        for (int j = 0; j < KPL; ++j) zv[ks * KPL + j] = ch.valid ? vv[j] * wv[j] : 0.f;
+    }
+    if (!ch.valid) {
+#pragma unroll
+        for (int n = 0; n < NCH; ++n) qv[n] = kv[n] = bv[n] = lv[n] = 0.f;
+    }
+    // in-block inclusive cumsum of log alpha (16 lanes = 16 rows) and the block totals
+#pragma unroll
+    for (int n = 0; n < NCH; ++n) lv[n] = row_scan16(lv[n]);  // lv := G_r - ref_R
+    if (rl == 15) {
+#pragma unroll
+        for (int n = 0; n < NCH; ++n) sm.tot[R][(n / KPL) * KS + KPL * g + n % KPL] = lv[n];
+    }
+    lds_barrier();
+
+    // per-channel tables from the block totals: ref_R = sum of earlier block totals,
+    // exp(ref_R), exp(G_C - ref_R), exp(ref_R - ref_S) (R > S) and gamma = exp(G_C)
+    for (int chn = threadIdx.x; chn < DK; chn += kThreads) {
+        float refs[4], run = 0.f;
+#pragma unroll
+        for (int Rp = 0; Rp < 4; ++Rp) {
+            refs[Rp] = run;
+            run += sm.tot[Rp][chn];
+        }
+#pragma unroll
+        for (int Rp = 0; Rp < 4; ++Rp) {
+            sm.gRt[Rp][chn] = __expf(refs[Rp]);
+            sm.hRt[Rp][chn] = __expf(run - refs[Rp]);
+#pragma unroll
+            for (int S = 0; S < Rp; ++S) sm.ctab[Rp * (Rp - 1) / 2 + S][chn] = __expf(refs[Rp] - refs[S]);
+        }
+        wy.gam[cix * DK + chn] = __expf(run);
+    }
+    lds_barrier();
+
+    // decay-absorbed factors
+    typename FR::t Ef[NKS], Qf[NKS];  // e . exp(G - ref_R), q . exp(G - ref_R) (Gram operands)
+    float eg[NCH];                     // e . exp(G), kept for Y
+    OT* qg_out = (OT*)wy.Qg + (cix * C + r) * DK;
+    OT* kt_out = (OT*)wy.Kt + (cix * C + r) * DK;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+        float ebk[KPL], qbk[KPL], kbk[KPL], qg[KPL], kt[KPL], gR[KPL], hR[KPL];
+        load_lane_f32<OT>(sm.gRt[R], ks, g, gR);
+        load_lane_f32<OT>(sm.hRt[R], ks, g, hR);
+#pragma unroll
+        for (int j = 0; j < KPL; ++j) {
+            const int n = ks * KPL + j;
+            const float x = __expf(lv[n]), y = __expf(-lv[n]);
+            const float e = bv[n] * kv[n];
+            ebk[j] = e * x;
+            qbk[j] = qv[n] * x;
+            kbk[j] = kv[n] * y;
+            eg[n] = ebk[j] * gR[j];
+            qg[j] = qbk[j] * gR[j];
+            kt[j] = kbk[j] * hR[j];
+        }
+        Ef[ks] = FR::from_f32(ebk);
+        Qf[ks] = FR::from_f32(qbk);
+        store_lane<OT>(sm.u.Kb + r * PK, ks, g, kbk);
+        store_lane<OT>(qg_out, ks, g, qg);
+        store_lane<OT>(kt_out, ks, g, kt);
+    }
+    lds_barrier();
+
+    // A^T and P^T blocks (S, R) for S <= R: rows s of block S, columns r of block R.
+    {
+        OT* prow = (OT*)wy.P + (cix * C + r) * C;
+#pragma unroll
+        for (int S = 0; S < 4; ++S) {
+            if (S > R) {
+                OT* d = prow + 16 * S + 4 * g;  // zero block above the diagonal
+                store4(d, f32x4{0.f, 0.f, 0.f, 0.f});
+                continue;
+            }
+            f32x4 aA = {0.f, 0.f, 0.f, 0.f}, aP = {0.f, 0.f, 0.f, 0.f};
+            const float* cs = S < R ? sm.ctab[R * (R - 1) / 2 + S] : nullptr;
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                typename FR::t a = FR::kc(sm.u.Kb, PK, 16 * S, ks * KS);
+                if (S < R) a = FR::scale(a, cs + ks * KS + KPL * g);
+                MM::mma(aA, a, Ef[ks]);
+                MM::mma(aP, a, Qf[ks]);
+            }
+            f32x4 am, pm;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int s = 16 * S + 4 * g + e;
+                am[e] = (S < R || s < r) ? aA[e] : 0.f;
+                pm[e] = (S < R || s <= r) ? aP[e] : 0.f;
+            }
+            *(f32x4*)(sm.Af + r * PAF + 16 * S + 4 * g) = am;
+            store4(prow + 16 * S + 4 * g, pm);
+        }
+    }
+    lds_barrier();
+    solve_unit_lower_64<OT, PAF, PC>(sm.Af, sm.Mf, sm.Tm);
+
+    // stage e . exp(G) and z for the WY products (Kb is dead now), copy T out
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) store_lane<OT>(sm.u.e.Eg + r * PK, ks, g, eg + ks * KPL);
+#pragma unroll
+    for (int ks = 0; ks < NVS; ++ks) store_lane<OT>(sm.u.e.Z + r * PV, ks, g, zv + ks * KPL);
+    {
+        OT* tg = (OT*)wy.Tm + cix * C * C;
+        constexpr int VEC = 16 / (int)sizeof(OT);
+        for (int x = threadIdx.x; x < C * C / VEC; x += kThreads) {
+            const int rr = (x * VEC) / C, ss = (x * VEC) % C;
+            *(uint4*)(tg + rr * C + ss) = *(const uint4*)(sm.Tm + rr * PC + ss);
+        }
+    }
+    lds_barrier();
+
+    // Y^T = Ebar^T T^T (stored negated, row-major -Y[r][i]) and U = T Z (accumulator order)
+    const int kend = ((16 * R + 16 + KS - 1) / KS) * KS;
+    {
+        OT* yrow = (OT*)wy.Yh + (cix * C + r) * DK;
+#pragma unroll
+        for (int ib = 0; ib < DK / 16; ++ib) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int k0 = 0; k0 < kend; k0 += KS)
+                MM::mma(acc, FR::tr(sm.u.e.Eg, PK, k0, 16 * ib), FR::kc(sm.Tm, PC, 16 * R, k0));
+            store4(yrow + 16 * ib + 4 * g, f32x4{-acc[0], -acc[1], -acc[2], -acc[3]});
+        }
+    }
+    {
+        OT* ub = (OT*)wy.U + cix * C * DVl;
+#pragma unroll
+        for (int jb = 0; jb < DV / 16; ++jb) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int k0 = 0; k0 < kend; k0 += KS)
+                MM::mma(acc, FR::kc(sm.Tm, PC, 16 * R, k0), FR::tr(sm.u.e.Z, PV, k0, 16 * jb));
+            store4(ub + ((long)(R * (DV / 16) + jb) * 64 + l) * 4, acc);
+        }
+    }
+}
+
+}  // namespace gdr2

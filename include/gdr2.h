@@ -27,7 +27,7 @@
  *     no output is written.  Launch failures return GDR2_E_HIP; faults during execution
  *     surface at the caller's next synchronisation.  No C++ exception crosses this ABI.
  *   - Results are bitwise deterministic run to run (no floating-point atomics).
- *   - Supported sizes: d_k, d_v in {64, 128}; the chunked passes in GDR2_F32 need d_k = 64.
+ *   - Supported sizes: d_k, d_v in {64, 128}.
  *     B, H >= 1 and T >= 0 (T = 0 produces no tokens; S_T then equals S0).
  */
 #ifndef GDR2_H
@@ -51,7 +51,7 @@ typedef enum gdr2_status {
     GDR2_E_UNSUPPORTED = 4, /* head sizes / dtype combination not built */
     GDR2_E_ALIGN = 5,       /* a pointer is not 16-byte aligned */
     GDR2_E_ALIAS = 6,       /* an output overlaps an input or another output */
-    GDR2_E_WORKSPACE = 7,   /* workspace missing or smaller than gdr2_bwd_workspace_bytes() */
+    GDR2_E_WORKSPACE = 7,   /* workspace missing or smaller than the size its query returns */
     GDR2_E_HIP = 8          /* the HIP runtime refused the launch */
 } gdr2_status;
 
@@ -64,10 +64,11 @@ size_t gdr2_dtype_size(gdr2_dtype dtype);
 int64_t gdr2_num_chunks(int64_t T);
 
 /*
- * Chunked forward: o_t = S_t^T q_t for all tokens, optionally the final state and the
- * chunk-entry states that the backward consumes.  Implements the chunkwise WY form in which the
- * cumulative channel-wise decay of a chunk is absorbed into the two factors of each rank-one
- * erase (ainews.random.gg article, section "Chunkwise training and gate-aware backward").
+ * Chunked forward: o_t = S_t^T q_t for all tokens, optionally the final state.  Implements the
+ * chunkwise WY form in which the cumulative channel-wise decay of a chunk is absorbed into the two
+ * factors of each rank-one erase (ainews.random.gg article on Gated DeltaNet-2, section "Chunkwise
+ * training and gate-aware backward"): a chunk-parallel kernel builds each chunk's WY factors, then
+ * a state-carry kernel walks the chunks.
  *
  *   q, k, b         [B][T][H][dk]  dtype          (inputs)
  *   v, w            [B][T][H][dv]  dtype          (inputs)
@@ -75,25 +76,25 @@ int64_t gdr2_num_chunks(int64_t T);
  *   S0              [B][H][dk][dv] fp32 or NULL   (input, initial state; NULL = zero)
  *   o               [B][T][H][dv]  dtype          (output)
  *   S_T             [B][H][dk][dv] fp32 or NULL   (output, final state; NULL = not wanted)
- *   chunk_states    NULL, or an opaque checkpoint of gdr2_chunk_states_bytes() bytes that
- *                   receives the state entering every chunk, in dtype, laid out
- *                   [B][H][num_chunks][dv][dk] (each state transposed).  Pass it to
- *                   gdr2_bwd_chunked to skip the state recompute there.
+ *   workspace       device memory of at least gdr2_fwd_workspace_bytes() bytes (required when
+ *                   T > 0).  On return it holds the per-chunk WY factors and the state entering
+ *                   every chunk; gdr2_bwd_chunked reads them, so keep it unchanged between the
+ *                   two calls when training.
  */
 gdr2_status gdr2_fwd_chunked(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
                              gdr2_dtype dtype, const void* q, const void* k, const void* v,
                              const float* log_alpha, const void* b, const void* w,
-                             const float* S0, void* o, float* S_T, void* chunk_states,
-                             void* stream);
+                             const float* S0, void* o, float* S_T, void* workspace,
+                             size_t workspace_bytes, void* stream);
 
-/* Size in bytes of the chunk_states checkpoint for these sizes (B*H*num_chunks*dv*dk elements). */
-size_t gdr2_chunk_states_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
-                               gdr2_dtype dtype);
+/* Bytes of device workspace gdr2_fwd_chunked needs (per token and head about
+ * (4*dk + 2*64 + dv) elements of dtype plus the chunk-entry states, dk*dv/64 elements). */
+size_t gdr2_fwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                                gdr2_dtype dtype);
 
-/* Bytes of device workspace gdr2_bwd_chunked needs: the per-chunk state gradients, plus the
- * chunk-entry states when the caller does not pass them (have_chunk_states == 0). */
+/* Bytes of device workspace gdr2_bwd_chunked needs (the per-chunk state gradients). */
 size_t gdr2_bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
-                                gdr2_dtype dtype, int have_chunk_states);
+                                gdr2_dtype dtype);
 
 /*
  * Gate-aware backward (vector-Jacobian product) of gdr2_fwd_chunked for the loss
@@ -101,22 +102,22 @@ size_t gdr2_bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int
  * products themselves rather than as one scalar factor (ainews.random.gg article, section
  * "Chunkwise training and gate-aware backward").
  *
- *   q, k, v, log_alpha, b, w, S0   as in gdr2_fwd_chunked (same values)
- *   chunk_states    the checkpoint written by gdr2_fwd_chunked for these inputs, or NULL
- *                   (then the states are recomputed into the workspace)
+ *   q, k, v, log_alpha, b, w   as passed to gdr2_fwd_chunked (same values)
+ *   fwd_workspace   the workspace of the gdr2_fwd_chunked call on these inputs, unchanged since
+ *                   (it holds the WY factors and the chunk-entry states, S0 included)
  *   dO              [B][T][H][dv]  dtype           (input)
  *   dS_T            [B][H][dk][dv] fp32 or NULL    (input; NULL = zero)
  *   dq, dk_, db     [B][T][H][dk]  dtype           (outputs)
  *   dv_, dw         [B][T][H][dv]  dtype           (outputs)
  *   dlog_alpha      [B][T][H][dk]  fp32            (output)
  *   dS0             [B][H][dk][dv] fp32 or NULL    (output; NULL = not wanted)
- *   workspace       device memory of at least gdr2_bwd_workspace_bytes(..., chunk_states != NULL)
+ *   workspace       device memory of at least gdr2_bwd_workspace_bytes() bytes
  */
 gdr2_status gdr2_bwd_chunked(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
                              gdr2_dtype dtype, const void* q, const void* k, const void* v,
                              const float* log_alpha, const void* b, const void* w,
-                             const float* S0, const void* chunk_states, const void* dO,
-                             const float* dS_T, void* dq, void* dk_, void* dv_,
+                             const void* fwd_workspace, size_t fwd_workspace_bytes,
+                             const void* dO, const float* dS_T, void* dq, void* dk_, void* dv_,
                              float* dlog_alpha, void* db, void* dw, float* dS0,
                              void* workspace, size_t workspace_bytes, void* stream);
 

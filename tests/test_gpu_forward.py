@@ -17,12 +17,25 @@ def _gpu(x):
     return {n: (None if t is None else t.to(DEV)) for n, t in x.items()}
 
 
-def _run_fwd(x, chunk_states=False):
+def _run_fwd(x):
     g = _gpu(x)
-    o, ST, cs = gdr2_fwd_chunked(g["q"], g["k"], g["v"], g["log_alpha"], g["b"], g["w"],
-                                 S0=g["S0"], want_chunk_states=chunk_states)
+    o, ST, ws = gdr2_fwd_chunked(g["q"], g["k"], g["v"], g["log_alpha"], g["b"], g["w"],
+                                 S0=g["S0"])
     torch.cuda.synchronize()
-    return o, ST, cs
+    return o, ST, ws
+
+
+def _states_view(ws, B, T, H, dk, dv, dtype):
+    """The chunk-entry states inside the forward workspace: the last region of the layout
+    (-Y, Qbar, Ktilde [C][dk]; P, T [C][C]; U [C][dv]; gamma [dk] fp32; states [dv][dk]), each
+    region rounded up to 256 bytes."""
+    es = 2 if dtype == torch.bfloat16 else 4
+    NC = (T + 63) // 64
+    ncc = B * H * NC
+    r = lambda n: (n + 255) // 256 * 256
+    off = 3 * r(ncc * 64 * dk * es) + 2 * r(ncc * 64 * 64 * es) + r(ncc * 64 * dv * es) + r(ncc * dk * 4)
+    n = ncc * dv * dk
+    return ws[off:off + n * es].view(dtype).view(B, H, NC, dv, dk)
 
 
 def _check_fwd(x, tol, tag):
@@ -32,7 +45,7 @@ def _check_fwd(x, tol, tag):
     ro, rS = orc.forward(f["q"], f["k"], f["v"], f["log_alpha"], f["b"], f["w"], f["S0"])
     eo = assert_close(f"{tag} o", to_np(o), ro, tol)
     eS = assert_close(f"{tag} S_T", to_np(ST), rS, tol)
-    print(f"  {tag}: o {eo:.2e}  S_T {eS:.2e}")
+    print(f"  {tag}: o {eo:.2e}  S_T {eS:.2e}", flush=True)
 
 
 def test_fwd_pr1_fp32():
@@ -47,10 +60,11 @@ def test_fwd_bf16_shapes(T, dk, dv):
     _check_fwd(x, TOL["bf16"], f"bf16 T={T} dk={dk} dv={dv}")
 
 
-@pytest.mark.parametrize("T,dv", [(1, 64), (130, 64), (130, 128), (256, 128)])
-def test_fwd_fp32_shapes(T, dv):
-    x = layer_inputs(2, T, 2, 64, dv, dtype="f32", seed=20 + T + dv, s0_std=0.05, grads=False)
-    _check_fwd(x, TOL["f32"], f"f32 T={T} dk=64 dv={dv}")
+@pytest.mark.parametrize("T,dk,dv", [(1, 64, 64), (130, 64, 64), (130, 64, 128), (256, 64, 128),
+                                     (200, 128, 128), (65, 128, 64)])
+def test_fwd_fp32_shapes(T, dk, dv):
+    x = layer_inputs(2, T, 2, dk, dv, dtype="f32", seed=20 + T + dv, s0_std=0.05, grads=False)
+    _check_fwd(x, TOL["f32"], f"f32 T={T} dk={dk} dv={dv}")
 
 
 def test_fwd_many_chains_slice_paths():
@@ -68,15 +82,17 @@ def test_fwd_strong_decay():
     _check_fwd(x, TOL["bf16"], "bf16 strong decay")
     x = strong_decay_inputs(1, 256, 2, 64, 64, dtype="f32", seed=4, floor=-5.0)
     _check_fwd(x, TOL["f32"], "f32 strong decay")
+    x = strong_decay_inputs(1, 256, 2, 128, 128, dtype="f32", seed=5, floor=-5.0)
+    _check_fwd(x, TOL["f32"], "f32 strong decay d=128")
 
 
 def test_fwd_chunk_states_checkpoint():
     """The chunk-entry checkpoint equals the oracle state after 64*c tokens (rounded to dtype)."""
     x = layer_inputs(1, 150, 2, 128, 64, dtype="bf16", seed=9, s0_std=0.05, grads=False)
     announce("chunk states")
-    o, ST, cs = _run_fwd(x, chunk_states=True)
+    o, ST, ws = _run_fwd(x)
     NC = 3
-    st = cs.view(torch.bfloat16).view(1, 2, NC, 64, 128).float().cpu().numpy()  # [B,H,NC,dv,dk]
+    st = _states_view(ws, 1, 150, 2, 128, 64, torch.bfloat16).float().cpu().numpy()  # [B,H,NC,dv,dk]
     f = to_f64(x)
     for c in range(NC):
         if c == 0:
