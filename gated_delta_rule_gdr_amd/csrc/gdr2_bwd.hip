@@ -1,7 +1,652 @@
 // gdr2_bwd.hip -- gate-aware backward of the chunked Gated Delta Rule-2 layer (gfx950).
+//
+// The ainews.random.gg article on Gated DeltaNet-2, section "Chunkwise training and gate-aware
+// backward", notes that KDA's scalar shortcut no longer applies: the erase and write gates are
+// different diagonal gates on the key and value channels, so they appear inside the dot products
+// that accumulate gradients.  Written out for one chunk (forward: Delta = U - Y S,
+// O = Qbar S + P Delta, S' = Diag(gamma) S + Ktilde^T Delta; see gdr2_fwd.hip), with dS' the
+// gradient of the state leaving the chunk:
+//     dDelta = Ktilde dS' + P^T dO
+//     dS     = Diag(gamma) dS' + Qbar^T dO - Y^T dDelta          (passed to the previous chunk)
+//     dX     = T^T dDelta,  X = Z - Ebar S = T^-1 Delta            (dZ = dX: dv = dX . w, dw = dX . v)
+//     dA     = strict_lower(-dX Delta^T),   dP = lower(dO Delta^T)
+//     dQbar  = dO S^T + dP Kbar,  dEbar = -dX S^T + dA Kbar,  dKbar = dP^T Qbar + dA^T Ebar,
+//     dKtilde = Delta dS'^T,  dgamma_i = sum_j dS'_ij S_ij
+// and the chain rule through Qbar = q e^G, Ebar = (b . k) e^G, Kbar = k e^-G,
+// Ktilde = k e^{G_C - G}, gamma = e^{G_C}, G = in-chunk cumsum of log alpha.
+//
+// Kernels:
+//   gdr2_dstate_kernel  sequential over chunks in reverse, one workgroup per (chain, value slice):
+//                       the dS carry; writes the gradient of every chunk's exit state and dS0.
+//   gdr2_bgrad_kernel   one workgroup per (chain, chunk), all chunks in parallel: every input
+//                       gradient of the chunk (see the comment above the kernel).
 #include "gdr2_common.hpp"
 #include "gdr2_kernels.hpp"
+#include "gdr2_wy.hpp"
 
 namespace gdr2 {
-hipError_t bwd_dispatch(int, int, int, const BwdParams&, hipStream_t) { return hipErrorNotSupported; }
+
+template <typename OT, int DK, int DVS>
+struct DsCfg {
+    static constexpr int C = kChunk;
+    static constexpr int KS = Mfma<OT>::KS;
+    static constexpr int ES = (int)sizeof(OT);
+    static constexpr int PAD = 16 / ES;
+    static constexpr int PK = DK + PAD, PC = C + PAD, PO = DVS + PAD;
+    static constexpr int NKS = DK / KS, NCK = C / KS;
+    static constexpr int NJB = DVS / 16, NIB = DK / 16;
+    static constexpr int BPW = NIB * NJB / kWaves;
+    static constexpr int VEC = 16 / ES;
+    static constexpr int KVEC = C * DK * ES / 16 / kThreads;   // [C][DK] tile, vectors per thread
+    static constexpr int PVEC = (C * C * ES / 16 + kThreads - 1) / kThreads;
+    static constexpr int NOV = C * DVS * ES / 16;                // [C][DVS] slice, vectors
+    static constexpr int OVEC = (NOV + kThreads - 1) / kThreads;
+    static_assert(BPW >= 1 && BPW * kWaves == NIB * NJB, "state block mapping");
+};
+
+template <typename OT, int DK, int DVS>
+struct alignas(16) DsSmem {
+    using Cf = DsCfg<OT, DK, DVS>;
+    OT Qt[kChunk * Cf::PK];   // Qbar                      [r][i]
+    OT Yt[kChunk * Cf::PK];   // -Y                        [r][i]
+    OT Pt[kChunk * Cf::PC];   // P                         [r][s]
+    OT dOt[kChunk * Cf::PO];  // dO slice                  [r][j]
+    OT dST[DVS * Cf::PK];     // dS^T operand copy         [j][i]
+    OT dDT[DVS * Cf::PC];     // dDelta^T                  [j][r]
+    float gam[DK];
+};
+
+template <typename OT, int DK, int DVS>
+__global__ __launch_bounds__(kThreads, 1) void gdr2_dstate_kernel(BwdParams p) {
+    using Cf = DsCfg<OT, DK, DVS>;
+    using MM = Mfma<OT>;
+    using FR = Frag<OT>;
+    constexpr int C = kChunk, KS = Cf::KS, PK = Cf::PK, PC = Cf::PC, PO = Cf::PO;
+    constexpr int NKS = Cf::NKS, NCK = Cf::NCK, NJB = Cf::NJB, BPW = Cf::BPW;
+    constexpr int VEC = Cf::VEC, KVEC = Cf::KVEC, PVEC = Cf::PVEC, NOV = Cf::NOV, OVEC = Cf::OVEC;
+    __shared__ DsSmem<OT, DK, DVS> sm;
+
+    const int tid = threadIdx.x, R = wave_id(), l = lane_id();
+    const int work = xcd_swizzle(blockIdx.x, gridDim.x);
+    const int chain = work / p.NS, slice = work % p.NS;
+    const int bb = chain / p.H, h = chain % p.H;
+    const int j0 = slice * DVS;
+    const long T = p.T, H = p.H, DV = p.DV;
+    const int NC = p.NC;
+    const OT* dO = (const OT*)p.dO + ((long)bb * T * H + h) * DV + j0;
+
+    f32x4 dS[BPW];
+#pragma unroll
+    for (int u = 0; u < BPW; ++u) {
+        const int bi = R * BPW + u, ib = bi / NJB, jb = bi % NJB;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float v = 0.f;
+            if (p.dST) v = p.dST[((long)chain * DK + 16 * ib + acc_row(e)) * DV + j0 + 16 * jb + acc_col()];
+            dS[u][e] = v;
+        }
+        store_acc_T(sm.dST, PK, 16 * jb, 16 * ib, dS[u]);
+    }
+
+    struct Buf {
+        typename FR::t K[NKS];
+        i32x4 Q[KVEC], Y[KVEC], P[PVEC], O[OVEC];
+        f32x4 g;
+    };
+    auto fetch = [&](Buf& b, int cc) __attribute__((always_inline)) {
+        const long cix = (long)chain * NC + cc;
+        const OT* Kc = (const OT*)p.wy.Kt + cix * C * DK;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) b.K[ks] = FR::gkc(Kc, DK, 16 * R, ks * KS);
+        const OT* Qc = (const OT*)p.wy.Qg + cix * C * DK;
+        const OT* Yc = (const OT*)p.wy.Yh + cix * C * DK;
+#pragma unroll
+        for (int m = 0; m < KVEC; ++m) {
+            b.Q[m] = *(const i32x4*)(Qc + (long)(tid + m * kThreads) * VEC);
+            b.Y[m] = *(const i32x4*)(Yc + (long)(tid + m * kThreads) * VEC);
+        }
+        const OT* Pc = (const OT*)p.wy.P + cix * C * C;
+#pragma unroll
+        for (int m = 0; m < PVEC; ++m) {
+            const int x = tid + m * kThreads;
+            if (x < C * C / VEC) b.P[m] = *(const i32x4*)(Pc + (long)x * VEC);
+        }
+#pragma unroll
+        for (int m = 0; m < OVEC; ++m) {
+            const int x = tid + m * kThreads;
+            const int rr = (x * VEC) / DVS, jj = (x * VEC) % DVS;
+            const long t = (long)cc * C + rr;
+            i32x4 z = {0, 0, 0, 0};
+            if (x < NOV && t < T) z = *(const i32x4*)(dO + t * H * DV + jj);
+            b.O[m] = z;
+        }
+        if (tid < DK / 4) b.g = *(const f32x4*)(p.wy.gam + cix * DK + 4 * tid);
+    };
+    auto chunk = [&](const Buf& cur, Buf& nxt, int c) __attribute__((always_inline)) {
+        // ---- stage the chunk's factors and dO slice, checkpoint dS' of this chunk
+#pragma unroll
+        for (int m = 0; m < KVEC; ++m) {
+            const int e0 = (tid + m * kThreads) * VEC;
+            *(i32x4*)(sm.Qt + (e0 / DK) * PK + e0 % DK) = cur.Q[m];
+            *(i32x4*)(sm.Yt + (e0 / DK) * PK + e0 % DK) = cur.Y[m];
+        }
+#pragma unroll
+        for (int m = 0; m < PVEC; ++m) {
+            const int x = tid + m * kThreads;
+            if (x < C * C / VEC) *(i32x4*)(sm.Pt + ((x * VEC) / C) * PC + (x * VEC) % C) = cur.P[m];
+        }
+#pragma unroll
+        for (int m = 0; m < OVEC; ++m) {
+            const int x = tid + m * kThreads;
+            if (x < NOV) *(i32x4*)(sm.dOt + ((x * VEC) / DVS) * PO + (x * VEC) % DVS) = cur.O[m];
+        }
+        if (tid < DK / 4) *(f32x4*)(sm.gam + 4 * tid) = cur.g;
+        if (c > 0) fetch(nxt, c - 1);
+        {
+            OT* dst = (OT*)p.dSx + (((long)chain * NC + c) * DV + j0) * DK;
+            constexpr int NSV = DVS * DK / VEC;
+#pragma unroll
+            for (int x0 = 0; x0 < NSV; x0 += kThreads) {
+                const int x = x0 + tid;
+                if (NSV % kThreads == 0 || x < NSV) {
+                    const int j = (x * VEC) / DK, i = (x * VEC) % DK;
+                    *(i32x4*)(dst + (long)j * DK + i) = *(const i32x4*)(sm.dST + j * PK + i);
+                }
+            }
+        }
+        lds_barrier();
+        // ---- dDelta = Ktilde dS' + P^T dO   (wave R: token block R)
+        {
+            f32x4 aD[NJB];
+#pragma unroll
+            for (int jb = 0; jb < NJB; ++jb) aD[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+                for (int jb = 0; jb < NJB; ++jb) MM::mma(aD[jb], cur.K[ks], FR::kc(sm.dST, PK, 16 * jb, ks * KS));
+#pragma unroll
+            for (int kk = 0; kk < NCK; ++kk) {
+                if (kk * KS + KS > 16 * R) {  // P^T is upper triangular: s >= r
+                    typename FR::t a = FR::tr(sm.Pt, PC, kk * KS, 16 * R);
+#pragma unroll
+                    for (int jb = 0; jb < NJB; ++jb) MM::mma(aD[jb], a, FR::tr(sm.dOt, PO, kk * KS, 16 * jb));
+                }
+            }
+#pragma unroll
+            for (int jb = 0; jb < NJB; ++jb) store_acc_T(sm.dDT, PC, 16 * jb, 16 * R, aD[jb]);
+        }
+        lds_barrier();
+        // ---- dS <- Diag(gamma) dS' + Qbar^T dO + (-Y)^T dDelta
+#pragma unroll
+        for (int u = 0; u < BPW; ++u) {
+            const int bi = R * BPW + u, ib = bi / NJB, jb = bi % NJB;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dS[u][e] *= sm.gam[16 * ib + acc_row(e)];
+#pragma unroll
+            for (int kk = 0; kk < NCK; ++kk) {
+                MM::mma(dS[u], FR::tr(sm.Qt, PK, kk * KS, 16 * ib), FR::tr(sm.dOt, PO, kk * KS, 16 * jb));
+                MM::mma(dS[u], FR::tr(sm.Yt, PK, kk * KS, 16 * ib), FR::kc(sm.dDT, PC, 16 * jb, kk * KS));
+            }
+            store_acc_T(sm.dST, PK, 16 * jb, 16 * ib, dS[u]);
+        }
+        lds_barrier();
+    };
+
+    Buf bA, bB;
+    if (NC > 0) fetch(bA, NC - 1);
+    lds_barrier();
+    for (int c = NC - 1; c >= 0; c -= 2) {
+        chunk(bA, bB, c);
+        if (c - 1 >= 0) chunk(bB, bA, c - 1);
+    }
+    if (p.dS0) {
+#pragma unroll
+        for (int u = 0; u < BPW; ++u) {
+            const int bi = R * BPW + u, ib = bi / NJB, jb = bi % NJB;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                p.dS0[((long)chain * DK + 16 * ib + acc_row(e)) * DV + j0 + 16 * jb + acc_col()] = dS[u][e];
+        }
+    }
+}
+
+template <typename OT, int DK, int DVS>
+static hipError_t launch_dstate(const BwdParams& p, hipStream_t s) {
+    const long nblk = (long)p.B * p.H * p.NS;
+    if (nblk == 0) return hipSuccess;
+    hipLaunchKernelGGL((gdr2_dstate_kernel<OT, DK, DVS>), dim3(nblk), dim3(kThreads), 0, s, p);
+    return hipGetLastError();
+}
+
+static hipError_t dstate_dispatch(int bf, int dk, int dvs, const BwdParams& p, hipStream_t s) {
+    if (bf) {
+        if (dk == 128 && dvs == 64) return launch_dstate<bf16, 128, 64>(p, s);
+        if (dk == 128 && dvs == 32) return launch_dstate<bf16, 128, 32>(p, s);
+        if (dk == 128 && dvs == 16) return launch_dstate<bf16, 128, 16>(p, s);
+        if (dk == 64 && dvs == 64) return launch_dstate<bf16, 64, 64>(p, s);
+        if (dk == 64 && dvs == 32) return launch_dstate<bf16, 64, 32>(p, s);
+        if (dk == 64 && dvs == 16) return launch_dstate<bf16, 64, 16>(p, s);
+    } else {
+        if (dk == 128 && dvs == 32) return launch_dstate<float, 128, 32>(p, s);
+        if (dk == 128 && dvs == 16) return launch_dstate<float, 128, 16>(p, s);
+        if (dk == 64 && dvs == 32) return launch_dstate<float, 64, 32>(p, s);
+        if (dk == 64 && dvs == 16) return launch_dstate<float, 64, 16>(p, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+// --------------------------------------------------------------------------------------------
+// Chunk gradients: one workgroup per (chain, chunk), all chunks in parallel.  Given the state S
+// entering the chunk (forward checkpoint), the gradient dS' of the state leaving it (state-carry
+// kernel above) and dO, it recomputes Delta, dDelta and dX for DVH value columns at a time and
+// reduces over the value columns in MFMA accumulators (held transposed, channel x token):
+//     R1 = S dO^T,  R2 = S dX^T,  R3 = dS' Delta^T,   R4 = dO Delta^T,  R5 = dX Delta^T,
+//     R6_i = sum_j dS'_ij S_ij.
+// dP = lower(R4) and dA = -strict_lower(R5) then meet the decay-absorbed key factors in the
+// blocked Gram gradients (same per-16-token-block references as the forward):
+//     G1 = dP Kbar,  G2 = dA Kbar,  G3 = dP^T Qbar + dA^T Ebar.
+// The epilogue runs with lane = token row: dq, dk, db, dv, dw, and dlog alpha as the in-chunk
+// reverse cumsum of dG (DPP suffix scan within 16-row blocks plus block suffix totals).
+template <typename OT, int DK, int DV, int DVH>
+struct BgCfg {
+    static constexpr int C = kChunk;
+    static constexpr int KS = Mfma<OT>::KS, KPL = Mfma<OT>::KPL;
+    static constexpr int ES = (int)sizeof(OT);
+    static constexpr int PAD = 16 / ES;
+    static constexpr int PK = DK + PAD, PC = C + PAD, PH = DVH + PAD;
+    static constexpr int NKS = DK / KS, NCK = C / KS, NIB = DK / 16, NJH = DVH / 16;
+    static constexpr int NCH = NKS * KPL;
+    static constexpr int VEC = 16 / ES;
+    static constexpr int NSV = DVH * DK / VEC;   // [DVH][DK] tile, vectors
+    static constexpr int NOV = C * DVH / VEC;    // [C][DVH] tile, vectors
+};
+
+template <typename OT, int DK, int DV, int DVH>
+struct alignas(16) BgSmem {
+    using Cf = BgCfg<OT, DK, DV, DVH>;
+    union {
+        struct {  // value-column phase
+            OT Tt[kChunk * Cf::PC];    // T                   [r][s]
+            OT Pt[kChunk * Cf::PC];    // P                   [r][s]
+            OT St[DVH * Cf::PK];       // S^T block           [j][i]
+            OT dSt[DVH * Cf::PK];      // dS'^T block         [j][i]
+            OT dOt[kChunk * Cf::PH];   // dO block            [r][j]
+            OT DlT[DVH * Cf::PC];      // Delta^T             [j][r]
+            OT dDT[DVH * Cf::PC];      // dDelta^T            [j][r]
+            OT dXt[kChunk * Cf::PH];   // dX block            [r][j]
+        } j;
+        struct {  // Gram-gradient phase
+            OT Kb[kChunk * Cf::PK];    // k . exp(ref_S - G)  [s][i]
+            OT Qb[kChunk * Cf::PK];    // q . exp(G - ref_R)  [r][i]
+            OT Eb[kChunk * Cf::PK];    // e . exp(G - ref_R)  [r][i]
+            OT dPT[kChunk * Cf::PC];   // dP^T                [s][r]
+            OT dAT[kChunk * Cf::PC];   // dA^T                [s][r]
+        } g;
+    } u;
+    float tot[4][DK];
+    float ctab[6][DK];
+    float gRt[4][DK];
+    float hRt[4][DK];
+    float r6[DK];
+    float btot[4][DK];
+    float ktot[4][DK];
+};
+
+template <typename OT, int DK, int DV, int DVH>
+__global__ __launch_bounds__(kThreads, 1) void gdr2_bgrad_kernel(BwdParams p) {
+    using Cf = BgCfg<OT, DK, DV, DVH>;
+    using MM = Mfma<OT>;
+    using FR = Frag<OT>;
+    constexpr int C = kChunk, KS = Cf::KS, KPL = Cf::KPL, PK = Cf::PK, PC = Cf::PC, PH = Cf::PH;
+    constexpr int NKS = Cf::NKS, NCK = Cf::NCK, NIB = Cf::NIB, NJH = Cf::NJH, NCH = Cf::NCH;
+    constexpr int VEC = Cf::VEC, NSV = Cf::NSV, NOV = Cf::NOV;
+    __shared__ BgSmem<OT, DK, DV, DVH> sm;
+
+    const int tid = threadIdx.x, R = wave_id(), l = lane_id(), rl = l & 15, g = l >> 4;
+    const int NC = p.NC;
+    const int chain = blockIdx.x / NC, c = blockIdx.x % NC;
+    const int bb = chain / p.H, h = chain % p.H;
+    const long T = p.T, H = p.H;
+    const long cix = (long)chain * NC + c;
+    const int r = 16 * R + rl;
+    const long t = (long)c * C + r;
+    const bool valid = t < T;
+    const long row = ((long)bb * T + (valid ? t : T - 1)) * H + h;
+
+    // ---------------- decay tables (lane = token row r, channels ks*KS + KPL*g + j)
+    {
+        float lv[NCH];
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) load_lane_f32<OT>(p.la + row * DK, ks, g, lv + ks * KPL);
+#pragma unroll
+        for (int n = 0; n < NCH; ++n) lv[n] = row_scan16(valid ? lv[n] : 0.f);
+        if (rl == 15) {
+#pragma unroll
+            for (int n = 0; n < NCH; ++n) sm.tot[R][(n / KPL) * KS + KPL * g + n % KPL] = lv[n];
+        }
+        const OT* Tc = (const OT*)p.wy.Tm + cix * C * C;
+        const OT* Pc = (const OT*)p.wy.P + cix * C * C;
+        for (int x = tid; x < C * C / VEC; x += kThreads) {
+            const int rr = (x * VEC) / C, ss = (x * VEC) % C;
+            *(i32x4*)(sm.u.j.Tt + rr * PC + ss) = *(const i32x4*)(Tc + (long)x * VEC);
+            *(i32x4*)(sm.u.j.Pt + rr * PC + ss) = *(const i32x4*)(Pc + (long)x * VEC);
+        }
+        if (tid < DK) sm.r6[tid] = 0.f;
+        lds_barrier();
+        for (int chn = tid; chn < DK; chn += kThreads) {
+            float refs[4], run = 0.f;
+#pragma unroll
+            for (int Rp = 0; Rp < 4; ++Rp) {
+                refs[Rp] = run;
+                run += sm.tot[Rp][chn];
+            }
+#pragma unroll
+            for (int Rp = 0; Rp < 4; ++Rp) {
+                sm.gRt[Rp][chn] = __expf(refs[Rp]);
+                sm.hRt[Rp][chn] = __expf(run - refs[Rp]);
+#pragma unroll
+                for (int S = 0; S < Rp; ++S) sm.ctab[Rp * (Rp - 1) / 2 + S][chn] = __expf(refs[Rp] - refs[S]);
+            }
+        }
+    }
+
+    // ---------------- value-column blocks: Delta, dDelta, dX, dv, dw and the reductions
+    typename FR::t Yf[NKS], Kf[NKS];
+    {
+        const OT* Yc = (const OT*)p.wy.Yh + cix * C * DK;
+        const OT* Kc = (const OT*)p.wy.Kt + cix * C * DK;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            Yf[ks] = FR::gkc(Yc, DK, 16 * R, ks * KS);
+            Kf[ks] = FR::gkc(Kc, DK, 16 * R, ks * KS);
+        }
+    }
+    f32x4 A1[NIB], A2[NIB], A3[NIB], A4[NIB];  // R1, R2, R3 (channel x token), then G3
+    f32x4 R4[4], R5[4];                         // dO Delta^T, dX Delta^T (token x token)
+#pragma unroll
+    for (int ib = 0; ib < NIB; ++ib) A1[ib] = A2[ib] = A3[ib] = A4[ib] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int S = 0; S < 4; ++S) R4[S] = R5[S] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const OT* Sx = (const OT*)p.states + cix * DV * DK;
+    const OT* dSxp = (const OT*)p.dSx + cix * DV * DK;
+    const long tok0 = ((long)bb * T + (long)c * C) * H + h;  // token row of the chunk's first token
+    const int kbeg = (16 * R / KS) * KS;                      // first k-step touching tokens >= 16R
+
+    for (int jq = 0; jq < DV / DVH; ++jq) {
+        const int jb0 = jq * DVH;
+        lds_barrier();  // previous block's readers are done
+        for (int x = tid; x < NSV; x += kThreads) {
+            const int jj = (x * VEC) / DK, i = (x * VEC) % DK;
+            *(i32x4*)(sm.u.j.St + jj * PK + i) = *(const i32x4*)(Sx + (long)(jb0 + jj) * DK + i);
+            *(i32x4*)(sm.u.j.dSt + jj * PK + i) = *(const i32x4*)(dSxp + (long)(jb0 + jj) * DK + i);
+        }
+        for (int x = tid; x < NOV; x += kThreads) {
+            const int rr = (x * VEC) / DVH, jj = (x * VEC) % DVH;
+            i32x4 z = {0, 0, 0, 0};
+            if ((long)c * C + rr < T) z = *(const i32x4*)((const OT*)p.dO + (tok0 + (long)rr * H) * DV + jb0 + jj);
+            *(i32x4*)(sm.u.j.dOt + rr * PH + jj) = z;
+        }
+        lds_barrier();
+        // Delta = U - Y S and dDelta = Ktilde dS' + P^T dO for token block R
+        {
+            const OT* Uc = (const OT*)p.wy.U + cix * C * DV;
+#pragma unroll
+            for (int jb = 0; jb < NJH; ++jb) {
+                f32x4 aD = Raw4<OT>::widen(*(const typename Raw4<OT>::t*)(Uc + ((long)(R * (DV / 16) + jb0 / 16 + jb) * 64 + l) * 4));
+                f32x4 adD = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+                    MM::mma(aD, Yf[ks], FR::kc(sm.u.j.St, PK, 16 * jb, ks * KS));
+                    MM::mma(adD, Kf[ks], FR::kc(sm.u.j.dSt, PK, 16 * jb, ks * KS));
+                }
+                for (int k0 = kbeg; k0 < C; k0 += KS)
+                    MM::mma(adD, FR::tr(sm.u.j.Pt, PC, k0, 16 * R), FR::tr(sm.u.j.dOt, PH, k0, 16 * jb));
+                store_acc_T(sm.u.j.DlT, PC, 16 * jb, 16 * R, aD);
+                store_acc_T(sm.u.j.dDT, PC, 16 * jb, 16 * R, adD);
+            }
+        }
+        lds_barrier();
+        // dX^T = dDelta^T T  (this wave: tokens r of block R); dv = dX . w, dw = dX . v
+#pragma unroll
+        for (int jb = 0; jb < NJH; ++jb) {
+            f32x4 ax = {0.f, 0.f, 0.f, 0.f};
+            for (int k0 = kbeg; k0 < C; k0 += KS)
+                MM::mma(ax, FR::kc(sm.u.j.dDT, PC, 16 * jb, k0), FR::tr(sm.u.j.Tt, PC, k0, 16 * R));
+            // lane: token r, value columns jb0 + 16jb + 4g .. +3
+            const int jc = 16 * jb + 4 * g;
+            store4(sm.u.j.dXt + r * PH + jc, ax);
+            if (valid) {
+                const long o = (tok0 + (long)r * H) * DV + jb0 + jc;
+                const f32x4 wv = load4((const OT*)p.w + o), vv = load4((const OT*)p.v + o);
+                store4((OT*)p.dv + o, ax * wv);
+                store4((OT*)p.dw + o, ax * vv);
+            }
+        }
+        lds_barrier();
+        // reductions over this block of value columns
+#pragma unroll
+        for (int k0 = 0; k0 < DVH; k0 += KS) {
+            const typename FR::t bO = FR::kc(sm.u.j.dOt, PH, 16 * R, k0);   // dO   (col r, k = j)
+            const typename FR::t bX = FR::kc(sm.u.j.dXt, PH, 16 * R, k0);   // dX   (col r, k = j)
+            const typename FR::t bD = FR::tr(sm.u.j.DlT, PC, k0, 16 * R);   // Delta(col r, k = j)
+#pragma unroll
+            for (int ib = 0; ib < NIB; ++ib) {
+                const typename FR::t aS = FR::tr(sm.u.j.St, PK, k0, 16 * ib);   // S   (row i, k = j)
+                const typename FR::t adS = FR::tr(sm.u.j.dSt, PK, k0, 16 * ib); // dS' (row i, k = j)
+                MM::mma(A1[ib], aS, bO);
+                MM::mma(A2[ib], aS, bX);
+                MM::mma(A3[ib], adS, bD);
+            }
+            const typename FR::t aO = FR::kc(sm.u.j.dOt, PH, 16 * R, k0);   // dO (row r, k = j)
+            const typename FR::t aX = FR::kc(sm.u.j.dXt, PH, 16 * R, k0);   // dX (row r, k = j)
+#pragma unroll
+            for (int S = 0; S < 4; ++S) {
+                if (S <= R) {
+                    const typename FR::t bDs = FR::tr(sm.u.j.DlT, PC, k0, 16 * S);  // Delta (col s, k = j)
+                    MM::mma(R4[S], aO, bDs);
+                    MM::mma(R5[S], aX, bDs);
+                }
+            }
+        }
+        if (tid < DK) {
+            float acc = 0.f;
+            for (int jj = 0; jj < DVH; ++jj)
+                acc += to_f(sm.u.j.dSt[jj * PK + tid]) * to_f(sm.u.j.St[jj * PK + tid]);
+            sm.r6[tid] += acc;
+        }
+    }
+    lds_barrier();
+
+    // ---------------- decay-absorbed key tiles for the Gram gradients (the value tiles are dead)
+    {
+        float qv[NCH], kv[NCH], bv[NCH], lv[NCH];
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            load_lane<OT>((const OT*)p.q + row * DK, ks, g, qv + ks * KPL);
+            load_lane<OT>((const OT*)p.k + row * DK, ks, g, kv + ks * KPL);
+            load_lane<OT>((const OT*)p.b + row * DK, ks, g, bv + ks * KPL);
+            load_lane_f32<OT>(p.la + row * DK, ks, g, lv + ks * KPL);
+        }
+        if (!valid) {
+#pragma unroll
+            for (int n = 0; n < NCH; ++n) qv[n] = kv[n] = bv[n] = lv[n] = 0.f;
+        }
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            float eb[KPL], qb[KPL], kb[KPL];
+#pragma unroll
+            for (int j = 0; j < KPL; ++j) {
+                const int n = ks * KPL + j;
+                const float sc = row_scan16(lv[n]);
+                const float x = __expf(sc), y = __expf(-sc);
+                eb[j] = bv[n] * kv[n] * x;
+                qb[j] = qv[n] * x;
+                kb[j] = kv[n] * y;
+            }
+            store_lane<OT>(sm.u.g.Eb + r * PK, ks, g, eb);
+            store_lane<OT>(sm.u.g.Qb + r * PK, ks, g, qb);
+            store_lane<OT>(sm.u.g.Kb + r * PK, ks, g, kb);
+        }
+    }
+    // ---------------- dP^T, dA^T tiles (token x token), then the blocked Gram gradients
+#pragma unroll
+    for (int S = 0; S < 4; ++S) {
+        f32x4 pm = {0.f, 0.f, 0.f, 0.f}, am = {0.f, 0.f, 0.f, 0.f};
+        if (S <= R) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int rr = 16 * R + acc_row(e), ss = 16 * S + acc_col();
+                pm[e] = ss <= rr ? R4[S][e] : 0.f;
+                am[e] = ss < rr ? -R5[S][e] : 0.f;
+            }
+        }
+        store_acc_T(sm.u.g.dPT, PC, 16 * S, 16 * R, pm);
+        store_acc_T(sm.u.g.dAT, PC, 16 * S, 16 * R, am);
+    }
+    lds_barrier();
+    // A1 <- exp(ref_R) . R1 + dP Kbar ; A2 <- -exp(ref_R) . R2 + dA Kbar   (channel x token r)
+#pragma unroll
+    for (int ib = 0; ib < NIB; ++ib) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float gr = sm.gRt[R][16 * ib + acc_row(e)];
+            A1[ib][e] *= gr;
+            A2[ib][e] *= -gr;
+        }
+    }
+    for (int k0 = 0; k0 < 16 * R + 16; k0 += KS) {
+        const typename FR::t bP = FR::tr(sm.u.g.dPT, PC, k0, 16 * R);  // dP (col r, k = s)
+        const typename FR::t bA = FR::tr(sm.u.g.dAT, PC, k0, 16 * R);  // dA (col r, k = s)
+        const int Sl = (k0 + KPL * g) / 16;                             // token block of this lane's k
+#pragma unroll
+        for (int ib = 0; ib < NIB; ++ib) {
+            typename FR::t a = FR::tr(sm.u.g.Kb, PK, k0, 16 * ib);          // Kbar^T (row i, k = s)
+            if (Sl < R) {
+                const float cs = sm.ctab[R * (R - 1) / 2 + Sl][16 * ib + rl];
+                a = FR::scale(a, cs);
+            }
+            MM::mma(A1[ib], a, bP);
+            MM::mma(A2[ib], a, bA);
+        }
+    }
+    // A4 <- dP^T Qbar + dA^T Ebar (channel x token s, s in block R)
+    for (int k0 = (16 * R / KS) * KS; k0 < C; k0 += KS) {
+        const typename FR::t bP = FR::kc(sm.u.g.dPT, PC, 16 * R, k0);  // dP (col s, k = r)
+        const typename FR::t bA = FR::kc(sm.u.g.dAT, PC, 16 * R, k0);  // dA (col s, k = r)
+        const int Rl = (k0 + KPL * g) / 16;
+#pragma unroll
+        for (int ib = 0; ib < NIB; ++ib) {
+            typename FR::t aq = FR::tr(sm.u.g.Qb, PK, k0, 16 * ib);         // Qbar^T (row i, k = r)
+            typename FR::t ae = FR::tr(sm.u.g.Eb, PK, k0, 16 * ib);         // Ebar^T (row i, k = r)
+            if (Rl > R) {
+                const float cs = sm.ctab[Rl * (Rl - 1) / 2 + R][16 * ib + rl];
+                aq = FR::scale(aq, cs);
+                ae = FR::scale(ae, cs);
+            }
+            MM::mma(A4[ib], aq, bP);
+            MM::mma(A4[ib], ae, bA);
+        }
+    }
+
+    // ---------------- epilogue: lane = token r (block R), channels 16 ib + 4 g + e
+    {
+        const OT* qr = (const OT*)p.q + row * DK;
+        const OT* kr = (const OT*)p.k + row * DK;
+        const OT* br = (const OT*)p.b + row * DK;
+        const float* lr = p.la + row * DK;
+        f32x4 dG[NIB], kdk[NIB], dqv[NIB], dkv[NIB], dbv[NIB];
+#pragma unroll
+        for (int ib = 0; ib < NIB; ++ib) {
+            const int i0 = 16 * ib + 4 * g;
+            f32x4 q4 = load4(qr + i0), k4 = load4(kr + i0), b4 = load4(br + i0), l4 = *(const f32x4*)(lr + i0);
+            if (!valid) q4 = k4 = b4 = l4 = f32x4{0.f, 0.f, 0.f, 0.f};
+            const f32x4 gr = *(const f32x4*)(&sm.gRt[R][i0]);
+            const f32x4 hr = *(const f32x4*)(&sm.hRt[R][i0]);
+            (void)gr;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float sc = row_scan16(l4[e]);  // G_r - ref_R
+                const float x = __expf(sc), y = __expf(-sc);
+                const float dq = x * A1[ib][e];
+                const float de = x * A2[ib][e];
+                const float dkb = y * A4[ib][e];
+                const float dkt = hr[e] * y * A3[ib][e];
+                const float ee = b4[e] * k4[e];
+                dqv[ib][e] = dq;
+                dkv[ib][e] = dkb + dkt + b4[e] * de;
+                dbv[ib][e] = k4[e] * de;
+                dG[ib][e] = q4[e] * dq + ee * de - k4[e] * (dkb + dkt);
+                kdk[ib][e] = k4[e] * dkt;
+            }
+        }
+        // suffix sums over the 16 tokens of the block; block totals to LDS
+#pragma unroll
+        for (int ib = 0; ib < NIB; ++ib) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                dG[ib][e] = row_rscan16(dG[ib][e]);
+                kdk[ib][e] = row_rscan16(kdk[ib][e]);
+            }
+            if (rl == 0) {
+                *(f32x4*)(&sm.btot[R][16 * ib + 4 * g]) = dG[ib];
+                *(f32x4*)(&sm.ktot[R][16 * ib + 4 * g]) = kdk[ib];
+            }
+        }
+        lds_barrier();
+        if (valid) {
+            const long o = row * DK;
+#pragma unroll
+            for (int ib = 0; ib < NIB; ++ib) {
+                const int i0 = 16 * ib + 4 * g;
+                f32x4 dl = dG[ib];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float add = sm.r6[i0 + e] * sm.hRt[0][i0 + e];  // dgamma . gamma
+#pragma unroll
+                    for (int Rp = 0; Rp < 4; ++Rp) {
+                        add += sm.ktot[Rp][i0 + e];
+                        if (Rp > R) add += sm.btot[Rp][i0 + e];
+                    }
+                    dl[e] += add;
+                }
+                store4((OT*)p.dq + o + i0, dqv[ib]);
+                store4((OT*)p.dk + o + i0, dkv[ib]);
+                store4((OT*)p.db + o + i0, dbv[ib]);
+                *(f32x4*)(p.dla + o + i0) = dl;
+            }
+        }
+    }
+}
+
+template <typename OT, int DK, int DV>
+static hipError_t launch_bgrad(const BwdParams& p, hipStream_t s) {
+    const long nblk = (long)p.B * p.H * p.NC;
+    if (nblk == 0) return hipSuccess;
+    hipLaunchKernelGGL((gdr2_bgrad_kernel<OT, DK, DV, 32>), dim3(nblk), dim3(kThreads), 0, s, p);
+    return hipGetLastError();
+}
+
+static hipError_t bgrad_dispatch(int bf, int dk, int dv, const BwdParams& p, hipStream_t s) {
+    if (bf) {
+        if (dk == 128 && dv == 128) return launch_bgrad<bf16, 128, 128>(p, s);
+        if (dk == 128 && dv == 64) return launch_bgrad<bf16, 128, 64>(p, s);
+        if (dk == 64 && dv == 128) return launch_bgrad<bf16, 64, 128>(p, s);
+        if (dk == 64 && dv == 64) return launch_bgrad<bf16, 64, 64>(p, s);
+    } else {
+        if (dk == 128 && dv == 128) return launch_bgrad<float, 128, 128>(p, s);
+        if (dk == 128 && dv == 64) return launch_bgrad<float, 128, 64>(p, s);
+        if (dk == 64 && dv == 128) return launch_bgrad<float, 64, 128>(p, s);
+        if (dk == 64 && dv == 64) return launch_bgrad<float, 64, 64>(p, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t bwd_dispatch(int bf, int dk, int dv, const BwdParams& p, hipStream_t s) {
+    const int dvs = (int)(dv / p.NS);
+    hipError_t e = dstate_dispatch(bf, dk, dvs, p, s);
+    if (e != hipSuccess) return e;
+    if (p.NC == 0) return hipSuccess;
+    return bgrad_dispatch(bf, dk, dv, p, s);
+}
+
 }  // namespace gdr2

@@ -214,6 +214,12 @@ template <> struct Frag<bf16> {
         for (int j = 0; j < 8; ++j) r[j] = (bf16)((float)x[j] * s[j]);
         return r;
     }
+    static __device__ __forceinline__ t scale(const t& x, float s) {
+        t r;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) r[j] = (bf16)((float)x[j] * s);
+        return r;
+    }
 };
 template <> struct Frag<float> {
     typedef float t;
@@ -231,7 +237,22 @@ template <> struct Frag<float> {
     }
     static __device__ __forceinline__ t from_f32(const float* v) { return v[0]; }
     static __device__ __forceinline__ t scale(const t& x, const float* s) { return x * s[0]; }
+    static __device__ __forceinline__ t scale(const t& x, float s) { return x * s; }
 };
+
+// Inclusive suffix sum over the 16 lanes of each DPP row: lane i gets the sum of lanes i..15.
+__device__ __forceinline__ float row_rscan16(float x) {
+    int v = __builtin_bit_cast(int, x);
+    float y;
+    y = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, v, 0x101, 0xf, 0xf, false));
+    x += y; v = __builtin_bit_cast(int, x);
+    y = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, v, 0x102, 0xf, 0xf, false));
+    x += y; v = __builtin_bit_cast(int, x);
+    y = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, v, 0x104, 0xf, 0xf, false));
+    x += y; v = __builtin_bit_cast(int, x);
+    y = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, v, 0x108, 0xf, 0xf, false));
+    return x + y;
+}
 
 // Inclusive prefix sum over the 16 lanes of each DPP row (lanes 16g .. 16g+15).
 __device__ __forceinline__ float row_scan16(float x) {

@@ -1,0 +1,191 @@
+"""GPU parity of the gate-aware backward (and the forward it depends on) against the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+from gated_delta_rule_gdr_amd import gdr2_bwd_chunked, gdr2_fwd_chunked
+from gated_delta_rule_gdr_amd.inputs import config_inputs, layer_inputs, strong_decay_inputs, to_f64
+from oracle import oracle as orc
+from tests._util import TOL, announce, assert_close, to_np
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+GRADS = ("dq", "dk", "dv", "dlog_alpha", "db", "dw", "dS0")
+
+
+def _gpu(x):
+    return {n: (None if t is None else t.to(DEV)) for n, t in x.items()}
+
+
+def _run(x):
+    g = _gpu(x)
+    o, ST, ws = gdr2_fwd_chunked(g["q"], g["k"], g["v"], g["log_alpha"], g["b"], g["w"], S0=g["S0"])
+    gr = gdr2_bwd_chunked(g["q"], g["k"], g["v"], g["log_alpha"], g["b"], g["w"], g["dO"], ws,
+                          dS_T=g.get("dST"))
+    torch.cuda.synchronize()
+    return o, ST, gr
+
+
+def _oracle(x):
+    f = to_f64(x)
+    ro, rS = orc.forward(f["q"], f["k"], f["v"], f["log_alpha"], f["b"], f["w"], f["S0"])
+    rg = orc.backward(f["q"], f["k"], f["v"], f["log_alpha"], f["b"], f["w"], f["dO"], S0=f["S0"],
+                      dST=f.get("dST"))
+    return ro, rS, rg
+
+
+def _check(x, tol, tag):
+    announce(tag)
+    o, ST, gr = _run(x)
+    ro, rS, rg = _oracle(x)
+    errs = {"o": assert_close(f"{tag} o", to_np(o), ro, tol),
+            "S_T": assert_close(f"{tag} S_T", to_np(ST), rS, tol)}
+    for n in GRADS:
+        errs[n] = assert_close(f"{tag} {n}", to_np(gr[n]), rg[n], tol)
+    print("  " + tag + ": " + "  ".join(f"{k} {v:.1e}" for k, v in errs.items()), flush=True)
+
+
+@pytest.mark.parametrize("T", [1, 37, 64, 65, 130])
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 128), (128, 64), (64, 64)])
+def test_bwd_bf16_shapes(T, dk, dv):
+    x = layer_inputs(2, T, 3, dk, dv, dtype="bf16", seed=300 + T + dk + dv, s0_std=0.05, dST=True)
+    _check(x, TOL["bf16"], f"bwd bf16 T={T} dk={dk} dv={dv}")
+
+
+@pytest.mark.parametrize("T,dk,dv", [(1, 64, 64), (100, 64, 64), (130, 64, 128), (256, 64, 64),
+                                     (200, 128, 128), (65, 128, 64)])
+def test_bwd_fp32_shapes(T, dk, dv):
+    x = layer_inputs(2, T, 2, dk, dv, dtype="f32", seed=400 + T + dk, s0_std=0.05, dST=True)
+    _check(x, TOL["f32"], f"bwd f32 T={T} dk={dk} dv={dv}")
+
+
+def test_bwd_pr1_fp32_workload():
+    """The fp32 reference workload shape (B=1, H=1, T=256, d=64), with a backward."""
+    c = dict(B=1, T=256, H=1, dk=64, dv=64)
+    x = layer_inputs(**c, dtype="f32", seed=1000)
+    _check(x, TOL["f32"], "bwd pr1 fp32")
+
+
+def test_bwd_many_chains():
+    """Enough chains that the state-gradient carry uses wide value slices."""
+    x = layer_inputs(4, 130, 64, 128, 128, dtype="bf16", seed=7, dST=True)
+    _check(x, TOL["bf16"], "bwd bf16 B=4 H=64")
+
+
+def test_bwd_strong_decay():
+    x = strong_decay_inputs(1, 192, 2, 128, 128, dtype="bf16", seed=11, floor=-5.0)
+    x["dST"] = torch.randn(x["q"].shape[0], 2, 128, 128, generator=torch.Generator().manual_seed(3))
+    _check(x, TOL["bf16"], "bwd bf16 strong decay")
+    x = strong_decay_inputs(1, 192, 2, 64, 64, dtype="f32", seed=12, floor=-5.0)
+    _check(x, TOL["f32"], "bwd f32 strong decay")
+
+
+def test_bwd_layer_1p3b_sampled_chains():
+    """Model-shaped 1.3B layer (B=4, T=4096, H=16, d=128) in the launch configuration the bench
+    times; the oracle recomputes forward and backward of two whole (b, h) chains."""
+    x = config_inputs("layer_1p3b")
+    announce("layer_1p3b fwd+bwd full size")
+    o, ST, gr = _run(x)
+    f = to_f64(x)
+    for (b, h) in [(0, 0), (3, 15)]:
+        sub = {n: (None if a is None else a[b:b + 1, :, h:h + 1]) for n, a in f.items()
+               if n in ("q", "k", "v", "log_alpha", "b", "w", "dO")}
+        ro, _ = orc.forward(sub["q"], sub["k"], sub["v"], sub["log_alpha"], sub["b"], sub["w"])
+        rg = orc.backward(sub["q"], sub["k"], sub["v"], sub["log_alpha"], sub["b"], sub["w"],
+                          sub["dO"])
+        assert_close(f"o ({b},{h})", to_np(o[b:b + 1, :, h:h + 1]), ro, TOL["bf16"])
+        for n in ("dq", "dk", "dv", "dlog_alpha", "db", "dw"):
+            e = assert_close(f"{n} ({b},{h})", to_np(gr[n][b:b + 1, :, h:h + 1]), rg[n], TOL["bf16"])
+            print(f"  {n} ({b},{h}) {e:.2e}", flush=True)
+        assert_close(f"dS0 ({b},{h})", to_np(gr["dS0"][b:b + 1, h:h + 1]), rg["dS0"], TOL["bf16"])
+
+
+def test_bwd_long_context_sampled_chain():
+    """Long context (B=1, T=32768, H=16, d=128) with S0 ~ N(0, 0.02^2), returning the final state;
+    the oracle recomputes one whole chain."""
+    x = config_inputs("long_ctx")
+    announce("long_ctx fwd+bwd full size")
+    o, ST, gr = _run(x)
+    f = to_f64(x)
+    h = 5
+    sub = {n: (None if a is None else a[:, :, h:h + 1]) for n, a in f.items()
+           if n in ("q", "k", "v", "log_alpha", "b", "w", "dO")}
+    s0 = f["S0"][:, h:h + 1]
+    ro, rS = orc.forward(sub["q"], sub["k"], sub["v"], sub["log_alpha"], sub["b"], sub["w"], s0)
+    rg = orc.backward(sub["q"], sub["k"], sub["v"], sub["log_alpha"], sub["b"], sub["w"], sub["dO"],
+                      S0=s0)
+    assert_close("o", to_np(o[:, :, h:h + 1]), ro, TOL["bf16"])
+    assert_close("S_T", to_np(ST[:, h:h + 1]), rS, TOL["bf16"])
+    for n in ("dq", "dk", "dv", "dlog_alpha", "db", "dw"):
+        e = assert_close(n, to_np(gr[n][:, :, h:h + 1]), rg[n], TOL["bf16"])
+        print(f"  {n} {e:.2e}", flush=True)
+    assert_close("dS0", to_np(gr["dS0"][:, h:h + 1]), rg["dS0"], TOL["bf16"])
+
+
+@pytest.mark.parametrize("variant", ["tied_kda", "tied_gdn", "tied_la"])
+def test_tied_gate_reductions(variant):
+    """Tied-gate sweep (B=2, T=2048, H=16, d=128): the forward must match the reduced rule's own
+    oracle (KDA, Gated DeltaNet, or the linear-attention closed form), and the gradients of the
+    tied parameters (sum of db and dw for beta; sum of dlog alpha for a scalar decay) must match
+    the main oracle's, on sampled chains."""
+    x = config_inputs(variant)
+    announce(variant)
+    o, ST, gr = _run(x)
+    f = to_f64(x)
+    for (b, h) in [(0, 3), (1, 12)]:
+        sub = {n: (None if a is None else a[b:b + 1, :, h:h + 1]) for n, a in f.items()
+               if n in ("q", "k", "v", "log_alpha", "b", "w", "dO")}
+        if variant == "tied_la":
+            ro, rS = orc.la_closed_form(sub["q"], sub["k"], sub["v"])
+        else:
+            beta = sub["b"][..., 0]
+            ro, rS = orc.kda_forward(sub["q"], sub["k"], sub["v"], sub["log_alpha"], beta,
+                                     scalar_decay=(variant == "tied_gdn"))
+        assert_close(f"{variant} o ({b},{h})", to_np(o[b:b + 1, :, h:h + 1]), ro, TOL["bf16"])
+        assert_close(f"{variant} S_T ({b},{h})", to_np(ST[b:b + 1, h:h + 1]), rS, TOL["bf16"])
+        rg = orc.backward(sub["q"], sub["k"], sub["v"], sub["log_alpha"], sub["b"], sub["w"],
+                          sub["dO"])
+        for n in ("dq", "dk", "dv"):
+            assert_close(f"{variant} {n}", to_np(gr[n][b:b + 1, :, h:h + 1]), rg[n], TOL["bf16"])
+        gb = to_np(gr["db"][b:b + 1, :, h:h + 1]).sum(-1) + to_np(gr["dw"][b:b + 1, :, h:h + 1]).sum(-1)
+        rb = rg["db"].sum(-1) + rg["dw"].sum(-1)
+        assert_close(f"{variant} dbeta", gb, rb, TOL["bf16"])
+        gl = to_np(gr["dlog_alpha"][b:b + 1, :, h:h + 1])
+        if variant == "tied_gdn":
+            assert_close(f"{variant} dlog_alpha (scalar)", gl.sum(-1), rg["dlog_alpha"].sum(-1), TOL["bf16"])
+        else:
+            assert_close(f"{variant} dlog_alpha", gl, rg["dlog_alpha"], TOL["bf16"])
+
+
+def test_bwd_split_sequence_handoff():
+    """Forward and backward over [0, t1) and [t1, T) with S_T -> S0 and dS0 -> dS_T hand-off equal
+    one pass over [0, T) (t1 not a multiple of the chunk)."""
+    x = layer_inputs(1, 300, 2, 128, 128, dtype="bf16", seed=21, s0_std=0.05)
+    announce("split hand-off")
+    g = _gpu(x)
+    o, ST, gr = _run(x)
+    t1 = 141
+    part = lambda a, sl: a[:, sl].contiguous()
+    A = {n: (part(g[n], slice(0, t1)) if n not in ("S0", "dST") else g[n]) for n in g}
+    Bp = {n: (part(g[n], slice(t1, None)) if n not in ("S0", "dST") else g[n]) for n in g}
+    oA, SA, wsA = gdr2_fwd_chunked(A["q"], A["k"], A["v"], A["log_alpha"], A["b"], A["w"], S0=A["S0"])
+    oB, SB, wsB = gdr2_fwd_chunked(Bp["q"], Bp["k"], Bp["v"], Bp["log_alpha"], Bp["b"], Bp["w"], S0=SA)
+    gB = gdr2_bwd_chunked(Bp["q"], Bp["k"], Bp["v"], Bp["log_alpha"], Bp["b"], Bp["w"], Bp["dO"], wsB)
+    gA = gdr2_bwd_chunked(A["q"], A["k"], A["v"], A["log_alpha"], A["b"], A["w"], A["dO"], wsA,
+                          dS_T=gB["dS0"])
+    torch.cuda.synchronize()
+    assert_close("o", to_np(torch.cat([oA, oB], 1)), to_np(o), TOL["bf16"])
+    assert_close("S_T", to_np(SB), to_np(ST), TOL["bf16"])
+    for n in ("dq", "dk", "dv", "dlog_alpha", "db", "dw"):
+        assert_close(n, to_np(torch.cat([gA[n], gB[n]], 1)), to_np(gr[n]), TOL["bf16"])
+    assert_close("dS0", to_np(gA["dS0"]), to_np(gr["dS0"]), TOL["bf16"])
+
+
+def test_bwd_deterministic():
+    """Two runs give bitwise identical results (no floating-point atomics)."""
+    x = layer_inputs(2, 200, 4, 128, 128, dtype="bf16", seed=31, dST=True)
+    announce("determinism")
+    _, _, g1 = _run(x)
+    _, _, g2 = _run(x)
+    for n in GRADS:
+        assert torch.equal(g1[n], g2[n]), n
