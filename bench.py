@@ -1,0 +1,206 @@
+"""Benchmark: Gated Delta Rule-2 layer, forward + gate-aware backward, on one MI355X.
+
+One step = one pass of the whole chunked hot path over one batch of the model-shaped 1.3B layer
+(B=4, T=4096, H=16, d_k=d_v=128, bf16 q/k/v/b/w, fp32 log-decay and state): the WY-factor
+kernel, the forward state carry (o), the backward state-gradient carry and the chunk-gradient
+kernel, in that order on one stream.  Inputs are synthetic (seeded), already resident in HBM when
+the timed region starts.  Prints one JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GDR-2 fwd+bwd Mtokens/s (H=16,d=128,T=4K) on 1 MI355X; % MFMA/HBM roofline"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA, published
+B, T, H, DK, DV = 4, 4096, 16, 128, 128
+
+# Algorithmic HBM bytes per head-token that each kernel is accountable for: the forward pass
+# reads q, k, b, v, w (bf16) and log alpha (fp32) once (14 d bytes, all in the factor kernel) and
+# writes o (2 d, the carry kernel); the backward reads those plus dO (16 d) and writes dq, dk, db,
+# dv, dw (bf16) and dlog alpha (fp32) (14 d) -- all in the chunk-gradient kernel.  Per-chunk
+# factors, checkpointed states and state gradients are design traffic, not algorithmic.
+ALG_BYTES_PER_HT = {"gdr2_wy_kernel": 14 * DK, "gdr2_carry_kernel": 2 * DV,
+                    "gdr2_dstate_kernel": 0, "gdr2_bgrad_kernel": 30 * DK}
+ALG_FLOPS_PER_HT = {"forward": 6 * DK * DK + 5 * 64 * DK + 64 * 64 / 3,
+                    "backward": 14 * DK * DK + 14 * 64 * DK + 64 * 64}
+KERNELS = ["gdr2_wy_kernel", "gdr2_carry_kernel", "gdr2_dstate_kernel", "gdr2_bgrad_kernel"]
+SOURCES = ["gdr2_common.hpp", "gdr2_wy.hpp", "gdr2_fwd.hip", "gdr2_bwd.hip"]
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for s in SOURCES:
+        with open(os.path.join(ROOT, "gated_delta_rule_gdr_amd", "csrc", s), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary, or None if
+    there is none or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "traffic_layer_1p3b.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"source_hash:\s*(\w+)", text)
+    if not m or m.group(1) != source_hash():
+        return None
+    m = re.search(rf"^{kernel}\s+fetch_bytes=(\d+)\s+write_bytes=(\d+)", text, re.M)
+    return int(m.group(1)) + int(m.group(2)) if m else None
+
+
+def cpu_baseline():
+    """The fp64 oracle (token recurrence + hand-derived backward) on the host cores, on the same
+    synthetic batch as the GPU step (B=4, T=4096, H=16): its cost is bounded (about 1.2e11 fp64
+    flops, seconds on a multi-core host)."""
+    from gated_delta_rule_gdr_amd.inputs import layer_inputs, to_f64
+    from oracle import oracle as orc
+    x = to_f64(layer_inputs(B, T, H, DK, DV, dtype="bf16", seed=1001))
+    orc.build(force=False)
+    t0 = time.perf_counter()
+    orc.forward(x["q"], x["k"], x["v"], x["log_alpha"], x["b"], x["w"])
+    orc.backward(x["q"], x["k"], x["v"], x["log_alpha"], x["b"], x["w"], x["dO"])
+    dt = time.perf_counter() - t0
+    return {"value": round(B * T / dt / 1e6, 6), "unit": "Mtokens/s", "cores": orc.num_threads(),
+            "kind": "oracle",
+            "sample": f"fp64 oracle forward + backward over the full timed batch (B={B} T={T} "
+                      f"H={H} d=128, one chain per OpenMP task), {dt:.1f} s wall"}
+
+
+def bench_decode(torch, lib_decode, steps):
+    """Recurrent decode: 256 sequences x 16 heads, fp32 state in HBM updated in place, bf16
+    token inputs (a new token per step, pre-generated for 8 steps and cycled)."""
+    from gated_delta_rule_gdr_amd.inputs import decode_inputs
+    N = 256
+    S = torch.zeros((N, H, DK, DV), dtype=torch.float32, device="cuda")
+    xs = [decode_inputs(s, N=N, H=H, dk=DK, dv=DV, device="cuda") for s in range(8)]
+    o = torch.empty((N, H, DV), dtype=torch.bfloat16, device="cuda")
+    for s in range(3):
+        x = xs[s % 8]
+        lib_decode(x["q"], x["k"], x["v"], x["log_alpha"], x["b"], x["w"], S_in=S, S_out=S)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for s in range(steps):
+        x = xs[s % 8]
+        lib_decode(x["q"], x["k"], x["v"], x["log_alpha"], x["b"], x["w"], S_in=S, S_out=S)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    bytes_step = N * H * (2 * 4 * DK * DV + 2 * (3 * DK + 3 * DV) + 4 * DK)
+    gbs = bytes_step / us / 1e3
+    return {"workload": "decode N=256 H=16 d=128, fp32 state in HBM, bf16 tokens",
+            "us_per_step": round(us, 2), "Mtokens_per_s": round(N / us, 4),
+            "achieved_GBs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "steps": steps}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--decode-steps", type=int, default=256)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for "
+              f"--gpus {args.gpus})", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gated_delta_rule_gdr_amd as g2
+    from gated_delta_rule_gdr_amd.inputs import layer_inputs
+
+    dev = "cuda"
+    x = layer_inputs(B, T, H, DK, DV, dtype="bf16", seed=1001, device=dev)
+    bf = torch.bfloat16
+    fws = torch.empty(g2.fwd_workspace_bytes(B, T, H, DK, DV, bf), dtype=torch.uint8, device=dev)
+    bws = torch.empty(g2.bwd_workspace_bytes(B, T, H, DK, DV, bf), dtype=torch.uint8, device=dev)
+    o = torch.empty((B, T, H, DV), dtype=bf, device=dev)
+    grads = dict(dq=torch.empty_like(x["q"]), dk=torch.empty_like(x["k"]), dv=torch.empty_like(x["v"]),
+                 dlog_alpha=torch.empty_like(x["log_alpha"]), db=torch.empty_like(x["b"]),
+                 dw=torch.empty_like(x["w"]))
+    dS0 = torch.empty((B, H, DK, DV), dtype=torch.float32, device=dev)
+    q, k, v, la, b, w, dO = (x[n] for n in ("q", "k", "v", "log_alpha", "b", "w", "dO"))
+
+    def step(ev=None):
+        if ev: ev[0].record()
+        g2.gdr2_fwd_factors(q, k, v, la, b, w, fws)
+        if ev: ev[1].record()
+        g2.gdr2_fwd_carry(B, T, H, DK, DV, bf, fws, o)
+        if ev: ev[2].record()
+        g2.gdr2_bwd_state(B, T, H, DK, DV, bf, fws, dO, bws, dS0=dS0)
+        if ev: ev[3].record()
+        g2.gdr2_bwd_grads(q, k, v, la, b, w, fws, dO, bws, grads)
+        if ev: ev[4].record()
+
+    for _ in range(args.warmup):
+        step()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    ms_step = wall * 1e3 / args.steps
+    tokens = B * T
+    value = tokens * args.steps / wall / 1e6
+    ht = B * T * H
+    kern_us = {kname: sum(e[i].elapsed_time(e[i + 1]) for e in evs) * 1e3 / args.steps
+               for i, kname in enumerate(KERNELS)}
+    dom = max(kern_us, key=kern_us.get)
+    ach = ALG_BYTES_PER_HT[dom] * ht / (kern_us[dom] * 1e-6) / 1e9
+    traffic = measured_traffic(dom)
+    flops = (ALG_FLOPS_PER_HT["forward"] + ALG_FLOPS_PER_HT["backward"]) * ht
+    step_alg_bytes = (16 * DK + 30 * DK) * ht
+    out = {
+        "metric": METRIC,
+        "value": round(value, 4),
+        "unit": "Mtokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; q,k L2-normalised N(0,1), v N(0,1), log alpha -softplus(N)*0.1, "
+                "sigmoid gates, dO N(0,1))",
+        "config": {"workload": "GDR-2 layer fwd+bwd, model-shaped 1.3B layer", "B": B, "T": T,
+                   "H": H, "d_k": DK, "d_v": DV, "chunk": 64,
+                   "inputs": "bf16 q,k,v,b,w; fp32 log-decay and state"},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                     "traffic": traffic},
+        "step_roofline": {"alg_bytes": step_alg_bytes, "alg_flops": flops,
+                          "hbm_frac": round(step_alg_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                          "mfma_frac": round(flops / (ms_step * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+                          "roofline_Mtokens_per_s": round(tokens / (step_alg_bytes / (HBM_PEAK_GBS * 1e9)) / 1e6, 2)},
+        "kernel_us": {kn: round(t_, 2) for kn, t_ in kern_us.items()},
+    }
+    if not args.no_decode:
+        out["decode"] = bench_decode(torch, g2.gdr2_decode_step, args.decode_steps)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

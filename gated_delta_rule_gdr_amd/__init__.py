@@ -17,8 +17,9 @@ import os
 
 import torch
 
-__all__ = ["gdr2_fwd_chunked", "gdr2_bwd_chunked", "gdr2_decode_step", "library_path",
-           "load_library", "Gdr2Error", "CHUNK"]
+__all__ = ["gdr2_fwd_chunked", "gdr2_bwd_chunked", "gdr2_decode_step", "gdr2_fwd_factors",
+           "gdr2_fwd_carry", "gdr2_bwd_state", "gdr2_bwd_grads", "fwd_workspace_bytes",
+           "bwd_workspace_bytes", "library_path", "load_library", "Gdr2Error", "CHUNK"]
 
 CHUNK = 64
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -56,6 +57,15 @@ def load_library():
     lib.gdr2_bwd_chunked.argtypes = ([I64] * 5 + [ctypes.c_int] + [P] * 7 + [SZ] + [P] * 10
                                      + [SZ, P])
     lib.gdr2_bwd_chunked.restype = ctypes.c_int
+    lib.gdr2_fwd_factors.argtypes = [I64] * 5 + [ctypes.c_int] + [P] * 7 + [SZ, P]
+    lib.gdr2_fwd_factors.restype = ctypes.c_int
+    lib.gdr2_fwd_carry.argtypes = [I64] * 5 + [ctypes.c_int] + [P] * 4 + [SZ, P]
+    lib.gdr2_fwd_carry.restype = ctypes.c_int
+    lib.gdr2_bwd_state.argtypes = [I64] * 5 + [ctypes.c_int, P, SZ, P, P, P, P, SZ, P]
+    lib.gdr2_bwd_state.restype = ctypes.c_int
+    lib.gdr2_bwd_grads.argtypes = ([I64] * 5 + [ctypes.c_int] + [P] * 7 + [SZ] + [P] * 8
+                                   + [SZ, P])
+    lib.gdr2_bwd_grads.restype = ctypes.c_int
     lib.gdr2_decode_step.argtypes = [I64] * 4 + [ctypes.c_int] + [P] * 10
     lib.gdr2_decode_step.restype = ctypes.c_int
     lib.gdr2_fwd_workspace_bytes.argtypes = [I64] * 5 + [ctypes.c_int]
@@ -147,6 +157,50 @@ def gdr2_bwd_chunked(q, k, v, log_alpha, b, w, dO, fwd_ws, dS_T=None, want_dS0=T
                               _ptr(g["dS0"]), _ptr(ws), ws.numel(), _stream())
     _check("gdr2_bwd_chunked", st)
     return g
+
+
+def fwd_workspace_bytes(B, T, H, dk, dv, dtype):
+    return load_library().gdr2_fwd_workspace_bytes(B, T, H, dk, dv, _DT[dtype])
+
+
+def bwd_workspace_bytes(B, T, H, dk, dv, dtype):
+    return load_library().gdr2_bwd_workspace_bytes(B, T, H, dk, dv, _DT[dtype])
+
+
+def gdr2_fwd_factors(q, k, v, log_alpha, b, w, ws):
+    """Stage 1 of the forward: per-chunk WY factors into ``ws`` (uint8 device tensor)."""
+    B, T, H, dk, dv = _shapes(q, v)
+    st = load_library().gdr2_fwd_factors(B, T, H, dk, dv, _dtype(q), _ptr(q), _ptr(k), _ptr(v),
+                                         _ptr(log_alpha), _ptr(b), _ptr(w), _ptr(ws), ws.numel(),
+                                         _stream())
+    _check("gdr2_fwd_factors", st)
+
+
+def gdr2_fwd_carry(B, T, H, dk, dv, dtype, ws, o, S0=None, S_T=None):
+    """Stage 2 of the forward: o (and S_T) from the factors in ``ws``."""
+    st = load_library().gdr2_fwd_carry(B, T, H, dk, dv, _DT[dtype], _ptr(S0), _ptr(o), _ptr(S_T),
+                                       _ptr(ws), ws.numel(), _stream())
+    _check("gdr2_fwd_carry", st)
+
+
+def gdr2_bwd_state(B, T, H, dk, dv, dtype, fwd_ws, dO, bws, dS_T=None, dS0=None):
+    """Stage 1 of the backward: per-chunk state gradients into ``bws`` and dS0."""
+    st = load_library().gdr2_bwd_state(B, T, H, dk, dv, _DT[dtype], _ptr(fwd_ws), fwd_ws.numel(),
+                                       _ptr(dO), _ptr(dS_T), _ptr(dS0), _ptr(bws), bws.numel(),
+                                       _stream())
+    _check("gdr2_bwd_state", st)
+
+
+def gdr2_bwd_grads(q, k, v, log_alpha, b, w, fwd_ws, dO, bws, g):
+    """Stage 2 of the backward: fills g["dq"], g["dk"], g["dv"], g["dlog_alpha"], g["db"],
+    g["dw"] (preallocated)."""
+    B, T, H, dk, dv = _shapes(q, v)
+    st = load_library().gdr2_bwd_grads(B, T, H, dk, dv, _dtype(q), _ptr(q), _ptr(k), _ptr(v),
+                                       _ptr(log_alpha), _ptr(b), _ptr(w), _ptr(fwd_ws),
+                                       fwd_ws.numel(), _ptr(dO), _ptr(g["dq"]), _ptr(g["dk"]),
+                                       _ptr(g["dv"]), _ptr(g["dlog_alpha"]), _ptr(g["db"]),
+                                       _ptr(g["dw"]), _ptr(bws), bws.numel(), _stream())
+    _check("gdr2_bwd_grads", st)
 
 
 def gdr2_decode_step(q, k, v, log_alpha, b, w, S_in=None, S_out=None):

@@ -144,36 +144,164 @@ static gdr2::FwdParams fwd_params(int64_t B, int64_t T, int64_t H, int64_t dv, c
     return p;
 }
 
+// Validation shared by the forward phases.  `need_inputs` / `need_out` select which pointers a
+// phase requires; every pointer given must be aligned and every output disjoint from the inputs.
+static gdr2_status check_fwd(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                             gdr2_dtype dt, const void* q, const void* k, const void* v,
+                             const float* la, const void* b, const void* w, const float* S0,
+                             void* o, float* S_T, void* ws, size_t ws_bytes, bool need_inputs,
+                             bool need_out) {
+    gdr2_status st = check_chunked(B, T, H, dk, dv, dt);
+    if (st != GDR2_OK) return st;
+    const bool have_tokens = B > 0 && H > 0 && T > 0;
+    if (have_tokens && need_inputs && (!q || !k || !v || !la || !b || !w)) return GDR2_E_NULL;
+    if (have_tokens && need_out && !o) return GDR2_E_NULL;
+    const void* ptrs[] = {q, k, v, la, b, w, S0, o, S_T, ws};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return GDR2_E_ALIGN;
+    const FwdWs L = fwd_ws_layout(B, T, H, dk, dv, dt);
+    if (have_tokens && (!ws || ws_bytes < L.total)) return GDR2_E_WORKSPACE;
+    const size_t es = gdr2_dtype_size(dt);
+    const size_t nk = (size_t)B * T * H * dk, nv = (size_t)B * T * H * dv;
+    const size_t ns = (size_t)B * H * dk * dv;
+    const Range ins[] = {{q, nk * es}, {k, nk * es}, {v, nv * es}, {la, nk * 4},
+                         {b, nk * es}, {w, nv * es}, {S0, ns * 4}};
+    const Range outs[] = {{o, nv * es}, {S_T, ns * 4}, {ws, have_tokens ? L.total : 0}};
+    if (any_alias(outs, 3, ins, 7)) return GDR2_E_ALIAS;
+    return GDR2_OK;
+}
+
+gdr2_status gdr2_fwd_factors(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                             gdr2_dtype dt, const void* q, const void* k, const void* v,
+                             const float* log_alpha, const void* b, const void* w,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+    gdr2_status st = check_fwd(B, T, H, dk, dv, dt, q, k, v, log_alpha, b, w, nullptr, nullptr,
+                               nullptr, workspace, workspace_bytes, true, false);
+    if (st != GDR2_OK || B == 0 || H == 0 || T == 0) return st;
+    const int bf = dt == GDR2_BF16;
+    const FwdWs L = fwd_ws_layout(B, T, H, dk, dv, dt);
+    gdr2::FwdParams p = fwd_params(B, T, H, dv, q, k, v, log_alpha, b, w, nullptr, nullptr,
+                                   nullptr, L, workspace, 16);
+    hipError_t e = gdr2::wy_dispatch(bf, (int)dk, (int)dv, p, (hipStream_t)stream);
+    return e == hipSuccess ? GDR2_OK : GDR2_E_HIP;
+}
+
+gdr2_status gdr2_fwd_carry(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                           gdr2_dtype dt, const float* S0, void* o, float* S_T, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    gdr2_status st = check_fwd(B, T, H, dk, dv, dt, nullptr, nullptr, nullptr, nullptr, nullptr,
+                               nullptr, S0, o, S_T, workspace, workspace_bytes, false, true);
+    if (st != GDR2_OK || B == 0 || H == 0) return st;
+    const int bf = dt == GDR2_BF16;
+    const FwdWs L = fwd_ws_layout(B, T, H, dk, dv, dt);
+    const int dvs = gdr2::carry_slice_width(bf, (int)dk, (int)dv, B * H);
+    gdr2::FwdParams p = fwd_params(B, T, H, dv, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                   nullptr, S0, o, S_T, L, T > 0 ? workspace : nullptr, dvs);
+    hipError_t e = gdr2::carry_fwd_dispatch(bf, (int)dk, dvs, p, (hipStream_t)stream);
+    return e == hipSuccess ? GDR2_OK : GDR2_E_HIP;
+}
+
 gdr2_status gdr2_fwd_chunked(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
                              gdr2_dtype dt, const void* q, const void* k, const void* v,
                              const float* log_alpha, const void* b, const void* w,
                              const float* S0, void* o, float* S_T, void* workspace,
                              size_t workspace_bytes, void* stream) {
+    gdr2_status st = check_fwd(B, T, H, dk, dv, dt, q, k, v, log_alpha, b, w, S0, o, S_T,
+                               workspace, workspace_bytes, true, true);
+    if (st != GDR2_OK || B == 0 || H == 0) return st;
+    if (T > 0) {
+        st = gdr2_fwd_factors(B, T, H, dk, dv, dt, q, k, v, log_alpha, b, w, workspace,
+                              workspace_bytes, stream);
+        if (st != GDR2_OK) return st;
+    }
+    return gdr2_fwd_carry(B, T, H, dk, dv, dt, S0, o, S_T, workspace, workspace_bytes, stream);
+}
+
+// Validation shared by the backward phases.
+static gdr2_status check_bwd(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                             gdr2_dtype dt, const void* q, const void* k, const void* v,
+                             const float* la, const void* b, const void* w, const void* fws,
+                             size_t fws_bytes, const void* dO, const float* dS_T, void* dq,
+                             void* dk_, void* dv_, float* dla, void* db, void* dw, float* dS0,
+                             const void* ws, size_t ws_bytes, bool need_inputs, bool need_grads) {
     gdr2_status st = check_chunked(B, T, H, dk, dv, dt);
     if (st != GDR2_OK) return st;
-    if (B == 0 || H == 0) return GDR2_OK;
-    const bool have_tokens = T > 0;
-    if (have_tokens && (!q || !k || !v || !log_alpha || !b || !w || !o)) return GDR2_E_NULL;
-    const void* ptrs[] = {q, k, v, log_alpha, b, w, S0, o, S_T, workspace};
+    const bool have_tokens = B > 0 && H > 0 && T > 0;
+    if (have_tokens && (!fws || !dO)) return GDR2_E_NULL;
+    if (have_tokens && need_inputs && (!q || !k || !v || !la || !b || !w)) return GDR2_E_NULL;
+    if (have_tokens && need_grads && (!dq || !dk_ || !dv_ || !dla || !db || !dw)) return GDR2_E_NULL;
+    const void* ptrs[] = {q, k, v, la, b, w, fws, dO, dS_T, dq, dk_, dv_, dla, db, dw, dS0, ws};
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return GDR2_E_ALIGN;
     const FwdWs L = fwd_ws_layout(B, T, H, dk, dv, dt);
-    if (have_tokens && (!workspace || workspace_bytes < L.total)) return GDR2_E_WORKSPACE;
+    const size_t need = gdr2_bwd_workspace_bytes(B, T, H, dk, dv, dt);
+    if (have_tokens && (fws_bytes < L.total || !ws || ws_bytes < need)) return GDR2_E_WORKSPACE;
     const size_t es = gdr2_dtype_size(dt);
     const size_t nk = (size_t)B * T * H * dk, nv = (size_t)B * T * H * dv;
     const size_t ns = (size_t)B * H * dk * dv;
-    const Range ins[] = {{q, nk * es}, {k, nk * es}, {v, nv * es}, {log_alpha, nk * 4},
-                         {b, nk * es}, {w, nv * es}, {S0, ns * 4}};
-    const Range outs[] = {{o, nv * es}, {S_T, ns * 4}, {workspace, have_tokens ? L.total : 0}};
-    if (any_alias(outs, 3, ins, 7)) return GDR2_E_ALIAS;
+    const Range ins[] = {{q, nk * es},  {k, nk * es},  {v, nv * es},   {la, nk * 4},
+                         {b, nk * es},  {w, nv * es},  {fws, have_tokens ? L.total : 0},
+                         {dO, nv * es}, {dS_T, ns * 4}};
+    // the state phase writes the workspace; the gradient phase reads it (then it is an input)
+    const Range outs[] = {{dq, nk * es}, {dk_, nk * es}, {dv_, nv * es}, {dla, nk * 4},
+                          {db, nk * es}, {dw, nv * es},  {dS0, ns * 4},
+                          {ws, have_tokens ? need : 0}};
+    if (any_alias(outs, 8, ins, 9)) return GDR2_E_ALIAS;
+    return GDR2_OK;
+}
 
+static gdr2::BwdParams bwd_params(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                                  gdr2_dtype dt, const void* q, const void* k, const void* v,
+                                  const float* la, const void* b, const void* w, const void* fws,
+                                  const void* dO, const float* dS_T, void* dq, void* dk_,
+                                  void* dv_, float* dla, void* db, void* dw, float* dS0,
+                                  const void* ws) {
     const int bf = dt == GDR2_BF16;
-    const int dvs = gdr2::carry_slice_width(bf, (int)dk, (int)dv, B * H);
-    gdr2::FwdParams p = fwd_params(B, T, H, dv, q, k, v, log_alpha, b, w, S0, o, S_T, L,
-                                   have_tokens ? workspace : nullptr, dvs);
-    hipError_t e = hipSuccess;
-    if (have_tokens) e = gdr2::wy_dispatch(bf, (int)dk, (int)dv, p, (hipStream_t)stream);
-    if (e == hipSuccess) e = gdr2::carry_fwd_dispatch(bf, (int)dk, dvs, p, (hipStream_t)stream);
+    const FwdWs L = fwd_ws_layout(B, T, H, dk, dv, dt);
+    gdr2::BwdParams p;
+    p.B = (int)B; p.H = (int)H; p.NC = (int)gdr2_num_chunks(T); p.T = T; p.DV = dv;
+    p.NS = (int)(dv / gdr2::carry_slice_width(bf, (int)dk, (int)dv, B * H));
+    p.q = q; p.k = k; p.v = v; p.b = b; p.w = w; p.la = la;
+    void* f = const_cast<void*>(fws);
+    p.states = f ? (const char*)f + L.states : nullptr;
+    p.wy = wy_bufs(L, f);
+    p.dO = dO; p.dST = dS_T; p.dSx = const_cast<void*>(ws); p.dS0 = dS0;
+    p.dq = dq; p.dk = dk_; p.dv = dv_; p.db = db; p.dw = dw; p.dla = dla;
+    return p;
+}
+
+gdr2_status gdr2_bwd_state(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                           gdr2_dtype dt, const void* fwd_workspace, size_t fwd_workspace_bytes,
+                           const void* dO, const float* dS_T, float* dS0, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    gdr2_status st = check_bwd(B, T, H, dk, dv, dt, nullptr, nullptr, nullptr, nullptr, nullptr,
+                               nullptr, fwd_workspace, fwd_workspace_bytes, dO, dS_T, nullptr,
+                               nullptr, nullptr, nullptr, nullptr, nullptr, dS0, workspace,
+                               workspace_bytes, false, false);
+    if (st != GDR2_OK || B == 0 || H == 0) return st;
+    const int bf = dt == GDR2_BF16;
+    gdr2::BwdParams p = bwd_params(B, T, H, dk, dv, dt, nullptr, nullptr, nullptr, nullptr,
+                                   nullptr, nullptr, fwd_workspace, dO, dS_T, nullptr, nullptr,
+                                   nullptr, nullptr, nullptr, nullptr, dS0, workspace);
+    hipError_t e = gdr2::dstate_dispatch(bf, (int)dk, (int)(dv / p.NS), p, (hipStream_t)stream);
+    return e == hipSuccess ? GDR2_OK : GDR2_E_HIP;
+}
+
+gdr2_status gdr2_bwd_grads(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                           gdr2_dtype dt, const void* q, const void* k, const void* v,
+                           const float* log_alpha, const void* b, const void* w,
+                           const void* fwd_workspace, size_t fwd_workspace_bytes, const void* dO,
+                           void* dq, void* dk_, void* dv_, float* dlog_alpha, void* db, void* dw,
+                           const void* workspace, size_t workspace_bytes, void* stream) {
+    gdr2_status st = check_bwd(B, T, H, dk, dv, dt, q, k, v, log_alpha, b, w, fwd_workspace,
+                               fwd_workspace_bytes, dO, nullptr, dq, dk_, dv_, dlog_alpha, db, dw,
+                               nullptr, workspace, workspace_bytes, true, true);
+    if (st != GDR2_OK || B == 0 || H == 0 || T == 0) return st;
+    const int bf = dt == GDR2_BF16;
+    gdr2::BwdParams p = bwd_params(B, T, H, dk, dv, dt, q, k, v, log_alpha, b, w, fwd_workspace,
+                                   dO, nullptr, dq, dk_, dv_, dlog_alpha, db, dw, nullptr,
+                                   workspace);
+    hipError_t e = gdr2::bgrad_dispatch(bf, (int)dk, (int)dv, p, (hipStream_t)stream);
     return e == hipSuccess ? GDR2_OK : GDR2_E_HIP;
 }
 
@@ -184,46 +312,16 @@ gdr2_status gdr2_bwd_chunked(int64_t B, int64_t T, int64_t H, int64_t dk, int64_
                              const void* dO, const float* dS_T, void* dq, void* dk_, void* dv_,
                              float* dlog_alpha, void* db, void* dw, float* dS0,
                              void* workspace, size_t workspace_bytes, void* stream) {
-    gdr2_status st = check_chunked(B, T, H, dk, dv, dt);
-    if (st != GDR2_OK) return st;
-    if (B == 0 || H == 0) return GDR2_OK;
-    const bool have_tokens = T > 0;
-    if (have_tokens && (!q || !k || !v || !log_alpha || !b || !w || !dO || !dq || !dk_ ||
-                        !dv_ || !dlog_alpha || !db || !dw || !fwd_workspace))
-        return GDR2_E_NULL;
-    const void* ptrs[] = {q, k, v, log_alpha, b, w, fwd_workspace, dO, dS_T, dq, dk_, dv_,
-                          dlog_alpha, db, dw, dS0, workspace};
-    for (const void* p : ptrs)
-        if (p && !aligned16(p)) return GDR2_E_ALIGN;
-    const FwdWs L = fwd_ws_layout(B, T, H, dk, dv, dt);
-    const size_t need = gdr2_bwd_workspace_bytes(B, T, H, dk, dv, dt);
-    if (have_tokens && (fwd_workspace_bytes < L.total || !workspace || workspace_bytes < need))
-        return GDR2_E_WORKSPACE;
-    const size_t es = gdr2_dtype_size(dt);
-    const size_t nk = (size_t)B * T * H * dk, nv = (size_t)B * T * H * dv;
-    const size_t ns = (size_t)B * H * dk * dv;
-    const Range ins[] = {{q, nk * es},     {k, nk * es},  {v, nv * es},
-                         {log_alpha, nk * 4}, {b, nk * es}, {w, nv * es},
-                         {fwd_workspace, have_tokens ? L.total : 0}, {dO, nv * es},
-                         {dS_T, ns * 4}};
-    const Range outs[] = {{dq, nk * es},  {dk_, nk * es}, {dv_, nv * es}, {dlog_alpha, nk * 4},
-                          {db, nk * es},  {dw, nv * es},  {dS0, ns * 4},
-                          {workspace, have_tokens ? need : 0}};
-    if (any_alias(outs, 8, ins, 9)) return GDR2_E_ALIAS;
-
-    const int bf = dt == GDR2_BF16;
-    gdr2::BwdParams p;
-    p.B = (int)B; p.H = (int)H; p.NC = (int)gdr2_num_chunks(T); p.T = T; p.DV = dv;
-    p.NS = (int)(dv / gdr2::carry_slice_width(bf, (int)dk, (int)dv, B * H));
-    p.q = q; p.k = k; p.v = v; p.b = b; p.w = w; p.la = log_alpha;
-    void* fws = const_cast<void*>(fwd_workspace);
-    p.states = fws ? (const char*)fws + L.states : nullptr;
-    p.wy = wy_bufs(L, fws);
-    p.dO = dO; p.dST = dS_T; p.dSx = workspace; p.dS0 = dS0;
-    p.dq = dq; p.dk = dk_; p.dv = dv_; p.db = db; p.dw = dw; p.dla = dlog_alpha;
-    hipError_t e = gdr2::bwd_dispatch(bf, (int)dk, (int)dv, p, (hipStream_t)stream);
-    if (e == hipErrorNotSupported) return GDR2_E_UNSUPPORTED;
-    return e == hipSuccess ? GDR2_OK : GDR2_E_HIP;
+    gdr2_status st = check_bwd(B, T, H, dk, dv, dt, q, k, v, log_alpha, b, w, fwd_workspace,
+                               fwd_workspace_bytes, dO, dS_T, dq, dk_, dv_, dlog_alpha, db, dw,
+                               dS0, workspace, workspace_bytes, true, true);
+    if (st != GDR2_OK || B == 0 || H == 0) return st;
+    st = gdr2_bwd_state(B, T, H, dk, dv, dt, fwd_workspace, fwd_workspace_bytes, dO, dS_T, dS0,
+                        workspace, workspace_bytes, stream);
+    if (st != GDR2_OK || T == 0) return st;
+    return gdr2_bwd_grads(B, T, H, dk, dv, dt, q, k, v, log_alpha, b, w, fwd_workspace,
+                          fwd_workspace_bytes, dO, dq, dk_, dv_, dlog_alpha, db, dw, workspace,
+                          workspace_bytes, stream);
 }
 
 gdr2_status gdr2_decode_step(int64_t N, int64_t H, int64_t dk, int64_t dv, gdr2_dtype dt,

@@ -218,7 +218,7 @@ static hipError_t launch_dstate(const BwdParams& p, hipStream_t s) {
     return hipGetLastError();
 }
 
-static hipError_t dstate_dispatch(int bf, int dk, int dvs, const BwdParams& p, hipStream_t s) {
+hipError_t dstate_dispatch(int bf, int dk, int dvs, const BwdParams& p, hipStream_t s) {
     if (bf) {
         if (dk == 128 && dvs == 64) return launch_dstate<bf16, 128, 64>(p, s);
         if (dk == 128 && dvs == 32) return launch_dstate<bf16, 128, 32>(p, s);
@@ -626,7 +626,7 @@ static hipError_t launch_bgrad(const BwdParams& p, hipStream_t s) {
     return hipGetLastError();
 }
 
-static hipError_t bgrad_dispatch(int bf, int dk, int dv, const BwdParams& p, hipStream_t s) {
+hipError_t bgrad_dispatch(int bf, int dk, int dv, const BwdParams& p, hipStream_t s) {
     if (bf) {
         if (dk == 128 && dv == 128) return launch_bgrad<bf16, 128, 128>(p, s);
         if (dk == 128 && dv == 64) return launch_bgrad<bf16, 128, 64>(p, s);
@@ -639,14 +639,6 @@ static hipError_t bgrad_dispatch(int bf, int dk, int dv, const BwdParams& p, hip
         if (dk == 64 && dv == 64) return launch_bgrad<float, 64, 64>(p, s);
     }
     return hipErrorInvalidValue;
-}
-
-hipError_t bwd_dispatch(int bf, int dk, int dv, const BwdParams& p, hipStream_t s) {
-    const int dvs = (int)(dv / p.NS);
-    hipError_t e = dstate_dispatch(bf, dk, dvs, p, s);
-    if (e != hipSuccess) return e;
-    if (p.NC == 0) return hipSuccess;
-    return bgrad_dispatch(bf, dk, dv, p, s);
 }
 
 }  // namespace gdr2

@@ -58,6 +58,7 @@ hipError_t wy_dispatch(int dtype_bf16, int dk, int dv, const FwdParams& p, hipSt
 int carry_slice_width(int dtype_bf16, int dk, int dv, long chains);
 hipError_t carry_fwd_dispatch(int dtype_bf16, int dk, int dvs, const FwdParams& p, hipStream_t s);
 hipError_t decode_dispatch(int dtype_bf16, int dk, int dv, const DecodeParams& p, hipStream_t s);
-hipError_t bwd_dispatch(int dtype_bf16, int dk, int dv, const BwdParams& p, hipStream_t s);
+hipError_t dstate_dispatch(int dtype_bf16, int dk, int dvs, const BwdParams& p, hipStream_t s);
+hipError_t bgrad_dispatch(int dtype_bf16, int dk, int dv, const BwdParams& p, hipStream_t s);
 
 }  // namespace gdr2

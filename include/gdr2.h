@@ -122,6 +122,34 @@ gdr2_status gdr2_bwd_chunked(int64_t B, int64_t T, int64_t H, int64_t dk, int64_
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Phase entry points.  gdr2_fwd_chunked is gdr2_fwd_factors followed by gdr2_fwd_carry on the same
+ * stream, gdr2_bwd_chunked is gdr2_bwd_state followed by gdr2_bwd_grads; the arguments mean the
+ * same as there.  They exist so that callers can time, overlap or reuse the stages.
+ *   gdr2_fwd_factors  chunk-parallel: writes each chunk's WY factors into `workspace`
+ *   gdr2_fwd_carry    sequential over chunks: o, S_T and the chunk-entry states from the factors
+ *   gdr2_bwd_state    sequential over chunks in reverse: the state gradient entering every
+ *                     chunk's exit (kept in `workspace`) and dS0
+ *   gdr2_bwd_grads    chunk-parallel: dq, dk, dv, dlog_alpha, db, dw from both workspaces
+ */
+gdr2_status gdr2_fwd_factors(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                             gdr2_dtype dtype, const void* q, const void* k, const void* v,
+                             const float* log_alpha, const void* b, const void* w,
+                             void* workspace, size_t workspace_bytes, void* stream);
+gdr2_status gdr2_fwd_carry(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                           gdr2_dtype dtype, const float* S0, void* o, float* S_T,
+                           void* workspace, size_t workspace_bytes, void* stream);
+gdr2_status gdr2_bwd_state(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                           gdr2_dtype dtype, const void* fwd_workspace, size_t fwd_workspace_bytes,
+                           const void* dO, const float* dS_T, float* dS0, void* workspace,
+                           size_t workspace_bytes, void* stream);
+gdr2_status gdr2_bwd_grads(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                           gdr2_dtype dtype, const void* q, const void* k, const void* v,
+                           const float* log_alpha, const void* b, const void* w,
+                           const void* fwd_workspace, size_t fwd_workspace_bytes, const void* dO,
+                           void* dq, void* dk_, void* dv_, float* dlog_alpha, void* db, void* dw,
+                           const void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * One recurrent token for N independent sequences x H heads (constant-memory decoding; forum
  * summary, section "The Memory Dilemma").  The state stays in HBM and is updated in place when
  * S_in == S_out.

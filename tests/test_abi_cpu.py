@@ -1,0 +1,118 @@
+"""The C-ABI library on a host without a GPU: it loads, exports every entry point that
+include/gdr2.h declares, answers the size queries, and rejects invalid arguments on the host
+before any launch (no GPU call is made by any test here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_delta_rule_gdr_amd import library_path, load_library
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdr2.h")
+
+NULL = None
+OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUP, E_ALIGN, E_ALIAS, E_WS = 0, 1, 2, 3, 4, 5, 6, 7
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdr2_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    assert os.path.exists(library_path()), "build the library first (gated_delta_rule_gdr_amd/build.py)"
+    lib = load_library()
+    names = declared_functions()
+    assert "gdr2_fwd_chunked" in names and "gdr2_bwd_chunked" in names and "gdr2_decode_step" in names
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in gdr2.h but not exported"
+
+
+def test_version_and_strings():
+    lib = load_library()
+    assert lib.gdr2_abi_version() == 1
+    for s in range(9):
+        assert lib.gdr2_status_string(s)
+    assert lib.gdr2_dtype_size(0) == 4 and lib.gdr2_dtype_size(1) == 2 and lib.gdr2_dtype_size(7) == 0
+    assert lib.gdr2_num_chunks(0) == 0 and lib.gdr2_num_chunks(1) == 1 and lib.gdr2_num_chunks(64) == 1
+    assert lib.gdr2_num_chunks(65) == 2
+
+
+def test_workspace_sizes():
+    lib = load_library()
+    B, T, H, dk, dv = 4, 4096, 16, 128, 128
+    nc = 64
+    per = B * H * nc
+    fws = lib.gdr2_fwd_workspace_bytes(B, T, H, dk, dv, 1)
+    # -Y, Qbar, Ktilde [64][dk]; P, T [64][64]; U [64][dv] in bf16; gamma fp32; states [dv][dk] bf16
+    expect = per * (3 * 64 * dk * 2 + 2 * 64 * 64 * 2 + 64 * dv * 2 + dk * 4 + dv * dk * 2)
+    assert fws == expect
+    assert lib.gdr2_bwd_workspace_bytes(B, T, H, dk, dv, 1) == per * dk * dv * 2
+    assert lib.gdr2_fwd_workspace_bytes(1, 0, 1, 64, 64, 0) == 0
+
+
+def _fake(addr):
+    """A non-null, 16-byte aligned address that is never dereferenced (validation fails first)."""
+    return ctypes.c_void_p(addr)
+
+
+def _fwd(lib, B=1, T=8, H=1, dk=64, dv=64, dt=1, q=0x10000, o=0x90000, ws=0x200000, ws_bytes=1 << 30,
+         stride=0x8000, S0=None, ST=None):
+    ptrs = [_fake(q + i * stride) if q else NULL for i in range(6)]
+    return lib.gdr2_fwd_chunked(B, T, H, dk, dv, dt, *ptrs, S0, _fake(o) if o else NULL, ST,
+                                _fake(ws) if ws else NULL, ws_bytes, NULL)
+
+
+def test_fwd_rejects_before_launch():
+    lib = load_library()
+    assert _fwd(lib, dt=5) == E_DTYPE
+    assert _fwd(lib, T=-1) == E_SHAPE
+    assert _fwd(lib, dk=96) == E_UNSUP
+    assert _fwd(lib, dv=256) == E_UNSUP
+    assert _fwd(lib, q=0) == E_NULL
+    assert _fwd(lib, o=0) == E_NULL
+    assert _fwd(lib, ws=0) == E_WS
+    assert _fwd(lib, ws_bytes=16) == E_WS
+    assert _fwd(lib, q=0x10004) == E_ALIGN
+    assert _fwd(lib, o=0x10000) == E_ALIAS            # output on top of q
+    assert _fwd(lib, ws=0x10000) == E_ALIAS           # workspace on top of the inputs
+    assert _fwd(lib, B=0) == OK                         # nothing to do, nothing launched
+    assert _fwd(lib, H=0) == OK
+
+
+def test_bwd_rejects_before_launch():
+    lib = load_library()
+    P = lambda a: _fake(a)
+    base = [P(0x10000 + i * 0x8000) for i in range(6)]
+
+    def call(dt=1, fws=0x400000, dO=0x300000, dq=0x500000, ws=0x900000, ws_bytes=1 << 30, fws_bytes=1 << 30):
+        grads = [P(dq + i * 0x8000) if dq else NULL for i in range(6)]
+        return lib.gdr2_bwd_chunked(1, 8, 1, 64, 64, dt, *base, P(fws) if fws else NULL, fws_bytes,
+                                    P(dO) if dO else NULL, NULL, grads[0], grads[1], grads[2],
+                                    grads[3], grads[4], grads[5], NULL, P(ws) if ws else NULL,
+                                    ws_bytes, NULL)
+    assert call(dt=9) == E_DTYPE
+    assert call(fws=0) == E_NULL
+    assert call(dO=0) == E_NULL
+    assert call(dq=0) == E_NULL
+    assert call(ws=0) == E_WS
+    assert call(fws_bytes=8) == E_WS
+    assert call(dq=0x10000) == E_ALIAS
+    assert call(ws=0x300000) == E_ALIAS
+
+
+def test_decode_rejects_before_launch():
+    lib = load_library()
+    P = lambda a: _fake(a)
+    ins = [P(0x10000 + i * 0x1000) for i in range(6)]
+    assert lib.gdr2_decode_step(2, 2, 64, 64, 3, *ins, NULL, P(0x100000), P(0x200000), NULL) == E_DTYPE
+    assert lib.gdr2_decode_step(2, 2, 64, 80, 1, *ins, NULL, P(0x100000), P(0x200000), NULL) == E_UNSUP
+    assert lib.gdr2_decode_step(2, 2, 64, 64, 1, *ins, NULL, NULL, P(0x200000), NULL) == E_NULL
+    assert lib.gdr2_decode_step(2, 2, 64, 64, 1, *ins, NULL, P(0x100008), P(0x200000), NULL) == E_ALIGN
+    assert lib.gdr2_decode_step(2, 2, 64, 64, 1, *ins, NULL, P(0x10000), P(0x200000), NULL) == E_ALIAS
+    # S_in may equal S_out exactly, but may not partially overlap it
+    assert lib.gdr2_decode_step(2, 2, 64, 64, 1, *ins, P(0x100010), P(0x100000), P(0x200000), NULL) == E_ALIAS
+    assert lib.gdr2_decode_step(0, 2, 64, 64, 1, *ins, NULL, P(0x100000), P(0x200000), NULL) == OK
