@@ -236,17 +236,20 @@ hipError_t dstate_dispatch(int bf, int dk, int dvs, const BwdParams& p, hipStrea
 }
 
 // --------------------------------------------------------------------------------------------
-// Chunk gradients: one workgroup per (chain, chunk), all chunks in parallel.  Given the state S
-// entering the chunk (forward checkpoint), the gradient dS' of the state leaving it (state-carry
-// kernel above) and dO, it recomputes Delta, dDelta and dX for DVH value columns at a time and
-// reduces over the value columns in MFMA accumulators (held transposed, channel x token):
+// Chunk gradients: one workgroup (8 waves) per (chain, chunk), all chunks in parallel.  Given the
+// state S entering the chunk (forward checkpoint), the gradient dS' of the state leaving it (the
+// state-carry kernel above) and dO, it recomputes Delta, dDelta and dX for DVH value columns at a
+// time and reduces over the value columns in MFMA accumulators (held transposed, channel x token):
 //     R1 = S dO^T,  R2 = S dX^T,  R3 = dS' Delta^T,   R4 = dO Delta^T,  R5 = dX Delta^T,
 //     R6_i = sum_j dS'_ij S_ij.
 // dP = lower(R4) and dA = -strict_lower(R5) then meet the decay-absorbed key factors in the
 // blocked Gram gradients (same per-16-token-block references as the forward):
 //     G1 = dP Kbar,  G2 = dA Kbar,  G3 = dP^T Qbar + dA^T Ebar.
-// The epilogue runs with lane = token row: dq, dk, db, dv, dw, and dlog alpha as the in-chunk
-// reverse cumsum of dG (DPP suffix scan within 16-row blocks plus block suffix totals).
+// Wave w = (R, half): token block R = w % 4, key-channel half = w / 4.  Lane = token row
+// r = 16R + l%16 with key channels 16 ib + 4 (l/16) + e for the half's ib: the DPP row scans
+// over the 16 tokens of a block give G and the in-chunk reverse cumsum of dG (dlog alpha).
+constexpr int kBgThreads = 512;
+
 template <typename OT, int DK, int DV, int DVH>
 struct BgCfg {
     static constexpr int C = kChunk;
@@ -254,11 +257,17 @@ struct BgCfg {
     static constexpr int ES = (int)sizeof(OT);
     static constexpr int PAD = 16 / ES;
     static constexpr int PK = DK + PAD, PC = C + PAD, PH = DVH + PAD;
-    static constexpr int NKS = DK / KS, NCK = C / KS, NIB = DK / 16, NJH = DVH / 16;
-    static constexpr int NCH = NKS * KPL;
+    static constexpr int NKS = DK / KS, NIB = DK / 16, NIBH = NIB / 2, NJH = DVH / 16;
     static constexpr int VEC = 16 / ES;
-    static constexpr int NSV = DVH * DK / VEC;   // [DVH][DK] tile, vectors
-    static constexpr int NOV = C * DVH / VEC;    // [C][DVH] tile, vectors
+    static constexpr int NSV = DVH * DK / VEC;   // [DVH][DK] tile, 16-byte vectors
+    static constexpr int SVEC = (NSV + kBgThreads - 1) / kBgThreads;
+    static constexpr int NOV = C * DVH / VEC;    // [C][DVH] tile, 16-byte vectors
+    static constexpr int OVEC = (NOV + kBgThreads - 1) / kBgThreads;
+    static constexpr int NTV = C * C / VEC;      // [C][C] tile
+    static constexpr int TVEC = (NTV + kBgThreads - 1) / kBgThreads;
+    static_assert((C * DK / VEC) % kBgThreads == 0, "Y / Ktilde staging");
+    static constexpr bool YK_LDS = ES == 2;
+    static_assert(NJH == 2, "one 16-column block per wave half");
 };
 
 template <typename OT, int DK, int DV, int DVH>
@@ -266,6 +275,8 @@ struct alignas(16) BgSmem {
     using Cf = BgCfg<OT, DK, DV, DVH>;
     union {
         struct {  // value-column phase
+            OT Yt[Cf::YK_LDS ? kChunk * Cf::PK : 1];  // -Y      [r][i] (16-bit operands)
+            OT Kt[Cf::YK_LDS ? kChunk * Cf::PK : 1];  // Ktilde  [r][i]
             OT Tt[kChunk * Cf::PC];    // T                   [r][s]
             OT Pt[kChunk * Cf::PC];    // P                   [r][s]
             OT St[DVH * Cf::PK];       // S^T block           [j][i]
@@ -293,16 +304,19 @@ struct alignas(16) BgSmem {
 };
 
 template <typename OT, int DK, int DV, int DVH>
-__global__ __launch_bounds__(kThreads, 1) void gdr2_bgrad_kernel(BwdParams p) {
+__global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) {
     using Cf = BgCfg<OT, DK, DV, DVH>;
     using MM = Mfma<OT>;
     using FR = Frag<OT>;
+    using RW = Raw4<OT>;
     constexpr int C = kChunk, KS = Cf::KS, KPL = Cf::KPL, PK = Cf::PK, PC = Cf::PC, PH = Cf::PH;
-    constexpr int NKS = Cf::NKS, NCK = Cf::NCK, NIB = Cf::NIB, NJH = Cf::NJH, NCH = Cf::NCH;
-    constexpr int VEC = Cf::VEC, NSV = Cf::NSV, NOV = Cf::NOV;
+    constexpr int NKS = Cf::NKS, NIBH = Cf::NIBH, VEC = Cf::VEC;
+    constexpr int NSV = Cf::NSV, SVEC = Cf::SVEC, NOV = Cf::NOV, OVEC = Cf::OVEC;
+    constexpr int NTV = Cf::NTV, TVEC = Cf::TVEC, NT = kBgThreads;
     __shared__ BgSmem<OT, DK, DV, DVH> sm;
 
-    const int tid = threadIdx.x, R = wave_id(), l = lane_id(), rl = l & 15, g = l >> 4;
+    const int tid = threadIdx.x, w = wave_id(), R = w & 3, half = w >> 2;
+    const int l = lane_id(), rl = l & 15, g = l >> 4;
     const int NC = p.NC;
     const int chain = blockIdx.x / NC, c = blockIdx.x % NC;
     const int bb = chain / p.H, h = chain % p.H;
@@ -312,204 +326,280 @@ __global__ __launch_bounds__(kThreads, 1) void gdr2_bgrad_kernel(BwdParams p) {
     const long t = (long)c * C + r;
     const bool valid = t < T;
     const long row = ((long)bb * T + (valid ? t : T - 1)) * H + h;
+    const long tok0 = ((long)bb * T + (long)c * C) * H + h;  // token row of the chunk's first token
+    const int ibase = NIBH * half;                            // this wave's first key-channel block
+    const int kbeg = (16 * R / KS) * KS;                      // first k-step touching tokens >= 16R
 
-    // ---------------- decay tables (lane = token row r, channels ks*KS + KPL*g + j)
-    {
-        float lv[NCH];
+    // ---- this lane's log alpha (token r, channels 16 (ibase+ib) + 4g + e); q, k, b come later
+    typename RW::t qr[NIBH], kr[NIBH], br[NIBH];
+    f32x4 sc[NIBH];  // log alpha, then G_r - ref_R
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) load_lane_f32<OT>(p.la + row * DK, ks, g, lv + ks * KPL);
-#pragma unroll
-        for (int n = 0; n < NCH; ++n) lv[n] = row_scan16(valid ? lv[n] : 0.f);
-        if (rl == 15) {
-#pragma unroll
-            for (int n = 0; n < NCH; ++n) sm.tot[R][(n / KPL) * KS + KPL * g + n % KPL] = lv[n];
-        }
-        const OT* Tc = (const OT*)p.wy.Tm + cix * C * C;
-        const OT* Pc = (const OT*)p.wy.P + cix * C * C;
-        for (int x = tid; x < C * C / VEC; x += kThreads) {
-            const int rr = (x * VEC) / C, ss = (x * VEC) % C;
-            *(i32x4*)(sm.u.j.Tt + rr * PC + ss) = *(const i32x4*)(Tc + (long)x * VEC);
-            *(i32x4*)(sm.u.j.Pt + rr * PC + ss) = *(const i32x4*)(Pc + (long)x * VEC);
-        }
-        if (tid < DK) sm.r6[tid] = 0.f;
-        lds_barrier();
-        for (int chn = tid; chn < DK; chn += kThreads) {
-            float refs[4], run = 0.f;
-#pragma unroll
-            for (int Rp = 0; Rp < 4; ++Rp) {
-                refs[Rp] = run;
-                run += sm.tot[Rp][chn];
-            }
-#pragma unroll
-            for (int Rp = 0; Rp < 4; ++Rp) {
-                sm.gRt[Rp][chn] = __expf(refs[Rp]);
-                sm.hRt[Rp][chn] = __expf(run - refs[Rp]);
-#pragma unroll
-                for (int S = 0; S < Rp; ++S) sm.ctab[Rp * (Rp - 1) / 2 + S][chn] = __expf(refs[Rp] - refs[S]);
-            }
-        }
-    }
-
-    // ---------------- value-column blocks: Delta, dDelta, dX, dv, dw and the reductions
-    typename FR::t Yf[NKS], Kf[NKS];
+    for (int ib = 0; ib < NIBH; ++ib) sc[ib] = *(const f32x4*)(p.la + row * DK + 16 * (ibase + ib) + 4 * g);
+    // ---- the chunk's -Y and Ktilde: staged into LDS with T and P below (16-bit operands), or
+    //      this wave's token block kept as fragments (fp32)
+    constexpr bool YK_LDS = Cf::YK_LDS;
+    constexpr int YVEC = YK_LDS ? C * DK / VEC / NT : 1;
+    constexpr int NKF = YK_LDS ? 1 : NKS;
+    i32x4 pY[YVEC], pK[YVEC];
+    typename FR::t Yf[NKF], Kf[NKF];
     {
         const OT* Yc = (const OT*)p.wy.Yh + cix * C * DK;
         const OT* Kc = (const OT*)p.wy.Kt + cix * C * DK;
+        if constexpr (YK_LDS) {
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            Yf[ks] = FR::gkc(Yc, DK, 16 * R, ks * KS);
-            Kf[ks] = FR::gkc(Kc, DK, 16 * R, ks * KS);
+            for (int m = 0; m < YVEC; ++m) {
+                pY[m] = *(const i32x4*)(Yc + (long)(tid + m * NT) * VEC);
+                pK[m] = *(const i32x4*)(Kc + (long)(tid + m * NT) * VEC);
+            }
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < NKF; ++ks) {
+                Yf[ks] = FR::gkc(Yc, DK, 16 * R, ks * KS);
+                Kf[ks] = FR::gkc(Kc, DK, 16 * R, ks * KS);
+            }
         }
     }
-    f32x4 A1[NIB], A2[NIB], A3[NIB], A4[NIB];  // R1, R2, R3 (channel x token), then G3
-    f32x4 R4[4], R5[4];                         // dO Delta^T, dX Delta^T (token x token)
-#pragma unroll
-    for (int ib = 0; ib < NIB; ++ib) A1[ib] = A2[ib] = A3[ib] = A4[ib] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int S = 0; S < 4; ++S) R4[S] = R5[S] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // ---- value-column block prefetch registers
     const OT* Sx = (const OT*)p.states + cix * DV * DK;
     const OT* dSxp = (const OT*)p.dSx + cix * DV * DK;
-    const long tok0 = ((long)bb * T + (long)c * C) * H + h;  // token row of the chunk's first token
-    const int kbeg = (16 * R / KS) * KS;                      // first k-step touching tokens >= 16R
-
-    for (int jq = 0; jq < DV / DVH; ++jq) {
+    i32x4 pS[SVEC], pdS[SVEC], pO[OVEC];
+    typename RW::t pv, pw, pU;
+    const OT* Uc = (const OT*)p.wy.U + cix * C * DV;
+    auto fetch_block = [&](int jq) __attribute__((always_inline)) {
         const int jb0 = jq * DVH;
-        lds_barrier();  // previous block's readers are done
-        for (int x = tid; x < NSV; x += kThreads) {
-            const int jj = (x * VEC) / DK, i = (x * VEC) % DK;
-            *(i32x4*)(sm.u.j.St + jj * PK + i) = *(const i32x4*)(Sx + (long)(jb0 + jj) * DK + i);
-            *(i32x4*)(sm.u.j.dSt + jj * PK + i) = *(const i32x4*)(dSxp + (long)(jb0 + jj) * DK + i);
+#pragma unroll
+        for (int m = 0; m < SVEC; ++m) {
+            const int x = tid + m * NT;
+            if (NSV % NT == 0 || x < NSV) {
+                const int jj = (x * VEC) / DK, i = (x * VEC) % DK;
+                pS[m] = *(const i32x4*)(Sx + (long)(jb0 + jj) * DK + i);
+                pdS[m] = *(const i32x4*)(dSxp + (long)(jb0 + jj) * DK + i);
+            }
         }
-        for (int x = tid; x < NOV; x += kThreads) {
+#pragma unroll
+        for (int m = 0; m < OVEC; ++m) {
+            const int x = tid + m * NT;
             const int rr = (x * VEC) / DVH, jj = (x * VEC) % DVH;
             i32x4 z = {0, 0, 0, 0};
-            if ((long)c * C + rr < T) z = *(const i32x4*)((const OT*)p.dO + (tok0 + (long)rr * H) * DV + jb0 + jj);
-            *(i32x4*)(sm.u.j.dOt + rr * PH + jj) = z;
+            if ((NOV % NT == 0 || x < NOV) && (long)c * C + rr < T)
+                z = *(const i32x4*)((const OT*)p.dO + (tok0 + (long)rr * H) * DV + jb0 + jj);
+            pO[m] = z;
         }
-        lds_barrier();
-        // Delta = U - Y S and dDelta = Ktilde dS' + P^T dO for token block R
-        {
-            const OT* Uc = (const OT*)p.wy.U + cix * C * DV;
+        // v, w of (token r, columns jb0 + 16 half + 4g .. +3) for dv, dw
+        const long o = (valid ? (tok0 + (long)r * H) : row) * DV + jb0 + 16 * half + 4 * g;
+        pv = *(const typename RW::t*)((const OT*)p.v + o);
+        pw = *(const typename RW::t*)((const OT*)p.w + o);
+        pU = *(const typename RW::t*)(Uc + ((long)(R * (DV / 16) + jb0 / 16 + half) * 64 + l) * 4);
+    };
+    i32x4 pT[TVEC], pP[TVEC];
+    {
+        const OT* Tc = (const OT*)p.wy.Tm + cix * C * C;
+        const OT* Pc = (const OT*)p.wy.P + cix * C * C;
 #pragma unroll
-            for (int jb = 0; jb < NJH; ++jb) {
-                f32x4 aD = Raw4<OT>::widen(*(const typename Raw4<OT>::t*)(Uc + ((long)(R * (DV / 16) + jb0 / 16 + jb) * 64 + l) * 4));
-                f32x4 adD = {0.f, 0.f, 0.f, 0.f};
+        for (int m = 0; m < TVEC; ++m) {
+            const int x = tid + m * NT;
+            if (NTV % NT == 0 || x < NTV) {
+                pT[m] = *(const i32x4*)(Tc + (long)x * VEC);
+                pP[m] = *(const i32x4*)(Pc + (long)x * VEC);
+            }
+        }
+    }
+    fetch_block(0);
 #pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) {
-                    MM::mma(aD, Yf[ks], FR::kc(sm.u.j.St, PK, 16 * jb, ks * KS));
-                    MM::mma(adD, Kf[ks], FR::kc(sm.u.j.dSt, PK, 16 * jb, ks * KS));
-                }
-                for (int k0 = kbeg; k0 < C; k0 += KS)
-                    MM::mma(adD, FR::tr(sm.u.j.Pt, PC, k0, 16 * R), FR::tr(sm.u.j.dOt, PH, k0, 16 * jb));
-                store_acc_T(sm.u.j.DlT, PC, 16 * jb, 16 * R, aD);
-                store_acc_T(sm.u.j.dDT, PC, 16 * jb, 16 * R, adD);
+    for (int m = 0; m < TVEC; ++m) {
+        const int x = tid + m * NT;
+        if (NTV % NT == 0 || x < NTV) {
+            const int rr = (x * VEC) / C, ss = (x * VEC) % C;
+            *(i32x4*)(sm.u.j.Tt + rr * PC + ss) = pT[m];
+            *(i32x4*)(sm.u.j.Pt + rr * PC + ss) = pP[m];
+        }
+    }
+    if constexpr (YK_LDS) {
+#pragma unroll
+        for (int m = 0; m < YVEC; ++m) {
+            const int e0 = (tid + m * NT) * VEC;
+            *(i32x4*)(sm.u.j.Yt + (e0 / DK) * PK + e0 % DK) = pY[m];
+            *(i32x4*)(sm.u.j.Kt + (e0 / DK) * PK + e0 % DK) = pK[m];
+        }
+    }
+    // ---- in-block cumsum of log alpha (DPP over the 16 tokens), block totals
+#pragma unroll
+    for (int ib = 0; ib < NIBH; ++ib)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sc[ib][e] = row_scan16(valid ? sc[ib][e] : 0.f);
+    if (rl == 15) {
+#pragma unroll
+        for (int ib = 0; ib < NIBH; ++ib) *(f32x4*)(&sm.tot[R][16 * (ibase + ib) + 4 * g]) = sc[ib];
+    }
+    if (tid < DK) sm.r6[tid] = 0.f;
+    lds_barrier();
+    for (int chn = tid; chn < DK; chn += NT) {
+        float refs[4], run = 0.f;
+#pragma unroll
+        for (int Rp = 0; Rp < 4; ++Rp) {
+            refs[Rp] = run;
+            run += sm.tot[Rp][chn];
+        }
+#pragma unroll
+        for (int Rp = 0; Rp < 4; ++Rp) {
+            sm.gRt[Rp][chn] = __expf(refs[Rp]);
+            sm.hRt[Rp][chn] = __expf(run - refs[Rp]);
+#pragma unroll
+            for (int S = 0; S < Rp; ++S) sm.ctab[Rp * (Rp - 1) / 2 + S][chn] = __expf(refs[Rp] - refs[S]);
+        }
+    }
+
+    f32x4 A1[NIBH], A2[NIBH], A3[NIBH];  // R1, R2, R3 (channel x token)
+    f32x4 R4[2], R5[2];                   // dO Delta^T, dX Delta^T for s-blocks 2half+{0,1}
+#pragma unroll
+    for (int ib = 0; ib < NIBH; ++ib) A1[ib] = A2[ib] = A3[ib] = f32x4{0.f, 0.f, 0.f, 0.f};
+    R4[0] = R4[1] = R5[0] = R5[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll 1
+    for (int jq = 0; jq < DV / DVH; ++jq) {
+        const int jb0 = jq * DVH;
+#pragma unroll
+        for (int m = 0; m < SVEC; ++m) {
+            const int x = tid + m * NT;
+            if (NSV % NT == 0 || x < NSV) {
+                const int jj = (x * VEC) / DK, i = (x * VEC) % DK;
+                *(i32x4*)(sm.u.j.St + jj * PK + i) = pS[m];
+                *(i32x4*)(sm.u.j.dSt + jj * PK + i) = pdS[m];
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < OVEC; ++m) {
+            const int x = tid + m * NT;
+            if (NOV % NT == 0 || x < NOV)
+                *(i32x4*)(sm.u.j.dOt + ((x * VEC) / DVH) * PH + (x * VEC) % DVH) = pO[m];
+        }
+        const typename RW::t cv = pv, cw = pw, cU = pU;
+        if (jq + 1 < DV / DVH) {
+            fetch_block(jq + 1);
+        } else {  // raw key inputs for the Gram phase and the epilogue
+#pragma unroll
+            for (int ib = 0; ib < NIBH; ++ib) {
+                const int i0 = 16 * (ibase + ib) + 4 * g;
+                qr[ib] = *(const typename RW::t*)((const OT*)p.q + row * DK + i0);
+                kr[ib] = *(const typename RW::t*)((const OT*)p.k + row * DK + i0);
+                br[ib] = *(const typename RW::t*)((const OT*)p.b + row * DK + i0);
             }
         }
         lds_barrier();
-        // dX^T = dDelta^T T  (this wave: tokens r of block R); dv = dX . w, dw = dX . v
+        // Delta = U - Y S, dDelta = Ktilde dS' + P^T dO: block (token R, columns 16 half)
+        {
+            const int jb = half;
+            f32x4 aD = RW::widen(cU);
+            f32x4 adD = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int jb = 0; jb < NJH; ++jb) {
+            for (int ks = 0; ks < NKS; ++ks) {
+                typename FR::t ay, ak;
+                if constexpr (YK_LDS) {
+                    ay = FR::kc(sm.u.j.Yt, PK, 16 * R, ks * KS);
+                    ak = FR::kc(sm.u.j.Kt, PK, 16 * R, ks * KS);
+                } else {
+                    ay = Yf[ks < NKF ? ks : 0];
+                    ak = Kf[ks < NKF ? ks : 0];
+                }
+                MM::mma(aD, ay, FR::kc(sm.u.j.St, PK, 16 * jb, ks * KS));
+                MM::mma(adD, ak, FR::kc(sm.u.j.dSt, PK, 16 * jb, ks * KS));
+            }
+            for (int k0 = kbeg; k0 < C; k0 += KS)
+                MM::mma(adD, FR::tr(sm.u.j.Pt, PC, k0, 16 * R), FR::tr(sm.u.j.dOt, PH, k0, 16 * jb));
+            store_acc_T(sm.u.j.DlT, PC, 16 * jb, 16 * R, aD);
+            store_acc_T(sm.u.j.dDT, PC, 16 * jb, 16 * R, adD);
+        }
+        lds_barrier();
+        // dX^T = dDelta^T T (lane: token r, columns 16 half + 4g .. +3); dv = dX . w, dw = dX . v
+        {
+            const int jb = half;
             f32x4 ax = {0.f, 0.f, 0.f, 0.f};
             for (int k0 = kbeg; k0 < C; k0 += KS)
                 MM::mma(ax, FR::kc(sm.u.j.dDT, PC, 16 * jb, k0), FR::tr(sm.u.j.Tt, PC, k0, 16 * R));
-            // lane: token r, value columns jb0 + 16jb + 4g .. +3
             const int jc = 16 * jb + 4 * g;
             store4(sm.u.j.dXt + r * PH + jc, ax);
             if (valid) {
                 const long o = (tok0 + (long)r * H) * DV + jb0 + jc;
-                const f32x4 wv = load4((const OT*)p.w + o), vv = load4((const OT*)p.v + o);
-                store4((OT*)p.dv + o, ax * wv);
-                store4((OT*)p.dw + o, ax * vv);
+                store4((OT*)p.dv + o, ax * RW::widen(cw));
+                store4((OT*)p.dw + o, ax * RW::widen(cv));
             }
         }
         lds_barrier();
         // reductions over this block of value columns
 #pragma unroll
         for (int k0 = 0; k0 < DVH; k0 += KS) {
-            const typename FR::t bO = FR::kc(sm.u.j.dOt, PH, 16 * R, k0);   // dO   (col r, k = j)
-            const typename FR::t bX = FR::kc(sm.u.j.dXt, PH, 16 * R, k0);   // dX   (col r, k = j)
-            const typename FR::t bD = FR::tr(sm.u.j.DlT, PC, k0, 16 * R);   // Delta(col r, k = j)
+            const typename FR::t bO = FR::kc(sm.u.j.dOt, PH, 16 * R, k0);   // dO    (col r, k = j)
+            const typename FR::t bX = FR::kc(sm.u.j.dXt, PH, 16 * R, k0);   // dX    (col r, k = j)
+            const typename FR::t bD = FR::tr(sm.u.j.DlT, PC, k0, 16 * R);   // Delta (col r, k = j)
 #pragma unroll
-            for (int ib = 0; ib < NIB; ++ib) {
-                const typename FR::t aS = FR::tr(sm.u.j.St, PK, k0, 16 * ib);   // S   (row i, k = j)
-                const typename FR::t adS = FR::tr(sm.u.j.dSt, PK, k0, 16 * ib); // dS' (row i, k = j)
+            for (int ib = 0; ib < NIBH; ++ib) {
+                const int i0 = 16 * (ibase + ib);
+                const typename FR::t aS = FR::tr(sm.u.j.St, PK, k0, i0);    // S   (row i, k = j)
+                const typename FR::t adS = FR::tr(sm.u.j.dSt, PK, k0, i0);  // dS' (row i, k = j)
                 MM::mma(A1[ib], aS, bO);
                 MM::mma(A2[ib], aS, bX);
                 MM::mma(A3[ib], adS, bD);
             }
-            const typename FR::t aO = FR::kc(sm.u.j.dOt, PH, 16 * R, k0);   // dO (row r, k = j)
-            const typename FR::t aX = FR::kc(sm.u.j.dXt, PH, 16 * R, k0);   // dX (row r, k = j)
 #pragma unroll
-            for (int S = 0; S < 4; ++S) {
+            for (int u = 0; u < 2; ++u) {
+                const int S = 2 * half + u;
                 if (S <= R) {
                     const typename FR::t bDs = FR::tr(sm.u.j.DlT, PC, k0, 16 * S);  // Delta (col s, k = j)
-                    MM::mma(R4[S], aO, bDs);
-                    MM::mma(R5[S], aX, bDs);
+                    MM::mma(R4[u], bO, bDs);
+                    MM::mma(R5[u], bX, bDs);
                 }
             }
         }
         if (tid < DK) {
             float acc = 0.f;
+#pragma unroll 8
             for (int jj = 0; jj < DVH; ++jj)
                 acc += to_f(sm.u.j.dSt[jj * PK + tid]) * to_f(sm.u.j.St[jj * PK + tid]);
             sm.r6[tid] += acc;
         }
+        lds_barrier();
     }
-    lds_barrier();
 
-    // ---------------- decay-absorbed key tiles for the Gram gradients (the value tiles are dead)
-    {
-        float qv[NCH], kv[NCH], bv[NCH], lv[NCH];
+    // ---- decay-absorbed key tiles (the value tiles are dead) and the dP^T, dA^T tiles
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            load_lane<OT>((const OT*)p.q + row * DK, ks, g, qv + ks * KPL);
-            load_lane<OT>((const OT*)p.k + row * DK, ks, g, kv + ks * KPL);
-            load_lane<OT>((const OT*)p.b + row * DK, ks, g, bv + ks * KPL);
-            load_lane_f32<OT>(p.la + row * DK, ks, g, lv + ks * KPL);
+    for (int ib = 0; ib < NIBH; ++ib) {
+        const int i0 = 16 * (ibase + ib) + 4 * g;
+        const f32x4 q4 = RW::widen(qr[ib]), k4 = RW::widen(kr[ib]), b4 = RW::widen(br[ib]);
+        f32x4 eb, qb, kb;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float x = valid ? __expf(sc[ib][e]) : 0.f, y = valid ? __expf(-sc[ib][e]) : 0.f;
+            eb[e] = b4[e] * k4[e] * x;
+            qb[e] = q4[e] * x;
+            kb[e] = k4[e] * y;
         }
-        if (!valid) {
-#pragma unroll
-            for (int n = 0; n < NCH; ++n) qv[n] = kv[n] = bv[n] = lv[n] = 0.f;
-        }
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            float eb[KPL], qb[KPL], kb[KPL];
-#pragma unroll
-            for (int j = 0; j < KPL; ++j) {
-                const int n = ks * KPL + j;
-                const float sc = row_scan16(lv[n]);
-                const float x = __expf(sc), y = __expf(-sc);
-                eb[j] = bv[n] * kv[n] * x;
-                qb[j] = qv[n] * x;
-                kb[j] = kv[n] * y;
-            }
-            store_lane<OT>(sm.u.g.Eb + r * PK, ks, g, eb);
-            store_lane<OT>(sm.u.g.Qb + r * PK, ks, g, qb);
-            store_lane<OT>(sm.u.g.Kb + r * PK, ks, g, kb);
-        }
+        store4(sm.u.g.Eb + r * PK + i0, eb);
+        store4(sm.u.g.Qb + r * PK + i0, qb);
+        store4(sm.u.g.Kb + r * PK + i0, kb);
     }
-    // ---------------- dP^T, dA^T tiles (token x token), then the blocked Gram gradients
 #pragma unroll
-    for (int S = 0; S < 4; ++S) {
+    for (int u = 0; u < 2; ++u) {
+        const int S = 2 * half + u;
         f32x4 pm = {0.f, 0.f, 0.f, 0.f}, am = {0.f, 0.f, 0.f, 0.f};
         if (S <= R) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int rr = 16 * R + acc_row(e), ss = 16 * S + acc_col();
-                pm[e] = ss <= rr ? R4[S][e] : 0.f;
-                am[e] = ss < rr ? -R5[S][e] : 0.f;
+                pm[e] = ss <= rr ? R4[u][e] : 0.f;
+                am[e] = ss < rr ? -R5[u][e] : 0.f;
             }
         }
         store_acc_T(sm.u.g.dPT, PC, 16 * S, 16 * R, pm);
         store_acc_T(sm.u.g.dAT, PC, 16 * S, 16 * R, am);
     }
     lds_barrier();
-    // A1 <- exp(ref_R) . R1 + dP Kbar ; A2 <- -exp(ref_R) . R2 + dA Kbar   (channel x token r)
+
+    // ---- A1 <- exp(ref_R) R1 + dP Kbar,  A2 <- -exp(ref_R) R2 + dA Kbar,  A4 <- dP^T Qbar + dA^T Ebar
 #pragma unroll
-    for (int ib = 0; ib < NIB; ++ib) {
+    for (int ib = 0; ib < NIBH; ++ib) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const float gr = sm.gRt[R][16 * ib + acc_row(e)];
+            const float gr = sm.gRt[R][16 * (ibase + ib) + acc_row(e)];
             A1[ib][e] *= gr;
             A2[ib][e] *= -gr;
         }
@@ -519,27 +609,28 @@ __global__ __launch_bounds__(kThreads, 1) void gdr2_bgrad_kernel(BwdParams p) {
         const typename FR::t bA = FR::tr(sm.u.g.dAT, PC, k0, 16 * R);  // dA (col r, k = s)
         const int Sl = (k0 + KPL * g) / 16;                             // token block of this lane's k
 #pragma unroll
-        for (int ib = 0; ib < NIB; ++ib) {
-            typename FR::t a = FR::tr(sm.u.g.Kb, PK, k0, 16 * ib);          // Kbar^T (row i, k = s)
-            if (Sl < R) {
-                const float cs = sm.ctab[R * (R - 1) / 2 + Sl][16 * ib + rl];
-                a = FR::scale(a, cs);
-            }
+        for (int ib = 0; ib < NIBH; ++ib) {
+            const int i0 = 16 * (ibase + ib);
+            typename FR::t a = FR::tr(sm.u.g.Kb, PK, k0, i0);            // Kbar^T (row i, k = s)
+            if (Sl < R) a = FR::scale(a, sm.ctab[R * (R - 1) / 2 + Sl][i0 + rl]);
             MM::mma(A1[ib], a, bP);
             MM::mma(A2[ib], a, bA);
         }
     }
-    // A4 <- dP^T Qbar + dA^T Ebar (channel x token s, s in block R)
-    for (int k0 = (16 * R / KS) * KS; k0 < C; k0 += KS) {
+    f32x4 A4[NIBH];  // G3 (channel x token s)
+#pragma unroll
+    for (int ib = 0; ib < NIBH; ++ib) A4[ib] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int k0 = kbeg; k0 < C; k0 += KS) {
         const typename FR::t bP = FR::kc(sm.u.g.dPT, PC, 16 * R, k0);  // dP (col s, k = r)
         const typename FR::t bA = FR::kc(sm.u.g.dAT, PC, 16 * R, k0);  // dA (col s, k = r)
         const int Rl = (k0 + KPL * g) / 16;
 #pragma unroll
-        for (int ib = 0; ib < NIB; ++ib) {
-            typename FR::t aq = FR::tr(sm.u.g.Qb, PK, k0, 16 * ib);         // Qbar^T (row i, k = r)
-            typename FR::t ae = FR::tr(sm.u.g.Eb, PK, k0, 16 * ib);         // Ebar^T (row i, k = r)
+        for (int ib = 0; ib < NIBH; ++ib) {
+            const int i0 = 16 * (ibase + ib);
+            typename FR::t aq = FR::tr(sm.u.g.Qb, PK, k0, i0);           // Qbar^T (row i, k = r)
+            typename FR::t ae = FR::tr(sm.u.g.Eb, PK, k0, i0);           // Ebar^T (row i, k = r)
             if (Rl > R) {
-                const float cs = sm.ctab[Rl * (Rl - 1) / 2 + R][16 * ib + rl];
+                const float cs = sm.ctab[Rl * (Rl - 1) / 2 + R][i0 + rl];
                 aq = FR::scale(aq, cs);
                 ae = FR::scale(ae, cs);
             }
@@ -548,72 +639,56 @@ __global__ __launch_bounds__(kThreads, 1) void gdr2_bgrad_kernel(BwdParams p) {
         }
     }
 
-    // ---------------- epilogue: lane = token r (block R), channels 16 ib + 4 g + e
-    {
-        const OT* qr = (const OT*)p.q + row * DK;
-        const OT* kr = (const OT*)p.k + row * DK;
-        const OT* br = (const OT*)p.b + row * DK;
-        const float* lr = p.la + row * DK;
-        f32x4 dG[NIB], kdk[NIB], dqv[NIB], dkv[NIB], dbv[NIB];
+    // ---- epilogue: lane = token r, channels 16 (ibase + ib) + 4g + e
+    f32x4 dG[NIBH];
+    const long orow = row * DK;
 #pragma unroll
-        for (int ib = 0; ib < NIB; ++ib) {
-            const int i0 = 16 * ib + 4 * g;
-            f32x4 q4 = load4(qr + i0), k4 = load4(kr + i0), b4 = load4(br + i0), l4 = *(const f32x4*)(lr + i0);
-            if (!valid) q4 = k4 = b4 = l4 = f32x4{0.f, 0.f, 0.f, 0.f};
-            const f32x4 gr = *(const f32x4*)(&sm.gRt[R][i0]);
-            const f32x4 hr = *(const f32x4*)(&sm.hRt[R][i0]);
-            (void)gr;
+    for (int ib = 0; ib < NIBH; ++ib) {
+        const int i0 = 16 * (ibase + ib) + 4 * g;
+        f32x4 q4 = RW::widen(qr[ib]), k4 = RW::widen(kr[ib]), b4 = RW::widen(br[ib]);
+        if (!valid) q4 = k4 = b4 = f32x4{0.f, 0.f, 0.f, 0.f};
+        const f32x4 hr = *(const f32x4*)(&sm.hRt[R][i0]);
+        f32x4 dqv, dkv, dbv, kdk;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float sc = row_scan16(l4[e]);  // G_r - ref_R
-                const float x = __expf(sc), y = __expf(-sc);
-                const float dq = x * A1[ib][e];
-                const float de = x * A2[ib][e];
-                const float dkb = y * A4[ib][e];
-                const float dkt = hr[e] * y * A3[ib][e];
-                const float ee = b4[e] * k4[e];
-                dqv[ib][e] = dq;
-                dkv[ib][e] = dkb + dkt + b4[e] * de;
-                dbv[ib][e] = k4[e] * de;
-                dG[ib][e] = q4[e] * dq + ee * de - k4[e] * (dkb + dkt);
-                kdk[ib][e] = k4[e] * dkt;
-            }
+        for (int e = 0; e < 4; ++e) {
+            const float x = __expf(sc[ib][e]), y = __expf(-sc[ib][e]);
+            const float dq = x * A1[ib][e];
+            const float de = x * A2[ib][e];
+            const float dkb = y * A4[ib][e];
+            const float dkt = hr[e] * y * A3[ib][e];
+            dqv[e] = dq;
+            dkv[e] = dkb + dkt + b4[e] * de;
+            dbv[e] = k4[e] * de;
+            dG[ib][e] = row_rscan16(q4[e] * dq + b4[e] * k4[e] * de - k4[e] * (dkb + dkt));
+            kdk[e] = row_rscan16(k4[e] * dkt);
         }
-        // suffix sums over the 16 tokens of the block; block totals to LDS
-#pragma unroll
-        for (int ib = 0; ib < NIB; ++ib) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                dG[ib][e] = row_rscan16(dG[ib][e]);
-                kdk[ib][e] = row_rscan16(kdk[ib][e]);
-            }
-            if (rl == 0) {
-                *(f32x4*)(&sm.btot[R][16 * ib + 4 * g]) = dG[ib];
-                *(f32x4*)(&sm.ktot[R][16 * ib + 4 * g]) = kdk[ib];
-            }
-        }
-        lds_barrier();
         if (valid) {
-            const long o = row * DK;
+            store4((OT*)p.dq + orow + i0, dqv);
+            store4((OT*)p.dk + orow + i0, dkv);
+            store4((OT*)p.db + orow + i0, dbv);
+        }
+        if (rl == 0) {
+            *(f32x4*)(&sm.btot[R][i0]) = dG[ib];
+            *(f32x4*)(&sm.ktot[R][i0]) = kdk;
+        }
+    }
+    lds_barrier();
+    if (valid) {
 #pragma unroll
-            for (int ib = 0; ib < NIB; ++ib) {
-                const int i0 = 16 * ib + 4 * g;
-                f32x4 dl = dG[ib];
+        for (int ib = 0; ib < NIBH; ++ib) {
+            const int i0 = 16 * (ibase + ib) + 4 * g;
+            f32x4 dl = dG[ib];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    float add = sm.r6[i0 + e] * sm.hRt[0][i0 + e];  // dgamma . gamma
+            for (int e = 0; e < 4; ++e) {
+                float add = sm.r6[i0 + e] * sm.hRt[0][i0 + e];  // dgamma . gamma
 #pragma unroll
-                    for (int Rp = 0; Rp < 4; ++Rp) {
-                        add += sm.ktot[Rp][i0 + e];
-                        if (Rp > R) add += sm.btot[Rp][i0 + e];
-                    }
-                    dl[e] += add;
+                for (int Rp = 0; Rp < 4; ++Rp) {
+                    add += sm.ktot[Rp][i0 + e];
+                    if (Rp > R) add += sm.btot[Rp][i0 + e];
                 }
-                store4((OT*)p.dq + o + i0, dqv[ib]);
-                store4((OT*)p.dk + o + i0, dkv[ib]);
-                store4((OT*)p.db + o + i0, dbv[ib]);
-                *(f32x4*)(p.dla + o + i0) = dl;
+                dl[e] += add;
             }
+            *(f32x4*)(p.dla + orow + i0) = dl;
         }
     }
 }
@@ -622,7 +697,7 @@ template <typename OT, int DK, int DV>
 static hipError_t launch_bgrad(const BwdParams& p, hipStream_t s) {
     const long nblk = (long)p.B * p.H * p.NC;
     if (nblk == 0) return hipSuccess;
-    hipLaunchKernelGGL((gdr2_bgrad_kernel<OT, DK, DV, 32>), dim3(nblk), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((gdr2_bgrad_kernel<OT, DK, DV, 32>), dim3(nblk), dim3(kBgThreads), 0, s, p);
     return hipGetLastError();
 }
 
