@@ -115,7 +115,14 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=256)
+    ap.add_argument("--profile-pass", action="store_true",
+                    help="short run for hardware-counter passes: 1 warm-up + 1 step, one decode "
+                         "step, then a 512 MiB device-to-device copy that calibrates FETCH_SIZE / "
+                         "WRITE_SIZE (no JSON line)")
     args = ap.parse_args()
+    if args.profile_pass:
+        args.warmup, args.steps, args.decode_steps = 1, 1, 1
+        args.no_cpu_baseline = True
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for "
               f"--gpus {args.gpus})", file=sys.stderr)
@@ -197,6 +204,13 @@ def main():
     }
     if not args.no_decode:
         out["decode"] = bench_decode(torch, g2.gdr2_decode_step, args.decode_steps)
+    if args.profile_pass:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print("profile pass done: 512 MiB copy issued for counter calibration", flush=True)
+        return
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)
