@@ -97,7 +97,7 @@ __global__ __launch_bounds__(kThreads, 1) void gdr2_dstate_kernel(BwdParams p) {
         const long cix = (long)chain * NC + cc;
         const OT* Kc = (const OT*)p.wy.Kt + cix * C * DK;
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) b.K[ks] = FR::gkc(Kc, DK, 16 * R, ks * KS);
+        for (int ks = 0; ks < NKS; ++ks) b.K[ks] = FFrag<OT>::fkc(Kc, DK, 16 * R, ks * KS);
         const OT* Qc = (const OT*)p.wy.Qg + cix * C * DK;
         const OT* Yc = (const OT*)p.wy.Yh + cix * C * DK;
 #pragma unroll
@@ -125,15 +125,17 @@ __global__ __launch_bounds__(kThreads, 1) void gdr2_dstate_kernel(BwdParams p) {
     auto chunk = [&](const Buf& cur, Buf& nxt, int c) __attribute__((always_inline)) {
         // ---- stage the chunk's factors and dO slice, checkpoint dS' of this chunk
 #pragma unroll
-        for (int m = 0; m < KVEC; ++m) {
-            const int e0 = (tid + m * kThreads) * VEC;
-            *(i32x4*)(sm.Qt + (e0 / DK) * PK + e0 % DK) = cur.Q[m];
-            *(i32x4*)(sm.Yt + (e0 / DK) * PK + e0 % DK) = cur.Y[m];
+        for (int m = 0; m < KVEC; ++m) {  // fragment order -> row-major
+            const int x = tid + m * kThreads;
+            const int o = FLay<OT>::unit_row(x, DK) * PK + FLay<OT>::unit_col(x, DK);
+            *(i32x4*)(sm.Qt + o) = cur.Q[m];
+            *(i32x4*)(sm.Yt + o) = cur.Y[m];
         }
 #pragma unroll
         for (int m = 0; m < PVEC; ++m) {
             const int x = tid + m * kThreads;
-            if (x < C * C / VEC) *(i32x4*)(sm.Pt + ((x * VEC) / C) * PC + (x * VEC) % C) = cur.P[m];
+            if (x < C * C / VEC)
+                *(i32x4*)(sm.Pt + FLay<OT>::unit_row(x, C) * PC + FLay<OT>::unit_col(x, C)) = cur.P[m];
         }
 #pragma unroll
         for (int m = 0; m < OVEC; ++m) {
@@ -354,8 +356,8 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
         } else {
 #pragma unroll
             for (int ks = 0; ks < NKF; ++ks) {
-                Yf[ks] = FR::gkc(Yc, DK, 16 * R, ks * KS);
-                Kf[ks] = FR::gkc(Kc, DK, 16 * R, ks * KS);
+                Yf[ks] = FFrag<OT>::fkc(Yc, DK, 16 * R, ks * KS);
+                Kf[ks] = FFrag<OT>::fkc(Kc, DK, 16 * R, ks * KS);
             }
         }
     }
@@ -408,18 +410,19 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
 #pragma unroll
     for (int m = 0; m < TVEC; ++m) {
         const int x = tid + m * NT;
-        if (NTV % NT == 0 || x < NTV) {
-            const int rr = (x * VEC) / C, ss = (x * VEC) % C;
-            *(i32x4*)(sm.u.j.Tt + rr * PC + ss) = pT[m];
-            *(i32x4*)(sm.u.j.Pt + rr * PC + ss) = pP[m];
+        if (NTV % NT == 0 || x < NTV) {  // fragment order -> row-major
+            const int o = FLay<OT>::unit_row(x, C) * PC + FLay<OT>::unit_col(x, C);
+            *(i32x4*)(sm.u.j.Tt + o) = pT[m];
+            *(i32x4*)(sm.u.j.Pt + o) = pP[m];
         }
     }
     if constexpr (YK_LDS) {
 #pragma unroll
-        for (int m = 0; m < YVEC; ++m) {
-            const int e0 = (tid + m * NT) * VEC;
-            *(i32x4*)(sm.u.j.Yt + (e0 / DK) * PK + e0 % DK) = pY[m];
-            *(i32x4*)(sm.u.j.Kt + (e0 / DK) * PK + e0 % DK) = pK[m];
+        for (int m = 0; m < YVEC; ++m) {  // fragment order -> row-major
+            const int x = tid + m * NT;
+            const int o = FLay<OT>::unit_row(x, DK) * PK + FLay<OT>::unit_col(x, DK);
+            *(i32x4*)(sm.u.j.Yt + o) = pY[m];
+            *(i32x4*)(sm.u.j.Kt + o) = pK[m];
         }
     }
     // ---- in-block cumsum of log alpha (DPP over the 16 tokens), block totals

@@ -240,6 +240,60 @@ template <> struct Frag<float> {
     static __device__ __forceinline__ t scale(const t& x, float s) { return x * s; }
 };
 
+// ------------------------------------------------------------------ fragment-order tiles
+// The per-chunk factor tiles ([64][cols], cols a multiple of KU) are stored in HBM in fragment
+// order: a sequence of 1 KB pieces of 16 rows x KU columns (row-block major), and inside a piece
+// the 16-byte unit u holds row u % 16, columns (u / 16) * VEC .. + VEC - 1.  Unit u is exactly
+// what lane u needs for a bf16 MFMA operand fragment, so a fragment load is one contiguous 1 KB
+// read (global or LDS) and a piece can be copied to LDS by one direct-to-LDS load per wave.
+template <typename OT> struct FLay {
+    static constexpr int ES = (int)sizeof(OT), VEC = 16 / ES, KU = 64 / ES;
+    // element offset of (row, col) in a tile of `cols` columns
+    static __device__ __forceinline__ int off(int row, int col, int cols) {
+        return (((row >> 4) * (cols / KU) + col / KU) * 64 + ((col % KU) / VEC) * 16 + (row & 15)) * VEC +
+               col % VEC;
+    }
+    // row and first column of 16-byte unit x
+    static __device__ __forceinline__ int unit_row(int x, int cols) {
+        const int piece = x >> 6;
+        return (piece / (cols / KU)) * 16 + (x & 15);
+    }
+    static __device__ __forceinline__ int unit_col(int x, int cols) {
+        const int piece = x >> 6;
+        return (piece % (cols / KU)) * KU + ((x & 63) >> 4) * VEC;
+    }
+};
+
+// Operand fragments read from a fragment-order tile of `cols` columns (LDS or global):
+//   fkc(X, cols, i0, k0): rows i0 + l%16 of the tile, k = columns (as Frag::kc on a row-major tile)
+//   ftr(X, cols, k0, i0): the transposed use, index = column i0 + l%16, k = rows (as Frag::tr)
+template <typename OT> struct FFrag;
+template <> struct FFrag<bf16> {
+    typedef bf16x8 t;
+    static __device__ __forceinline__ t fkc(const bf16* X, int cols, int i0, int k0) {
+        const int l = lane_id();
+        return *(const bf16x8*)(X + FLay<bf16>::off(i0 + (l & 15), k0 + 8 * (l >> 4), cols));
+    }
+    static __device__ __forceinline__ t ftr(const bf16* X, int cols, int k0, int i0) {
+        const int l = lane_id(), p = l & 15, kb = k0 + 8 * (l >> 4) + (p >> 2);
+        const int c = i0 + 4 * (p & 3);
+        bf16x4 lo = ds_read_tr4(X + FLay<bf16>::off(kb, c, cols));
+        bf16x4 hi = ds_read_tr4(X + FLay<bf16>::off(kb + 4, c, cols));
+        return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+};
+template <> struct FFrag<float> {
+    typedef float t;
+    static __device__ __forceinline__ t fkc(const float* X, int cols, int i0, int k0) {
+        const int l = lane_id();
+        return X[FLay<float>::off(i0 + (l & 15), k0 + (l >> 4), cols)];
+    }
+    static __device__ __forceinline__ t ftr(const float* X, int cols, int k0, int i0) {
+        const int l = lane_id();
+        return X[FLay<float>::off(k0 + (l >> 4), i0 + (l & 15), cols)];
+    }
+};
+
 // Inclusive suffix sum over the 16 lanes of each DPP row: lane i gets the sum of lanes i..15.
 __device__ __forceinline__ float row_rscan16(float x) {
     int v = __builtin_bit_cast(int, x);

@@ -113,11 +113,11 @@ __global__ __launch_bounds__(kThreads, 1) void gdr2_carry_kernel(FwdParams p) {
         const OT* Pc = (const OT*)p.wy.P + cix * C * C;
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
-            b.Y[ks] = FR::gkc(Yc, DK, 16 * R, ks * KS);
-            b.Q[ks] = FR::gkc(Qc, DK, 16 * R, ks * KS);
+            b.Y[ks] = FFrag<OT>::fkc(Yc, DK, 16 * R, ks * KS);
+            b.Q[ks] = FFrag<OT>::fkc(Qc, DK, 16 * R, ks * KS);
         }
 #pragma unroll
-        for (int kk = 0; kk < NCK; ++kk) b.P[kk] = FR::gkc(Pc, C, 16 * R, kk * KS);
+        for (int kk = 0; kk < NCK; ++kk) b.P[kk] = FFrag<OT>::fkc(Pc, C, 16 * R, kk * KS);
         const OT* Uc = (const OT*)p.wy.U + cix * C * DV;
 #pragma unroll
         for (int jb = 0; jb < NJB; ++jb)
@@ -131,9 +131,9 @@ __global__ __launch_bounds__(kThreads, 1) void gdr2_carry_kernel(FwdParams p) {
         const long t0 = (long)c * C;
         // ---- step 1: stage Ktilde / gamma, checkpoint, Delta = U - Y S, O = Qbar S
 #pragma unroll
-        for (int m = 0; m < KVEC; ++m) {
-            const int e0 = (tid + m * kThreads) * VEC;
-            *(i32x4*)(sm.Kt + (e0 / DK) * PK + e0 % DK) = cur.K[m];
+        for (int m = 0; m < KVEC; ++m) {  // fragment order -> row-major
+            const int x = tid + m * kThreads;
+            *(i32x4*)(sm.Kt + FLay<OT>::unit_row(x, DK) * PK + FLay<OT>::unit_col(x, DK)) = cur.K[m];
         }
         if (tid < DK / 4) *(f32x4*)(sm.gam + 4 * tid) = cur.g;
         if (c + 1 < NC) fetch(nxt, c + 1);

@@ -6,9 +6,10 @@ namespace gdr2 {
 
 // Per-chunk WY factors written by the chunk-parallel factor kernel and read by the state-carry
 // kernels (forward and backward) and the chunk-gradient kernel.  Element type = input dtype
-// except gam.  Every array is indexed [chain = b*H + h][chunk][...].
+// except gam.  Every array is indexed [chain = b*H + h][chunk][...]; the [C][*] tiles are in
+// fragment order (FLay in gdr2_common.hpp).
 struct WyBufs {
-    void* Yh;    // -Y = -(T Ebar),                          [C][DK] row-major
+    void* Yh;    // -Y = -(T Ebar),                          [C][DK]
     void* Qg;    // Qbar = Q . exp(G),                        [C][DK]
     void* Kt;    // Ktilde = K . exp(G_C - G),                [C][DK]
     void* P;     // P = lower(Qbar Kbar^T),                   [C][C]

@@ -148,6 +148,15 @@ __device__ __forceinline__ void store_lane(OT* row, int ks, int g, const float* 
         row[ks * 4 + g] = v[0];
     }
 }
+// The same KPL values stored into a fragment-order tile of `cols` columns (row r).
+template <typename OT>
+__device__ __forceinline__ void store_lane_F(OT* tile, int cols, int r, int ks, int g, const float* v) {
+    if constexpr (sizeof(OT) == 2) {
+        *(bf16x8*)(tile + FLay<OT>::off(r, ks * 32 + 8 * g, cols)) = Frag<bf16>::from_f32(v);
+    } else {
+        tile[FLay<OT>::off(r, ks * 4 + g, cols)] = v[0];
+    }
+}
 __device__ __forceinline__ void store_lane_f32(float* row, int ks, int g, const float* v, int kpl) {
     if (kpl == 8) {
         *(f32x4*)(row + ks * 32 + 8 * g) = f32x4{v[0], v[1], v[2], v[3]};
@@ -259,8 +268,8 @@ __device__ void wy_factors(WySmem<OT, DK, DV>& sm, const WyChunk<OT, DK, DV>& ch
     // decay-absorbed factors
     typename FR::t Ef[NKS], Qf[NKS];  // e . exp(G - ref_R), q . exp(G - ref_R) (Gram operands)
     float eg[NCH];                     // e . exp(G), kept for Y
-    OT* qg_out = (OT*)wy.Qg + (cix * C + r) * DK;
-    OT* kt_out = (OT*)wy.Kt + (cix * C + r) * DK;
+    OT* qg_out = (OT*)wy.Qg + cix * C * DK;  // fragment-order tiles
+    OT* kt_out = (OT*)wy.Kt + cix * C * DK;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
         float ebk[KPL], qbk[KPL], kbk[KPL], qg[KPL], kt[KPL], gR[KPL], hR[KPL];
@@ -281,18 +290,18 @@ __device__ void wy_factors(WySmem<OT, DK, DV>& sm, const WyChunk<OT, DK, DV>& ch
         Ef[ks] = FR::from_f32(ebk);
         Qf[ks] = FR::from_f32(qbk);
         store_lane<OT>(sm.u.Kb + r * PK, ks, g, kbk);
-        store_lane<OT>(qg_out, ks, g, qg);
-        store_lane<OT>(kt_out, ks, g, kt);
+        store_lane_F<OT>(qg_out, DK, r, ks, g, qg);
+        store_lane_F<OT>(kt_out, DK, r, ks, g, kt);
     }
     lds_barrier();
 
     // A^T and P^T blocks (S, R) for S <= R: rows s of block S, columns r of block R.
     {
-        OT* prow = (OT*)wy.P + (cix * C + r) * C;
+        OT* pt = (OT*)wy.P + cix * C * C;  // fragment order
 #pragma unroll
         for (int S = 0; S < 4; ++S) {
             if (S > R) {
-                OT* d = prow + 16 * S + 4 * g;  // zero block above the diagonal
+                OT* d = pt + FLay<OT>::off(r, 16 * S + 4 * g, C);  // zero block above the diagonal
                 store4(d, f32x4{0.f, 0.f, 0.f, 0.f});
                 continue;
             }
@@ -313,7 +322,7 @@ __device__ void wy_factors(WySmem<OT, DK, DV>& sm, const WyChunk<OT, DK, DV>& ch
                 pm[e] = (S < R || s <= r) ? aP[e] : 0.f;
             }
             *(f32x4*)(sm.Af + r * PAF + 16 * S + 4 * g) = am;
-            store4(prow + 16 * S + 4 * g, pm);
+            store4(pt + FLay<OT>::off(r, 16 * S + 4 * g, C), pm);
         }
     }
     lds_barrier();
@@ -327,9 +336,9 @@ __device__ void wy_factors(WySmem<OT, DK, DV>& sm, const WyChunk<OT, DK, DV>& ch
     {
         OT* tg = (OT*)wy.Tm + cix * C * C;
         constexpr int VEC = 16 / (int)sizeof(OT);
-        for (int x = threadIdx.x; x < C * C / VEC; x += kThreads) {
-            const int rr = (x * VEC) / C, ss = (x * VEC) % C;
-            *(uint4*)(tg + rr * C + ss) = *(const uint4*)(sm.Tm + rr * PC + ss);
+        for (int x = threadIdx.x; x < C * C / VEC; x += kThreads) {  // fragment order
+            const int rr = FLay<OT>::unit_row(x, C), ss = FLay<OT>::unit_col(x, C);
+            *(i32x4*)(tg + (long)x * VEC) = *(const i32x4*)(sm.Tm + rr * PC + ss);
         }
     }
     lds_barrier();
@@ -337,13 +346,13 @@ __device__ void wy_factors(WySmem<OT, DK, DV>& sm, const WyChunk<OT, DK, DV>& ch
     // Y^T = Ebar^T T^T (stored negated, row-major -Y[r][i]) and U = T Z (accumulator order)
     const int kend = ((16 * R + 16 + KS - 1) / KS) * KS;
     {
-        OT* yrow = (OT*)wy.Yh + (cix * C + r) * DK;
+        OT* yt = (OT*)wy.Yh + cix * C * DK;  // fragment order
 #pragma unroll
         for (int ib = 0; ib < DK / 16; ++ib) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             for (int k0 = 0; k0 < kend; k0 += KS)
                 MM::mma(acc, FR::tr(sm.u.e.Eg, PK, k0, 16 * ib), FR::kc(sm.Tm, PC, 16 * R, k0));
-            store4(yrow + 16 * ib + 4 * g, f32x4{-acc[0], -acc[1], -acc[2], -acc[3]});
+            store4(yt + FLay<OT>::off(r, 16 * ib + 4 * g, DK), f32x4{-acc[0], -acc[1], -acc[2], -acc[3]});
         }
     }
     {
