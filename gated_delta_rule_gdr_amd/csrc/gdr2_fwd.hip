@@ -226,6 +226,258 @@ __global__ __launch_bounds__(kThreads, 1) void gdr2_carry_kernel(FwdParams p) {
     }
 }
 
+// --------------------------------------------------------------------------------------------
+// State carry with loader waves (16-bit operands).  Eight waves: waves 0-3 compute (wave R owns
+// token block R, as in gdr2_carry_kernel) and write the outputs; waves 4-7 only load.  While
+// chunk c computes out of one LDS slot, the loader waves copy chunk c + 1 (loaded into their
+// registers two steps earlier) into the other slot and issue the loads of chunk c + 3, so a
+// load has two steps to arrive.  The compute waves issue no global load, so the memory pipeline
+// never stalls them, and the loader waves issue no store, so their waits cover loads only.
+template <int DK, int DVS>
+struct CarryLCfg {
+    static constexpr int C = kChunk, KS = 32;
+    static constexpr int PK = DK + 8, PC = C + 8, PO = DVS + 8;
+    static constexpr int NKS = DK / KS, NCK = C / KS, NJB = DVS / 16, NIB = DK / 16;
+    static constexpr int BPW = NIB * NJB / kWaves;
+    // slot layout (bf16 elements): Y, Q, K [C][DK] and P [C][C] in fragment order, then the U
+    // slice [4 token blocks][NJB][64 lanes][4] (accumulator order)
+    static constexpr int OY = 0, OQ = C * DK, OK = 2 * C * DK, OP = 3 * C * DK, OU = OP + C * C;
+    static constexpr int SLOT = OU + C * DVS;
+    // 16-byte units of one chunk: the slot, then gamma (DK fp32)
+    static constexpr int UM = C * DK / 8, UP = C * C / 8, UU = C * DVS / 8, UG = DK / 4;
+    static constexpr int NUNIT = 3 * UM + UP + UU + UG;
+    static constexpr int LPT = (NUNIT + kThreads - 1) / kThreads;   // units per loader thread
+    static_assert(BPW >= 1 && BPW * kWaves == NIB * NJB, "state block mapping");
+    static_assert(UM % kThreads == 0 && UP % kThreads == 0, "loader unit regions");
+};
+
+template <int DK, int DVS>
+struct alignas(16) CarryLSmem {
+    using Cf = CarryLCfg<DK, DVS>;
+    bf16 slot[2][Cf::SLOT];
+    float gam[2][DK];
+    bf16 ST[DVS * Cf::PK];     // S^T operand copy   [j][i]
+    bf16 DT[DVS * Cf::PC];     // Delta^T            [j][r]
+    bf16 Ost[kChunk * Cf::PO]; // output staging     [r][j]
+};
+
+template <int DK, int DVS>
+__global__ __launch_bounds__(2 * kThreads, 1) void gdr2_carry_lds_kernel(FwdParams p) {
+    using Cf = CarryLCfg<DK, DVS>;
+    using MM = Mfma<bf16>;
+    using FR = Frag<bf16>;
+    using FF = FFrag<bf16>;
+    constexpr int C = kChunk, KS = Cf::KS, PK = Cf::PK, PC = Cf::PC, PO = Cf::PO;
+    constexpr int NKS = Cf::NKS, NCK = Cf::NCK, NJB = Cf::NJB, BPW = Cf::BPW, LPT = Cf::LPT;
+    __shared__ CarryLSmem<DK, DVS> sm;
+
+    const int tid = threadIdx.x, w = wave_id(), l = lane_id();
+    const bool loader = w >= kWaves;
+    const int R = w & 3, lt = tid & (kThreads - 1);
+    const int work = xcd_swizzle(blockIdx.x, gridDim.x);
+    const int chain = work / p.NS, slice = work % p.NS;
+    const int bb = chain / p.H, h = chain % p.H;
+    const int j0 = slice * DVS;
+    const long T = p.T, H = p.H, DV = p.DV;
+    const int NC = p.NC;
+    bf16* o = p.o ? (bf16*)p.o + ((long)bb * T * H + h) * DV + j0 : nullptr;
+
+    // ---- loader: unit x = lt + kThreads * m of chunk cc (the region of x depends on m only)
+    auto src_unit = [&](int cc, int m) __attribute__((always_inline)) -> const i32x4* {
+        const long cix = (long)chain * NC + cc;
+        int x = lt + kThreads * m;
+        if (x >= Cf::NUNIT) x = Cf::NUNIT - 1;  // padding lanes reload the last unit
+        if (x < 3 * Cf::UM) {
+            const int mat = x / Cf::UM, u = x % Cf::UM;
+            const bf16* base = mat == 0 ? (const bf16*)p.wy.Yh : mat == 1 ? (const bf16*)p.wy.Qg : (const bf16*)p.wy.Kt;
+            return (const i32x4*)(base + cix * C * DK + u * 8);
+        }
+        x -= 3 * Cf::UM;
+        if (x < Cf::UP) return (const i32x4*)((const bf16*)p.wy.P + cix * C * C + x * 8);
+        x -= Cf::UP;
+        if (x < Cf::UU) {
+            const int rb = x / (NJB * 32), within = x % (NJB * 32);
+            return (const i32x4*)((const bf16*)p.wy.U + cix * C * DV +
+                                  ((long)(rb * (DV / 16) + slice * NJB) * 64) * 4 + within * 8);
+        }
+        x -= Cf::UU;
+        return (const i32x4*)(p.wy.gam + cix * DK + 4 * x);
+    };
+    auto put_unit = [&](int sl, int m, const i32x4& v) __attribute__((always_inline)) {
+        int x = lt + kThreads * m;
+        if (x >= Cf::NUNIT) return;
+        if (x < 3 * Cf::UM + Cf::UP + Cf::UU) {
+            *(i32x4*)(sm.slot[sl] + x * 8) = v;  // Y, Q, K, P, U are contiguous in the slot
+        } else {
+            *(i32x4*)(sm.gam[sl] + 4 * (x - 3 * Cf::UM - Cf::UP - Cf::UU)) = v;
+        }
+    };
+    i32x4 lbA[LPT], lbB[LPT];  // loader registers: chunk k >= 1 lives in lbA (k odd) or lbB (k even)
+
+    f32x4 Sacc[BPW];
+    if (!loader) {
+#pragma unroll
+        for (int u = 0; u < BPW; ++u) {
+            const int bi = R * BPW + u, ib = bi / NJB, jb = bi % NJB;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float s0 = 0.f;
+                if (p.S0) s0 = p.S0[((long)chain * DK + 16 * ib + acc_row(e)) * DV + j0 + 16 * jb + acc_col()];
+                Sacc[u][e] = s0;
+            }
+            store_acc_T(sm.ST, PK, 16 * jb, 16 * ib, Sacc[u]);
+        }
+    } else if (NC > 0) {
+        // chunk 0 into slot 0 (through lbB), then chunks 1 and 2 into the registers (clamped)
+#pragma unroll
+        for (int m = 0; m < LPT; ++m) lbB[m] = *src_unit(0, m);
+#pragma unroll
+        for (int m = 0; m < LPT; ++m) put_unit(0, m, lbB[m]);
+#pragma unroll
+        for (int m = 0; m < LPT; ++m) lbA[m] = *src_unit(NC > 1 ? 1 : NC - 1, m);
+#pragma unroll
+        for (int m = 0; m < LPT; ++m) lbB[m] = *src_unit(NC > 2 ? 2 : NC - 1, m);
+    }
+    lds_barrier();
+
+    // loader step cc: chunk cc + 1 (registers `cur`) into slot (cc + 1) & 1, then the loads of
+    // chunk cc + 3 into the same registers (clamped to the last chunk, so that every step issues
+    // the same loads and the waits stay exact), half before and half after the mid-step barrier
+    auto loader_step = [&](int cc, i32x4* cur) __attribute__((always_inline)) {
+        if (cc + 1 < NC) {
+#pragma unroll
+            for (int m = 0; m < LPT; ++m) put_unit((cc + 1) & 1, m, cur[m]);
+        }
+        const int c3 = cc + 3 < NC ? cc + 3 : NC - 1;
+#pragma unroll
+        for (int m = 0; m < LPT / 2; ++m) cur[m] = *src_unit(c3, m);
+        lds_barrier();
+#pragma unroll
+        for (int m = LPT / 2; m < LPT; ++m) cur[m] = *src_unit(c3, m);
+        lds_barrier();
+    };
+    auto compute_step = [&](int c, int sl) __attribute__((always_inline)) {
+        const long t0 = (long)c * C;
+        // outputs of the previous step: checkpoint of the state entering chunk c, O of chunk c-1
+        if (p.states) {
+            bf16* dst = (bf16*)p.states + (((long)chain * NC + c) * DV + j0) * DK;
+            constexpr int NSV = DVS * DK / 8;
+#pragma unroll
+            for (int x0 = 0; x0 < NSV; x0 += kThreads) {
+                const int x = x0 + tid;
+                if (NSV % kThreads == 0 || x < NSV) {
+                    const int j = (x * 8) / DK, i = (x * 8) % DK;
+                    *(i32x4*)(dst + (long)j * DK + i) = *(const i32x4*)(sm.ST + j * PK + i);
+                }
+            }
+        }
+        if (o && c > 0) {
+            constexpr int NV = C * DVS / 8;
+#pragma unroll
+            for (int x0 = 0; x0 < NV; x0 += kThreads) {
+                const int x = x0 + tid;
+                const int rr = (x * 8) / DVS, j = (x * 8) % DVS;
+                const long t = t0 - C + rr;
+                if ((NV % kThreads == 0 || x < NV) && t < T)
+                    *(i32x4*)(o + t * H * DV + j) = *(const i32x4*)(sm.Ost + rr * PO + j);
+            }
+        }
+        const bf16* Ys = sm.slot[sl] + Cf::OY;
+        const bf16* Qs = sm.slot[sl] + Cf::OQ;
+        const bf16* Ks = sm.slot[sl] + Cf::OK;
+        const bf16* Ps = sm.slot[sl] + Cf::OP;
+        const bf16* Us = sm.slot[sl] + Cf::OU;
+        // ---- Delta = U - Y S (stored -Y), O = Qbar S
+        f32x4 aD[NJB], aO[NJB];
+#pragma unroll
+        for (int jb = 0; jb < NJB; ++jb) {
+            aD[jb] = Raw4<bf16>::widen(*(const bf16x4*)(Us + ((R * NJB + jb) * 64 + l) * 4));
+            aO[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            const bf16x8 ay = FF::fkc(Ys, DK, 16 * R, ks * KS), aq = FF::fkc(Qs, DK, 16 * R, ks * KS);
+#pragma unroll
+            for (int jb = 0; jb < NJB; ++jb) {
+                const bf16x8 bS = FR::kc(sm.ST, PK, 16 * jb, ks * KS);
+                MM::mma(aD[jb], ay, bS);
+                MM::mma(aO[jb], aq, bS);
+            }
+        }
+#pragma unroll
+        for (int jb = 0; jb < NJB; ++jb) store_acc_T(sm.DT, PC, 16 * jb, 16 * R, aD[jb]);
+        lds_barrier();
+        // ---- O += P Delta, S' = Diag(gamma) S + Ktilde^T Delta
+#pragma unroll
+        for (int kk = 0; kk < NCK; ++kk) {
+            if (kk * KS < 16 * R + 16) {
+                const bf16x8 ap = FF::fkc(Ps, C, 16 * R, kk * KS);
+#pragma unroll
+                for (int jb = 0; jb < NJB; ++jb) MM::mma(aO[jb], ap, FR::kc(sm.DT, PC, 16 * jb, kk * KS));
+            }
+        }
+#pragma unroll
+        for (int jb = 0; jb < NJB; ++jb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                sm.Ost[(16 * R + acc_row(e)) * PO + 16 * jb + acc_col()] = (bf16)aO[jb][e];
+#pragma unroll
+        for (int u = 0; u < BPW; ++u) {
+            const int bi = R * BPW + u, ib = bi / NJB, jb = bi % NJB;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Sacc[u][e] *= sm.gam[sl][16 * ib + acc_row(e)];
+#pragma unroll
+            for (int kk = 0; kk < NCK; ++kk)
+                MM::mma(Sacc[u], FF::ftr(Ks, DK, kk * KS, 16 * ib), FR::kc(sm.DT, PC, 16 * jb, kk * KS));
+            store_acc_T(sm.ST, PK, 16 * jb, 16 * ib, Sacc[u]);
+        }
+        lds_barrier();
+    };
+
+    // Steps run in pairs (the register alternation); a step past the last chunk only keeps the
+    // barrier count of the two roles equal.
+    const int NCR = (NC + 1) / 2 * 2;
+    if (loader) {
+        for (int c = 0; c < NCR; c += 2) {
+            loader_step(c, lbA);
+            loader_step(c + 1, lbB);
+        }
+    } else {
+        for (int c = 0; c < NCR; c += 2) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                if (c + u < NC) {
+                    compute_step(c + u, (c + u) & 1);
+                } else {
+                    lds_barrier();
+                    lds_barrier();
+                }
+            }
+        }
+        if (o && NC > 0) {  // output tile of the last chunk
+            const long t0 = (long)(NC - 1) * C;
+            constexpr int NV = C * DVS / 8;
+#pragma unroll
+            for (int x0 = 0; x0 < NV; x0 += kThreads) {
+                const int x = x0 + tid;
+                const int rr = (x * 8) / DVS, j = (x * 8) % DVS;
+                const long t = t0 + rr;
+                if ((NV % kThreads == 0 || x < NV) && t < T)
+                    *(i32x4*)(o + t * H * DV + j) = *(const i32x4*)(sm.Ost + rr * PO + j);
+            }
+        }
+        if (p.ST) {
+#pragma unroll
+            for (int u = 0; u < BPW; ++u) {
+                const int bi = R * BPW + u, ib = bi / NJB, jb = bi % NJB;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    p.ST[((long)chain * DK + 16 * ib + acc_row(e)) * DV + j0 + 16 * jb + acc_col()] = Sacc[u][e];
+            }
+        }
+    }
+}
+
 template <typename OT, int DK, int DV>
 static hipError_t launch_wy(const FwdParams& p, hipStream_t s) {
     const long nblk = (long)p.B * p.H * p.NC;
@@ -257,22 +509,30 @@ static hipError_t launch_carry(const FwdParams& p, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <int DK, int DVS>
+static hipError_t launch_carry_lds(const FwdParams& p, hipStream_t s) {
+    const long nblk = (long)p.B * p.H * p.NS;
+    if (nblk == 0) return hipSuccess;
+    hipLaunchKernelGGL((gdr2_carry_lds_kernel<DK, DVS>), dim3(nblk), dim3(2 * kThreads), 0, s, p);
+    return hipGetLastError();
+}
+
 int carry_slice_width(int bf, int dk, int dv, long chains) {
+    // widest slice that still gives >= 256 workgroups; 64-wide slices only where the bf16
+    // two-slot LDS carry fits (d_k = 64)
     const int cands[3] = {64, 32, 16};
-    for (int x = bf ? 0 : 1; x < 3; ++x)
+    for (int x = (bf && dk == 64) ? 0 : 1; x < 3; ++x)
         if (cands[x] <= dv && chains * (dv / cands[x]) >= 256) return cands[x];
-    (void)dk;
     return 16;
 }
 
 hipError_t carry_fwd_dispatch(int bf, int dk, int dvs, const FwdParams& p, hipStream_t s) {
     if (bf) {
-        if (dk == 128 && dvs == 64) return launch_carry<bf16, 128, 64>(p, s);
-        if (dk == 128 && dvs == 32) return launch_carry<bf16, 128, 32>(p, s);
-        if (dk == 128 && dvs == 16) return launch_carry<bf16, 128, 16>(p, s);
-        if (dk == 64 && dvs == 64) return launch_carry<bf16, 64, 64>(p, s);
-        if (dk == 64 && dvs == 32) return launch_carry<bf16, 64, 32>(p, s);
-        if (dk == 64 && dvs == 16) return launch_carry<bf16, 64, 16>(p, s);
+        if (dk == 128 && dvs == 32) return launch_carry_lds<128, 32>(p, s);
+        if (dk == 128 && dvs == 16) return launch_carry_lds<128, 16>(p, s);
+        if (dk == 64 && dvs == 64) return launch_carry_lds<64, 64>(p, s);
+        if (dk == 64 && dvs == 32) return launch_carry_lds<64, 32>(p, s);
+        if (dk == 64 && dvs == 16) return launch_carry_lds<64, 16>(p, s);
     } else {
         if (dk == 128 && dvs == 32) return launch_carry<float, 128, 32>(p, s);
         if (dk == 128 && dvs == 16) return launch_carry<float, 128, 16>(p, s);
