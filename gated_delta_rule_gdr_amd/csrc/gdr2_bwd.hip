@@ -212,6 +212,234 @@ __global__ __launch_bounds__(kThreads, 1) void gdr2_dstate_kernel(BwdParams p) {
     }
 }
 
+// --------------------------------------------------------------------------------------------
+// State-gradient carry with loader waves (16-bit operands), the backward twin of
+// gdr2_carry_lds_kernel: waves 0-3 compute (wave R owns token block R) and write the dS'
+// checkpoints, waves 4-7 stream the factors and the dO slice of chunk c - 1 into the other LDS
+// slot (loaded two steps ahead into their registers) while chunk c computes.
+template <int DK, int DVS>
+struct DsLCfg {
+    static constexpr int C = kChunk, KS = 32;
+    static constexpr int PK = DK + 8, PC = C + 8, PO = DVS + 8;
+    static constexpr int NKS = DK / KS, NCK = C / KS, NJB = DVS / 16, NIB = DK / 16;
+    static constexpr int BPW = NIB * NJB / kWaves;
+    // slot layout (bf16 elements): Q, Y, K [C][DK] and P [C][C] in fragment order, then the dO
+    // slice [C][PO] (row-major, padded)
+    static constexpr int OQ = 0, OY = C * DK, OK = 2 * C * DK, OP = 3 * C * DK, OO = OP + C * C;
+    static constexpr int SLOT = OO + C * PO;
+    // 16-byte units of one chunk: Q, Y, K, P (contiguous in the slot), dO rows, gamma
+    static constexpr int UM = C * DK / 8, UP = C * C / 8, UO = C * DVS / 8, UG = DK / 4;
+    static constexpr int NUNIT = 3 * UM + UP + UO + UG;
+    static constexpr int LPT = (NUNIT + kThreads - 1) / kThreads;
+    static_assert(BPW >= 1 && BPW * kWaves == NIB * NJB, "state block mapping");
+};
+
+template <int DK, int DVS>
+struct alignas(16) DsLSmem {
+    using Cf = DsLCfg<DK, DVS>;
+    bf16 slot[2][Cf::SLOT];
+    float gam[2][DK];
+    bf16 dST[DVS * Cf::PK];   // dS^T operand copy   [j][i]
+    bf16 dDT[DVS * Cf::PC];   // dDelta^T            [j][r]
+};
+
+template <int DK, int DVS>
+__global__ __launch_bounds__(2 * kThreads, 1) void gdr2_dstate_lds_kernel(BwdParams p) {
+    using Cf = DsLCfg<DK, DVS>;
+    using MM = Mfma<bf16>;
+    using FR = Frag<bf16>;
+    using FF = FFrag<bf16>;
+    constexpr int C = kChunk, KS = Cf::KS, PK = Cf::PK, PC = Cf::PC, PO = Cf::PO;
+    constexpr int NKS = Cf::NKS, NCK = Cf::NCK, NJB = Cf::NJB, BPW = Cf::BPW, LPT = Cf::LPT;
+    __shared__ DsLSmem<DK, DVS> sm;
+
+    const int tid = threadIdx.x, w = wave_id(), l = lane_id();
+    const bool loader = w >= kWaves;
+    const int R = w & 3, lt = tid & (kThreads - 1);
+    const int work = xcd_swizzle(blockIdx.x, gridDim.x);
+    const int chain = work / p.NS, slice = work % p.NS;
+    const int bb = chain / p.H, h = chain % p.H;
+    const int j0 = slice * DVS;
+    const long T = p.T, H = p.H, DV = p.DV;
+    const int NC = p.NC;
+    const bf16* dO = (const bf16*)p.dO + ((long)bb * T * H + h) * DV + j0;
+
+    // ---- loader units of chunk cc (the region of unit lt + kThreads * m depends on m only)
+    auto src_unit = [&](int cc, int m) __attribute__((always_inline)) -> const i32x4* {
+        const long cix = (long)chain * NC + cc;
+        int x = lt + kThreads * m;
+        if (x >= Cf::NUNIT) x = Cf::NUNIT - 1;
+        if (x < 3 * Cf::UM) {
+            const int mat = x / Cf::UM, u = x % Cf::UM;
+            const bf16* base = mat == 0 ? (const bf16*)p.wy.Qg : mat == 1 ? (const bf16*)p.wy.Yh : (const bf16*)p.wy.Kt;
+            return (const i32x4*)(base + cix * C * DK + u * 8);
+        }
+        x -= 3 * Cf::UM;
+        if (x < Cf::UP) return (const i32x4*)((const bf16*)p.wy.P + cix * C * C + x * 8);
+        x -= Cf::UP;
+        if (x < Cf::UO) {
+            const int rr = x / (DVS / 8), c8 = x % (DVS / 8);
+            const long t = (long)cc * C + rr < T ? (long)cc * C + rr : T - 1;  // zeroed when put
+            return (const i32x4*)(dO + t * H * DV + 8 * c8);
+        }
+        x -= Cf::UO;
+        return (const i32x4*)(p.wy.gam + cix * DK + 4 * x);
+    };
+    auto put_unit = [&](int sl, int cc, int m, const i32x4& v) __attribute__((always_inline)) {
+        int x = lt + kThreads * m;
+        if (x >= Cf::NUNIT) return;
+        if (x < 3 * Cf::UM + Cf::UP) {
+            *(i32x4*)(sm.slot[sl] + x * 8) = v;
+            return;
+        }
+        x -= 3 * Cf::UM + Cf::UP;
+        if (x < Cf::UO) {
+            const int rr = x / (DVS / 8), c8 = x % (DVS / 8);
+            const i32x4 z = {0, 0, 0, 0};
+            *(i32x4*)(sm.slot[sl] + Cf::OO + rr * PO + 8 * c8) = (long)cc * C + rr < T ? v : z;
+            return;
+        }
+        x -= Cf::UO;
+        *(i32x4*)(sm.gam[sl] + 4 * x) = v;
+    };
+    i32x4 lbA[LPT], lbB[LPT];  // loader registers; step s handles chunk NC - 1 - s
+
+    f32x4 dS[BPW];
+    if (!loader) {
+#pragma unroll
+        for (int u = 0; u < BPW; ++u) {
+            const int bi = R * BPW + u, ib = bi / NJB, jb = bi % NJB;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float v = 0.f;
+                if (p.dST) v = p.dST[((long)chain * DK + 16 * ib + acc_row(e)) * DV + j0 + 16 * jb + acc_col()];
+                dS[u][e] = v;
+            }
+            store_acc_T(sm.dST, PK, 16 * jb, 16 * ib, dS[u]);
+        }
+    } else if (NC > 0) {
+        const int c0 = NC - 1, c1 = NC > 1 ? NC - 2 : 0, c2 = NC > 2 ? NC - 3 : 0;
+#pragma unroll
+        for (int m = 0; m < LPT; ++m) lbB[m] = *src_unit(c0, m);
+#pragma unroll
+        for (int m = 0; m < LPT; ++m) put_unit(0, c0, m, lbB[m]);
+#pragma unroll
+        for (int m = 0; m < LPT; ++m) lbA[m] = *src_unit(c1, m);
+#pragma unroll
+        for (int m = 0; m < LPT; ++m) lbB[m] = *src_unit(c2, m);
+    }
+    lds_barrier();
+
+    // loader step st: the chunk of step st + 1 (registers `cur`) into slot (st + 1) & 1, then the
+    // loads of the chunk of step st + 3 (clamped) into the same registers
+    auto loader_step = [&](int st, i32x4* cur) __attribute__((always_inline)) {
+        if (st + 1 < NC) {
+#pragma unroll
+            for (int m = 0; m < LPT; ++m) put_unit((st + 1) & 1, NC - 2 - st, m, cur[m]);
+        }
+        const int c3 = st + 3 < NC ? NC - 4 - st : 0;
+#pragma unroll
+        for (int m = 0; m < LPT / 2; ++m) cur[m] = *src_unit(c3, m);
+        lds_barrier();
+#pragma unroll
+        for (int m = LPT / 2; m < LPT; ++m) cur[m] = *src_unit(c3, m);
+        lds_barrier();
+    };
+    auto compute_step = [&](int c, int sl) __attribute__((always_inline)) {
+        {   // checkpoint: gradient of the state leaving chunk c
+            bf16* dst = (bf16*)p.dSx + (((long)chain * NC + c) * DV + j0) * DK;
+            constexpr int NSV = DVS * DK / 8;
+#pragma unroll
+            for (int x0 = 0; x0 < NSV; x0 += kThreads) {
+                const int x = x0 + tid;
+                if (NSV % kThreads == 0 || x < NSV) {
+                    const int j = (x * 8) / DK, i = (x * 8) % DK;
+                    *(i32x4*)(dst + (long)j * DK + i) = *(const i32x4*)(sm.dST + j * PK + i);
+                }
+            }
+        }
+        const bf16* Qs = sm.slot[sl] + Cf::OQ;
+        const bf16* Ys = sm.slot[sl] + Cf::OY;
+        const bf16* Ks = sm.slot[sl] + Cf::OK;
+        const bf16* Ps = sm.slot[sl] + Cf::OP;
+        const bf16* Os = sm.slot[sl] + Cf::OO;
+        // ---- dDelta = Ktilde dS' + P^T dO   (wave R: token block R)
+        {
+            f32x4 aD[NJB];
+#pragma unroll
+            for (int jb = 0; jb < NJB; ++jb) aD[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                const bf16x8 ak = FF::fkc(Ks, DK, 16 * R, ks * KS);
+#pragma unroll
+                for (int jb = 0; jb < NJB; ++jb) MM::mma(aD[jb], ak, FR::kc(sm.dST, PK, 16 * jb, ks * KS));
+            }
+#pragma unroll
+            for (int kk = 0; kk < NCK; ++kk) {
+                if (kk * KS + KS > 16 * R) {  // P^T is upper triangular: s >= r
+                    const bf16x8 a = FF::ftr(Ps, C, kk * KS, 16 * R);
+#pragma unroll
+                    for (int jb = 0; jb < NJB; ++jb) MM::mma(aD[jb], a, FR::tr(Os, PO, kk * KS, 16 * jb));
+                }
+            }
+#pragma unroll
+            for (int jb = 0; jb < NJB; ++jb) store_acc_T(sm.dDT, PC, 16 * jb, 16 * R, aD[jb]);
+        }
+        lds_barrier();
+        // ---- dS <- Diag(gamma) dS' + Qbar^T dO + (-Y)^T dDelta
+#pragma unroll
+        for (int u = 0; u < BPW; ++u) {
+            const int bi = R * BPW + u, ib = bi / NJB, jb = bi % NJB;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dS[u][e] *= sm.gam[sl][16 * ib + acc_row(e)];
+#pragma unroll
+            for (int kk = 0; kk < NCK; ++kk) {
+                MM::mma(dS[u], FF::ftr(Qs, DK, kk * KS, 16 * ib), FR::tr(Os, PO, kk * KS, 16 * jb));
+                MM::mma(dS[u], FF::ftr(Ys, DK, kk * KS, 16 * ib), FR::kc(sm.dDT, PC, 16 * jb, kk * KS));
+            }
+            store_acc_T(sm.dST, PK, 16 * jb, 16 * ib, dS[u]);
+        }
+        lds_barrier();
+    };
+
+    const int NCR = (NC + 1) / 2 * 2;
+    if (loader) {
+        for (int st = 0; st < NCR; st += 2) {
+            loader_step(st, lbA);
+            loader_step(st + 1, lbB);
+        }
+    } else {
+        for (int st = 0; st < NCR; st += 2) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                if (st + u < NC) {
+                    compute_step(NC - 1 - st - u, (st + u) & 1);
+                } else {
+                    lds_barrier();
+                    lds_barrier();
+                }
+            }
+        }
+        if (p.dS0) {
+#pragma unroll
+            for (int u = 0; u < BPW; ++u) {
+                const int bi = R * BPW + u, ib = bi / NJB, jb = bi % NJB;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    p.dS0[((long)chain * DK + 16 * ib + acc_row(e)) * DV + j0 + 16 * jb + acc_col()] = dS[u][e];
+            }
+        }
+    }
+}
+
+template <int DK, int DVS>
+static hipError_t launch_dstate_lds(const BwdParams& p, hipStream_t s) {
+    const long nblk = (long)p.B * p.H * p.NS;
+    if (nblk == 0) return hipSuccess;
+    hipLaunchKernelGGL((gdr2_dstate_lds_kernel<DK, DVS>), dim3(nblk), dim3(2 * kThreads), 0, s, p);
+    return hipGetLastError();
+}
+
 template <typename OT, int DK, int DVS>
 static hipError_t launch_dstate(const BwdParams& p, hipStream_t s) {
     const long nblk = (long)p.B * p.H * p.NS;
@@ -222,12 +450,11 @@ static hipError_t launch_dstate(const BwdParams& p, hipStream_t s) {
 
 hipError_t dstate_dispatch(int bf, int dk, int dvs, const BwdParams& p, hipStream_t s) {
     if (bf) {
-        if (dk == 128 && dvs == 64) return launch_dstate<bf16, 128, 64>(p, s);
-        if (dk == 128 && dvs == 32) return launch_dstate<bf16, 128, 32>(p, s);
-        if (dk == 128 && dvs == 16) return launch_dstate<bf16, 128, 16>(p, s);
-        if (dk == 64 && dvs == 64) return launch_dstate<bf16, 64, 64>(p, s);
-        if (dk == 64 && dvs == 32) return launch_dstate<bf16, 64, 32>(p, s);
-        if (dk == 64 && dvs == 16) return launch_dstate<bf16, 64, 16>(p, s);
+        if (dk == 128 && dvs == 32) return launch_dstate_lds<128, 32>(p, s);
+        if (dk == 128 && dvs == 16) return launch_dstate_lds<128, 16>(p, s);
+        if (dk == 64 && dvs == 64) return launch_dstate_lds<64, 64>(p, s);
+        if (dk == 64 && dvs == 32) return launch_dstate_lds<64, 32>(p, s);
+        if (dk == 64 && dvs == 16) return launch_dstate_lds<64, 16>(p, s);
     } else {
         if (dk == 128 && dvs == 32) return launch_dstate<float, 128, 32>(p, s);
         if (dk == 128 && dvs == 16) return launch_dstate<float, 128, 16>(p, s);
