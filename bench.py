@@ -31,11 +31,11 @@ B, T, H, DK, DV = 4, 4096, 16, 128, 128
 # writes o (2 d, the carry kernel); the backward reads those plus dO (16 d) and writes dq, dk, db,
 # dv, dw (bf16) and dlog alpha (fp32) (14 d) -- all in the chunk-gradient kernel.  Per-chunk
 # factors, checkpointed states and state gradients are design traffic, not algorithmic.
-ALG_BYTES_PER_HT = {"gdr2_wy_kernel": 14 * DK, "gdr2_carry_kernel": 2 * DV,
-                    "gdr2_dstate_kernel": 0, "gdr2_bgrad_kernel": 30 * DK}
+ALG_BYTES_PER_HT = {"gdr2_wy_kernel": 14 * DK, "gdr2_carry_lds_kernel": 2 * DV,
+                    "gdr2_dstate_lds_kernel": 0, "gdr2_bgrad_kernel": 30 * DK}
 ALG_FLOPS_PER_HT = {"forward": 6 * DK * DK + 5 * 64 * DK + 64 * 64 / 3,
                     "backward": 14 * DK * DK + 14 * 64 * DK + 64 * 64}
-KERNELS = ["gdr2_wy_kernel", "gdr2_carry_kernel", "gdr2_dstate_kernel", "gdr2_bgrad_kernel"]
+KERNELS = ["gdr2_wy_kernel", "gdr2_carry_lds_kernel", "gdr2_dstate_lds_kernel", "gdr2_bgrad_kernel"]
 SOURCES = ["gdr2_common.hpp", "gdr2_wy.hpp", "gdr2_fwd.hip", "gdr2_bwd.hip"]
 
 
