@@ -107,6 +107,51 @@ def bench_decode(torch, lib_decode, steps):
             "steps": steps}
 
 
+def bench_gate_variants(torch, g2, steps):
+    """The same fwd+bwd step with scalar-per-head gates (one value per token and head instead of
+    one per channel): erase and write gates ("bw"), and additionally the decay ("bwa").  Each
+    scalar gate saves its channel traffic in both passes."""
+    from gated_delta_rule_gdr_amd.inputs import layer_inputs
+    bf = torch.bfloat16
+    out = {}
+    for scalar in ("bw", "bwa"):
+        x = layer_inputs(B, T, H, DK, DV, dtype="bf16", seed=1001, device="cuda", scalar=scalar)
+        fws = torch.empty(g2.fwd_workspace_bytes(B, T, H, DK, DV, bf), dtype=torch.uint8, device="cuda")
+        bws = torch.empty(g2.bwd_workspace_bytes(B, T, H, DK, DV, bf), dtype=torch.uint8, device="cuda")
+        o = torch.empty((B, T, H, DV), dtype=bf, device="cuda")
+        gr = {n: torch.empty_like(x[s_]) for n, s_ in (("dq", "q"), ("dk", "k"), ("dv", "v"),
+                                                       ("dlog_alpha", "log_alpha"), ("db", "b"),
+                                                       ("dw", "w"))}
+        q, k, v, la, b, w, dO = (x[n] for n in ("q", "k", "v", "log_alpha", "b", "w", "dO"))
+
+        def step():
+            g2.gdr2_fwd_factors(q, k, v, la, b, w, fws)
+            g2.gdr2_fwd_carry(B, T, H, DK, DV, bf, fws, o)
+            g2.gdr2_bwd_state(B, T, H, DK, DV, bf, fws, dO, bws)
+            g2.gdr2_bwd_grads(q, k, v, la, b, w, fws, dO, bws, gr)
+
+        for _ in range(2):
+            step()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        # algorithmic bytes per head-token: a scalar bf16 gate moves 2 B instead of 2 d, a scalar
+        # decay 4 B instead of 4 d (read in both passes; its gradient written once)
+        fwd = 16 * DK - 4 * DK + 4 - (4 * DK - 4 if "a" in scalar else 0)
+        bwd = 30 * DK - 8 * DK + 8 - (8 * DK - 8 if "a" in scalar else 0)
+        out["scalar_" + scalar] = {"ms_per_step": round(ms, 4),
+                                   "Mtokens_per_s": round(B * T / ms / 1e3, 3),
+                                   "alg_bytes_per_head_token": fwd + bwd,
+                                   "hbm_frac": round((fwd + bwd) * B * T * H / (ms * 1e-3) / 1e9
+                                                     / HBM_PEAK_GBS, 4)}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -204,6 +249,8 @@ def main():
     }
     if not args.no_decode:
         out["decode"] = bench_decode(torch, g2.gdr2_decode_step, args.decode_steps)
+    if not args.profile_pass:
+        out["gate_variants"] = bench_gate_variants(torch, g2, 5)
     if args.profile_pass:
         src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)

@@ -9,6 +9,9 @@ Entry points (same names as the C ABI):
   gdr2_fwd_chunked(q, k, v, log_alpha, b, w, S0=None, want_final_state=True) -> (o, S_T, fwd_ws)
   gdr2_bwd_chunked(q, k, v, log_alpha, b, w, dO, fwd_ws, dS_T=None, want_dS0=True) -> grads
   gdr2_decode_step(q, k, v, log_alpha, b, w, S_in=None, S_out=None)
+Each of b, w and log_alpha may be channel-wise ([..., d]) or a scalar per head (the token shape of
+q without its channel axis); the gate-shape bits passed to the *_ex entry points follow from the
+shapes, and the gradients come back in the shape of their gate.
 """
 from __future__ import annotations
 
@@ -19,7 +22,8 @@ import torch
 
 __all__ = ["gdr2_fwd_chunked", "gdr2_bwd_chunked", "gdr2_decode_step", "gdr2_fwd_factors",
            "gdr2_fwd_carry", "gdr2_bwd_state", "gdr2_bwd_grads", "fwd_workspace_bytes",
-           "bwd_workspace_bytes", "library_path", "load_library", "Gdr2Error", "CHUNK"]
+           "bwd_workspace_bytes", "library_path", "load_library", "Gdr2Error", "CHUNK", "gate_bits",
+           "ERASE_SCALAR", "WRITE_SCALAR", "DECAY_SCALAR"]
 
 CHUNK = 64
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -68,6 +72,19 @@ def load_library():
     lib.gdr2_bwd_grads.restype = ctypes.c_int
     lib.gdr2_decode_step.argtypes = [I64] * 4 + [ctypes.c_int] + [P] * 10
     lib.gdr2_decode_step.restype = ctypes.c_int
+    U = ctypes.c_uint
+    lib.gdr2_fwd_chunked_ex.argtypes = [I64] * 5 + [ctypes.c_int, U] + [P] * 10 + [SZ, P]
+    lib.gdr2_fwd_chunked_ex.restype = ctypes.c_int
+    lib.gdr2_bwd_chunked_ex.argtypes = ([I64] * 5 + [ctypes.c_int, U] + [P] * 7 + [SZ] + [P] * 10
+                                        + [SZ, P])
+    lib.gdr2_bwd_chunked_ex.restype = ctypes.c_int
+    lib.gdr2_fwd_factors_ex.argtypes = [I64] * 5 + [ctypes.c_int, U] + [P] * 7 + [SZ, P]
+    lib.gdr2_fwd_factors_ex.restype = ctypes.c_int
+    lib.gdr2_bwd_grads_ex.argtypes = ([I64] * 5 + [ctypes.c_int, U] + [P] * 7 + [SZ] + [P] * 8
+                                      + [SZ, P])
+    lib.gdr2_bwd_grads_ex.restype = ctypes.c_int
+    lib.gdr2_decode_step_ex.argtypes = [I64] * 4 + [ctypes.c_int, U] + [P] * 10
+    lib.gdr2_decode_step_ex.restype = ctypes.c_int
     lib.gdr2_fwd_workspace_bytes.argtypes = [I64] * 5 + [ctypes.c_int]
     lib.gdr2_fwd_workspace_bytes.restype = SZ
     lib.gdr2_bwd_workspace_bytes.argtypes = [I64] * 5 + [ctypes.c_int]
@@ -108,6 +125,24 @@ def _dtype(q):
     return _DT[q.dtype]
 
 
+# gate-shape bits (gdr2_gates in include/gdr2.h)
+ERASE_SCALAR, WRITE_SCALAR, DECAY_SCALAR = 1, 2, 4
+
+
+def gate_bits(q, log_alpha, b, w):
+    """Gate shapes from the tensor shapes: a gate with the token shape of q without its channel
+    axis ([B, T, H], or [N, H] for decode) is a scalar per head; otherwise it must have the full
+    channel shape."""
+    bits = 0
+    for t, bit, name in ((b, ERASE_SCALAR, "b"), (w, WRITE_SCALAR, "w"), (log_alpha, DECAY_SCALAR, "log_alpha")):
+        if tuple(t.shape) == tuple(q.shape[:-1]):
+            bits |= bit
+        elif t.dim() != q.dim() or tuple(t.shape[:-1]) != tuple(q.shape[:-1]):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}; expected the token shape "
+                             f"{tuple(q.shape[:-1])} (scalar per head) or that plus a channel axis")
+    return bits
+
+
 def _contig(*ts):
     for t in ts:
         if t is not None and not t.is_contiguous():
@@ -127,9 +162,9 @@ def gdr2_fwd_chunked(q, k, v, log_alpha, b, w, S0=None, want_final_state=True, w
     need = lib.gdr2_fwd_workspace_bytes(B, T, H, dk, dv, dt)
     ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8,
                                                              device=q.device)
-    st = lib.gdr2_fwd_chunked(B, T, H, dk, dv, dt, _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
-                              _ptr(b), _ptr(w), _ptr(S0), _ptr(o), _ptr(ST), _ptr(ws),
-                              ws.numel(), _stream())
+    st = lib.gdr2_fwd_chunked_ex(B, T, H, dk, dv, dt, gate_bits(q, log_alpha, b, w), _ptr(q),
+                                 _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w), _ptr(S0),
+                                 _ptr(o), _ptr(ST), _ptr(ws), ws.numel(), _stream())
     _check("gdr2_fwd_chunked", st)
     return o, ST, ws
 
@@ -150,11 +185,12 @@ def gdr2_bwd_chunked(q, k, v, log_alpha, b, w, dO, fwd_ws, dS_T=None, want_dS0=T
     need = lib.gdr2_bwd_workspace_bytes(B, T, H, dk, dv, dt)
     ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8,
                                                              device=dev)
-    st = lib.gdr2_bwd_chunked(B, T, H, dk, dv, dt, _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
-                              _ptr(b), _ptr(w), _ptr(fwd_ws), fwd_ws.numel(), _ptr(dO),
-                              _ptr(dS_T), _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]),
-                              _ptr(g["dlog_alpha"]), _ptr(g["db"]), _ptr(g["dw"]),
-                              _ptr(g["dS0"]), _ptr(ws), ws.numel(), _stream())
+    st = lib.gdr2_bwd_chunked_ex(B, T, H, dk, dv, dt, gate_bits(q, log_alpha, b, w), _ptr(q),
+                                 _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w),
+                                 _ptr(fwd_ws), fwd_ws.numel(), _ptr(dO), _ptr(dS_T),
+                                 _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]),
+                                 _ptr(g["dlog_alpha"]), _ptr(g["db"]), _ptr(g["dw"]),
+                                 _ptr(g["dS0"]), _ptr(ws), ws.numel(), _stream())
     _check("gdr2_bwd_chunked", st)
     return g
 
@@ -170,9 +206,10 @@ def bwd_workspace_bytes(B, T, H, dk, dv, dtype):
 def gdr2_fwd_factors(q, k, v, log_alpha, b, w, ws):
     """Stage 1 of the forward: per-chunk WY factors into ``ws`` (uint8 device tensor)."""
     B, T, H, dk, dv = _shapes(q, v)
-    st = load_library().gdr2_fwd_factors(B, T, H, dk, dv, _dtype(q), _ptr(q), _ptr(k), _ptr(v),
-                                         _ptr(log_alpha), _ptr(b), _ptr(w), _ptr(ws), ws.numel(),
-                                         _stream())
+    st = load_library().gdr2_fwd_factors_ex(B, T, H, dk, dv, _dtype(q),
+                                            gate_bits(q, log_alpha, b, w), _ptr(q), _ptr(k),
+                                            _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w), _ptr(ws),
+                                            ws.numel(), _stream())
     _check("gdr2_fwd_factors", st)
 
 
@@ -195,11 +232,13 @@ def gdr2_bwd_grads(q, k, v, log_alpha, b, w, fwd_ws, dO, bws, g):
     """Stage 2 of the backward: fills g["dq"], g["dk"], g["dv"], g["dlog_alpha"], g["db"],
     g["dw"] (preallocated)."""
     B, T, H, dk, dv = _shapes(q, v)
-    st = load_library().gdr2_bwd_grads(B, T, H, dk, dv, _dtype(q), _ptr(q), _ptr(k), _ptr(v),
-                                       _ptr(log_alpha), _ptr(b), _ptr(w), _ptr(fwd_ws),
-                                       fwd_ws.numel(), _ptr(dO), _ptr(g["dq"]), _ptr(g["dk"]),
-                                       _ptr(g["dv"]), _ptr(g["dlog_alpha"]), _ptr(g["db"]),
-                                       _ptr(g["dw"]), _ptr(bws), bws.numel(), _stream())
+    st = load_library().gdr2_bwd_grads_ex(B, T, H, dk, dv, _dtype(q),
+                                          gate_bits(q, log_alpha, b, w), _ptr(q), _ptr(k),
+                                          _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w),
+                                          _ptr(fwd_ws), fwd_ws.numel(), _ptr(dO), _ptr(g["dq"]),
+                                          _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["dlog_alpha"]),
+                                          _ptr(g["db"]), _ptr(g["dw"]), _ptr(bws), bws.numel(),
+                                          _stream())
     _check("gdr2_bwd_grads", st)
 
 
@@ -215,7 +254,8 @@ def gdr2_decode_step(q, k, v, log_alpha, b, w, S_in=None, S_out=None):
         S_out = S_in if S_in is not None else torch.empty((N, H, dk, dv), dtype=torch.float32,
                                                           device=q.device)
     o = torch.empty((N, H, dv), dtype=q.dtype, device=q.device)
-    st = lib.gdr2_decode_step(N, H, dk, dv, dt, _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
-                              _ptr(b), _ptr(w), _ptr(S_in), _ptr(S_out), _ptr(o), _stream())
+    st = lib.gdr2_decode_step_ex(N, H, dk, dv, dt, gate_bits(q, log_alpha, b, w), _ptr(q),
+                                 _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w), _ptr(S_in),
+                                 _ptr(S_out), _ptr(o), _stream())
     _check("gdr2_decode_step", st)
     return o, S_out

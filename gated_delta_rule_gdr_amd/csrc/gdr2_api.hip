@@ -36,6 +36,18 @@ bool any_alias(const Range* outs, int no, const Range* ins, int ni) {
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+bool gates_ok(unsigned gates) { return (gates & ~7u) == 0; }
+
+// Elements of b, w and log alpha (and of db, dw, dlog alpha) for `tokens` token-heads.
+struct GateSizes {
+    size_t nb, nw, na;
+};
+GateSizes gate_sizes(unsigned gates, size_t tokens, int64_t dk, int64_t dv) {
+    return {(gates & GDR2_ERASE_SCALAR) ? tokens : tokens * dk,
+            (gates & GDR2_WRITE_SCALAR) ? tokens : tokens * dv,
+            (gates & GDR2_DECAY_SCALAR) ? tokens : tokens * dk};
+}
+
 }  // namespace
 
 extern "C" {
@@ -126,8 +138,9 @@ static gdr2_status check_chunked(int64_t B, int64_t T, int64_t H, int64_t dk, in
 static gdr2::FwdParams fwd_params(int64_t B, int64_t T, int64_t H, int64_t dv, const void* q,
                                   const void* k, const void* v, const float* la, const void* b,
                                   const void* w, const float* S0, void* o, float* S_T,
-                                  const FwdWs& L, void* ws, int dvs) {
+                                  const FwdWs& L, void* ws, int dvs, unsigned gates = 0) {
     gdr2::FwdParams p;
+    p.gates = (int)gates;
     p.B = (int)B;
     p.H = (int)H;
     p.NS = (int)(dv / dvs);
@@ -150,9 +163,10 @@ static gdr2_status check_fwd(int64_t B, int64_t T, int64_t H, int64_t dk, int64_
                              gdr2_dtype dt, const void* q, const void* k, const void* v,
                              const float* la, const void* b, const void* w, const float* S0,
                              void* o, float* S_T, void* ws, size_t ws_bytes, bool need_inputs,
-                             bool need_out) {
+                             bool need_out, unsigned gates = 0) {
     gdr2_status st = check_chunked(B, T, H, dk, dv, dt);
     if (st != GDR2_OK) return st;
+    if (!gates_ok(gates)) return GDR2_E_UNSUPPORTED;
     const bool have_tokens = B > 0 && H > 0 && T > 0;
     if (have_tokens && need_inputs && (!q || !k || !v || !la || !b || !w)) return GDR2_E_NULL;
     if (have_tokens && need_out && !o) return GDR2_E_NULL;
@@ -164,26 +178,36 @@ static gdr2_status check_fwd(int64_t B, int64_t T, int64_t H, int64_t dk, int64_
     const size_t es = gdr2_dtype_size(dt);
     const size_t nk = (size_t)B * T * H * dk, nv = (size_t)B * T * H * dv;
     const size_t ns = (size_t)B * H * dk * dv;
-    const Range ins[] = {{q, nk * es}, {k, nk * es}, {v, nv * es}, {la, nk * 4},
-                         {b, nk * es}, {w, nv * es}, {S0, ns * 4}};
+    const GateSizes gs = gate_sizes(gates, (size_t)B * T * H, dk, dv);
+    const Range ins[] = {{q, nk * es}, {k, nk * es}, {v, nv * es}, {la, gs.na * 4},
+                         {b, gs.nb * es}, {w, gs.nw * es}, {S0, ns * 4}};
     const Range outs[] = {{o, nv * es}, {S_T, ns * 4}, {ws, have_tokens ? L.total : 0}};
     if (any_alias(outs, 3, ins, 7)) return GDR2_E_ALIAS;
     return GDR2_OK;
+}
+
+gdr2_status gdr2_fwd_factors_ex(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                                gdr2_dtype dt, unsigned gates, const void* q, const void* k,
+                                const void* v, const float* log_alpha, const void* b,
+                                const void* w, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+    gdr2_status st = check_fwd(B, T, H, dk, dv, dt, q, k, v, log_alpha, b, w, nullptr, nullptr,
+                               nullptr, workspace, workspace_bytes, true, false, gates);
+    if (st != GDR2_OK || B == 0 || H == 0 || T == 0) return st;
+    const int bf = dt == GDR2_BF16;
+    const FwdWs L = fwd_ws_layout(B, T, H, dk, dv, dt);
+    gdr2::FwdParams p = fwd_params(B, T, H, dv, q, k, v, log_alpha, b, w, nullptr, nullptr,
+                                   nullptr, L, workspace, 16, gates);
+    hipError_t e = gdr2::wy_dispatch(bf, (int)dk, (int)dv, p, (hipStream_t)stream);
+    return e == hipSuccess ? GDR2_OK : GDR2_E_HIP;
 }
 
 gdr2_status gdr2_fwd_factors(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
                              gdr2_dtype dt, const void* q, const void* k, const void* v,
                              const float* log_alpha, const void* b, const void* w,
                              void* workspace, size_t workspace_bytes, void* stream) {
-    gdr2_status st = check_fwd(B, T, H, dk, dv, dt, q, k, v, log_alpha, b, w, nullptr, nullptr,
-                               nullptr, workspace, workspace_bytes, true, false);
-    if (st != GDR2_OK || B == 0 || H == 0 || T == 0) return st;
-    const int bf = dt == GDR2_BF16;
-    const FwdWs L = fwd_ws_layout(B, T, H, dk, dv, dt);
-    gdr2::FwdParams p = fwd_params(B, T, H, dv, q, k, v, log_alpha, b, w, nullptr, nullptr,
-                                   nullptr, L, workspace, 16);
-    hipError_t e = gdr2::wy_dispatch(bf, (int)dk, (int)dv, p, (hipStream_t)stream);
-    return e == hipSuccess ? GDR2_OK : GDR2_E_HIP;
+    return gdr2_fwd_factors_ex(B, T, H, dk, dv, dt, 0u, q, k, v, log_alpha, b, w, workspace,
+                               workspace_bytes, stream);
 }
 
 gdr2_status gdr2_fwd_carry(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
@@ -201,20 +225,29 @@ gdr2_status gdr2_fwd_carry(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t 
     return e == hipSuccess ? GDR2_OK : GDR2_E_HIP;
 }
 
+gdr2_status gdr2_fwd_chunked_ex(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                                gdr2_dtype dt, unsigned gates, const void* q, const void* k,
+                                const void* v, const float* log_alpha, const void* b,
+                                const void* w, const float* S0, void* o, float* S_T,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+    gdr2_status st = check_fwd(B, T, H, dk, dv, dt, q, k, v, log_alpha, b, w, S0, o, S_T,
+                               workspace, workspace_bytes, true, true, gates);
+    if (st != GDR2_OK || B == 0 || H == 0) return st;
+    if (T > 0) {
+        st = gdr2_fwd_factors_ex(B, T, H, dk, dv, dt, gates, q, k, v, log_alpha, b, w, workspace,
+                                 workspace_bytes, stream);
+        if (st != GDR2_OK) return st;
+    }
+    return gdr2_fwd_carry(B, T, H, dk, dv, dt, S0, o, S_T, workspace, workspace_bytes, stream);
+}
+
 gdr2_status gdr2_fwd_chunked(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
                              gdr2_dtype dt, const void* q, const void* k, const void* v,
                              const float* log_alpha, const void* b, const void* w,
                              const float* S0, void* o, float* S_T, void* workspace,
                              size_t workspace_bytes, void* stream) {
-    gdr2_status st = check_fwd(B, T, H, dk, dv, dt, q, k, v, log_alpha, b, w, S0, o, S_T,
-                               workspace, workspace_bytes, true, true);
-    if (st != GDR2_OK || B == 0 || H == 0) return st;
-    if (T > 0) {
-        st = gdr2_fwd_factors(B, T, H, dk, dv, dt, q, k, v, log_alpha, b, w, workspace,
-                              workspace_bytes, stream);
-        if (st != GDR2_OK) return st;
-    }
-    return gdr2_fwd_carry(B, T, H, dk, dv, dt, S0, o, S_T, workspace, workspace_bytes, stream);
+    return gdr2_fwd_chunked_ex(B, T, H, dk, dv, dt, 0u, q, k, v, log_alpha, b, w, S0, o, S_T,
+                               workspace, workspace_bytes, stream);
 }
 
 // Validation shared by the backward phases.
@@ -223,9 +256,11 @@ static gdr2_status check_bwd(int64_t B, int64_t T, int64_t H, int64_t dk, int64_
                              const float* la, const void* b, const void* w, const void* fws,
                              size_t fws_bytes, const void* dO, const float* dS_T, void* dq,
                              void* dk_, void* dv_, float* dla, void* db, void* dw, float* dS0,
-                             const void* ws, size_t ws_bytes, bool need_inputs, bool need_grads) {
+                             const void* ws, size_t ws_bytes, bool need_inputs, bool need_grads,
+                             unsigned gates = 0) {
     gdr2_status st = check_chunked(B, T, H, dk, dv, dt);
     if (st != GDR2_OK) return st;
+    if (!gates_ok(gates)) return GDR2_E_UNSUPPORTED;
     const bool have_tokens = B > 0 && H > 0 && T > 0;
     if (have_tokens && (!fws || !dO)) return GDR2_E_NULL;
     if (have_tokens && need_inputs && (!q || !k || !v || !la || !b || !w)) return GDR2_E_NULL;
@@ -239,13 +274,14 @@ static gdr2_status check_bwd(int64_t B, int64_t T, int64_t H, int64_t dk, int64_
     const size_t es = gdr2_dtype_size(dt);
     const size_t nk = (size_t)B * T * H * dk, nv = (size_t)B * T * H * dv;
     const size_t ns = (size_t)B * H * dk * dv;
-    const Range ins[] = {{q, nk * es},  {k, nk * es},  {v, nv * es},   {la, nk * 4},
-                         {b, nk * es},  {w, nv * es},  {fws, have_tokens ? L.total : 0},
-                         {dO, nv * es}, {dS_T, ns * 4}};
+    const GateSizes gs = gate_sizes(gates, (size_t)B * T * H, dk, dv);
+    const Range ins[] = {{q, nk * es},      {k, nk * es},      {v, nv * es},
+                         {la, gs.na * 4},   {b, gs.nb * es},   {w, gs.nw * es},
+                         {fws, have_tokens ? L.total : 0}, {dO, nv * es}, {dS_T, ns * 4}};
     // the state phase writes the workspace; the gradient phase reads it (then it is an input)
-    const Range outs[] = {{dq, nk * es}, {dk_, nk * es}, {dv_, nv * es}, {dla, nk * 4},
-                          {db, nk * es}, {dw, nv * es},  {dS0, ns * 4},
-                          {ws, have_tokens ? need : 0}};
+    const Range outs[] = {{dq, nk * es},     {dk_, nk * es},    {dv_, nv * es},
+                          {dla, gs.na * 4},  {db, gs.nb * es},  {dw, gs.nw * es},
+                          {dS0, ns * 4},     {ws, have_tokens ? need : 0}};
     if (any_alias(outs, 8, ins, 9)) return GDR2_E_ALIAS;
     return GDR2_OK;
 }
@@ -255,10 +291,11 @@ static gdr2::BwdParams bwd_params(int64_t B, int64_t T, int64_t H, int64_t dk, i
                                   const float* la, const void* b, const void* w, const void* fws,
                                   const void* dO, const float* dS_T, void* dq, void* dk_,
                                   void* dv_, float* dla, void* db, void* dw, float* dS0,
-                                  const void* ws) {
+                                  const void* ws, unsigned gates = 0) {
     const int bf = dt == GDR2_BF16;
     const FwdWs L = fwd_ws_layout(B, T, H, dk, dv, dt);
     gdr2::BwdParams p;
+    p.gates = (int)gates;
     p.B = (int)B; p.H = (int)H; p.NC = (int)gdr2_num_chunks(T); p.T = T; p.DV = dv;
     p.NS = (int)(dv / gdr2::carry_slice_width(bf, (int)dk, (int)dv, B * H));
     p.q = q; p.k = k; p.v = v; p.b = b; p.w = w; p.la = la;
@@ -287,22 +324,54 @@ gdr2_status gdr2_bwd_state(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t 
     return e == hipSuccess ? GDR2_OK : GDR2_E_HIP;
 }
 
+gdr2_status gdr2_bwd_grads_ex(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                              gdr2_dtype dt, unsigned gates, const void* q, const void* k,
+                              const void* v, const float* log_alpha, const void* b, const void* w,
+                              const void* fwd_workspace, size_t fwd_workspace_bytes,
+                              const void* dO, void* dq, void* dk_, void* dv_, float* dlog_alpha,
+                              void* db, void* dw, const void* workspace, size_t workspace_bytes,
+                              void* stream) {
+    gdr2_status st = check_bwd(B, T, H, dk, dv, dt, q, k, v, log_alpha, b, w, fwd_workspace,
+                               fwd_workspace_bytes, dO, nullptr, dq, dk_, dv_, dlog_alpha, db, dw,
+                               nullptr, workspace, workspace_bytes, true, true, gates);
+    if (st != GDR2_OK || B == 0 || H == 0 || T == 0) return st;
+    const int bf = dt == GDR2_BF16;
+    gdr2::BwdParams p = bwd_params(B, T, H, dk, dv, dt, q, k, v, log_alpha, b, w, fwd_workspace,
+                                   dO, nullptr, dq, dk_, dv_, dlog_alpha, db, dw, nullptr,
+                                   workspace, gates);
+    hipError_t e = gdr2::bgrad_dispatch(bf, (int)dk, (int)dv, p, (hipStream_t)stream);
+    return e == hipSuccess ? GDR2_OK : GDR2_E_HIP;
+}
+
 gdr2_status gdr2_bwd_grads(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
                            gdr2_dtype dt, const void* q, const void* k, const void* v,
                            const float* log_alpha, const void* b, const void* w,
                            const void* fwd_workspace, size_t fwd_workspace_bytes, const void* dO,
                            void* dq, void* dk_, void* dv_, float* dlog_alpha, void* db, void* dw,
                            const void* workspace, size_t workspace_bytes, void* stream) {
+    return gdr2_bwd_grads_ex(B, T, H, dk, dv, dt, 0u, q, k, v, log_alpha, b, w, fwd_workspace,
+                             fwd_workspace_bytes, dO, dq, dk_, dv_, dlog_alpha, db, dw, workspace,
+                             workspace_bytes, stream);
+}
+
+gdr2_status gdr2_bwd_chunked_ex(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                                gdr2_dtype dt, unsigned gates, const void* q, const void* k,
+                                const void* v, const float* log_alpha, const void* b,
+                                const void* w, const void* fwd_workspace,
+                                size_t fwd_workspace_bytes, const void* dO, const float* dS_T,
+                                void* dq, void* dk_, void* dv_, float* dlog_alpha, void* db,
+                                void* dw, float* dS0, void* workspace, size_t workspace_bytes,
+                                void* stream) {
     gdr2_status st = check_bwd(B, T, H, dk, dv, dt, q, k, v, log_alpha, b, w, fwd_workspace,
-                               fwd_workspace_bytes, dO, nullptr, dq, dk_, dv_, dlog_alpha, db, dw,
-                               nullptr, workspace, workspace_bytes, true, true);
-    if (st != GDR2_OK || B == 0 || H == 0 || T == 0) return st;
-    const int bf = dt == GDR2_BF16;
-    gdr2::BwdParams p = bwd_params(B, T, H, dk, dv, dt, q, k, v, log_alpha, b, w, fwd_workspace,
-                                   dO, nullptr, dq, dk_, dv_, dlog_alpha, db, dw, nullptr,
-                                   workspace);
-    hipError_t e = gdr2::bgrad_dispatch(bf, (int)dk, (int)dv, p, (hipStream_t)stream);
-    return e == hipSuccess ? GDR2_OK : GDR2_E_HIP;
+                               fwd_workspace_bytes, dO, dS_T, dq, dk_, dv_, dlog_alpha, db, dw,
+                               dS0, workspace, workspace_bytes, true, true, gates);
+    if (st != GDR2_OK || B == 0 || H == 0) return st;
+    st = gdr2_bwd_state(B, T, H, dk, dv, dt, fwd_workspace, fwd_workspace_bytes, dO, dS_T, dS0,
+                        workspace, workspace_bytes, stream);
+    if (st != GDR2_OK || T == 0) return st;
+    return gdr2_bwd_grads_ex(B, T, H, dk, dv, dt, gates, q, k, v, log_alpha, b, w, fwd_workspace,
+                             fwd_workspace_bytes, dO, dq, dk_, dv_, dlog_alpha, db, dw, workspace,
+                             workspace_bytes, stream);
 }
 
 gdr2_status gdr2_bwd_chunked(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
@@ -312,25 +381,18 @@ gdr2_status gdr2_bwd_chunked(int64_t B, int64_t T, int64_t H, int64_t dk, int64_
                              const void* dO, const float* dS_T, void* dq, void* dk_, void* dv_,
                              float* dlog_alpha, void* db, void* dw, float* dS0,
                              void* workspace, size_t workspace_bytes, void* stream) {
-    gdr2_status st = check_bwd(B, T, H, dk, dv, dt, q, k, v, log_alpha, b, w, fwd_workspace,
+    return gdr2_bwd_chunked_ex(B, T, H, dk, dv, dt, 0u, q, k, v, log_alpha, b, w, fwd_workspace,
                                fwd_workspace_bytes, dO, dS_T, dq, dk_, dv_, dlog_alpha, db, dw,
-                               dS0, workspace, workspace_bytes, true, true);
-    if (st != GDR2_OK || B == 0 || H == 0) return st;
-    st = gdr2_bwd_state(B, T, H, dk, dv, dt, fwd_workspace, fwd_workspace_bytes, dO, dS_T, dS0,
-                        workspace, workspace_bytes, stream);
-    if (st != GDR2_OK || T == 0) return st;
-    return gdr2_bwd_grads(B, T, H, dk, dv, dt, q, k, v, log_alpha, b, w, fwd_workspace,
-                          fwd_workspace_bytes, dO, dq, dk_, dv_, dlog_alpha, db, dw, workspace,
-                          workspace_bytes, stream);
+                               dS0, workspace, workspace_bytes, stream);
 }
 
-gdr2_status gdr2_decode_step(int64_t N, int64_t H, int64_t dk, int64_t dv, gdr2_dtype dt,
-                             const void* q, const void* k, const void* v,
-                             const float* log_alpha, const void* b, const void* w,
-                             const float* S_in, float* S_out, void* o, void* stream) {
+gdr2_status gdr2_decode_step_ex(int64_t N, int64_t H, int64_t dk, int64_t dv, gdr2_dtype dt,
+                                unsigned gates, const void* q, const void* k, const void* v,
+                                const float* log_alpha, const void* b, const void* w,
+                                const float* S_in, float* S_out, void* o, void* stream) {
     if (dt != GDR2_F32 && dt != GDR2_BF16) return GDR2_E_DTYPE;
     if (N < 0 || H < 0 || dk < 0 || dv < 0) return GDR2_E_SHAPE;
-    if (!dims_ok(dk) || !dims_ok(dv)) return GDR2_E_UNSUPPORTED;
+    if (!dims_ok(dk) || !dims_ok(dv) || !gates_ok(gates)) return GDR2_E_UNSUPPORTED;
     if (N * H > ((int64_t)1 << 31) - 1) return GDR2_E_SHAPE;
     if (N == 0 || H == 0) return GDR2_OK;
     if (!q || !k || !v || !log_alpha || !b || !w || !S_out || !o) return GDR2_E_NULL;
@@ -339,8 +401,9 @@ gdr2_status gdr2_decode_step(int64_t N, int64_t H, int64_t dk, int64_t dv, gdr2_
         if (p && !aligned16(p)) return GDR2_E_ALIGN;
     const size_t es = gdr2_dtype_size(dt);
     const size_t nk = (size_t)N * H * dk, nv = (size_t)N * H * dv, ns = (size_t)N * H * dk * dv;
-    const Range ins[] = {{q, nk * es}, {k, nk * es}, {v, nv * es}, {log_alpha, nk * 4},
-                         {b, nk * es}, {w, nv * es}};
+    const GateSizes gs = gate_sizes(gates, (size_t)N * H, dk, dv);
+    const Range ins[] = {{q, nk * es}, {k, nk * es}, {v, nv * es}, {log_alpha, gs.na * 4},
+                         {b, gs.nb * es}, {w, gs.nw * es}};
     const Range outs[] = {{S_out, ns * 4}, {o, nv * es}};
     if (any_alias(outs, 2, ins, 6)) return GDR2_E_ALIAS;
     // S_in may be S_out exactly; any other overlap with an output is an error
@@ -348,11 +411,19 @@ gdr2_status gdr2_decode_step(int64_t N, int64_t H, int64_t dk, int64_t dv, gdr2_
         return GDR2_E_ALIAS;
     if (S_in && S_in == S_out && overlap({S_in, ns * 4}, outs[1])) return GDR2_E_ALIAS;
     gdr2::DecodeParams p;
-    p.N = N; p.H = H;
+    p.N = N; p.H = H; p.gates = (int)gates;
     p.q = q; p.k = k; p.v = v; p.b = b; p.w = w; p.la = log_alpha;
     p.S_in = S_in; p.S_out = S_out; p.o = o;
     hipError_t e = gdr2::decode_dispatch(dt == GDR2_BF16, (int)dk, (int)dv, p, (hipStream_t)stream);
     return e == hipSuccess ? GDR2_OK : GDR2_E_HIP;
+}
+
+gdr2_status gdr2_decode_step(int64_t N, int64_t H, int64_t dk, int64_t dv, gdr2_dtype dt,
+                             const void* q, const void* k, const void* v,
+                             const float* log_alpha, const void* b, const void* w,
+                             const float* S_in, float* S_out, void* o, void* stream) {
+    return gdr2_decode_step_ex(N, H, dk, dv, dt, 0u, q, k, v, log_alpha, b, w, S_in, S_out, o,
+                               stream);
 }
 
 }  // extern "C"

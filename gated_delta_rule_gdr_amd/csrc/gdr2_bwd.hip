@@ -530,9 +530,10 @@ struct alignas(16) BgSmem {
     float r6[DK];
     float btot[4][DK];
     float ktot[4][DK];
+    float gred[2][kChunk][3];  // per-token partial sums of db, dw, dlog alpha (scalar gates)
 };
 
-template <typename OT, int DK, int DV, int DVH>
+template <typename OT, int DK, int DV, int DVH, bool GS>
 __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) {
     using Cf = BgCfg<OT, DK, DV, DVH>;
     using MM = Mfma<OT>;
@@ -561,9 +562,18 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
 
     // ---- this lane's log alpha (token r, channels 16 (ibase+ib) + 4g + e); q, k, b come later
     typename RW::t qr[NIBH], kr[NIBH], br[NIBH];
+    // scalar gates (GS instances only: the channel-wise instance carries no gate branches)
+    const bool b_sc = GS && (p.gates & kEraseScalar), w_sc = GS && (p.gates & kWriteScalar);
+    const bool a_sc = GS && (p.gates & kDecayScalar);
     f32x4 sc[NIBH];  // log alpha, then G_r - ref_R
+    if (a_sc) {
+        const float x = p.la[row];
 #pragma unroll
-    for (int ib = 0; ib < NIBH; ++ib) sc[ib] = *(const f32x4*)(p.la + row * DK + 16 * (ibase + ib) + 4 * g);
+        for (int ib = 0; ib < NIBH; ++ib) sc[ib] = f32x4{x, x, x, x};
+    } else {
+#pragma unroll
+        for (int ib = 0; ib < NIBH; ++ib) sc[ib] = *(const f32x4*)(p.la + row * DK + 16 * (ibase + ib) + 4 * g);
+    }
     // ---- the chunk's -Y and Ktilde: staged into LDS with T and P below (16-bit operands), or
     //      this wave's token block kept as fragments (fp32)
     constexpr bool YK_LDS = Cf::YK_LDS;
@@ -615,9 +625,15 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
             pO[m] = z;
         }
         // v, w of (token r, columns jb0 + 16 half + 4g .. +3) for dv, dw
-        const long o = (valid ? (tok0 + (long)r * H) : row) * DV + jb0 + 16 * half + 4 * g;
+        const long trow = valid ? (tok0 + (long)r * H) : row;
+        const long o = trow * DV + jb0 + 16 * half + 4 * g;
         pv = *(const typename RW::t*)((const OT*)p.v + o);
-        pw = *(const typename RW::t*)((const OT*)p.w + o);
+        if (w_sc) {
+            const OT x = ((const OT*)p.w)[trow];
+            pw = typename RW::t{x, x, x, x};
+        } else {
+            pw = *(const typename RW::t*)((const OT*)p.w + o);
+        }
         pU = *(const typename RW::t*)(Uc + ((long)(R * (DV / 16) + jb0 / 16 + half) * 64 + l) * 4);
     };
     i32x4 pT[TVEC], pP[TVEC];
@@ -679,6 +695,7 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
         }
     }
 
+    float dw_acc = 0.f;                   // sum_j dX_j v_j of this lane's columns (scalar w)
     f32x4 A1[NIBH], A2[NIBH], A3[NIBH];  // R1, R2, R3 (channel x token)
     f32x4 R4[2], R5[2];                   // dO Delta^T, dX Delta^T for s-blocks 2half+{0,1}
 #pragma unroll
@@ -712,7 +729,12 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
                 const int i0 = 16 * (ibase + ib) + 4 * g;
                 qr[ib] = *(const typename RW::t*)((const OT*)p.q + row * DK + i0);
                 kr[ib] = *(const typename RW::t*)((const OT*)p.k + row * DK + i0);
-                br[ib] = *(const typename RW::t*)((const OT*)p.b + row * DK + i0);
+                if (b_sc) {
+                    const OT x = ((const OT*)p.b)[row];
+                    br[ib] = typename RW::t{x, x, x, x};
+                } else {
+                    br[ib] = *(const typename RW::t*)((const OT*)p.b + row * DK + i0);
+                }
             }
         }
         lds_barrier();
@@ -748,10 +770,14 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
                 MM::mma(ax, FR::kc(sm.u.j.dDT, PC, 16 * jb, k0), FR::tr(sm.u.j.Tt, PC, k0, 16 * R));
             const int jc = 16 * jb + 4 * g;
             store4(sm.u.j.dXt + r * PH + jc, ax);
+            if (w_sc) {
+                const f32x4 xv = ax * RW::widen(cv);
+                dw_acc += (xv[0] + xv[1]) + (xv[2] + xv[3]);
+            }
             if (valid) {
                 const long o = (tok0 + (long)r * H) * DV + jb0 + jc;
                 store4((OT*)p.dv + o, ax * RW::widen(cw));
-                store4((OT*)p.dw + o, ax * RW::widen(cv));
+                if (!w_sc) store4((OT*)p.dw + o, ax * RW::widen(cv));
             }
         }
         lds_barrier();
@@ -872,6 +898,7 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
     // ---- epilogue: lane = token r, channels 16 (ibase + ib) + 4g + e
     f32x4 dG[NIBH];
     const long orow = row * DK;
+    float db_acc = 0.f;
 #pragma unroll
     for (int ib = 0; ib < NIBH; ++ib) {
         const int i0 = 16 * (ibase + ib) + 4 * g;
@@ -892,17 +919,31 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
             dG[ib][e] = row_rscan16(q4[e] * dq + b4[e] * k4[e] * de - k4[e] * (dkb + dkt));
             kdk[e] = row_rscan16(k4[e] * dkt);
         }
+        if (b_sc) db_acc += (dbv[0] + dbv[1]) + (dbv[2] + dbv[3]);
         if (valid) {
             store4((OT*)p.dq + orow + i0, dqv);
             store4((OT*)p.dk + orow + i0, dkv);
-            store4((OT*)p.db + orow + i0, dbv);
+            if (!b_sc) store4((OT*)p.db + orow + i0, dbv);
         }
         if (rl == 0) {
             *(f32x4*)(&sm.btot[R][i0]) = dG[ib];
             *(f32x4*)(&sm.ktot[R][i0]) = kdk;
         }
     }
+    // scalar gates: the gradient is the sum over this token's channels (lanes 16g + rl of both
+    // channel halves)
+    if (b_sc || w_sc) {
+        db_acc += __shfl_xor(db_acc, 16);
+        db_acc += __shfl_xor(db_acc, 32);
+        dw_acc += __shfl_xor(dw_acc, 16);
+        dw_acc += __shfl_xor(dw_acc, 32);
+        if (g == 0) {
+            sm.gred[half][r][0] = db_acc;
+            sm.gred[half][r][1] = dw_acc;
+        }
+    }
     lds_barrier();
+    float dl_acc = 0.f;
     if (valid) {
 #pragma unroll
         for (int ib = 0; ib < NIBH; ++ib) {
@@ -918,8 +959,23 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
                 }
                 dl[e] += add;
             }
-            *(f32x4*)(p.dla + orow + i0) = dl;
+            if (a_sc) {
+                dl_acc += (dl[0] + dl[1]) + (dl[2] + dl[3]);
+            } else {
+                *(f32x4*)(p.dla + orow + i0) = dl;
+            }
         }
+    }
+    if (a_sc) {
+        dl_acc += __shfl_xor(dl_acc, 16);
+        dl_acc += __shfl_xor(dl_acc, 32);
+        if (g == 0) sm.gred[half][r][2] = dl_acc;
+        lds_barrier();
+    }
+    if ((b_sc || w_sc || a_sc) && half == 0 && g == 0 && valid) {
+        if (b_sc) ((OT*)p.db)[row] = from_f<OT>(sm.gred[0][r][0] + sm.gred[1][r][0]);
+        if (w_sc) ((OT*)p.dw)[row] = from_f<OT>(sm.gred[0][r][1] + sm.gred[1][r][1]);
+        if (a_sc) p.dla[row] = sm.gred[0][r][2] + sm.gred[1][r][2];
     }
 }
 
@@ -927,7 +983,10 @@ template <typename OT, int DK, int DV>
 static hipError_t launch_bgrad(const BwdParams& p, hipStream_t s) {
     const long nblk = (long)p.B * p.H * p.NC;
     if (nblk == 0) return hipSuccess;
-    hipLaunchKernelGGL((gdr2_bgrad_kernel<OT, DK, DV, 32>), dim3(nblk), dim3(kBgThreads), 0, s, p);
+    if (p.gates)
+        hipLaunchKernelGGL((gdr2_bgrad_kernel<OT, DK, DV, 32, true>), dim3(nblk), dim3(kBgThreads), 0, s, p);
+    else
+        hipLaunchKernelGGL((gdr2_bgrad_kernel<OT, DK, DV, 32, false>), dim3(nblk), dim3(kBgThreads), 0, s, p);
     return hipGetLastError();
 }
 

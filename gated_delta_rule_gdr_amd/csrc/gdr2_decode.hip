@@ -16,7 +16,7 @@
 
 namespace gdr2 {
 
-template <typename IT, int DK, int DV>
+template <typename IT, int DK, int DV, bool GS>
 __global__ __launch_bounds__(kThreads) void gdr2_decode_kernel(DecodeParams p) {
     constexpr int CGR = DV / 4;           // 4-column groups
     constexpr int RGR = kThreads / CGR;   // row groups
@@ -32,10 +32,14 @@ __global__ __launch_bounds__(kThreads) void gdr2_decode_kernel(DecodeParams p) {
     const int j0 = 4 * jg, ibase = ig * RPT;
     const IT* q = (const IT*)p.q + nh * DK;
     const IT* k = (const IT*)p.k + nh * DK;
-    const IT* b = (const IT*)p.b + nh * DK;
-    const float* la = p.la + nh * DK;
+    // a scalar gate is one value per (sequence, head): index 0 with a zero channel stride
+    // (GS instances only; the channel-wise instance has unit strides known at compile time)
+    const int sb = (GS && (p.gates & kEraseScalar)) ? 0 : 1, sa = (GS && (p.gates & kDecayScalar)) ? 0 : 1;
+    const int sw = (GS && (p.gates & kWriteScalar)) ? 0 : 1;
+    const IT* b = (const IT*)p.b + nh * (sb ? DK : 1);
+    const float* la = p.la + nh * (sa ? DK : 1);
     const IT* v = (const IT*)p.v + nh * DV;
-    const IT* w = (const IT*)p.w + nh * DV;
+    const IT* w = (const IT*)p.w + nh * (sw ? DV : 1);
     const float* Sin = p.S_in ? p.S_in + nh * DK * DV : nullptr;
     float* Sout = p.S_out + nh * DK * DV;
 
@@ -50,9 +54,9 @@ __global__ __launch_bounds__(kThreads) void gdr2_decode_kernel(DecodeParams p) {
 #pragma unroll
     for (int u = 0; u < RPT; ++u) {
         const int i = ibase + u;
-        const float a = __expf(la[i]);
+        const float a = __expf(la[sa * i]);
         const float ki = to_f(k[i]), qi = to_f(q[i]);
-        const float e = to_f(b[i]) * ki;
+        const float e = to_f(b[sb * i]) * ki;
         kk[u] = ki;
         pqk += qi * ki;
         if (!Sin) s[u] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -77,7 +81,7 @@ __global__ __launch_bounds__(kThreads) void gdr2_decode_kernel(DecodeParams p) {
     }
     f32x4 u4;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) u4[j] = to_f(w[j0 + j]) * to_f(v[j0 + j]) - r[j];
+    for (int j = 0; j < 4; ++j) u4[j] = to_f(w[sw * (j0 + j)]) * to_f(v[j0 + j]) - r[j];
 #pragma unroll
     for (int u = 0; u < RPT; ++u) {
         f32x4 x;
@@ -95,7 +99,10 @@ __global__ __launch_bounds__(kThreads) void gdr2_decode_kernel(DecodeParams p) {
 
 template <typename IT, int DK, int DV>
 static hipError_t launch_decode(const DecodeParams& p, hipStream_t s) {
-    hipLaunchKernelGGL((gdr2_decode_kernel<IT, DK, DV>), dim3(p.N * p.H), dim3(kThreads), 0, s, p);
+    if (p.gates)
+        hipLaunchKernelGGL((gdr2_decode_kernel<IT, DK, DV, true>), dim3(p.N * p.H), dim3(kThreads), 0, s, p);
+    else
+        hipLaunchKernelGGL((gdr2_decode_kernel<IT, DK, DV, false>), dim3(p.N * p.H), dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
 

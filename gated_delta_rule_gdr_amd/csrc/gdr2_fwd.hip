@@ -35,11 +35,11 @@
 
 namespace gdr2 {
 
-template <typename OT, int DK, int DV>
+template <typename OT, int DK, int DV, bool GS>
 __global__ __launch_bounds__(kThreads, 2) void gdr2_wy_kernel(FwdParams p) {
     __shared__ WySmem<OT, DK, DV> sm;
-    WyChunk<OT, DK, DV> ch(p.B, p.H, p.T, p.DV, p.NC, blockIdx.x, p.q, p.k, p.b, p.la, p.v, p.w);
-    wy_factors<OT, DK, DV>(sm, ch, p.wy);
+    WyChunk<OT, DK, DV> ch(p.B, p.H, p.T, p.DV, p.NC, p.gates, blockIdx.x, p.q, p.k, p.b, p.la, p.v, p.w);
+    wy_factors<OT, DK, DV, GS>(sm, ch, p.wy);
 }
 
 template <typename OT, int DK, int DVS>
@@ -482,7 +482,10 @@ template <typename OT, int DK, int DV>
 static hipError_t launch_wy(const FwdParams& p, hipStream_t s) {
     const long nblk = (long)p.B * p.H * p.NC;
     if (nblk == 0) return hipSuccess;
-    hipLaunchKernelGGL((gdr2_wy_kernel<OT, DK, DV>), dim3(nblk), dim3(kThreads), 0, s, p);
+    if (p.gates)
+        hipLaunchKernelGGL((gdr2_wy_kernel<OT, DK, DV, true>), dim3(nblk), dim3(kThreads), 0, s, p);
+    else
+        hipLaunchKernelGGL((gdr2_wy_kernel<OT, DK, DV, false>), dim3(nblk), dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
 

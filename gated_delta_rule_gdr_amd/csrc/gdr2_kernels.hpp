@@ -4,6 +4,12 @@
 
 namespace gdr2 {
 
+// Gate shapes (bit mask, same values as gdr2_gates in gdr2.h): a set bit means that gate is one
+// value per (batch, token, head) instead of one per channel.
+constexpr int kEraseScalar = 1;   // b
+constexpr int kWriteScalar = 2;   // w
+constexpr int kDecayScalar = 4;   // log alpha
+
 // Per-chunk WY factors written by the chunk-parallel factor kernel and read by the state-carry
 // kernels (forward and backward) and the chunk-gradient kernel.  Element type = input dtype
 // except gam.  Every array is indexed [chain = b*H + h][chunk][...]; the [C][*] tiles are in
@@ -20,6 +26,7 @@ struct WyBufs {
 
 struct FwdParams {
     int B, H, NS, NC;   // batch, heads, value slices per chain, chunks
+    int gates;          // gate shapes (kEraseScalar | kWriteScalar | kDecayScalar)
     long T, DV;         // tokens, value width (DK is a template parameter)
     const void *q, *k, *v, *b, *w;  // input dtype
     const float* la;    // log decay, fp32
@@ -32,6 +39,7 @@ struct FwdParams {
 
 struct DecodeParams {
     long N, H;
+    int gates;
     const void *q, *k, *v, *b, *w;
     const float* la;
     const float* S_in;  // may equal S_out; null = zero state
@@ -41,6 +49,7 @@ struct DecodeParams {
 
 struct BwdParams {
     int B, H, NS, NC;
+    int gates;
     long T, DV;
     const void *q, *k, *v, *b, *w;
     const float* la;

@@ -174,9 +174,11 @@ struct WyChunk {
     bool valid;
     const OT *q, *k, *b, *v, *w;
     const float* la;
-    __device__ WyChunk(int B, int H_, long T_, long DV_, int NC, int bid, const void* q_,
+    int gates;
+    __device__ WyChunk(int B, int H_, long T_, long DV_, int NC, int gates_, int bid, const void* q_,
                        const void* k_, const void* b_, const float* la_, const void* v_,
                        const void* w_) {
+        gates = gates_;
         (void)B;
         chain = bid / NC;
         c = bid % NC;
@@ -196,16 +198,17 @@ struct WyChunk {
         cix = (long)chain * NC + c;
         q = (const OT*)q_ + row * DK;
         k = (const OT*)k_ + row * DK;
-        b = (const OT*)b_ + row * DK;
-        la = la_ + row * DK;
+        b = (const OT*)b_ + row * ((gates & kEraseScalar) ? 1 : DK);
+        la = la_ + row * ((gates & kDecayScalar) ? 1 : DK);
         v = (const OT*)v_ + row * DV_;
-        w = (const OT*)w_ + row * DV_;
+        w = (const OT*)w_ + row * ((gates & kWriteScalar) ? 1 : DV_);
     }
 };
 
 // Compute and store the WY factors of one chunk (see the file comment); every thread of the
-// workgroup calls it.
-template <typename OT, int DK, int DV>
+// workgroup calls it.  GS: some gate is a scalar per head (ch.gates says which); the all
+// channel-wise instance has no gate branches, so its loads issue back to back.
+template <typename OT, int DK, int DV, bool GS>
 __device__ void wy_factors(WySmem<OT, DK, DV>& sm, const WyChunk<OT, DK, DV>& ch, const WyBufs& wy) {
     using Cf = WyCfg<OT, DK, DV>;
     using MM = Mfma<OT>;
@@ -221,14 +224,32 @@ __device__ void wy_factors(WySmem<OT, DK, DV>& sm, const WyChunk<OT, DK, DV>& ch
     for (int ks = 0; ks < NKS; ++ks) {
         load_lane<OT>(ch.q, ks, g, qv + ks * KPL);
         load_lane<OT>(ch.k, ks, g, kv + ks * KPL);
-        load_lane<OT>(ch.b, ks, g, bv + ks * KPL);
-        load_lane_f32<OT>(ch.la, ks, g, lv + ks * KPL);
+        if (GS && (ch.gates & kEraseScalar)) {
+            const float bs = to_f(ch.b[0]);
+#pragma unroll
+            for (int j = 0; j < KPL; ++j) bv[ks * KPL + j] = bs;
+        } else {
+            load_lane<OT>(ch.b, ks, g, bv + ks * KPL);
+        }
+        if (GS && (ch.gates & kDecayScalar)) {
+            const float ls = ch.la[0];
+#pragma unroll
+            for (int j = 0; j < KPL; ++j) lv[ks * KPL + j] = ls;
+        } else {
+            load_lane_f32<OT>(ch.la, ks, g, lv + ks * KPL);
+        }
     }
 #pragma unroll
     for (int ks = 0; ks < NVS; ++ks) {
         float vv[KPL], wv[KPL];
         load_lane<OT>(ch.v, ks, g, vv);
-        load_lane<OT>(ch.w, ks, g, wv);
+        if (GS && (ch.gates & kWriteScalar)) {
+            const float ws = to_f(ch.w[0]);
+#pragma unroll
+            for (int j = 0; j < KPL; ++j) wv[j] = ws;
+        } else {
+            load_lane<OT>(ch.w, ks, g, wv);
+        }
 #pragma unroll
         for (int j = 0; j < KPL; ++j) zv[ks * KPL + j] = ch.valid ? vv[j] * wv[j] : 0.f;
     }

@@ -17,6 +17,11 @@ Recipe (the pages' layer shape and value structure, synthetic values):
 Draw order per call: q, k, v, log alpha, b, w, S0, dO, dS_T, from one ``torch.Generator`` seeded
 with ``seed``.
 
+Scalar gates (``scalar`` containing "b", "w" and/or "a"): that gate -- b, w or log alpha -- is
+drawn once per (batch, token, head), same distribution, and has shape [B, T, H] (the gate-shape
+variants of the ablation in the forum summary on zhichai.net, section "Ablation: the erase gate
+matters more", and Gated DeltaNet's scalar decay).
+
 Variants (tied-gate reductions):
   * ``"kda"``: beta = sigmoid(N(0,1)) per (batch, token, head), b = w = beta broadcast;
   * ``"gdn"``: as ``"kda"`` plus one log alpha per (batch, token, head) broadcast over channels;
@@ -53,7 +58,7 @@ def _normal(shape, gen, device):
 
 
 def layer_inputs(B, T, H, dk, dv, dtype="bf16", seed=0, variant="gdr2", s0_std=0.0,
-                 grads=True, dST=False, device="cpu", decay_scale=0.1):
+                 grads=True, dST=False, device="cpu", decay_scale=0.1, scalar=""):
     """Draw one batch of layer inputs.  Returns a dict of tensors on ``device``:
     q, k, b: [B,T,H,dk] (dtype); v, w, dO: [B,T,H,dv] (dtype); log_alpha: [B,T,H,dk] fp32;
     S0: [B,H,dk,dv] fp32 or None; dST: [B,H,dk,dv] fp32 or None."""
@@ -70,6 +75,8 @@ def layer_inputs(B, T, H, dk, dv, dtype="bf16", seed=0, variant="gdr2", s0_std=0
         la = la.expand(B, T, H, dk).contiguous()
     elif variant == "la":
         la = torch.zeros((B, T, H, dk), device=device)
+    elif "a" in scalar:
+        la = -torch.nn.functional.softplus(_normal((B, T, H), g, device)) * decay_scale
     else:
         la = -torch.nn.functional.softplus(_normal((B, T, H, dk), g, device)) * decay_scale
     if variant in ("kda", "gdn"):
@@ -80,8 +87,8 @@ def layer_inputs(B, T, H, dk, dv, dtype="bf16", seed=0, variant="gdr2", s0_std=0
         b = torch.zeros((B, T, H, dk), device=device, dtype=dt)
         w = torch.ones((B, T, H, dv), device=device, dtype=dt)
     else:
-        b = torch.sigmoid(_normal((B, T, H, dk), g, device)).to(dt)
-        w = torch.sigmoid(_normal((B, T, H, dv), g, device)).to(dt)
+        b = torch.sigmoid(_normal((B, T, H) if "b" in scalar else (B, T, H, dk), g, device)).to(dt)
+        w = torch.sigmoid(_normal((B, T, H) if "w" in scalar else (B, T, H, dv), g, device)).to(dt)
     S0 = (_normal((B, H, dk, dv), g, device) * s0_std) if s0_std > 0 else None
     out = dict(q=q.to(dt), k=k.to(dt), v=v.to(dt), log_alpha=la.float().contiguous(), b=b, w=w,
                S0=S0)
@@ -101,11 +108,12 @@ def config_inputs(name, device="cpu", **override):
 
 
 def decode_inputs(step, N=DECODE["N"], H=DECODE["H"], dk=DECODE["dk"], dv=DECODE["dv"],
-                  dtype=DECODE["dtype"], seed_base=DECODE["seed_base"], device="cpu"):
+                  dtype=DECODE["dtype"], seed_base=DECODE["seed_base"], device="cpu", scalar=""):
     """Per-step decode token inputs (one token for each of N sequences x H heads), same recipe as
-    the layer inputs, seeded with seed_base + step.  q, k, b, log_alpha: [N,H,dk]; v, w: [N,H,dv]."""
+    the layer inputs, seeded with seed_base + step.  q, k, b, log_alpha: [N,H,dk]; v, w: [N,H,dv]
+    (a scalar gate: [N,H])."""
     x = layer_inputs(N, 1, H, dk, dv, dtype=dtype, seed=seed_base + step, grads=False,
-                     device=device)
+                     device=device, scalar=scalar)
     return {n: x[n][:, 0].contiguous() for n in ("q", "k", "v", "log_alpha", "b", "w")}
 
 

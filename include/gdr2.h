@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define GDR2_ABI_VERSION 1
+#define GDR2_ABI_VERSION 2
 #define GDR2_CHUNK 64 /* tokens per chunk of the chunked passes */
 
 typedef enum gdr2_status {
@@ -56,6 +56,27 @@ typedef enum gdr2_status {
 } gdr2_status;
 
 typedef enum gdr2_dtype { GDR2_F32 = 0, GDR2_BF16 = 1 } gdr2_dtype;
+
+/*
+ * Gate shapes for the *_ex entry points (bit mask; 0 = every gate channel-wise, as in the plain
+ * entry points).  A set bit makes that gate one value per (batch, token, head) -- [B][T][H], or
+ * [N][H] for decode -- broadcast over its channels, and makes its gradient the sum over those
+ * channels, in the same [B][T][H] shape:
+ *   GDR2_ERASE_SCALAR  b is a scalar per head: the ablation arm that keeps only the write gate
+ *                      channel-wise (forum summary "Gated DeltaNet-2: Decoupling Erase and Write
+ *                      Gates ..." on zhichai.net, section "Ablation: the erase gate matters more")
+ *   GDR2_WRITE_SCALAR  w is a scalar per head: the arm of the same ablation that keeps only the
+ *                      erase gate channel-wise
+ *   GDR2_DECAY_SCALAR  log_alpha is a scalar per head (the scalar decay of Gated DeltaNet)
+ * With b = w (both scalar) the update is KDA's; adding GDR2_DECAY_SCALAR gives Gated DeltaNet's
+ * (same summary, section "Gated Delta Rule-2": the two reductions).
+ */
+typedef enum gdr2_gates {
+    GDR2_GATES_CHANNEL = 0,
+    GDR2_ERASE_SCALAR = 1,
+    GDR2_WRITE_SCALAR = 2,
+    GDR2_DECAY_SCALAR = 4
+} gdr2_gates;
 
 /* Bytes of one element of `dtype` (4 or 2), 0 for an unknown dtype. */
 size_t gdr2_dtype_size(gdr2_dtype dtype);
@@ -165,6 +186,42 @@ gdr2_status gdr2_decode_step(int64_t N, int64_t H, int64_t dk, int64_t dv, gdr2_
                              const void* q, const void* k, const void* v,
                              const float* log_alpha, const void* b, const void* w,
                              const float* S_in, float* S_out, void* o, void* stream);
+
+/*
+ * The same entry points with the gate shapes of `gates` (a gdr2_gates bit mask; any other bit
+ * returns GDR2_E_UNSUPPORTED).  Every argument means what it means in the plain entry point,
+ * except that b / w / log_alpha and their gradients db / dw / dlog_alpha have the [B][T][H]
+ * ([N][H] for decode) shape when their bit is set.  With gates = 0 each equals the plain call.
+ */
+gdr2_status gdr2_fwd_chunked_ex(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                                gdr2_dtype dtype, unsigned gates, const void* q, const void* k,
+                                const void* v, const float* log_alpha, const void* b,
+                                const void* w, const float* S0, void* o, float* S_T,
+                                void* workspace, size_t workspace_bytes, void* stream);
+gdr2_status gdr2_bwd_chunked_ex(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                                gdr2_dtype dtype, unsigned gates, const void* q, const void* k,
+                                const void* v, const float* log_alpha, const void* b,
+                                const void* w, const void* fwd_workspace,
+                                size_t fwd_workspace_bytes, const void* dO, const float* dS_T,
+                                void* dq, void* dk_, void* dv_, float* dlog_alpha, void* db,
+                                void* dw, float* dS0, void* workspace, size_t workspace_bytes,
+                                void* stream);
+gdr2_status gdr2_fwd_factors_ex(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                                gdr2_dtype dtype, unsigned gates, const void* q, const void* k,
+                                const void* v, const float* log_alpha, const void* b,
+                                const void* w, void* workspace, size_t workspace_bytes,
+                                void* stream);
+gdr2_status gdr2_bwd_grads_ex(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                              gdr2_dtype dtype, unsigned gates, const void* q, const void* k,
+                              const void* v, const float* log_alpha, const void* b, const void* w,
+                              const void* fwd_workspace, size_t fwd_workspace_bytes,
+                              const void* dO, void* dq, void* dk_, void* dv_, float* dlog_alpha,
+                              void* db, void* dw, const void* workspace, size_t workspace_bytes,
+                              void* stream);
+gdr2_status gdr2_decode_step_ex(int64_t N, int64_t H, int64_t dk, int64_t dv, gdr2_dtype dtype,
+                                unsigned gates, const void* q, const void* k, const void* v,
+                                const float* log_alpha, const void* b, const void* w,
+                                const float* S_in, float* S_out, void* o, void* stream);
 
 /* Static description of a status code. */
 const char* gdr2_status_string(gdr2_status s);

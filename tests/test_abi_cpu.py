@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_strings():
     lib = load_library()
-    assert lib.gdr2_abi_version() == 1
+    assert lib.gdr2_abi_version() == 2
     for s in range(9):
         assert lib.gdr2_status_string(s)
     assert lib.gdr2_dtype_size(0) == 4 and lib.gdr2_dtype_size(1) == 2 and lib.gdr2_dtype_size(7) == 0
@@ -116,3 +116,27 @@ def test_decode_rejects_before_launch():
     # S_in may equal S_out exactly, but may not partially overlap it
     assert lib.gdr2_decode_step(2, 2, 64, 64, 1, *ins, P(0x100010), P(0x100000), P(0x200000), NULL) == E_ALIAS
     assert lib.gdr2_decode_step(0, 2, 64, 64, 1, *ins, NULL, P(0x100000), P(0x200000), NULL) == OK
+
+
+def test_gate_shape_entry_points_validate():
+    """The *_ex entry points: unknown gate bits are rejected; a channel-wise gate's extent is
+    checked for overlap, and a scalar gate's smaller extent still is (every call here fails
+    validation, so nothing is launched)."""
+    lib = load_library()
+    P = lambda a: _fake(a)
+    B, T, H, dk, dv = 1, 8, 1, 64, 64
+
+    def fwd(gates, b=0x18000, o=0x90000):
+        ins = [P(0x10000), P(0x20000), P(0x30000), P(0x40000), P(b), P(0x60000)]
+        return lib.gdr2_fwd_chunked_ex(B, T, H, dk, dv, 1, gates, *ins, NULL, P(o), NULL,
+                                       P(0x200000), 1 << 30, NULL)
+    assert fwd(8) == E_UNSUP
+    assert fwd(1 << 31) == E_UNSUP
+    # channel-wise b spans 8 x 64 bf16 = 1 KB from 0x18000: o at 0x18010 overlaps it
+    assert fwd(0, b=0x18000, o=0x18010) == E_ALIAS
+    # scalar b spans 16 bytes: o at 0x18000 still overlaps it
+    assert fwd(1, b=0x18000, o=0x18000) == E_ALIAS
+    # decode with every gate scalar: rejects bad bits, accepts the sizes
+    ins = [P(0x10000 + i * 0x1000) for i in range(6)]
+    assert lib.gdr2_decode_step_ex(2, 2, 64, 64, 1, 16, *ins, NULL, P(0x100000), P(0x200000), NULL) == E_UNSUP
+    assert lib.gdr2_decode_step_ex(2, 2, 64, 64, 1, 7, *ins, NULL, P(0x10008), P(0x200000), NULL) == E_ALIGN
