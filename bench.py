@@ -152,6 +152,35 @@ def bench_gate_variants(torch, g2, steps):
     return out
 
 
+def bench_out_gate(torch, g2, steps):
+    """Output epilogue (RMS norm x weight x SiLU gate) forward and backward on the layer's output
+    shape, [B, T, H, d_v] bf16.  Algorithmic bytes per row: forward reads o, g and writes y
+    (3 * 2 d_v); backward reads o, g, dy and writes do, dg (5 * 2 d_v)."""
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    shape = (B, T, H, DV)
+    o = torch.randn(shape, generator=gen, device="cuda").to(torch.bfloat16)
+    g = torch.randn(shape, generator=gen, device="cuda").to(torch.bfloat16)
+    dy = torch.randn(shape, generator=gen, device="cuda").to(torch.bfloat16)
+    w = torch.ones(DV, device="cuda")
+    res = {}
+    for name, fn, nbytes in (("fwd", lambda: g2.gdr2_out_gate_fwd(o, g, w), 6 * DV),
+                             ("bwd", lambda: g2.gdr2_out_gate_bwd(o, g, w, dy), 10 * DV)):
+        for _ in range(2):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        gbs = nbytes * B * T * H / us / 1e3
+        res[name] = {"us": round(us, 2), "achieved_GBs": round(gbs, 1),
+                     "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -251,6 +280,7 @@ def main():
         out["decode"] = bench_decode(torch, g2.gdr2_decode_step, args.decode_steps)
     if not args.profile_pass:
         out["gate_variants"] = bench_gate_variants(torch, g2, 5)
+        out["out_gate"] = bench_out_gate(torch, g2, 10)
     if args.profile_pass:
         src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)

@@ -9,6 +9,7 @@ Entry points (same names as the C ABI):
   gdr2_fwd_chunked(q, k, v, log_alpha, b, w, S0=None, want_final_state=True) -> (o, S_T, fwd_ws)
   gdr2_bwd_chunked(q, k, v, log_alpha, b, w, dO, fwd_ws, dS_T=None, want_dS0=True) -> grads
   gdr2_decode_step(q, k, v, log_alpha, b, w, S_in=None, S_out=None)
+  gdr2_out_gate_fwd(o, g, weight, eps) / gdr2_out_gate_bwd(o, g, weight, dy, eps)
 Each of b, w and log_alpha may be channel-wise ([..., d]) or a scalar per head (the token shape of
 q without its channel axis); the gate-shape bits passed to the *_ex entry points follow from the
 shapes, and the gradients come back in the shape of their gate.
@@ -23,7 +24,7 @@ import torch
 __all__ = ["gdr2_fwd_chunked", "gdr2_bwd_chunked", "gdr2_decode_step", "gdr2_fwd_factors",
            "gdr2_fwd_carry", "gdr2_bwd_state", "gdr2_bwd_grads", "fwd_workspace_bytes",
            "bwd_workspace_bytes", "library_path", "load_library", "Gdr2Error", "CHUNK", "gate_bits",
-           "ERASE_SCALAR", "WRITE_SCALAR", "DECAY_SCALAR"]
+           "ERASE_SCALAR", "WRITE_SCALAR", "DECAY_SCALAR", "gdr2_out_gate_fwd", "gdr2_out_gate_bwd"]
 
 CHUNK = 64
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -32,7 +33,7 @@ _lib = None
 
 _STATUS = {0: "ok", 1: "GDR2_E_NULL", 2: "GDR2_E_SHAPE", 3: "GDR2_E_DTYPE",
            4: "GDR2_E_UNSUPPORTED", 5: "GDR2_E_ALIGN", 6: "GDR2_E_ALIAS", 7: "GDR2_E_WORKSPACE",
-           8: "GDR2_E_HIP"}
+           8: "GDR2_E_HIP", 9: "GDR2_E_VALUE"}
 _DT = {torch.float32: 0, torch.bfloat16: 1}
 
 
@@ -85,6 +86,13 @@ def load_library():
     lib.gdr2_bwd_grads_ex.restype = ctypes.c_int
     lib.gdr2_decode_step_ex.argtypes = [I64] * 4 + [ctypes.c_int, U] + [P] * 10
     lib.gdr2_decode_step_ex.restype = ctypes.c_int
+    F = ctypes.c_float
+    lib.gdr2_out_gate_fwd.argtypes = [I64, I64, ctypes.c_int, P, P, P, F, P, P]
+    lib.gdr2_out_gate_fwd.restype = ctypes.c_int
+    lib.gdr2_out_gate_bwd.argtypes = [I64, I64, ctypes.c_int, P, P, P, F, P, P, P, P, P, SZ, P]
+    lib.gdr2_out_gate_bwd.restype = ctypes.c_int
+    lib.gdr2_out_gate_bwd_workspace_bytes.argtypes = [I64, I64]
+    lib.gdr2_out_gate_bwd_workspace_bytes.restype = SZ
     lib.gdr2_fwd_workspace_bytes.argtypes = [I64] * 5 + [ctypes.c_int]
     lib.gdr2_fwd_workspace_bytes.restype = SZ
     lib.gdr2_bwd_workspace_bytes.argtypes = [I64] * 5 + [ctypes.c_int]
@@ -259,3 +267,35 @@ def gdr2_decode_step(q, k, v, log_alpha, b, w, S_in=None, S_out=None):
                                  _ptr(S_out), _ptr(o), _stream())
     _check("gdr2_decode_step", st)
     return o, S_out
+
+
+def gdr2_out_gate_fwd(o, g, weight, eps=1e-6):
+    """Output epilogue y = RMSNorm(o) * weight * silu(g) over the last (d_v) axis of o [..., dv];
+    g has o's shape and dtype, weight is [dv] fp32.  Returns y."""
+    lib = load_library()
+    _contig(o, g, weight)
+    dv = o.shape[-1]
+    rows = o.numel() // dv
+    y = torch.empty_like(o)
+    st = lib.gdr2_out_gate_fwd(rows, dv, _dtype(o), _ptr(o), _ptr(g), _ptr(weight), float(eps),
+                               _ptr(y), _stream())
+    _check("gdr2_out_gate_fwd", st)
+    return y
+
+
+def gdr2_out_gate_bwd(o, g, weight, dy, eps=1e-6, workspace=None):
+    """Backward of gdr2_out_gate_fwd for the cotangent dy.  Returns dict do, dg, dweight."""
+    lib = load_library()
+    _contig(o, g, weight, dy)
+    dv = o.shape[-1]
+    rows = o.numel() // dv
+    need = lib.gdr2_out_gate_bwd_workspace_bytes(rows, dv)
+    ws = workspace if workspace is not None else torch.empty(max(need, 16), dtype=torch.uint8,
+                                                             device=o.device)
+    out = dict(do=torch.empty_like(o), dg=torch.empty_like(g),
+               dweight=torch.empty((dv,), dtype=torch.float32, device=o.device))
+    st = lib.gdr2_out_gate_bwd(rows, dv, _dtype(o), _ptr(o), _ptr(g), _ptr(weight), float(eps),
+                               _ptr(dy), _ptr(out["do"]), _ptr(out["dg"]), _ptr(out["dweight"]),
+                               _ptr(ws), ws.numel(), _stream())
+    _check("gdr2_out_gate_bwd", st)
+    return out

@@ -12,7 +12,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libgdr2.so")
 OBJ_DIR = os.path.join(PKG, "_build")
-SOURCES = ["gdr2_api.hip", "gdr2_fwd.hip", "gdr2_bwd.hip", "gdr2_decode.hip"]
+SOURCES = ["gdr2_api.hip", "gdr2_fwd.hip", "gdr2_bwd.hip", "gdr2_decode.hip", "gdr2_epilogue.hip"]
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-I", INCLUDE, "-I", CSRC,
          "-Wall", "-Wno-unused-function",

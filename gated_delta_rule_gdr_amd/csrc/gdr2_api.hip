@@ -69,6 +69,7 @@ const char* gdr2_status_string(gdr2_status s) {
         case GDR2_E_ALIAS: return "output overlaps an input or another output";
         case GDR2_E_WORKSPACE: return "workspace missing or too small";
         case GDR2_E_HIP: return "HIP launch failed";
+        case GDR2_E_VALUE: return "invalid scalar argument";
     }
     return "unknown status";
 }
@@ -424,6 +425,63 @@ gdr2_status gdr2_decode_step(int64_t N, int64_t H, int64_t dk, int64_t dv, gdr2_
                              const float* S_in, float* S_out, void* o, void* stream) {
     return gdr2_decode_step_ex(N, H, dk, dv, dt, 0u, q, k, v, log_alpha, b, w, S_in, S_out, o,
                                stream);
+}
+
+// ------------------------------------------------------------------ output epilogue
+static gdr2_status check_epi(int64_t rows, int64_t dv, gdr2_dtype dt, float eps) {
+    if (dt != GDR2_F32 && dt != GDR2_BF16) return GDR2_E_DTYPE;
+    if (rows < 0 || dv < 0 || rows > ((int64_t)1 << 40)) return GDR2_E_SHAPE;
+    if (!dims_ok(dv)) return GDR2_E_UNSUPPORTED;
+    if (!(eps > 0.f) || !(eps < 1e30f)) return GDR2_E_VALUE;
+    return GDR2_OK;
+}
+
+size_t gdr2_out_gate_bwd_workspace_bytes(int64_t rows, int64_t dv) {
+    if (rows <= 0 || dv <= 0) return 0;
+    return (size_t)gdr2::epi_blocks(rows) * dv * sizeof(float);
+}
+
+gdr2_status gdr2_out_gate_fwd(int64_t rows, int64_t dv, gdr2_dtype dt, const void* o,
+                              const void* g, const float* weight, float eps, void* y,
+                              void* stream) {
+    gdr2_status st = check_epi(rows, dv, dt, eps);
+    if (st != GDR2_OK || rows == 0) return st;
+    if (!o || !g || !weight || !y) return GDR2_E_NULL;
+    const void* ptrs[] = {o, g, weight, y};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return GDR2_E_ALIGN;
+    const size_t n = (size_t)rows * dv * gdr2_dtype_size(dt);
+    const Range ins[] = {{o, n}, {g, n}, {weight, (size_t)dv * 4}};
+    const Range outs[] = {{y, n}};
+    if (any_alias(outs, 1, ins, 3)) return GDR2_E_ALIAS;
+    gdr2::EpiParams p{};
+    p.rows = rows; p.eps = eps; p.o = o; p.g = g; p.weight = weight; p.y = y;
+    hipError_t e = gdr2::epi_dispatch(dt == GDR2_BF16, (int)dv, false, p, (hipStream_t)stream);
+    return e == hipSuccess ? GDR2_OK : GDR2_E_HIP;
+}
+
+gdr2_status gdr2_out_gate_bwd(int64_t rows, int64_t dv, gdr2_dtype dt, const void* o,
+                              const void* g, const float* weight, float eps, const void* dy,
+                              void* do_, void* dg, float* dweight, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+    gdr2_status st = check_epi(rows, dv, dt, eps);
+    if (st != GDR2_OK) return st;
+    if (!dweight) return GDR2_E_NULL;
+    if (rows > 0 && (!o || !g || !weight || !dy || !do_ || !dg)) return GDR2_E_NULL;
+    const void* ptrs[] = {o, g, weight, dy, do_, dg, dweight, workspace};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return GDR2_E_ALIGN;
+    const size_t need = gdr2_out_gate_bwd_workspace_bytes(rows, dv);
+    if (rows > 0 && (!workspace || workspace_bytes < need)) return GDR2_E_WORKSPACE;
+    const size_t n = (size_t)rows * dv * gdr2_dtype_size(dt);
+    const Range ins[] = {{o, n}, {g, n}, {weight, (size_t)dv * 4}, {dy, n}};
+    const Range outs[] = {{do_, n}, {dg, n}, {dweight, (size_t)dv * 4}, {workspace, need}};
+    if (any_alias(outs, 4, ins, 4)) return GDR2_E_ALIAS;
+    gdr2::EpiParams p{};  // (no rows: only the weight gradient, zero, is written)
+    p.rows = rows; p.eps = eps; p.o = o; p.g = g; p.weight = weight; p.dy = dy;
+    p.dox = do_; p.dg = dg; p.dweight = dweight; p.dw_part = (float*)workspace;
+    hipError_t e = gdr2::epi_dispatch(dt == GDR2_BF16, (int)dv, true, p, (hipStream_t)stream);
+    return e == hipSuccess ? GDR2_OK : GDR2_E_HIP;
 }
 
 }  // extern "C"

@@ -63,6 +63,19 @@ struct BwdParams {
     float* dla;
 };
 
+// Output epilogue: y = RMSNorm(o) * weight * silu(g) per row of DV channels, and its backward.
+struct EpiParams {
+    long rows;              // B * T * H
+    float eps;
+    const void *o, *g;      // [rows][DV] input dtype
+    const float* weight;    // [DV] fp32
+    void* y;                // forward output [rows][DV]
+    const void* dy;         // backward: cotangent of y
+    void *dox, *dg;         // backward outputs [rows][DV]
+    float* dweight;         // backward output [DV] fp32
+    float* dw_part;         // backward workspace [epi_blocks(rows)][DV] fp32
+};
+
 // forward: factor kernel (chunk-parallel) + state carry (sequential over chunks)
 hipError_t wy_dispatch(int dtype_bf16, int dk, int dv, const FwdParams& p, hipStream_t s);
 int carry_slice_width(int dtype_bf16, int dk, int dv, long chains);
@@ -70,5 +83,7 @@ hipError_t carry_fwd_dispatch(int dtype_bf16, int dk, int dvs, const FwdParams& 
 hipError_t decode_dispatch(int dtype_bf16, int dk, int dv, const DecodeParams& p, hipStream_t s);
 hipError_t dstate_dispatch(int dtype_bf16, int dk, int dvs, const BwdParams& p, hipStream_t s);
 hipError_t bgrad_dispatch(int dtype_bf16, int dk, int dv, const BwdParams& p, hipStream_t s);
+long epi_blocks(long rows);
+hipError_t epi_dispatch(int dtype_bf16, int dv, bool bwd, const EpiParams& p, hipStream_t s);
 
 }  // namespace gdr2

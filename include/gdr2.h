@@ -52,7 +52,8 @@ typedef enum gdr2_status {
     GDR2_E_ALIGN = 5,       /* a pointer is not 16-byte aligned */
     GDR2_E_ALIAS = 6,       /* an output overlaps an input or another output */
     GDR2_E_WORKSPACE = 7,   /* workspace missing or smaller than the size its query returns */
-    GDR2_E_HIP = 8          /* the HIP runtime refused the launch */
+    GDR2_E_HIP = 8,         /* the HIP runtime refused the launch */
+    GDR2_E_VALUE = 9        /* a scalar argument is out of range (e.g. eps <= 0) */
 } gdr2_status;
 
 typedef enum gdr2_dtype { GDR2_F32 = 0, GDR2_BF16 = 1 } gdr2_dtype;
@@ -222,6 +223,28 @@ gdr2_status gdr2_decode_step_ex(int64_t N, int64_t H, int64_t dk, int64_t dv, gd
                                 unsigned gates, const void* q, const void* k, const void* v,
                                 const float* log_alpha, const void* b, const void* w,
                                 const float* S_in, float* S_out, void* o, void* stream);
+
+/*
+ * Output epilogue of the block (ainews.random.gg article on Gated DeltaNet-2, section "Block design
+ * and hybrid model": the mixer output is RMS-normalised and multiplied by a SiLU output gate before
+ * the output projection).  For every row (one token of one head; rows = B*T*H) of dv channels:
+ *     y_j = o_j / sqrt(mean_i o_i^2 + eps) * weight_j * silu(g_j),   silu(x) = x / (1 + exp(-x))
+ * with one weight vector shared by all heads.
+ *   o, g, y         [rows][dv]  dtype       (o: the mixer output, g: gate pre-activation; y: output)
+ *   weight          [dv]        fp32
+ *   eps             > 0, finite (else GDR2_E_VALUE)
+ * The backward takes dy [rows][dv] and writes do_, dg [rows][dv] (dtype) and dweight [dv] (fp32,
+ * the sum over all rows, reduced in a fixed order: bitwise deterministic); it needs a workspace
+ * of gdr2_out_gate_bwd_workspace_bytes(rows, dv) bytes.  dv in {64, 128}.
+ */
+gdr2_status gdr2_out_gate_fwd(int64_t rows, int64_t dv, gdr2_dtype dtype, const void* o,
+                              const void* g, const float* weight, float eps, void* y,
+                              void* stream);
+size_t gdr2_out_gate_bwd_workspace_bytes(int64_t rows, int64_t dv);
+gdr2_status gdr2_out_gate_bwd(int64_t rows, int64_t dv, gdr2_dtype dtype, const void* o,
+                              const void* g, const float* weight, float eps, const void* dy,
+                              void* do_, void* dg, float* dweight, void* workspace,
+                              size_t workspace_bytes, void* stream);
 
 /* Static description of a status code. */
 const char* gdr2_status_string(gdr2_status s);

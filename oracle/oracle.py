@@ -11,7 +11,11 @@ What lives here:
   * ``la_closed_form``: causal linear attention written as masked matrix products (the textbook
     definition), which is what GDR-2 must reduce to at alpha = 1, b = 0, w = 1;
   * ``gla_closed_form``: the b = 0 case as an explicit double sum over (query token, key token)
-    with cumulative decay products, i.e. channel-wise gated linear attention.
+    with cumulative decay products, i.e. channel-wise gated linear attention;
+  * ``out_gate_forward`` / ``out_gate_backward``: the block's output epilogue (RMS normalisation
+    of each head's output over its d_v channels, a per-channel weight, a SiLU output gate) and its
+    hand-derived vector-Jacobian product -- ainews.random.gg article, section "Block design and
+    hybrid model".
 
 Citations (page title, section):
   * update rule and the KDA / Gated DeltaNet reductions -- forum summary "Gated DeltaNet-2:
@@ -209,3 +213,32 @@ def gla_closed_form(q, k, v, log_alpha, w, S0=None):
                     acc += coef * w[bb, s, h] * v[bb, s, h]
                 o[bb, t, h] = acc
     return o
+
+
+def _silu(x):
+    return x / (1.0 + np.exp(-x))
+
+
+def out_gate_forward(o, g, weight, eps):
+    """Output epilogue, per row (last axis = d_v channels):
+        y = o / sqrt(mean(o^2) + eps) * weight * silu(g).   Returns y (float64)."""
+    o, g, weight = map(_f64, (o, g, weight))
+    r = 1.0 / np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + eps)
+    return o * r * weight * _silu(g)
+
+
+def out_gate_backward(o, g, weight, eps, dy):
+    """Vector-Jacobian product of out_gate_forward for the cotangent dy, derived by hand:
+        r = (mean(o^2) + eps)^(-1/2),  a = dy * weight * silu(g)
+        do = r * a - r^3 * o * mean(a * o)           (dr/do_j = -r^3 o_j / d_v)
+        dg = dy * o * r * weight * silu'(g),  silu'(x) = s + x s (1 - s),  s = sigmoid(x)
+        dweight = sum over all rows of dy * o * r * silu(g)
+    Returns dict do, dg, dweight."""
+    o, g, weight, dy = map(_f64, (o, g, weight, dy))
+    r = 1.0 / np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + eps)
+    s = 1.0 / (1.0 + np.exp(-g))
+    a = dy * weight * (g * s)
+    do = r * a - r ** 3 * o * np.mean(a * o, axis=-1, keepdims=True)
+    dg = dy * o * r * weight * (s + g * s * (1.0 - s))
+    dweight = (dy * o * r * (g * s)).reshape(-1, o.shape[-1]).sum(axis=0)
+    return {"do": do, "dg": dg, "dweight": dweight}

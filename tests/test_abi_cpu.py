@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 def test_version_and_strings():
     lib = load_library()
     assert lib.gdr2_abi_version() == 2
-    for s in range(9):
+    for s in range(10):
         assert lib.gdr2_status_string(s)
     assert lib.gdr2_dtype_size(0) == 4 and lib.gdr2_dtype_size(1) == 2 and lib.gdr2_dtype_size(7) == 0
     assert lib.gdr2_num_chunks(0) == 0 and lib.gdr2_num_chunks(1) == 1 and lib.gdr2_num_chunks(64) == 1
@@ -140,3 +140,26 @@ def test_gate_shape_entry_points_validate():
     ins = [P(0x10000 + i * 0x1000) for i in range(6)]
     assert lib.gdr2_decode_step_ex(2, 2, 64, 64, 1, 16, *ins, NULL, P(0x100000), P(0x200000), NULL) == E_UNSUP
     assert lib.gdr2_decode_step_ex(2, 2, 64, 64, 1, 7, *ins, NULL, P(0x10008), P(0x200000), NULL) == E_ALIGN
+
+
+def test_out_gate_rejects_before_launch():
+    lib = load_library()
+    P = lambda a: _fake(a)
+    F = ctypes.c_float
+    fwd = lambda rows=64, dv=128, dt=1, eps=1e-6, o=0x10000, y=0x90000: lib.gdr2_out_gate_fwd(
+        rows, dv, dt, P(o) if o else NULL, P(0x30000), P(0x50000), F(eps), P(y), NULL)
+    assert fwd(dt=4) == E_DTYPE
+    assert fwd(dv=96) == E_UNSUP
+    assert fwd(eps=0.0) == 9 and fwd(eps=-1.0) == 9 and fwd(eps=float("nan")) == 9
+    assert fwd(o=0) == E_NULL
+    assert fwd(o=0x10008) == E_ALIGN
+    assert fwd(y=0x30000) == E_ALIAS
+    assert fwd(rows=0) == OK
+    assert lib.gdr2_out_gate_bwd_workspace_bytes(1 << 18, 128) > 0
+    bwd = lambda ws=0x400000, wsb=1 << 30, dw=0x200000: lib.gdr2_out_gate_bwd(
+        64, 128, 1, P(0x10000), P(0x30000), P(0x50000), F(1e-6), P(0x60000), P(0x70000),
+        P(0x80000), P(dw) if dw else NULL, P(ws) if ws else NULL, wsb, NULL)
+    assert bwd(dw=0) == E_NULL
+    assert bwd(ws=0) == E_WS
+    assert bwd(wsb=4) == E_WS
+    assert bwd(dw=0x10000) == E_ALIAS

@@ -307,3 +307,51 @@ def test_tied_gate_chain_rules():
         em[0, t, 0] -= h
         fd = (L(beta, ep) - L(beta, em)) / (2 * h)
         assert abs(fd - g["dlog_alpha"][0, t, 0].sum()) < 1e-6
+
+
+# ---- output epilogue (RMS normalisation x weight x SiLU gate)
+def test_out_gate_special_values():
+    """Hand-checkable rows: a constant row c normalises to c / sqrt(c^2 + eps); a zero gate
+    closes the output; a large gate passes silu(g) ~ g; the row scale cancels (up to eps)."""
+    d = 8
+    w = np.linspace(0.5, 2.0, d)
+    c, eps = 3.0, 1e-3
+    o = np.full((1, d), c)
+    g = np.full((1, d), 40.0)
+    y = orc.out_gate_forward(o, g, w, eps)
+    np.testing.assert_allclose(y[0], c / np.sqrt(c * c + eps) * w * 40.0, rtol=1e-12)
+    assert np.all(orc.out_gate_forward(o, np.zeros((1, d)), w, eps) == 0.0)
+    rng = np.random.default_rng(3)
+    o = rng.standard_normal((5, d))
+    g = rng.standard_normal((5, d))
+    np.testing.assert_allclose(orc.out_gate_forward(o * 7.0, g, w, 1e-14),
+                               orc.out_gate_forward(o, g, w, 1e-14), rtol=1e-9)
+    # silu(g) = g * sigmoid(g): at g = ln(3), sigmoid = 3/4
+    g1 = np.full((1, d), np.log(3.0))
+    y1 = orc.out_gate_forward(np.ones((1, d)), g1, np.ones(d), 0.0 + 1e-300)
+    np.testing.assert_allclose(y1[0], np.log(3.0) * 0.75, rtol=1e-12)
+
+
+def test_out_gate_backward_finite_differences():
+    rng = np.random.default_rng(5)
+    R, d, eps = 3, 6, 1e-2
+    o = rng.standard_normal((R, d))
+    g = rng.standard_normal((R, d))
+    w = rng.standard_normal(d)
+    dy = rng.standard_normal((R, d))
+    gr = orc.out_gate_backward(o, g, w, eps, dy)
+    L = lambda o_, g_, w_: float(np.sum(dy * orc.out_gate_forward(o_, g_, w_, eps)))
+    h = 1e-6
+    for name, x in (("do", o), ("dg", g), ("dweight", w)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p = [o, g, w]
+            args_m = [o, g, w]
+            pos = {"do": 0, "dg": 1, "dweight": 2}[name]
+            args_p[pos], args_m[pos] = xp, xm
+            num[idx] = (L(*args_p) - L(*args_m)) / (2 * h)
+        err = np.max(np.abs(num - gr[name])) / np.max(np.abs(num))
+        assert err < 1e-7, (name, err)
