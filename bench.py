@@ -110,12 +110,16 @@ def bench_decode(torch, lib_decode, steps):
 def bench_gate_variants(torch, g2, steps):
     """The same fwd+bwd step with scalar-per-head gates (one value per token and head instead of
     one per channel): erase and write gates ("bw"), and additionally the decay ("bwa").  Each
-    scalar gate saves its channel traffic in both passes."""
+    scalar gate saves its channel traffic in both passes.  "prologue": channel-wise gates handed
+    over as pre-activations, the kernels applying the q/k normalisation, the sigmoid gates and the
+    softplus decay themselves (same bytes as the plain step)."""
     from gated_delta_rule_gdr_amd.inputs import layer_inputs
     bf = torch.bfloat16
     out = {}
-    for scalar in ("bw", "bwa"):
-        x = layer_inputs(B, T, H, DK, DV, dtype="bf16", seed=1001, device="cuda", scalar=scalar)
+    for name, scalar, pro in (("scalar_bw", "bw", None), ("scalar_bwa", "bwa", None),
+                              ("prologue", "", g2.Prologue(0.1, 1e-6))):
+        x = layer_inputs(B, T, H, DK, DV, dtype="bf16", seed=1001, device="cuda", scalar=scalar,
+                         raw=pro is not None)
         fws = torch.empty(g2.fwd_workspace_bytes(B, T, H, DK, DV, bf), dtype=torch.uint8, device="cuda")
         bws = torch.empty(g2.bwd_workspace_bytes(B, T, H, DK, DV, bf), dtype=torch.uint8, device="cuda")
         o = torch.empty((B, T, H, DV), dtype=bf, device="cuda")
@@ -125,10 +129,10 @@ def bench_gate_variants(torch, g2, steps):
         q, k, v, la, b, w, dO = (x[n] for n in ("q", "k", "v", "log_alpha", "b", "w", "dO"))
 
         def step():
-            g2.gdr2_fwd_factors(q, k, v, la, b, w, fws)
+            g2.gdr2_fwd_factors(q, k, v, la, b, w, fws, prologue=pro)
             g2.gdr2_fwd_carry(B, T, H, DK, DV, bf, fws, o)
             g2.gdr2_bwd_state(B, T, H, DK, DV, bf, fws, dO, bws)
-            g2.gdr2_bwd_grads(q, k, v, la, b, w, fws, dO, bws, gr)
+            g2.gdr2_bwd_grads(q, k, v, la, b, w, fws, dO, bws, gr, prologue=pro)
 
         for _ in range(2):
             step()
@@ -144,7 +148,7 @@ def bench_gate_variants(torch, g2, steps):
         # decay 4 B instead of 4 d (read in both passes; its gradient written once)
         fwd = 16 * DK - 4 * DK + 4 - (4 * DK - 4 if "a" in scalar else 0)
         bwd = 30 * DK - 8 * DK + 8 - (8 * DK - 8 if "a" in scalar else 0)
-        out["scalar_" + scalar] = {"ms_per_step": round(ms, 4),
+        out[name] = {"ms_per_step": round(ms, 4),
                                    "Mtokens_per_s": round(B * T / ms / 1e3, 3),
                                    "alg_bytes_per_head_token": fwd + bwd,
                                    "hbm_frac": round((fwd + bwd) * B * T * H / (ms * 1e-3) / 1e9

@@ -12,7 +12,10 @@ Entry points (same names as the C ABI):
   gdr2_out_gate_fwd(o, g, weight, eps) / gdr2_out_gate_bwd(o, g, weight, dy, eps)
 Each of b, w and log_alpha may be channel-wise ([..., d]) or a scalar per head (the token shape of
 q without its channel axis); the gate-shape bits passed to the *_ex entry points follow from the
-shapes, and the gradients come back in the shape of their gate.
+shapes, and the gradients come back in the shape of their gate.  ``prologue=Prologue(c, eps)``
+(forward, backward and decode) makes q, k, log_alpha, b and w pre-activations: the kernels apply
+the L2 normalisation of q and k, the sigmoid gates and log alpha = -c * softplus(a) themselves,
+and the backward returns gradients with respect to the pre-activations.
 """
 from __future__ import annotations
 
@@ -24,7 +27,8 @@ import torch
 __all__ = ["gdr2_fwd_chunked", "gdr2_bwd_chunked", "gdr2_decode_step", "gdr2_fwd_factors",
            "gdr2_fwd_carry", "gdr2_bwd_state", "gdr2_bwd_grads", "fwd_workspace_bytes",
            "bwd_workspace_bytes", "library_path", "load_library", "Gdr2Error", "CHUNK", "gate_bits",
-           "ERASE_SCALAR", "WRITE_SCALAR", "DECAY_SCALAR", "gdr2_out_gate_fwd", "gdr2_out_gate_bwd"]
+           "ERASE_SCALAR", "WRITE_SCALAR", "DECAY_SCALAR", "gdr2_out_gate_fwd", "gdr2_out_gate_bwd",
+           "Prologue"]
 
 CHUNK = 64
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -35,6 +39,23 @@ _STATUS = {0: "ok", 1: "GDR2_E_NULL", 2: "GDR2_E_SHAPE", 3: "GDR2_E_DTYPE",
            4: "GDR2_E_UNSUPPORTED", 5: "GDR2_E_ALIGN", 6: "GDR2_E_ALIAS", 7: "GDR2_E_WORKSPACE",
            8: "GDR2_E_HIP", 9: "GDR2_E_VALUE"}
 _DT = {torch.float32: 0, torch.bfloat16: 1}
+
+
+class Prologue(ctypes.Structure):
+    """gdr2_prologue: decay_scale c (log alpha = -c * softplus(a)) and norm_eps (q, k are divided
+    by sqrt(sum of squares + norm_eps))."""
+    _fields_ = [("decay_scale", ctypes.c_float), ("norm_eps", ctypes.c_float)]
+
+    def __init__(self, decay_scale=1.0, norm_eps=1e-6):
+        super().__init__(float(decay_scale), float(norm_eps))
+
+
+def _pro(prologue):
+    if prologue is None:
+        return None
+    if not isinstance(prologue, Prologue):
+        raise TypeError("prologue must be a Prologue or None")
+    return ctypes.byref(prologue)
 
 
 class Gdr2Error(RuntimeError):
@@ -74,17 +95,17 @@ def load_library():
     lib.gdr2_decode_step.argtypes = [I64] * 4 + [ctypes.c_int] + [P] * 10
     lib.gdr2_decode_step.restype = ctypes.c_int
     U = ctypes.c_uint
-    lib.gdr2_fwd_chunked_ex.argtypes = [I64] * 5 + [ctypes.c_int, U] + [P] * 10 + [SZ, P]
+    lib.gdr2_fwd_chunked_ex.argtypes = [I64] * 5 + [ctypes.c_int, U, P] + [P] * 10 + [SZ, P]
     lib.gdr2_fwd_chunked_ex.restype = ctypes.c_int
-    lib.gdr2_bwd_chunked_ex.argtypes = ([I64] * 5 + [ctypes.c_int, U] + [P] * 7 + [SZ] + [P] * 10
+    lib.gdr2_bwd_chunked_ex.argtypes = ([I64] * 5 + [ctypes.c_int, U, P] + [P] * 7 + [SZ] + [P] * 10
                                         + [SZ, P])
     lib.gdr2_bwd_chunked_ex.restype = ctypes.c_int
-    lib.gdr2_fwd_factors_ex.argtypes = [I64] * 5 + [ctypes.c_int, U] + [P] * 7 + [SZ, P]
+    lib.gdr2_fwd_factors_ex.argtypes = [I64] * 5 + [ctypes.c_int, U, P] + [P] * 7 + [SZ, P]
     lib.gdr2_fwd_factors_ex.restype = ctypes.c_int
-    lib.gdr2_bwd_grads_ex.argtypes = ([I64] * 5 + [ctypes.c_int, U] + [P] * 7 + [SZ] + [P] * 8
+    lib.gdr2_bwd_grads_ex.argtypes = ([I64] * 5 + [ctypes.c_int, U, P] + [P] * 7 + [SZ] + [P] * 8
                                       + [SZ, P])
     lib.gdr2_bwd_grads_ex.restype = ctypes.c_int
-    lib.gdr2_decode_step_ex.argtypes = [I64] * 4 + [ctypes.c_int, U] + [P] * 10
+    lib.gdr2_decode_step_ex.argtypes = [I64] * 4 + [ctypes.c_int, U, P] + [P] * 10
     lib.gdr2_decode_step_ex.restype = ctypes.c_int
     F = ctypes.c_float
     lib.gdr2_out_gate_fwd.argtypes = [I64, I64, ctypes.c_int, P, P, P, F, P, P]
@@ -157,7 +178,8 @@ def _contig(*ts):
             raise ValueError("all tensors must be contiguous")
 
 
-def gdr2_fwd_chunked(q, k, v, log_alpha, b, w, S0=None, want_final_state=True, workspace=None):
+def gdr2_fwd_chunked(q, k, v, log_alpha, b, w, S0=None, want_final_state=True, workspace=None,
+                     prologue=None):
     """Chunked forward.  Returns (o, S_T or None, fwd_ws); fwd_ws holds the per-chunk factors and
     chunk-entry states that gdr2_bwd_chunked needs.  ``workspace`` may pass a preallocated uint8
     device tensor of at least the required size."""
@@ -170,7 +192,8 @@ def gdr2_fwd_chunked(q, k, v, log_alpha, b, w, S0=None, want_final_state=True, w
     need = lib.gdr2_fwd_workspace_bytes(B, T, H, dk, dv, dt)
     ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8,
                                                              device=q.device)
-    st = lib.gdr2_fwd_chunked_ex(B, T, H, dk, dv, dt, gate_bits(q, log_alpha, b, w), _ptr(q),
+    st = lib.gdr2_fwd_chunked_ex(B, T, H, dk, dv, dt, gate_bits(q, log_alpha, b, w),
+                                 _pro(prologue), _ptr(q),
                                  _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w), _ptr(S0),
                                  _ptr(o), _ptr(ST), _ptr(ws), ws.numel(), _stream())
     _check("gdr2_fwd_chunked", st)
@@ -178,9 +201,10 @@ def gdr2_fwd_chunked(q, k, v, log_alpha, b, w, S0=None, want_final_state=True, w
 
 
 def gdr2_bwd_chunked(q, k, v, log_alpha, b, w, dO, fwd_ws, dS_T=None, want_dS0=True,
-                     workspace=None):
+                     workspace=None, prologue=None):
     """Gate-aware backward.  ``fwd_ws`` is the third result of gdr2_fwd_chunked on the same inputs.
-    Returns a dict dq, dk, dv, dlog_alpha, db, dw, dS0 (None if not wanted)."""
+    Returns a dict dq, dk, dv, dlog_alpha, db, dw, dS0 (None if not wanted).  ``prologue`` must
+    be the one the forward ran with."""
     lib = load_library()
     _contig(q, k, v, log_alpha, b, w, dO, dS_T)
     B, T, H, dk, dv = _shapes(q, v)
@@ -193,7 +217,8 @@ def gdr2_bwd_chunked(q, k, v, log_alpha, b, w, dO, fwd_ws, dS_T=None, want_dS0=T
     need = lib.gdr2_bwd_workspace_bytes(B, T, H, dk, dv, dt)
     ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8,
                                                              device=dev)
-    st = lib.gdr2_bwd_chunked_ex(B, T, H, dk, dv, dt, gate_bits(q, log_alpha, b, w), _ptr(q),
+    st = lib.gdr2_bwd_chunked_ex(B, T, H, dk, dv, dt, gate_bits(q, log_alpha, b, w),
+                                 _pro(prologue), _ptr(q),
                                  _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w),
                                  _ptr(fwd_ws), fwd_ws.numel(), _ptr(dO), _ptr(dS_T),
                                  _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]),
@@ -211,11 +236,12 @@ def bwd_workspace_bytes(B, T, H, dk, dv, dtype):
     return load_library().gdr2_bwd_workspace_bytes(B, T, H, dk, dv, _DT[dtype])
 
 
-def gdr2_fwd_factors(q, k, v, log_alpha, b, w, ws):
+def gdr2_fwd_factors(q, k, v, log_alpha, b, w, ws, prologue=None):
     """Stage 1 of the forward: per-chunk WY factors into ``ws`` (uint8 device tensor)."""
     B, T, H, dk, dv = _shapes(q, v)
     st = load_library().gdr2_fwd_factors_ex(B, T, H, dk, dv, _dtype(q),
-                                            gate_bits(q, log_alpha, b, w), _ptr(q), _ptr(k),
+                                            gate_bits(q, log_alpha, b, w), _pro(prologue),
+                                            _ptr(q), _ptr(k),
                                             _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w), _ptr(ws),
                                             ws.numel(), _stream())
     _check("gdr2_fwd_factors", st)
@@ -236,12 +262,13 @@ def gdr2_bwd_state(B, T, H, dk, dv, dtype, fwd_ws, dO, bws, dS_T=None, dS0=None)
     _check("gdr2_bwd_state", st)
 
 
-def gdr2_bwd_grads(q, k, v, log_alpha, b, w, fwd_ws, dO, bws, g):
+def gdr2_bwd_grads(q, k, v, log_alpha, b, w, fwd_ws, dO, bws, g, prologue=None):
     """Stage 2 of the backward: fills g["dq"], g["dk"], g["dv"], g["dlog_alpha"], g["db"],
     g["dw"] (preallocated)."""
     B, T, H, dk, dv = _shapes(q, v)
     st = load_library().gdr2_bwd_grads_ex(B, T, H, dk, dv, _dtype(q),
-                                          gate_bits(q, log_alpha, b, w), _ptr(q), _ptr(k),
+                                          gate_bits(q, log_alpha, b, w), _pro(prologue),
+                                          _ptr(q), _ptr(k),
                                           _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w),
                                           _ptr(fwd_ws), fwd_ws.numel(), _ptr(dO), _ptr(g["dq"]),
                                           _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["dlog_alpha"]),
@@ -250,7 +277,7 @@ def gdr2_bwd_grads(q, k, v, log_alpha, b, w, fwd_ws, dO, bws, g):
     _check("gdr2_bwd_grads", st)
 
 
-def gdr2_decode_step(q, k, v, log_alpha, b, w, S_in=None, S_out=None):
+def gdr2_decode_step(q, k, v, log_alpha, b, w, S_in=None, S_out=None, prologue=None):
     """One decode token for [N, H] sequences-heads.  S_out defaults to S_in (in place) or a new
     buffer.  Returns (o, S_out)."""
     lib = load_library()
@@ -262,7 +289,8 @@ def gdr2_decode_step(q, k, v, log_alpha, b, w, S_in=None, S_out=None):
         S_out = S_in if S_in is not None else torch.empty((N, H, dk, dv), dtype=torch.float32,
                                                           device=q.device)
     o = torch.empty((N, H, dv), dtype=q.dtype, device=q.device)
-    st = lib.gdr2_decode_step_ex(N, H, dk, dv, dt, gate_bits(q, log_alpha, b, w), _ptr(q),
+    st = lib.gdr2_decode_step_ex(N, H, dk, dv, dt, gate_bits(q, log_alpha, b, w),
+                                 _pro(prologue), _ptr(q),
                                  _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w), _ptr(S_in),
                                  _ptr(S_out), _ptr(o), _stream())
     _check("gdr2_decode_step", st)

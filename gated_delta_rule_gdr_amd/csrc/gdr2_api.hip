@@ -38,6 +38,19 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 bool gates_ok(unsigned gates) { return (gates & ~7u) == 0; }
 
+bool prologue_ok(const gdr2_prologue* pro) {
+    if (!pro) return true;
+    const float c = pro->decay_scale, e = pro->norm_eps;
+    return c > 0.f && c < 1e30f && e > 0.f && e < 1e30f;
+}
+
+gdr2::Prologue prologue_of(const gdr2_prologue* pro) {
+    gdr2::Prologue x;
+    x.decay_scale = pro ? pro->decay_scale : 0.f;
+    x.norm_eps = pro ? pro->norm_eps : 0.f;
+    return x;
+}
+
 // Elements of b, w and log alpha (and of db, dw, dlog alpha) for `tokens` token-heads.
 struct GateSizes {
     size_t nb, nw, na;
@@ -142,6 +155,8 @@ static gdr2::FwdParams fwd_params(int64_t B, int64_t T, int64_t H, int64_t dv, c
                                   const FwdWs& L, void* ws, int dvs, unsigned gates = 0) {
     gdr2::FwdParams p;
     p.gates = (int)gates;
+    p.prologue = 0;
+    p.pro = prologue_of(nullptr);
     p.B = (int)B;
     p.H = (int)H;
     p.NS = (int)(dv / dvs);
@@ -188,17 +203,21 @@ static gdr2_status check_fwd(int64_t B, int64_t T, int64_t H, int64_t dk, int64_
 }
 
 gdr2_status gdr2_fwd_factors_ex(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
-                                gdr2_dtype dt, unsigned gates, const void* q, const void* k,
+                                gdr2_dtype dt, unsigned gates, const gdr2_prologue* pro,
+                                const void* q, const void* k,
                                 const void* v, const float* log_alpha, const void* b,
                                 const void* w, void* workspace, size_t workspace_bytes,
                                 void* stream) {
     gdr2_status st = check_fwd(B, T, H, dk, dv, dt, q, k, v, log_alpha, b, w, nullptr, nullptr,
                                nullptr, workspace, workspace_bytes, true, false, gates);
+    if (st == GDR2_OK && !prologue_ok(pro)) st = GDR2_E_VALUE;
     if (st != GDR2_OK || B == 0 || H == 0 || T == 0) return st;
     const int bf = dt == GDR2_BF16;
     const FwdWs L = fwd_ws_layout(B, T, H, dk, dv, dt);
     gdr2::FwdParams p = fwd_params(B, T, H, dv, q, k, v, log_alpha, b, w, nullptr, nullptr,
                                    nullptr, L, workspace, 16, gates);
+    p.prologue = pro != nullptr;
+    p.pro = prologue_of(pro);
     hipError_t e = gdr2::wy_dispatch(bf, (int)dk, (int)dv, p, (hipStream_t)stream);
     return e == hipSuccess ? GDR2_OK : GDR2_E_HIP;
 }
@@ -207,8 +226,8 @@ gdr2_status gdr2_fwd_factors(int64_t B, int64_t T, int64_t H, int64_t dk, int64_
                              gdr2_dtype dt, const void* q, const void* k, const void* v,
                              const float* log_alpha, const void* b, const void* w,
                              void* workspace, size_t workspace_bytes, void* stream) {
-    return gdr2_fwd_factors_ex(B, T, H, dk, dv, dt, 0u, q, k, v, log_alpha, b, w, workspace,
-                               workspace_bytes, stream);
+    return gdr2_fwd_factors_ex(B, T, H, dk, dv, dt, 0u, nullptr, q, k, v, log_alpha, b, w,
+                               workspace, workspace_bytes, stream);
 }
 
 gdr2_status gdr2_fwd_carry(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
@@ -227,16 +246,18 @@ gdr2_status gdr2_fwd_carry(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t 
 }
 
 gdr2_status gdr2_fwd_chunked_ex(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
-                                gdr2_dtype dt, unsigned gates, const void* q, const void* k,
+                                gdr2_dtype dt, unsigned gates, const gdr2_prologue* pro,
+                                const void* q, const void* k,
                                 const void* v, const float* log_alpha, const void* b,
                                 const void* w, const float* S0, void* o, float* S_T,
                                 void* workspace, size_t workspace_bytes, void* stream) {
     gdr2_status st = check_fwd(B, T, H, dk, dv, dt, q, k, v, log_alpha, b, w, S0, o, S_T,
                                workspace, workspace_bytes, true, true, gates);
+    if (st == GDR2_OK && !prologue_ok(pro)) st = GDR2_E_VALUE;
     if (st != GDR2_OK || B == 0 || H == 0) return st;
     if (T > 0) {
-        st = gdr2_fwd_factors_ex(B, T, H, dk, dv, dt, gates, q, k, v, log_alpha, b, w, workspace,
-                                 workspace_bytes, stream);
+        st = gdr2_fwd_factors_ex(B, T, H, dk, dv, dt, gates, pro, q, k, v, log_alpha, b, w,
+                                 workspace, workspace_bytes, stream);
         if (st != GDR2_OK) return st;
     }
     return gdr2_fwd_carry(B, T, H, dk, dv, dt, S0, o, S_T, workspace, workspace_bytes, stream);
@@ -247,8 +268,8 @@ gdr2_status gdr2_fwd_chunked(int64_t B, int64_t T, int64_t H, int64_t dk, int64_
                              const float* log_alpha, const void* b, const void* w,
                              const float* S0, void* o, float* S_T, void* workspace,
                              size_t workspace_bytes, void* stream) {
-    return gdr2_fwd_chunked_ex(B, T, H, dk, dv, dt, 0u, q, k, v, log_alpha, b, w, S0, o, S_T,
-                               workspace, workspace_bytes, stream);
+    return gdr2_fwd_chunked_ex(B, T, H, dk, dv, dt, 0u, nullptr, q, k, v, log_alpha, b, w, S0, o,
+                               S_T, workspace, workspace_bytes, stream);
 }
 
 // Validation shared by the backward phases.
@@ -297,6 +318,8 @@ static gdr2::BwdParams bwd_params(int64_t B, int64_t T, int64_t H, int64_t dk, i
     const FwdWs L = fwd_ws_layout(B, T, H, dk, dv, dt);
     gdr2::BwdParams p;
     p.gates = (int)gates;
+    p.prologue = 0;
+    p.pro = prologue_of(nullptr);
     p.B = (int)B; p.H = (int)H; p.NC = (int)gdr2_num_chunks(T); p.T = T; p.DV = dv;
     p.NS = (int)(dv / gdr2::carry_slice_width(bf, (int)dk, (int)dv, B * H));
     p.q = q; p.k = k; p.v = v; p.b = b; p.w = w; p.la = la;
@@ -326,7 +349,8 @@ gdr2_status gdr2_bwd_state(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t 
 }
 
 gdr2_status gdr2_bwd_grads_ex(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
-                              gdr2_dtype dt, unsigned gates, const void* q, const void* k,
+                              gdr2_dtype dt, unsigned gates, const gdr2_prologue* pro,
+                              const void* q, const void* k,
                               const void* v, const float* log_alpha, const void* b, const void* w,
                               const void* fwd_workspace, size_t fwd_workspace_bytes,
                               const void* dO, void* dq, void* dk_, void* dv_, float* dlog_alpha,
@@ -335,11 +359,14 @@ gdr2_status gdr2_bwd_grads_ex(int64_t B, int64_t T, int64_t H, int64_t dk, int64
     gdr2_status st = check_bwd(B, T, H, dk, dv, dt, q, k, v, log_alpha, b, w, fwd_workspace,
                                fwd_workspace_bytes, dO, nullptr, dq, dk_, dv_, dlog_alpha, db, dw,
                                nullptr, workspace, workspace_bytes, true, true, gates);
+    if (st == GDR2_OK && !prologue_ok(pro)) st = GDR2_E_VALUE;
     if (st != GDR2_OK || B == 0 || H == 0 || T == 0) return st;
     const int bf = dt == GDR2_BF16;
     gdr2::BwdParams p = bwd_params(B, T, H, dk, dv, dt, q, k, v, log_alpha, b, w, fwd_workspace,
                                    dO, nullptr, dq, dk_, dv_, dlog_alpha, db, dw, nullptr,
                                    workspace, gates);
+    p.prologue = pro != nullptr;
+    p.pro = prologue_of(pro);
     hipError_t e = gdr2::bgrad_dispatch(bf, (int)dk, (int)dv, p, (hipStream_t)stream);
     return e == hipSuccess ? GDR2_OK : GDR2_E_HIP;
 }
@@ -350,13 +377,14 @@ gdr2_status gdr2_bwd_grads(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t 
                            const void* fwd_workspace, size_t fwd_workspace_bytes, const void* dO,
                            void* dq, void* dk_, void* dv_, float* dlog_alpha, void* db, void* dw,
                            const void* workspace, size_t workspace_bytes, void* stream) {
-    return gdr2_bwd_grads_ex(B, T, H, dk, dv, dt, 0u, q, k, v, log_alpha, b, w, fwd_workspace,
-                             fwd_workspace_bytes, dO, dq, dk_, dv_, dlog_alpha, db, dw, workspace,
-                             workspace_bytes, stream);
+    return gdr2_bwd_grads_ex(B, T, H, dk, dv, dt, 0u, nullptr, q, k, v, log_alpha, b, w,
+                             fwd_workspace, fwd_workspace_bytes, dO, dq, dk_, dv_, dlog_alpha, db,
+                             dw, workspace, workspace_bytes, stream);
 }
 
 gdr2_status gdr2_bwd_chunked_ex(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
-                                gdr2_dtype dt, unsigned gates, const void* q, const void* k,
+                                gdr2_dtype dt, unsigned gates, const gdr2_prologue* pro,
+                                const void* q, const void* k,
                                 const void* v, const float* log_alpha, const void* b,
                                 const void* w, const void* fwd_workspace,
                                 size_t fwd_workspace_bytes, const void* dO, const float* dS_T,
@@ -366,13 +394,14 @@ gdr2_status gdr2_bwd_chunked_ex(int64_t B, int64_t T, int64_t H, int64_t dk, int
     gdr2_status st = check_bwd(B, T, H, dk, dv, dt, q, k, v, log_alpha, b, w, fwd_workspace,
                                fwd_workspace_bytes, dO, dS_T, dq, dk_, dv_, dlog_alpha, db, dw,
                                dS0, workspace, workspace_bytes, true, true, gates);
+    if (st == GDR2_OK && !prologue_ok(pro)) st = GDR2_E_VALUE;
     if (st != GDR2_OK || B == 0 || H == 0) return st;
     st = gdr2_bwd_state(B, T, H, dk, dv, dt, fwd_workspace, fwd_workspace_bytes, dO, dS_T, dS0,
                         workspace, workspace_bytes, stream);
     if (st != GDR2_OK || T == 0) return st;
-    return gdr2_bwd_grads_ex(B, T, H, dk, dv, dt, gates, q, k, v, log_alpha, b, w, fwd_workspace,
-                             fwd_workspace_bytes, dO, dq, dk_, dv_, dlog_alpha, db, dw, workspace,
-                             workspace_bytes, stream);
+    return gdr2_bwd_grads_ex(B, T, H, dk, dv, dt, gates, pro, q, k, v, log_alpha, b, w,
+                             fwd_workspace, fwd_workspace_bytes, dO, dq, dk_, dv_, dlog_alpha, db,
+                             dw, workspace, workspace_bytes, stream);
 }
 
 gdr2_status gdr2_bwd_chunked(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
@@ -382,18 +411,20 @@ gdr2_status gdr2_bwd_chunked(int64_t B, int64_t T, int64_t H, int64_t dk, int64_
                              const void* dO, const float* dS_T, void* dq, void* dk_, void* dv_,
                              float* dlog_alpha, void* db, void* dw, float* dS0,
                              void* workspace, size_t workspace_bytes, void* stream) {
-    return gdr2_bwd_chunked_ex(B, T, H, dk, dv, dt, 0u, q, k, v, log_alpha, b, w, fwd_workspace,
-                               fwd_workspace_bytes, dO, dS_T, dq, dk_, dv_, dlog_alpha, db, dw,
-                               dS0, workspace, workspace_bytes, stream);
+    return gdr2_bwd_chunked_ex(B, T, H, dk, dv, dt, 0u, nullptr, q, k, v, log_alpha, b, w,
+                               fwd_workspace, fwd_workspace_bytes, dO, dS_T, dq, dk_, dv_,
+                               dlog_alpha, db, dw, dS0, workspace, workspace_bytes, stream);
 }
 
 gdr2_status gdr2_decode_step_ex(int64_t N, int64_t H, int64_t dk, int64_t dv, gdr2_dtype dt,
-                                unsigned gates, const void* q, const void* k, const void* v,
+                                unsigned gates, const gdr2_prologue* pro, const void* q,
+                                const void* k, const void* v,
                                 const float* log_alpha, const void* b, const void* w,
                                 const float* S_in, float* S_out, void* o, void* stream) {
     if (dt != GDR2_F32 && dt != GDR2_BF16) return GDR2_E_DTYPE;
     if (N < 0 || H < 0 || dk < 0 || dv < 0) return GDR2_E_SHAPE;
     if (!dims_ok(dk) || !dims_ok(dv) || !gates_ok(gates)) return GDR2_E_UNSUPPORTED;
+    if (!prologue_ok(pro)) return GDR2_E_VALUE;
     if (N * H > ((int64_t)1 << 31) - 1) return GDR2_E_SHAPE;
     if (N == 0 || H == 0) return GDR2_OK;
     if (!q || !k || !v || !log_alpha || !b || !w || !S_out || !o) return GDR2_E_NULL;
@@ -413,6 +444,8 @@ gdr2_status gdr2_decode_step_ex(int64_t N, int64_t H, int64_t dk, int64_t dv, gd
     if (S_in && S_in == S_out && overlap({S_in, ns * 4}, outs[1])) return GDR2_E_ALIAS;
     gdr2::DecodeParams p;
     p.N = N; p.H = H; p.gates = (int)gates;
+    p.prologue = pro != nullptr;
+    p.pro = prologue_of(pro);
     p.q = q; p.k = k; p.v = v; p.b = b; p.w = w; p.la = log_alpha;
     p.S_in = S_in; p.S_out = S_out; p.o = o;
     hipError_t e = gdr2::decode_dispatch(dt == GDR2_BF16, (int)dk, (int)dv, p, (hipStream_t)stream);
@@ -423,8 +456,8 @@ gdr2_status gdr2_decode_step(int64_t N, int64_t H, int64_t dk, int64_t dv, gdr2_
                              const void* q, const void* k, const void* v,
                              const float* log_alpha, const void* b, const void* w,
                              const float* S_in, float* S_out, void* o, void* stream) {
-    return gdr2_decode_step_ex(N, H, dk, dv, dt, 0u, q, k, v, log_alpha, b, w, S_in, S_out, o,
-                               stream);
+    return gdr2_decode_step_ex(N, H, dk, dv, dt, 0u, nullptr, q, k, v, log_alpha, b, w, S_in,
+                               S_out, o, stream);
 }
 
 // ------------------------------------------------------------------ output epilogue

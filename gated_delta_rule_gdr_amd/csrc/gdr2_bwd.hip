@@ -531,9 +531,10 @@ struct alignas(16) BgSmem {
     float btot[4][DK];
     float ktot[4][DK];
     float gred[2][kChunk][3];  // per-token partial sums of db, dw, dlog alpha (scalar gates)
+    float nrm[2][kChunk][4];   // fused prologue: per-token |q|^2, |k|^2, qhat.dq, khat.dk partials
 };
 
-template <typename OT, int DK, int DV, int DVH, bool GS>
+template <typename OT, int DK, int DV, int DVH, int MODE>
 __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) {
     using Cf = BgCfg<OT, DK, DV, DVH>;
     using MM = Mfma<OT>;
@@ -562,7 +563,8 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
 
     // ---- this lane's log alpha (token r, channels 16 (ibase+ib) + 4g + e); q, k, b come later
     typename RW::t qr[NIBH], kr[NIBH], br[NIBH];
-    // scalar gates (GS instances only: the channel-wise instance carries no gate branches)
+    // scalar gates and the fused prologue (the plain instance carries no gate branches)
+    constexpr bool GS = MODE != kModePlain, PRO = MODE == kModePrologue;
     const bool b_sc = GS && (p.gates & kEraseScalar), w_sc = GS && (p.gates & kWriteScalar);
     const bool a_sc = GS && (p.gates & kDecayScalar);
     f32x4 sc[NIBH];  // log alpha, then G_r - ref_R
@@ -573,6 +575,12 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
     } else {
 #pragma unroll
         for (int ib = 0; ib < NIBH; ++ib) sc[ib] = *(const f32x4*)(p.la + row * DK + 16 * (ibase + ib) + 4 * g);
+    }
+    if (PRO) {  // log alpha = -decay_scale * softplus(a)
+#pragma unroll
+        for (int ib = 0; ib < NIBH; ++ib)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sc[ib][e] = -p.pro.decay_scale * softplus_f(sc[ib][e]);
     }
     // ---- the chunk's -Y and Ktilde: staged into LDS with T and P below (16-bit operands), or
     //      this wave's token block kept as fragments (fp32)
@@ -770,14 +778,19 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
                 MM::mma(ax, FR::kc(sm.u.j.dDT, PC, 16 * jb, k0), FR::tr(sm.u.j.Tt, PC, k0, 16 * R));
             const int jc = 16 * jb + 4 * g;
             store4(sm.u.j.dXt + r * PH + jc, ax);
-            if (w_sc) {
-                const f32x4 xv = ax * RW::widen(cv);
-                dw_acc += (xv[0] + xv[1]) + (xv[2] + xv[3]);
+            f32x4 wg = RW::widen(cw), dwv = ax * RW::widen(cv);
+            if (PRO) {  // w = sigmoid(w pre-activation): dw_pre = dw . w (1 - w)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    wg[e] = sigmoid_f(wg[e]);
+                    dwv[e] *= wg[e] * (1.f - wg[e]);
+                }
             }
+            if (w_sc) dw_acc += (dwv[0] + dwv[1]) + (dwv[2] + dwv[3]);
             if (valid) {
                 const long o = (tok0 + (long)r * H) * DV + jb0 + jc;
-                store4((OT*)p.dv + o, ax * RW::widen(cw));
-                if (!w_sc) store4((OT*)p.dw + o, ax * RW::widen(cv));
+                store4((OT*)p.dv + o, ax * wg);
+                if (!w_sc) store4((OT*)p.dw + o, dwv);
             }
         }
         lds_barrier();
@@ -816,11 +829,47 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
         lds_barrier();
     }
 
+    // ---- fused prologue: the row norms of q and k (lanes 16g + rl of both channel halves)
+    float rq = 1.f, rk = 1.f;
+    if (PRO) {
+        float sq = 0.f, sk = 0.f;
+#pragma unroll
+        for (int ib = 0; ib < NIBH; ++ib) {
+            const f32x4 q4 = RW::widen(qr[ib]), k4 = RW::widen(kr[ib]);
+            sq += (q4[0] * q4[0] + q4[1] * q4[1]) + (q4[2] * q4[2] + q4[3] * q4[3]);
+            sk += (k4[0] * k4[0] + k4[1] * k4[1]) + (k4[2] * k4[2] + k4[3] * k4[3]);
+        }
+        sq += __shfl_xor(sq, 16);
+        sq += __shfl_xor(sq, 32);
+        sk += __shfl_xor(sk, 16);
+        sk += __shfl_xor(sk, 32);
+        if (g == 0) {
+            sm.nrm[half][r][0] = sq;
+            sm.nrm[half][r][1] = sk;
+        }
+        lds_barrier();
+        rq = rsqrtf(sm.nrm[0][r][0] + sm.nrm[1][r][0] + p.pro.norm_eps);
+        rk = rsqrtf(sm.nrm[0][r][1] + sm.nrm[1][r][1] + p.pro.norm_eps);
+    }
+    // the activations the forward used: q, k normalised, b through the sigmoid
+    auto act = [&](int ib, f32x4& q4, f32x4& k4, f32x4& b4) __attribute__((always_inline)) {
+        q4 = RW::widen(qr[ib]);
+        k4 = RW::widen(kr[ib]);
+        b4 = RW::widen(br[ib]);
+        if (PRO) {
+            q4 *= rq;
+            k4 *= rk;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) b4[e] = sigmoid_f(b4[e]);
+        }
+    };
+
     // ---- decay-absorbed key tiles (the value tiles are dead) and the dP^T, dA^T tiles
 #pragma unroll
     for (int ib = 0; ib < NIBH; ++ib) {
         const int i0 = 16 * (ibase + ib) + 4 * g;
-        const f32x4 q4 = RW::widen(qr[ib]), k4 = RW::widen(kr[ib]), b4 = RW::widen(br[ib]);
+        f32x4 q4, k4, b4;
+        act(ib, q4, k4, b4);
         f32x4 eb, qb, kb;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -899,10 +948,13 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
     f32x4 dG[NIBH];
     const long orow = row * DK;
     float db_acc = 0.f;
+    f32x4 dqs[PRO ? NIBH : 1], dks[PRO ? NIBH : 1];  // prologue: gradients held for the norm step
+    float Dq = 0.f, Dk = 0.f;                          // prologue: qhat . dq, khat . dk partials
 #pragma unroll
     for (int ib = 0; ib < NIBH; ++ib) {
         const int i0 = 16 * (ibase + ib) + 4 * g;
-        f32x4 q4 = RW::widen(qr[ib]), k4 = RW::widen(kr[ib]), b4 = RW::widen(br[ib]);
+        f32x4 q4, k4, b4;
+        act(ib, q4, k4, b4);
         if (!valid) q4 = k4 = b4 = f32x4{0.f, 0.f, 0.f, 0.f};
         const f32x4 hr = *(const f32x4*)(&sm.hRt[R][i0]);
         f32x4 dqv, dkv, dbv, kdk;
@@ -919,10 +971,20 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
             dG[ib][e] = row_rscan16(q4[e] * dq + b4[e] * k4[e] * de - k4[e] * (dkb + dkt));
             kdk[e] = row_rscan16(k4[e] * dkt);
         }
+        if (PRO) {  // b = sigmoid(b pre-activation); q, k wait for their row dots
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dbv[e] *= b4[e] * (1.f - b4[e]);
+            dqs[PRO ? ib : 0] = dqv;
+            dks[PRO ? ib : 0] = dkv;
+            Dq += (q4[0] * dqv[0] + q4[1] * dqv[1]) + (q4[2] * dqv[2] + q4[3] * dqv[3]);
+            Dk += (k4[0] * dkv[0] + k4[1] * dkv[1]) + (k4[2] * dkv[2] + k4[3] * dkv[3]);
+        }
         if (b_sc) db_acc += (dbv[0] + dbv[1]) + (dbv[2] + dbv[3]);
         if (valid) {
-            store4((OT*)p.dq + orow + i0, dqv);
-            store4((OT*)p.dk + orow + i0, dkv);
+            if (!PRO) {
+                store4((OT*)p.dq + orow + i0, dqv);
+                store4((OT*)p.dk + orow + i0, dkv);
+            }
             if (!b_sc) store4((OT*)p.db + orow + i0, dbv);
         }
         if (rl == 0) {
@@ -942,7 +1004,28 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
             sm.gred[half][r][1] = dw_acc;
         }
     }
+    if (PRO) {
+        Dq += __shfl_xor(Dq, 16);
+        Dq += __shfl_xor(Dq, 32);
+        Dk += __shfl_xor(Dk, 16);
+        Dk += __shfl_xor(Dk, 32);
+        if (g == 0) {
+            sm.nrm[half][r][2] = Dq;
+            sm.nrm[half][r][3] = Dk;
+        }
+    }
     lds_barrier();
+    if (PRO && valid) {  // d q_pre = r_q (dq - qhat (qhat . dq)), the same for k
+        const float Dqt = sm.nrm[0][r][2] + sm.nrm[1][r][2], Dkt = sm.nrm[0][r][3] + sm.nrm[1][r][3];
+#pragma unroll
+        for (int ib = 0; ib < NIBH; ++ib) {
+            const int i0 = 16 * (ibase + ib) + 4 * g;
+            f32x4 q4, k4, b4;
+            act(ib, q4, k4, b4);
+            store4((OT*)p.dq + orow + i0, rq * (dqs[PRO ? ib : 0] - q4 * Dqt));
+            store4((OT*)p.dk + orow + i0, rk * (dks[PRO ? ib : 0] - k4 * Dkt));
+        }
+    }
     float dl_acc = 0.f;
     if (valid) {
 #pragma unroll
@@ -958,6 +1041,11 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
                     if (Rp > R) add += sm.btot[Rp][i0 + e];
                 }
                 dl[e] += add;
+            }
+            if (PRO && !a_sc) {  // log alpha = -c softplus(a): d a = d log alpha . (-c sigmoid(a))
+                const f32x4 a4 = *(const f32x4*)(p.la + orow + i0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dl[e] *= -p.pro.decay_scale * sigmoid_f(a4[e]);
             }
             if (a_sc) {
                 dl_acc += (dl[0] + dl[1]) + (dl[2] + dl[3]);
@@ -975,7 +1063,10 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
     if ((b_sc || w_sc || a_sc) && half == 0 && g == 0 && valid) {
         if (b_sc) ((OT*)p.db)[row] = from_f<OT>(sm.gred[0][r][0] + sm.gred[1][r][0]);
         if (w_sc) ((OT*)p.dw)[row] = from_f<OT>(sm.gred[0][r][1] + sm.gred[1][r][1]);
-        if (a_sc) p.dla[row] = sm.gred[0][r][2] + sm.gred[1][r][2];
+        if (a_sc) {
+            const float d = sm.gred[0][r][2] + sm.gred[1][r][2];
+            p.dla[row] = PRO ? d * (-p.pro.decay_scale * sigmoid_f(p.la[row])) : d;
+        }
     }
 }
 
@@ -983,10 +1074,12 @@ template <typename OT, int DK, int DV>
 static hipError_t launch_bgrad(const BwdParams& p, hipStream_t s) {
     const long nblk = (long)p.B * p.H * p.NC;
     if (nblk == 0) return hipSuccess;
-    if (p.gates)
-        hipLaunchKernelGGL((gdr2_bgrad_kernel<OT, DK, DV, 32, true>), dim3(nblk), dim3(kBgThreads), 0, s, p);
+    if (p.prologue)
+        hipLaunchKernelGGL((gdr2_bgrad_kernel<OT, DK, DV, 32, kModePrologue>), dim3(nblk), dim3(kBgThreads), 0, s, p);
+    else if (p.gates)
+        hipLaunchKernelGGL((gdr2_bgrad_kernel<OT, DK, DV, 32, kModeGates>), dim3(nblk), dim3(kBgThreads), 0, s, p);
     else
-        hipLaunchKernelGGL((gdr2_bgrad_kernel<OT, DK, DV, 32, false>), dim3(nblk), dim3(kBgThreads), 0, s, p);
+        hipLaunchKernelGGL((gdr2_bgrad_kernel<OT, DK, DV, 32, kModePlain>), dim3(nblk), dim3(kBgThreads), 0, s, p);
     return hipGetLastError();
 }
 

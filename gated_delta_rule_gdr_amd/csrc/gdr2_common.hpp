@@ -294,6 +294,10 @@ template <> struct FFrag<float> {
     }
 };
 
+// Activations of the fused prologue.
+__device__ __forceinline__ float sigmoid_f(float x) { return 1.f / (1.f + __expf(-x)); }
+__device__ __forceinline__ float softplus_f(float x) { return x > 20.f ? x : __logf(1.f + __expf(x)); }
+
 // Inclusive suffix sum over the 16 lanes of each DPP row: lane i gets the sum of lanes i..15.
 __device__ __forceinline__ float row_rscan16(float x) {
     int v = __builtin_bit_cast(int, x);

@@ -16,8 +16,9 @@
 
 namespace gdr2 {
 
-template <typename IT, int DK, int DV, bool GS>
+template <typename IT, int DK, int DV, int MODE>
 __global__ __launch_bounds__(kThreads) void gdr2_decode_kernel(DecodeParams p) {
+    constexpr bool GS = MODE != kModePlain, PRO = MODE == kModePrologue;
     constexpr int CGR = DV / 4;           // 4-column groups
     constexpr int RGR = kThreads / CGR;   // row groups
     constexpr int RPT = DK / RGR;         // rows per thread
@@ -25,6 +26,7 @@ __global__ __launch_bounds__(kThreads) void gdr2_decode_kernel(DecodeParams p) {
     __shared__ float red_r[RGR][DV];
     __shared__ float red_p[RGR][DV];
     __shared__ float red_qk[RGR];
+    __shared__ float red_n[RGR][2];  // fused prologue: |q|^2, |k|^2 partials
 
     const long nh = blockIdx.x;
     const int tid = threadIdx.x;
@@ -50,15 +52,21 @@ __global__ __launch_bounds__(kThreads) void gdr2_decode_kernel(DecodeParams p) {
     }
     float kk[RPT];
     f32x4 pr = {0.f, 0.f, 0.f, 0.f}, pp = {0.f, 0.f, 0.f, 0.f};
-    float pqk = 0.f;
+    float pqk = 0.f, nq = 0.f, nk = 0.f;
 #pragma unroll
     for (int u = 0; u < RPT; ++u) {
         const int i = ibase + u;
-        const float a = __expf(la[sa * i]);
+        // with the fused prologue q, k are raw (their norms scale the sums below afterwards),
+        // b and log alpha are pre-activations
+        const float lai = PRO ? -p.pro.decay_scale * softplus_f(la[sa * i]) : la[sa * i];
+        const float a = __expf(lai);
         const float ki = to_f(k[i]), qi = to_f(q[i]);
-        const float e = to_f(b[sb * i]) * ki;
+        const float bi = PRO ? sigmoid_f(to_f(b[sb * i])) : to_f(b[sb * i]);
+        const float e = bi * ki;
         kk[u] = ki;
         pqk += qi * ki;
+        nq += qi * qi;
+        nk += ki * ki;
         if (!Sin) s[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -69,19 +77,39 @@ __global__ __launch_bounds__(kThreads) void gdr2_decode_kernel(DecodeParams p) {
     }
     *(f32x4*)&red_r[ig][j0] = pr;
     *(f32x4*)&red_p[ig][j0] = pp;
-    if (jg == 0) red_qk[ig] = pqk;
+    if (jg == 0) {
+        red_qk[ig] = pqk;
+        red_n[ig][0] = nq;
+        red_n[ig][1] = nk;
+    }
     __syncthreads();
     f32x4 r = {0.f, 0.f, 0.f, 0.f}, pq = {0.f, 0.f, 0.f, 0.f};
     float qk = 0.f;
+    float tq = 0.f, tk = 0.f;
 #pragma unroll
     for (int g = 0; g < RGR; ++g) {
         r += *(const f32x4*)&red_r[g][j0];
         pq += *(const f32x4*)&red_p[g][j0];
         qk += red_qk[g];
+        if (PRO) {
+            tq += red_n[g][0];
+            tk += red_n[g][1];
+        }
+    }
+    if (PRO) {  // q, k were raw: scale every sum by the row norms
+        const float rq = rsqrtf(tq + p.pro.norm_eps), rk = rsqrtf(tk + p.pro.norm_eps);
+        r *= rk;
+        pq *= rq;
+        qk *= rq * rk;
+#pragma unroll
+        for (int u = 0; u < RPT; ++u) kk[u] *= rk;
     }
     f32x4 u4;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) u4[j] = to_f(w[sw * (j0 + j)]) * to_f(v[j0 + j]) - r[j];
+    for (int j = 0; j < 4; ++j) {
+        const float wj = PRO ? sigmoid_f(to_f(w[sw * (j0 + j)])) : to_f(w[sw * (j0 + j)]);
+        u4[j] = wj * to_f(v[j0 + j]) - r[j];
+    }
 #pragma unroll
     for (int u = 0; u < RPT; ++u) {
         f32x4 x;
@@ -99,10 +127,12 @@ __global__ __launch_bounds__(kThreads) void gdr2_decode_kernel(DecodeParams p) {
 
 template <typename IT, int DK, int DV>
 static hipError_t launch_decode(const DecodeParams& p, hipStream_t s) {
-    if (p.gates)
-        hipLaunchKernelGGL((gdr2_decode_kernel<IT, DK, DV, true>), dim3(p.N * p.H), dim3(kThreads), 0, s, p);
+    if (p.prologue)
+        hipLaunchKernelGGL((gdr2_decode_kernel<IT, DK, DV, kModePrologue>), dim3(p.N * p.H), dim3(kThreads), 0, s, p);
+    else if (p.gates)
+        hipLaunchKernelGGL((gdr2_decode_kernel<IT, DK, DV, kModeGates>), dim3(p.N * p.H), dim3(kThreads), 0, s, p);
     else
-        hipLaunchKernelGGL((gdr2_decode_kernel<IT, DK, DV, false>), dim3(p.N * p.H), dim3(kThreads), 0, s, p);
+        hipLaunchKernelGGL((gdr2_decode_kernel<IT, DK, DV, kModePlain>), dim3(p.N * p.H), dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
 

@@ -35,11 +35,12 @@
 
 namespace gdr2 {
 
-template <typename OT, int DK, int DV, bool GS>
+template <typename OT, int DK, int DV, int MODE>
 __global__ __launch_bounds__(kThreads, 2) void gdr2_wy_kernel(FwdParams p) {
     __shared__ WySmem<OT, DK, DV> sm;
-    WyChunk<OT, DK, DV> ch(p.B, p.H, p.T, p.DV, p.NC, p.gates, blockIdx.x, p.q, p.k, p.b, p.la, p.v, p.w);
-    wy_factors<OT, DK, DV, GS>(sm, ch, p.wy);
+    WyChunk<OT, DK, DV> ch(p.B, p.H, p.T, p.DV, p.NC, p.gates, p.pro, blockIdx.x, p.q, p.k, p.b,
+                           p.la, p.v, p.w);
+    wy_factors<OT, DK, DV, MODE>(sm, ch, p.wy);
 }
 
 template <typename OT, int DK, int DVS>
@@ -482,10 +483,12 @@ template <typename OT, int DK, int DV>
 static hipError_t launch_wy(const FwdParams& p, hipStream_t s) {
     const long nblk = (long)p.B * p.H * p.NC;
     if (nblk == 0) return hipSuccess;
-    if (p.gates)
-        hipLaunchKernelGGL((gdr2_wy_kernel<OT, DK, DV, true>), dim3(nblk), dim3(kThreads), 0, s, p);
+    if (p.prologue)
+        hipLaunchKernelGGL((gdr2_wy_kernel<OT, DK, DV, kModePrologue>), dim3(nblk), dim3(kThreads), 0, s, p);
+    else if (p.gates)
+        hipLaunchKernelGGL((gdr2_wy_kernel<OT, DK, DV, kModeGates>), dim3(nblk), dim3(kThreads), 0, s, p);
     else
-        hipLaunchKernelGGL((gdr2_wy_kernel<OT, DK, DV, false>), dim3(nblk), dim3(kThreads), 0, s, p);
+        hipLaunchKernelGGL((gdr2_wy_kernel<OT, DK, DV, kModePlain>), dim3(nblk), dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
 

@@ -10,6 +10,16 @@ constexpr int kEraseScalar = 1;   // b
 constexpr int kWriteScalar = 2;   // w
 constexpr int kDecayScalar = 4;   // log alpha
 
+// Kernel instances: plain (every gate channel-wise, post-activation inputs), scalar gates (the
+// gates bits read at run time), fused prologue (pre-activation inputs, gate bits at run time).
+constexpr int kModePlain = 0, kModeGates = 1, kModePrologue = 2;
+
+// Fused prologue parameters: q, k scaled by (sum of squares + norm_eps)^-1/2, b = sigmoid(b),
+// w = sigmoid(w), log alpha = -decay_scale * softplus(a).
+struct Prologue {
+    float decay_scale, norm_eps;
+};
+
 // Per-chunk WY factors written by the chunk-parallel factor kernel and read by the state-carry
 // kernels (forward and backward) and the chunk-gradient kernel.  Element type = input dtype
 // except gam.  Every array is indexed [chain = b*H + h][chunk][...]; the [C][*] tiles are in
@@ -27,6 +37,8 @@ struct WyBufs {
 struct FwdParams {
     int B, H, NS, NC;   // batch, heads, value slices per chain, chunks
     int gates;          // gate shapes (kEraseScalar | kWriteScalar | kDecayScalar)
+    int prologue;       // inputs are pre-activations (see Prologue)
+    Prologue pro;
     long T, DV;         // tokens, value width (DK is a template parameter)
     const void *q, *k, *v, *b, *w;  // input dtype
     const float* la;    // log decay, fp32
@@ -39,7 +51,8 @@ struct FwdParams {
 
 struct DecodeParams {
     long N, H;
-    int gates;
+    int gates, prologue;
+    Prologue pro;
     const void *q, *k, *v, *b, *w;
     const float* la;
     const float* S_in;  // may equal S_out; null = zero state
@@ -49,7 +62,8 @@ struct DecodeParams {
 
 struct BwdParams {
     int B, H, NS, NC;
-    int gates;
+    int gates, prologue;
+    Prologue pro;
     long T, DV;
     const void *q, *k, *v, *b, *w;
     const float* la;

@@ -175,10 +175,12 @@ struct WyChunk {
     const OT *q, *k, *b, *v, *w;
     const float* la;
     int gates;
-    __device__ WyChunk(int B, int H_, long T_, long DV_, int NC, int gates_, int bid, const void* q_,
+    Prologue pro;
+    __device__ WyChunk(int B, int H_, long T_, long DV_, int NC, int gates_, Prologue pro_, int bid, const void* q_,
                        const void* k_, const void* b_, const float* la_, const void* v_,
                        const void* w_) {
         gates = gates_;
+        pro = pro_;
         (void)B;
         chain = bid / NC;
         c = bid % NC;
@@ -206,9 +208,10 @@ struct WyChunk {
 };
 
 // Compute and store the WY factors of one chunk (see the file comment); every thread of the
-// workgroup calls it.  GS: some gate is a scalar per head (ch.gates says which); the all
-// channel-wise instance has no gate branches, so its loads issue back to back.
-template <typename OT, int DK, int DV, bool GS>
+// workgroup calls it.  MODE (kModePlain / kModeGates / kModePrologue): the plain instance has no
+// gate branches, so its loads issue back to back; the others read the gate bits (and apply the
+// fused prologue) at run time.
+template <typename OT, int DK, int DV, int MODE>
 __device__ void wy_factors(WySmem<OT, DK, DV>& sm, const WyChunk<OT, DK, DV>& ch, const WyBufs& wy) {
     using Cf = WyCfg<OT, DK, DV>;
     using MM = Mfma<OT>;
@@ -218,6 +221,7 @@ __device__ void wy_factors(WySmem<OT, DK, DV>& sm, const WyChunk<OT, DK, DV>& ch
     constexpr int NCV = Cf::NCV;
     const int R = ch.R, l = ch.l, rl = ch.rl, g = ch.g, r = ch.r;
     const long cix = ch.cix, DVl = ch.DVl;
+    constexpr bool GS = MODE != kModePlain, PRO = MODE == kModePrologue;
 
     float qv[NCH], kv[NCH], bv[NCH], lv[NCH], zv[NCV];
 #pragma unroll
@@ -250,8 +254,33 @@ __device__ void wy_factors(WySmem<OT, DK, DV>& sm, const WyChunk<OT, DK, DV>& ch
         } else {
             load_lane<OT>(ch.w, ks, g, wv);
         }
+        if (PRO) {
+#pragma unroll
+            for (int j = 0; j < KPL; ++j) wv[j] = sigmoid_f(wv[j]);
+        }
 #pragma unroll
         for (int j = 0; j < KPL; ++j) zv[ks * KPL + j] = ch.valid ? vv[j] * wv[j] : 0.f;
+    }
+    if (PRO) {  // fused prologue: L2-normalised q, k; sigmoid gates; log alpha from softplus
+        float sq = 0.f, sk = 0.f;
+#pragma unroll
+        for (int n = 0; n < NCH; ++n) {
+            sq += qv[n] * qv[n];
+            sk += kv[n] * kv[n];
+        }
+        // the row's channels sit in the four lanes rl + 16 g
+        sq += __shfl_xor(sq, 16);
+        sq += __shfl_xor(sq, 32);
+        sk += __shfl_xor(sk, 16);
+        sk += __shfl_xor(sk, 32);
+        const float rq = rsqrtf(sq + ch.pro.norm_eps), rk = rsqrtf(sk + ch.pro.norm_eps);
+#pragma unroll
+        for (int n = 0; n < NCH; ++n) {
+            qv[n] *= rq;
+            kv[n] *= rk;
+            bv[n] = sigmoid_f(bv[n]);
+            lv[n] = -ch.pro.decay_scale * softplus_f(lv[n]);
+        }
     }
     if (!ch.valid) {
 #pragma unroll

@@ -22,6 +22,10 @@ drawn once per (batch, token, head), same distribution, and has shape [B, T, H] 
 variants of the ablation in the forum summary on zhichai.net, section "Ablation: the erase gate
 matters more", and Gated DeltaNet's scalar decay).
 
+Pre-activations (``raw=True``, for the fused prologue): the same draws without their
+activations -- q, k ~ N(0, 1) unnormalised, a ~ N(0, 1) in the log alpha slot (fp32), b, w ~ N(0, 1)
+-- which the prologue maps to the recipe above (q/|q|, -c softplus(a), sigmoid(b), sigmoid(w)).
+
 Variants (tied-gate reductions):
   * ``"kda"``: beta = sigmoid(N(0,1)) per (batch, token, head), b = w = beta broadcast;
   * ``"gdn"``: as ``"kda"`` plus one log alpha per (batch, token, head) broadcast over channels;
@@ -58,7 +62,7 @@ def _normal(shape, gen, device):
 
 
 def layer_inputs(B, T, H, dk, dv, dtype="bf16", seed=0, variant="gdr2", s0_std=0.0,
-                 grads=True, dST=False, device="cpu", decay_scale=0.1, scalar=""):
+                 grads=True, dST=False, device="cpu", decay_scale=0.1, scalar="", raw=False):
     """Draw one batch of layer inputs.  Returns a dict of tensors on ``device``:
     q, k, b: [B,T,H,dk] (dtype); v, w, dO: [B,T,H,dv] (dtype); log_alpha: [B,T,H,dk] fp32;
     S0: [B,H,dk,dv] fp32 or None; dST: [B,H,dk,dv] fp32 or None."""
@@ -66,11 +70,19 @@ def layer_inputs(B, T, H, dk, dv, dtype="bf16", seed=0, variant="gdr2", s0_std=0
     g = torch.Generator(device=device)
     g.manual_seed(int(seed))
     q = _normal((B, T, H, dk), g, device)
-    q = q / q.norm(dim=-1, keepdim=True).clamp_min(1e-6)
+    if not raw:
+        q = q / q.norm(dim=-1, keepdim=True).clamp_min(1e-6)
     k = _normal((B, T, H, dk), g, device)
-    k = k / k.norm(dim=-1, keepdim=True).clamp_min(1e-6)
+    if not raw:
+        k = k / k.norm(dim=-1, keepdim=True).clamp_min(1e-6)
     v = _normal((B, T, H, dv), g, device)
-    if variant == "gdn":
+    if raw:
+        if variant != "gdr2":
+            raise ValueError("raw inputs are drawn for the plain recipe only")
+        la = _normal((B, T, H) if "a" in scalar else (B, T, H, dk), g, device)
+        b = _normal((B, T, H) if "b" in scalar else (B, T, H, dk), g, device).to(dt)
+        w = _normal((B, T, H) if "w" in scalar else (B, T, H, dv), g, device).to(dt)
+    elif variant == "gdn":
         la = -torch.nn.functional.softplus(_normal((B, T, H, 1), g, device)) * decay_scale
         la = la.expand(B, T, H, dk).contiguous()
     elif variant == "la":
@@ -79,7 +91,9 @@ def layer_inputs(B, T, H, dk, dv, dtype="bf16", seed=0, variant="gdr2", s0_std=0
         la = -torch.nn.functional.softplus(_normal((B, T, H), g, device)) * decay_scale
     else:
         la = -torch.nn.functional.softplus(_normal((B, T, H, dk), g, device)) * decay_scale
-    if variant in ("kda", "gdn"):
+    if raw:
+        pass
+    elif variant in ("kda", "gdn"):
         beta = torch.sigmoid(_normal((B, T, H, 1), g, device)).to(dt)
         b = beta.expand(B, T, H, dk).contiguous()
         w = beta.expand(B, T, H, dv).contiguous()
@@ -108,12 +122,13 @@ def config_inputs(name, device="cpu", **override):
 
 
 def decode_inputs(step, N=DECODE["N"], H=DECODE["H"], dk=DECODE["dk"], dv=DECODE["dv"],
-                  dtype=DECODE["dtype"], seed_base=DECODE["seed_base"], device="cpu", scalar=""):
+                  dtype=DECODE["dtype"], seed_base=DECODE["seed_base"], device="cpu", scalar="",
+                  raw=False):
     """Per-step decode token inputs (one token for each of N sequences x H heads), same recipe as
     the layer inputs, seeded with seed_base + step.  q, k, b, log_alpha: [N,H,dk]; v, w: [N,H,dv]
     (a scalar gate: [N,H])."""
     x = layer_inputs(N, 1, H, dk, dv, dtype=dtype, seed=seed_base + step, grads=False,
-                     device=device, scalar=scalar)
+                     device=device, scalar=scalar, raw=raw)
     return {n: x[n][:, 0].contiguous() for n in ("q", "k", "v", "log_alpha", "b", "w")}
 
 

@@ -79,6 +79,22 @@ typedef enum gdr2_gates {
     GDR2_DECAY_SCALAR = 4
 } gdr2_gates;
 
+/*
+ * Fused prologue for the *_ex entry points (NULL = off).  With it, q, k, log_alpha, b and w are
+ * the pre-activations of the block's branches and the library applies, inside its kernels, what
+ * the ainews.random.gg article on Gated DeltaNet-2 (section "Block design and hybrid model", and
+ * "Gated Delta Rule-2: two gates instead of one" for the sigmoid gates) puts between the
+ * projections and the mixer:
+ *     q <- q / sqrt(sum_i q_i^2 + norm_eps),   k <- k / sqrt(sum_i k_i^2 + norm_eps)
+ *     b <- sigmoid(b),   w <- sigmoid(w),   log_alpha <- -decay_scale * softplus(log_alpha)
+ * and the backward returns dq, dk, dlog_alpha, db and dw with respect to those pre-activations
+ * (v and dv are unchanged).  Both parameters must be > 0 and finite (else GDR2_E_VALUE).
+ */
+typedef struct gdr2_prologue {
+    float decay_scale;
+    float norm_eps;
+} gdr2_prologue;
+
 /* Bytes of one element of `dtype` (4 or 2), 0 for an unknown dtype. */
 size_t gdr2_dtype_size(gdr2_dtype dtype);
 
@@ -190,17 +206,21 @@ gdr2_status gdr2_decode_step(int64_t N, int64_t H, int64_t dk, int64_t dv, gdr2_
 
 /*
  * The same entry points with the gate shapes of `gates` (a gdr2_gates bit mask; any other bit
- * returns GDR2_E_UNSUPPORTED).  Every argument means what it means in the plain entry point,
- * except that b / w / log_alpha and their gradients db / dw / dlog_alpha have the [B][T][H]
- * ([N][H] for decode) shape when their bit is set.  With gates = 0 each equals the plain call.
+ * returns GDR2_E_UNSUPPORTED) and the optional fused prologue `pro` (NULL = off).  Every argument
+ * means what it means in the plain entry point, except that b / w / log_alpha and their gradients
+ * db / dw / dlog_alpha have the [B][T][H] ([N][H] for decode) shape when their bit is set, and
+ * that with `pro` the inputs and their gradients are pre-activations.  With gates = 0 and
+ * pro = NULL each equals the plain call.
  */
 gdr2_status gdr2_fwd_chunked_ex(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
-                                gdr2_dtype dtype, unsigned gates, const void* q, const void* k,
+                                gdr2_dtype dtype, unsigned gates, const gdr2_prologue* pro,
+                                const void* q, const void* k,
                                 const void* v, const float* log_alpha, const void* b,
                                 const void* w, const float* S0, void* o, float* S_T,
                                 void* workspace, size_t workspace_bytes, void* stream);
 gdr2_status gdr2_bwd_chunked_ex(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
-                                gdr2_dtype dtype, unsigned gates, const void* q, const void* k,
+                                gdr2_dtype dtype, unsigned gates, const gdr2_prologue* pro,
+                                const void* q, const void* k,
                                 const void* v, const float* log_alpha, const void* b,
                                 const void* w, const void* fwd_workspace,
                                 size_t fwd_workspace_bytes, const void* dO, const float* dS_T,
@@ -208,19 +228,22 @@ gdr2_status gdr2_bwd_chunked_ex(int64_t B, int64_t T, int64_t H, int64_t dk, int
                                 void* dw, float* dS0, void* workspace, size_t workspace_bytes,
                                 void* stream);
 gdr2_status gdr2_fwd_factors_ex(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
-                                gdr2_dtype dtype, unsigned gates, const void* q, const void* k,
+                                gdr2_dtype dtype, unsigned gates, const gdr2_prologue* pro,
+                                const void* q, const void* k,
                                 const void* v, const float* log_alpha, const void* b,
                                 const void* w, void* workspace, size_t workspace_bytes,
                                 void* stream);
 gdr2_status gdr2_bwd_grads_ex(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
-                              gdr2_dtype dtype, unsigned gates, const void* q, const void* k,
+                              gdr2_dtype dtype, unsigned gates, const gdr2_prologue* pro,
+                              const void* q, const void* k,
                               const void* v, const float* log_alpha, const void* b, const void* w,
                               const void* fwd_workspace, size_t fwd_workspace_bytes,
                               const void* dO, void* dq, void* dk_, void* dv_, float* dlog_alpha,
                               void* db, void* dw, const void* workspace, size_t workspace_bytes,
                               void* stream);
 gdr2_status gdr2_decode_step_ex(int64_t N, int64_t H, int64_t dk, int64_t dv, gdr2_dtype dtype,
-                                unsigned gates, const void* q, const void* k, const void* v,
+                                unsigned gates, const gdr2_prologue* pro, const void* q,
+                                const void* k, const void* v,
                                 const float* log_alpha, const void* b, const void* w,
                                 const float* S_in, float* S_out, void* o, void* stream);
 

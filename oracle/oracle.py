@@ -15,7 +15,11 @@ What lives here:
   * ``out_gate_forward`` / ``out_gate_backward``: the block's output epilogue (RMS normalisation
     of each head's output over its d_v channels, a per-channel weight, a SiLU output gate) and its
     hand-derived vector-Jacobian product -- ainews.random.gg article, section "Block design and
-    hybrid model".
+    hybrid model";
+  * ``prologue_forward`` / ``prologue_backward``: the transforms between the block's projections and
+    the mixer (L2 normalisation of q and k, sigmoid erase and write gates, a decay log alpha =
+    -c * softplus(a)) and their chain rule -- same article, sections "Block design and hybrid
+    model" and "Gated Delta Rule-2: two gates instead of one".
 
 Citations (page title, section):
   * update rule and the KDA / Gated DeltaNet reductions -- forum summary "Gated DeltaNet-2:
@@ -242,3 +246,40 @@ def out_gate_backward(o, g, weight, eps, dy):
     dg = dy * o * r * weight * (s + g * s * (1.0 - s))
     dweight = (dy * o * r * (g * s)).reshape(-1, o.shape[-1]).sum(axis=0)
     return {"do": do, "dg": dg, "dweight": dweight}
+
+
+def _softplus(x):
+    return np.logaddexp(0.0, x)
+
+
+def _sigmoid(x):
+    return 1.0 / (1.0 + np.exp(-x))
+
+
+def prologue_forward(q, k, a, b, w, decay_scale, norm_eps):
+    """Pre-activations -> the mixer's inputs (elementwise on gates of any shape):
+        q_hat = q / sqrt(sum_i q_i^2 + eps)   (and likewise k, over the last axis)
+        log_alpha = -decay_scale * softplus(a),   b = sigmoid(b),   w = sigmoid(w)
+    Returns dict q, k, log_alpha, b, w (float64)."""
+    q, k, a, b, w = map(_f64, (q, k, a, b, w))
+    nq = 1.0 / np.sqrt(np.sum(q * q, axis=-1, keepdims=True) + norm_eps)
+    nk = 1.0 / np.sqrt(np.sum(k * k, axis=-1, keepdims=True) + norm_eps)
+    return {"q": q * nq, "k": k * nk, "log_alpha": -decay_scale * _softplus(a),
+            "b": _sigmoid(b), "w": _sigmoid(w)}
+
+
+def prologue_backward(q, k, a, b, w, decay_scale, norm_eps, g):
+    """Chain rule through prologue_forward: ``g`` holds the gradients with respect to its outputs
+    (dq, dk, dlog_alpha, db, dw); returns them with respect to the pre-activations.
+        n = (sum q^2 + eps)^(-1/2):  d(q n)/dq applied to g = n g - n^3 q (q . g)
+        d softplus(a)/da = sigmoid(a),   d sigmoid(x)/dx = s (1 - s)"""
+    q, k, a, b, w = map(_f64, (q, k, a, b, w))
+
+    def l2(x, gx):
+        n = 1.0 / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + norm_eps)
+        return n * gx - n ** 3 * x * np.sum(x * gx, axis=-1, keepdims=True)
+
+    sb, sw = _sigmoid(b), _sigmoid(w)
+    return {"dq": l2(q, _f64(g["dq"])), "dk": l2(k, _f64(g["dk"])),
+            "dlog_alpha": -decay_scale * _sigmoid(a) * _f64(g["dlog_alpha"]),
+            "db": sb * (1.0 - sb) * _f64(g["db"]), "dw": sw * (1.0 - sw) * _f64(g["dw"])}

@@ -128,7 +128,7 @@ def test_gate_shape_entry_points_validate():
 
     def fwd(gates, b=0x18000, o=0x90000):
         ins = [P(0x10000), P(0x20000), P(0x30000), P(0x40000), P(b), P(0x60000)]
-        return lib.gdr2_fwd_chunked_ex(B, T, H, dk, dv, 1, gates, *ins, NULL, P(o), NULL,
+        return lib.gdr2_fwd_chunked_ex(B, T, H, dk, dv, 1, gates, NULL, *ins, NULL, P(o), NULL,
                                        P(0x200000), 1 << 30, NULL)
     assert fwd(8) == E_UNSUP
     assert fwd(1 << 31) == E_UNSUP
@@ -138,8 +138,36 @@ def test_gate_shape_entry_points_validate():
     assert fwd(1, b=0x18000, o=0x18000) == E_ALIAS
     # decode with every gate scalar: rejects bad bits, accepts the sizes
     ins = [P(0x10000 + i * 0x1000) for i in range(6)]
-    assert lib.gdr2_decode_step_ex(2, 2, 64, 64, 1, 16, *ins, NULL, P(0x100000), P(0x200000), NULL) == E_UNSUP
-    assert lib.gdr2_decode_step_ex(2, 2, 64, 64, 1, 7, *ins, NULL, P(0x10008), P(0x200000), NULL) == E_ALIGN
+    assert lib.gdr2_decode_step_ex(2, 2, 64, 64, 1, 16, NULL, *ins, NULL, P(0x100000), P(0x200000), NULL) == E_UNSUP
+    assert lib.gdr2_decode_step_ex(2, 2, 64, 64, 1, 7, NULL, *ins, NULL, P(0x10008), P(0x200000), NULL) == E_ALIGN
+
+
+def test_prologue_parameters_validated_before_launch():
+    """A fused-prologue parameter block with a non-positive or non-finite member is rejected with
+    GDR2_E_VALUE by every *_ex entry point (otherwise valid calls, so the prologue check is what
+    stops them; nothing is launched)."""
+    from gated_delta_rule_gdr_amd import Prologue
+    lib = load_library()
+    P = lambda a: _fake(a)
+    B, T, H, dk, dv = 1, 8, 1, 64, 64
+    ins = [P(0x10000 + i * 0x1000) for i in range(6)]
+    bad = [Prologue(0.0, 1e-6), Prologue(-1.0, 1e-6), Prologue(1.0, 0.0), Prologue(1.0, -1.0),
+           Prologue(float("nan"), 1e-6), Prologue(1.0, float("inf"))]
+    for pro in bad:
+        r = ctypes.byref(pro)
+        assert lib.gdr2_fwd_chunked_ex(B, T, H, dk, dv, 1, 0, r, *ins, NULL, P(0x90000), NULL,
+                                       P(0x200000), 1 << 30, NULL) == 9
+        assert lib.gdr2_fwd_factors_ex(B, T, H, dk, dv, 1, 0, r, *ins, P(0x200000), 1 << 30,
+                                       NULL) == 9
+        assert lib.gdr2_bwd_grads_ex(B, T, H, dk, dv, 1, 0, r, *ins, P(0x200000), 1 << 30,
+                                     P(0x300000), *[P(0x400000 + i * 0x1000) for i in range(6)],
+                                     P(0x500000), 1 << 30, NULL) == 9
+        assert lib.gdr2_bwd_chunked_ex(B, T, H, dk, dv, 1, 0, r, *ins, P(0x200000), 1 << 30,
+                                       P(0x300000), NULL,
+                                       *[P(0x400000 + i * 0x1000) for i in range(6)], NULL,
+                                       P(0x500000), 1 << 30, NULL) == 9
+        assert lib.gdr2_decode_step_ex(2, 2, 64, 64, 1, 0, r, *ins, NULL, P(0x100000),
+                                       P(0x200000), NULL) == 9
 
 
 def test_out_gate_rejects_before_launch():

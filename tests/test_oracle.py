@@ -355,3 +355,76 @@ def test_out_gate_backward_finite_differences():
             num[idx] = (L(*args_p) - L(*args_m)) / (2 * h)
         err = np.max(np.abs(num - gr[name])) / np.max(np.abs(num))
         assert err < 1e-7, (name, err)
+
+
+# ---- fused prologue (L2-normalised q, k; sigmoid gates; softplus decay)
+def test_prologue_special_values():
+    """Closed forms: softplus(0) = ln 2, softplus(ln(e - 1)) = 1, softplus(a) -> a for large a;
+    sigmoid(0) = 1/2, sigmoid(ln 3) = 3/4; (3, 4) normalises to (3, 4) / sqrt(25 + eps); a
+    normalised row has unit norm as eps -> 0 and does not change when the row is scaled."""
+    c, eps = 0.7, 1e-3
+    a = np.array([0.0, np.log(np.e - 1.0), 60.0])
+    q = np.array([[3.0, 4.0]])
+    p = orc.prologue_forward(q, q, a, np.array([0.0, np.log(3.0)]), np.array([0.0]), c, eps)
+    np.testing.assert_allclose(p["log_alpha"], [-c * np.log(2.0), -c, -c * 60.0], rtol=1e-12)
+    np.testing.assert_allclose(p["b"], [0.5, 0.75], rtol=1e-12)
+    np.testing.assert_allclose(p["w"], [0.5], rtol=1e-12)
+    np.testing.assert_allclose(p["q"], [[3.0 / np.sqrt(25 + eps), 4.0 / np.sqrt(25 + eps)]],
+                               rtol=1e-12)
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((3, 5, 16))
+    z = np.zeros(1)
+    p1 = orc.prologue_forward(x, x, z, z, z, 1.0, 1e-300)
+    np.testing.assert_allclose(np.linalg.norm(p1["k"], axis=-1), 1.0, rtol=1e-12)
+    p2 = orc.prologue_forward(x * 9.0, x, z, z, z, 1.0, 1e-300)
+    np.testing.assert_allclose(p2["q"], p1["q"], rtol=1e-12)
+
+
+@pytest.mark.parametrize("scalar", [False, True])
+def test_prologue_backward_finite_differences(scalar):
+    """The layer fed through the prologue: central differences of <o, dO> + <S_T, dS_T> with
+    respect to every pre-activation, against prologue_backward(backward(prologue_forward(.)));
+    ``scalar`` uses one gate value per (token, head), broadcast over the channels."""
+    B, T, H, dk, dv = 1, 6, 2, 3, 2
+    c, eps = 0.8, 1e-2
+    r = rng0(310 + scalar)
+    raw = {"q": r.standard_normal((B, T, H, dk)), "k": r.standard_normal((B, T, H, dk)),
+           "v": r.standard_normal((B, T, H, dv))}
+    gshape = (B, T, H) if scalar else None
+    raw["a"] = r.standard_normal(gshape or (B, T, H, dk))
+    raw["b"] = r.standard_normal(gshape or (B, T, H, dk))
+    raw["w"] = r.standard_normal(gshape or (B, T, H, dv))
+    S0 = r.standard_normal((B, H, dk, dv)) * 0.3
+    dO = r.standard_normal((B, T, H, dv))
+    dST = r.standard_normal((B, H, dk, dv))
+
+    def widen(x, d):
+        return np.repeat(x[..., None], d, axis=-1) if scalar else x
+
+    def post(x):
+        p = orc.prologue_forward(x["q"], x["k"], x["a"], x["b"], x["w"], c, eps)
+        return p["q"], p["k"], widen(p["log_alpha"], dk), widen(p["b"], dk), widen(p["w"], dv)
+
+    def L(x):
+        q, k, la, b, w = post(x)
+        o, ST = orc.forward(q, k, x["v"], la, b, w, S0)
+        return float(np.sum(o * dO) + np.sum(ST * dST))
+
+    q, k, la, b, w = post(raw)
+    g = orc.backward(q, k, raw["v"], la, b, w, dO, S0=S0, dST=dST)
+    if scalar:
+        g = dict(g, dlog_alpha=g["dlog_alpha"].sum(-1), db=g["db"].sum(-1), dw=g["dw"].sum(-1))
+    gr = orc.prologue_backward(raw["q"], raw["k"], raw["a"], raw["b"], raw["w"], c, eps, g)
+    gr["dv"] = g["dv"]
+    h = 1e-6
+    for n, gn in (("q", "dq"), ("k", "dk"), ("v", "dv"), ("a", "dlog_alpha"), ("b", "db"),
+                  ("w", "dw")):
+        num = np.zeros_like(raw[n])
+        for idx in np.ndindex(raw[n].shape):
+            xp = {m: t.copy() for m, t in raw.items()}
+            xm = {m: t.copy() for m, t in raw.items()}
+            xp[n][idx] += h
+            xm[n][idx] -= h
+            num[idx] = (L(xp) - L(xm)) / (2 * h)
+        err = np.max(np.abs(num - gr[gn])) / max(1.0, np.max(np.abs(num)))
+        assert err < 1e-7, (n, err)
