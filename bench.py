@@ -146,8 +146,11 @@ def bench_gate_variants(torch, g2, steps):
         ms = e0.elapsed_time(e1) / steps
         # algorithmic bytes per head-token: a scalar bf16 gate moves 2 B instead of 2 d, a scalar
         # decay 4 B instead of 4 d (read in both passes; its gradient written once)
-        fwd = 16 * DK - 4 * DK + 4 - (4 * DK - 4 if "a" in scalar else 0)
-        bwd = 30 * DK - 8 * DK + 8 - (8 * DK - 8 if "a" in scalar else 0)
+        fwd, bwd = 16 * DK, 30 * DK
+        for gate in scalar:
+            wide = 2 if gate == "a" else 1
+            fwd -= wide * (2 * DK - 2)
+            bwd -= wide * (4 * DK - 4)
         out[name] = {"ms_per_step": round(ms, 4),
                                    "Mtokens_per_s": round(B * T / ms / 1e3, 3),
                                    "alg_bytes_per_head_token": fwd + bwd,

@@ -295,8 +295,13 @@ template <> struct FFrag<float> {
 };
 
 // Activations of the fused prologue.
-__device__ __forceinline__ float sigmoid_f(float x) { return 1.f / (1.f + __expf(-x)); }
-__device__ __forceinline__ float softplus_f(float x) { return x > 20.f ? x : __logf(1.f + __expf(x)); }
+// sigmoid with the hardware reciprocal (v_rcp_f32, 1 ulp) instead of a correctly rounded divide
+__device__ __forceinline__ float sigmoid_f(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
+// softplus(x) = ln(1 + e^x) with the hardware log2 (v_log_f32); its argument is >= 1, so the
+// denormal handling of a full logf is not needed
+__device__ __forceinline__ float softplus_f(float x) {
+    return x > 20.f ? x : 0.69314718f * __builtin_amdgcn_logf(1.f + __expf(x));
+}
 
 // Inclusive suffix sum over the 16 lanes of each DPP row: lane i gets the sum of lanes i..15.
 __device__ __forceinline__ float row_rscan16(float x) {

@@ -57,7 +57,7 @@ __global__ __launch_bounds__(kThreads) void gdr2_epi_fwd_kernel(EpiParams p) {
         const float rs = rsqrtf(ss / DV + p.eps);
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
-            const float s = 1.f / (1.f + __expf(-gv[c]));
+            const float s = sigmoid_f(gv[c]);
             y[base + c] = from_f<OT>(ov[c] * rs * wt[c] * gv[c] * s);
         }
     }
@@ -99,7 +99,7 @@ __global__ __launch_bounds__(kThreads) void gdr2_epi_bwd_kernel(EpiParams p) {
         float a[CPL], ao = 0.f;
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
-            const float s = 1.f / (1.f + __expf(-gv[c]));
+            const float s = sigmoid_f(gv[c]);
             const float sl = gv[c] * s;
             a[c] = dv_[c] * wt[c] * sl;
             ao += a[c] * ov[c];
