@@ -528,6 +528,7 @@ struct alignas(16) BgSmem {
     float gRt[4][DK];
     float hRt[4][DK];
     float r6[DK];
+    float r6x[4][DK];  // R6 partials: [lane group l / 16][channel]
     float btot[4][DK];
     float ktot[4][DK];
     float gred[2][kChunk][3];  // per-token partial sums of db, dw, dlog alpha (scalar gates)
@@ -546,7 +547,8 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
     constexpr int NTV = Cf::NTV, TVEC = Cf::TVEC, NT = kBgThreads;
     __shared__ BgSmem<OT, DK, DV, DVH> sm;
 
-    const int tid = threadIdx.x, w = wave_id(), R = w & 3, half = w >> 2;
+    // wave index made wave-uniform, so that branches on R and half are scalar branches
+    const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(wave_id()), R = w & 3, half = w >> 2;
     const int l = lane_id(), rl = l & 15, g = l >> 4;
     const int NC = p.NC;
     const int chain = blockIdx.x / NC, c = blockIdx.x % NC;
@@ -685,7 +687,10 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
 #pragma unroll
         for (int ib = 0; ib < NIBH; ++ib) *(f32x4*)(&sm.tot[R][16 * (ibase + ib) + 4 * g]) = sc[ib];
     }
-    if (tid < DK) sm.r6[tid] = 0.f;
+    if (tid < DK) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sm.r6x[q][tid] = 0.f;
+    }
     lds_barrier();
     for (int chn = tid; chn < DK; chn += NT) {
         float refs[4], run = 0.f;
@@ -808,6 +813,12 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
                 MM::mma(A1[ib], aS, bO);
                 MM::mma(A2[ib], aS, bX);
                 MM::mma(A3[ib], adS, bD);
+                if (R == 0) {  // R6 partial: channel i0 + l%16, the fragment's k (= value columns)
+                    float acc = 0.f;
+#pragma unroll
+                    for (int e = 0; e < FR::N; ++e) acc += FR::at(aS, e) * FR::at(adS, e);
+                    sm.r6x[g][i0 + rl] += acc;
+                }
             }
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
@@ -818,13 +829,6 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
                     MM::mma(R5[u], bX, bDs);
                 }
             }
-        }
-        if (tid < DK) {
-            float acc = 0.f;
-#pragma unroll 8
-            for (int jj = 0; jj < DVH; ++jj)
-                acc += to_f(sm.u.j.dSt[jj * PK + tid]) * to_f(sm.u.j.St[jj * PK + tid]);
-            sm.r6[tid] += acc;
         }
         lds_barrier();
     }
@@ -898,6 +902,7 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
         store_acc_T(sm.u.g.dAT, PC, 16 * S, 16 * R, am);
     }
     lds_barrier();
+    if (tid < DK) sm.r6[tid] = (sm.r6x[0][tid] + sm.r6x[1][tid]) + (sm.r6x[2][tid] + sm.r6x[3][tid]);
 
     // ---- A1 <- exp(ref_R) R1 + dP Kbar,  A2 <- -exp(ref_R) R2 + dA Kbar,  A4 <- dP^T Qbar + dA^T Ebar
 #pragma unroll
@@ -1031,16 +1036,12 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
 #pragma unroll
         for (int ib = 0; ib < NIBH; ++ib) {
             const int i0 = 16 * (ibase + ib) + 4 * g;
-            f32x4 dl = dG[ib];
+            // + dgamma . gamma, the key-side block totals and the erase totals of the later blocks
+            f32x4 dl = dG[ib] + *(const f32x4*)&sm.r6[i0] * *(const f32x4*)&sm.hRt[0][i0];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                float add = sm.r6[i0 + e] * sm.hRt[0][i0 + e];  // dgamma . gamma
-#pragma unroll
-                for (int Rp = 0; Rp < 4; ++Rp) {
-                    add += sm.ktot[Rp][i0 + e];
-                    if (Rp > R) add += sm.btot[Rp][i0 + e];
-                }
-                dl[e] += add;
+            for (int Rp = 0; Rp < 4; ++Rp) {
+                dl += *(const f32x4*)&sm.ktot[Rp][i0];
+                if (Rp > R) dl += *(const f32x4*)&sm.btot[Rp][i0];
             }
             if (PRO && !a_sc) {  // log alpha = -c softplus(a): d a = d log alpha . (-c sigmoid(a))
                 const f32x4 a4 = *(const f32x4*)(p.la + orow + i0);

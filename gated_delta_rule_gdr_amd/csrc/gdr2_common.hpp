@@ -188,6 +188,8 @@ __device__ __forceinline__ bf16x4 ds_read_tr4(const bf16* p) {
 template <typename OT> struct Frag;
 template <> struct Frag<bf16> {
     typedef bf16x8 t;
+    static constexpr int N = 8;
+    static __device__ __forceinline__ float at(const t& x, int e) { return (float)x[e]; }
     static __device__ __forceinline__ t kc(const bf16* X, int pitch, int i0, int k0) {
         const int l = lane_id();
         return *(const bf16x8*)(X + (i0 + (l & 15)) * pitch + k0 + 8 * (l >> 4));
@@ -223,6 +225,8 @@ template <> struct Frag<bf16> {
 };
 template <> struct Frag<float> {
     typedef float t;
+    static constexpr int N = 1;
+    static __device__ __forceinline__ float at(const t& x, int) { return x; }
     static __device__ __forceinline__ t kc(const float* X, int pitch, int i0, int k0) {
         const int l = lane_id();
         return X[(i0 + (l & 15)) * pitch + k0 + (l >> 4)];
