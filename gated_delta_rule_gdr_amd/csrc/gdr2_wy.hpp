@@ -60,7 +60,7 @@ __device__ __forceinline__ float* tblk(float* Af, int R, int S) {
 // T_RS = -T_RR sum_{S <= K < R} A_RK T_KS level by level with fp32 MFMA.  T is also written, in
 // operand precision, to Tm (row-major, zero above the diagonal).  Ends with a barrier.
 template <typename OT, int PAF, int PC>
-__device__ void solve_unit_lower_64(float* Af, float (*Mf)[16 * 17], OT* Tm) {
+__device__ __forceinline__ void solve_unit_lower_64(float* Af, float (*Mf)[16 * 17], OT* Tm) {
     const int w = wave_id(), l = lane_id();
     for (int x = threadIdx.x; x < 6 * 256; x += kThreads) {
         const int blk = x >> 8, e = x & 255;
@@ -212,7 +212,7 @@ struct WyChunk {
 // gate branches, so its loads issue back to back; the others read the gate bits (and apply the
 // fused prologue) at run time.
 template <typename OT, int DK, int DV, int MODE>
-__device__ void wy_factors(WySmem<OT, DK, DV>& sm, const WyChunk<OT, DK, DV>& ch, const WyBufs& wy) {
+__device__ __forceinline__ void wy_factors(WySmem<OT, DK, DV>& sm, const WyChunk<OT, DK, DV>& ch, const WyBufs& wy) {
     using Cf = WyCfg<OT, DK, DV>;
     using MM = Mfma<OT>;
     using FR = Frag<OT>;
