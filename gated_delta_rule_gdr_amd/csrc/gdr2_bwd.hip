@@ -496,6 +496,7 @@ struct BgCfg {
     static constexpr int TVEC = (NTV + kBgThreads - 1) / kBgThreads;
     static_assert((C * DK / VEC) % kBgThreads == 0, "Y / Ktilde staging");
     static constexpr bool YK_LDS = ES == 2;
+    static constexpr int NBUF = ES == 2 ? 2 : 1;  // value-column block buffers (fp32: LDS-bound)
     static_assert(NJH == 2, "one 16-column block per wave half");
 };
 
@@ -508,9 +509,9 @@ struct alignas(16) BgSmem {
             OT Kt[Cf::YK_LDS ? kChunk * Cf::PK : 1];  // Ktilde  [r][i]
             OT Tt[kChunk * Cf::PC];    // T                   [r][s]
             OT Pt[kChunk * Cf::PC];    // P                   [r][s]
-            OT St[DVH * Cf::PK];       // S^T block           [j][i]
-            OT dSt[DVH * Cf::PK];      // dS'^T block         [j][i]
-            OT dOt[kChunk * Cf::PH];   // dO block            [r][j]
+            OT St[Cf::NBUF][DVH * Cf::PK];      // S^T block   [j][i]  (16-bit: two buffers, the
+            OT dSt[Cf::NBUF][DVH * Cf::PK];     // dS'^T block [j][i]   next block is staged
+            OT dOt[Cf::NBUF][kChunk * Cf::PH];  // dO block    [r][j]   while this one is reduced)
             OT DlT[DVH * Cf::PC];      // Delta^T             [j][r]
             OT dDT[DVH * Cf::PC];      // dDelta^T            [j][r]
             OT dXt[kChunk * Cf::PH];   // dX block            [r][j]
@@ -569,21 +570,19 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
     constexpr bool GS = MODE != kModePlain, PRO = MODE == kModePrologue;
     const bool b_sc = GS && (p.gates & kEraseScalar), w_sc = GS && (p.gates & kWriteScalar);
     const bool a_sc = GS && (p.gates & kDecayScalar);
-    f32x4 sc[NIBH];  // log alpha, then G_r - ref_R
-    if (a_sc) {
-        const float x = p.la[row];
+    // log alpha, then G_r - ref_R: not needed before the Gram phase, so it is loaded with the last
+    // value-column block (off the start-up path)
+    f32x4 sc[NIBH];
+    auto load_la = [&]() __attribute__((always_inline)) {
+        if (a_sc) {
+            const float x = p.la[row];
 #pragma unroll
-        for (int ib = 0; ib < NIBH; ++ib) sc[ib] = f32x4{x, x, x, x};
-    } else {
+            for (int ib = 0; ib < NIBH; ++ib) sc[ib] = f32x4{x, x, x, x};
+        } else {
 #pragma unroll
-        for (int ib = 0; ib < NIBH; ++ib) sc[ib] = *(const f32x4*)(p.la + row * DK + 16 * (ibase + ib) + 4 * g);
-    }
-    if (PRO) {  // log alpha = -decay_scale * softplus(a)
-#pragma unroll
-        for (int ib = 0; ib < NIBH; ++ib)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) sc[ib][e] = -p.pro.decay_scale * softplus_f(sc[ib][e]);
-    }
+            for (int ib = 0; ib < NIBH; ++ib) sc[ib] = *(const f32x4*)(p.la + row * DK + 16 * (ibase + ib) + 4 * g);
+        }
+    };
     // ---- the chunk's -Y and Ktilde: staged into LDS with T and P below (16-bit operands), or
     //      this wave's token block kept as fragments (fp32)
     constexpr bool YK_LDS = Cf::YK_LDS;
@@ -611,18 +610,21 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
     // ---- value-column block prefetch registers
     const OT* Sx = (const OT*)p.states + cix * DV * DK;
     const OT* dSxp = (const OT*)p.dSx + cix * DV * DK;
-    i32x4 pS[SVEC], pdS[SVEC], pO[OVEC];
-    typename RW::t pv, pw, pU;
+    // NS register sets: 16-bit operands fetch two blocks ahead (the loads take longer than one
+    // block's work), fp32 one
+    constexpr int NS = Cf::NBUF;
+    i32x4 pS[NS][SVEC], pdS[NS][SVEC], pO[NS][OVEC];
+    typename RW::t pv[NS], pw[NS], pU[NS];
     const OT* Uc = (const OT*)p.wy.U + cix * C * DV;
-    auto fetch_block = [&](int jq) __attribute__((always_inline)) {
+    auto fetch_block = [&](int jq, int st) __attribute__((always_inline)) {
         const int jb0 = jq * DVH;
 #pragma unroll
         for (int m = 0; m < SVEC; ++m) {
             const int x = tid + m * NT;
             if (NSV % NT == 0 || x < NSV) {
                 const int jj = (x * VEC) / DK, i = (x * VEC) % DK;
-                pS[m] = *(const i32x4*)(Sx + (long)(jb0 + jj) * DK + i);
-                pdS[m] = *(const i32x4*)(dSxp + (long)(jb0 + jj) * DK + i);
+                pS[st][m] = *(const i32x4*)(Sx + (long)(jb0 + jj) * DK + i);
+                pdS[st][m] = *(const i32x4*)(dSxp + (long)(jb0 + jj) * DK + i);
             }
         }
 #pragma unroll
@@ -632,19 +634,19 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
             i32x4 z = {0, 0, 0, 0};
             if ((NOV % NT == 0 || x < NOV) && (long)c * C + rr < T)
                 z = *(const i32x4*)((const OT*)p.dO + (tok0 + (long)rr * H) * DV + jb0 + jj);
-            pO[m] = z;
+            pO[st][m] = z;
         }
         // v, w of (token r, columns jb0 + 16 half + 4g .. +3) for dv, dw
         const long trow = valid ? (tok0 + (long)r * H) : row;
         const long o = trow * DV + jb0 + 16 * half + 4 * g;
-        pv = *(const typename RW::t*)((const OT*)p.v + o);
+        pv[st] = *(const typename RW::t*)((const OT*)p.v + o);
         if (w_sc) {
             const OT x = ((const OT*)p.w)[trow];
-            pw = typename RW::t{x, x, x, x};
+            pw[st] = typename RW::t{x, x, x, x};
         } else {
-            pw = *(const typename RW::t*)((const OT*)p.w + o);
+            pw[st] = *(const typename RW::t*)((const OT*)p.w + o);
         }
-        pU = *(const typename RW::t*)(Uc + ((long)(R * (DV / 16) + jb0 / 16 + half) * 64 + l) * 4);
+        pU[st] = *(const typename RW::t*)(Uc + ((long)(R * (DV / 16) + jb0 / 16 + half) * 64 + l) * 4);
     };
     i32x4 pT[TVEC], pP[TVEC];
     {
@@ -659,7 +661,8 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
             }
         }
     }
-    fetch_block(0);
+    fetch_block(0, 0);
+    if (NS == 2 && DV / DVH > 1) fetch_block(1, 1);
 #pragma unroll
     for (int m = 0; m < TVEC; ++m) {
         const int x = tid + m * NT;
@@ -678,34 +681,9 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
             *(i32x4*)(sm.u.j.Kt + o) = pK[m];
         }
     }
-    // ---- in-block cumsum of log alpha (DPP over the 16 tokens), block totals
-#pragma unroll
-    for (int ib = 0; ib < NIBH; ++ib)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sc[ib][e] = row_scan16(valid ? sc[ib][e] : 0.f);
-    if (rl == 15) {
-#pragma unroll
-        for (int ib = 0; ib < NIBH; ++ib) *(f32x4*)(&sm.tot[R][16 * (ibase + ib) + 4 * g]) = sc[ib];
-    }
     if (tid < DK) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) sm.r6x[q][tid] = 0.f;
-    }
-    lds_barrier();
-    for (int chn = tid; chn < DK; chn += NT) {
-        float refs[4], run = 0.f;
-#pragma unroll
-        for (int Rp = 0; Rp < 4; ++Rp) {
-            refs[Rp] = run;
-            run += sm.tot[Rp][chn];
-        }
-#pragma unroll
-        for (int Rp = 0; Rp < 4; ++Rp) {
-            sm.gRt[Rp][chn] = __expf(refs[Rp]);
-            sm.hRt[Rp][chn] = __expf(run - refs[Rp]);
-#pragma unroll
-            for (int S = 0; S < Rp; ++S) sm.ctab[Rp * (Rp - 1) / 2 + S][chn] = __expf(refs[Rp] - refs[S]);
-        }
     }
 
     float dw_acc = 0.f;                   // sum_j dX_j v_j of this lane's columns (scalar w)
@@ -715,28 +693,35 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
     for (int ib = 0; ib < NIBH; ++ib) A1[ib] = A2[ib] = A3[ib] = f32x4{0.f, 0.f, 0.f, 0.f};
     R4[0] = R4[1] = R5[0] = R5[1] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-#pragma unroll 1
-    for (int jq = 0; jq < DV / DVH; ++jq) {
-        const int jb0 = jq * DVH;
+    // staging of a fetched value-column block into LDS buffer b, and the next fetch (block jn, or
+    // after the last block the raw key inputs for the Gram phase and the epilogue)
+    constexpr int NJ = DV / DVH;
+    typename RW::t cv, cw, cU;
+    auto stage = [&](int b, int st) __attribute__((always_inline)) {
 #pragma unroll
         for (int m = 0; m < SVEC; ++m) {
             const int x = tid + m * NT;
             if (NSV % NT == 0 || x < NSV) {
                 const int jj = (x * VEC) / DK, i = (x * VEC) % DK;
-                *(i32x4*)(sm.u.j.St + jj * PK + i) = pS[m];
-                *(i32x4*)(sm.u.j.dSt + jj * PK + i) = pdS[m];
+                *(i32x4*)(sm.u.j.St[b] + jj * PK + i) = pS[st][m];
+                *(i32x4*)(sm.u.j.dSt[b] + jj * PK + i) = pdS[st][m];
             }
         }
 #pragma unroll
         for (int m = 0; m < OVEC; ++m) {
             const int x = tid + m * NT;
             if (NOV % NT == 0 || x < NOV)
-                *(i32x4*)(sm.u.j.dOt + ((x * VEC) / DVH) * PH + (x * VEC) % DVH) = pO[m];
+                *(i32x4*)(sm.u.j.dOt[b] + ((x * VEC) / DVH) * PH + (x * VEC) % DVH) = pO[st][m];
         }
-        const typename RW::t cv = pv, cw = pw, cU = pU;
-        if (jq + 1 < DV / DVH) {
-            fetch_block(jq + 1);
-        } else {  // raw key inputs for the Gram phase and the epilogue
+        cv = pv[st];
+        cw = pw[st];
+        cU = pU[st];
+    };
+    auto fetch_next = [&](int jn, int st) __attribute__((always_inline)) {
+        if (jn < NJ) {
+            fetch_block(jn, st);
+        } else if (jn == NJ) {
+            load_la();
 #pragma unroll
             for (int ib = 0; ib < NIBH; ++ib) {
                 const int i0 = 16 * (ibase + ib) + 4 * g;
@@ -750,7 +735,20 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
                 }
             }
         }
-        lds_barrier();
+    };
+    stage(0, 0);
+    fetch_next(NS, 0);
+    lds_barrier();
+
+    constexpr int JUNROLL = NS == 2 ? NJ : 1;  // two register sets: unrolled, set indices static
+    typename RW::t dvk[NS == 2 ? NJ : 1], dwk[NS == 2 ? NJ : 1];  // dv, dw of every block
+#pragma unroll JUNROLL
+    for (int jq = 0; jq < NJ; ++jq) {
+        constexpr int NBUF = Cf::NBUF;
+        const int jb0 = jq * DVH, bq = NBUF == 1 ? 0 : (jq & 1);
+        const OT* St = sm.u.j.St[bq];
+        const OT* dSt = sm.u.j.dSt[bq];
+        const OT* dOt = sm.u.j.dOt[bq];
         // Delta = U - Y S, dDelta = Ktilde dS' + P^T dO: block (token R, columns 16 half)
         {
             const int jb = half;
@@ -766,11 +764,11 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
                     ay = Yf[ks < NKF ? ks : 0];
                     ak = Kf[ks < NKF ? ks : 0];
                 }
-                MM::mma(aD, ay, FR::kc(sm.u.j.St, PK, 16 * jb, ks * KS));
-                MM::mma(adD, ak, FR::kc(sm.u.j.dSt, PK, 16 * jb, ks * KS));
+                MM::mma(aD, ay, FR::kc(St, PK, 16 * jb, ks * KS));
+                MM::mma(adD, ak, FR::kc(dSt, PK, 16 * jb, ks * KS));
             }
             for (int k0 = kbeg; k0 < C; k0 += KS)
-                MM::mma(adD, FR::tr(sm.u.j.Pt, PC, k0, 16 * R), FR::tr(sm.u.j.dOt, PH, k0, 16 * jb));
+                MM::mma(adD, FR::tr(sm.u.j.Pt, PC, k0, 16 * R), FR::tr(dOt, PH, k0, 16 * jb));
             store_acc_T(sm.u.j.DlT, PC, 16 * jb, 16 * R, aD);
             store_acc_T(sm.u.j.dDT, PC, 16 * jb, 16 * R, adD);
         }
@@ -792,7 +790,10 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
                 }
             }
             if (w_sc) dw_acc += (dwv[0] + dwv[1]) + (dwv[2] + dwv[3]);
-            if (valid) {
+            if constexpr (NS == 2) {  // held until the loop ends: no stores between the fetches
+                dvk[jq] = RW::narrow(ax * wg);
+                dwk[jq] = RW::narrow(dwv);
+            } else if (valid) {
                 const long o = (tok0 + (long)r * H) * DV + jb0 + jc;
                 store4((OT*)p.dv + o, ax * wg);
                 if (!w_sc) store4((OT*)p.dw + o, dwv);
@@ -802,14 +803,14 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
         // reductions over this block of value columns
 #pragma unroll
         for (int k0 = 0; k0 < DVH; k0 += KS) {
-            const typename FR::t bO = FR::kc(sm.u.j.dOt, PH, 16 * R, k0);   // dO    (col r, k = j)
+            const typename FR::t bO = FR::kc(dOt, PH, 16 * R, k0);          // dO    (col r, k = j)
             const typename FR::t bX = FR::kc(sm.u.j.dXt, PH, 16 * R, k0);   // dX    (col r, k = j)
             const typename FR::t bD = FR::tr(sm.u.j.DlT, PC, k0, 16 * R);   // Delta (col r, k = j)
 #pragma unroll
             for (int ib = 0; ib < NIBH; ++ib) {
                 const int i0 = 16 * (ibase + ib);
-                const typename FR::t aS = FR::tr(sm.u.j.St, PK, k0, i0);    // S   (row i, k = j)
-                const typename FR::t adS = FR::tr(sm.u.j.dSt, PK, k0, i0);  // dS' (row i, k = j)
+                const typename FR::t aS = FR::tr(St, PK, k0, i0);    // S   (row i, k = j)
+                const typename FR::t adS = FR::tr(dSt, PK, k0, i0);  // dS' (row i, k = j)
                 MM::mma(A1[ib], aS, bO);
                 MM::mma(A2[ib], aS, bX);
                 MM::mma(A3[ib], adS, bD);
@@ -830,7 +831,57 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
                 }
             }
         }
+        // the next block into the other buffer while the slow waves finish this one (one buffer:
+        // after every wave is done with it)
+        if (jq + 1 < NJ) {
+            if constexpr (NBUF == 1) lds_barrier();
+            stage(NBUF == 1 ? 0 : (bq ^ 1), (jq + 1) % NS);
+            fetch_next(jq + 1 + NS, (jq + 1) % NS);
+        }
         lds_barrier();
+    }
+    if constexpr (NS == 2) {
+        if (valid) {
+#pragma unroll
+            for (int jq = 0; jq < NJ; ++jq) {
+                const long o = (tok0 + (long)r * H) * DV + jq * DVH + 16 * half + 4 * g;
+                *(typename RW::t*)((OT*)p.dv + o) = dvk[jq];
+                if (!w_sc) *(typename RW::t*)((OT*)p.dw + o) = dwk[jq];
+            }
+        }
+    }
+
+    // ---- in-block cumsum of log alpha (DPP over the 16 tokens), block totals, and the
+    //      per-channel tables exp(ref_R), exp(G_C - ref_R), exp(ref_R - ref_S)
+    if (PRO) {  // log alpha = -decay_scale * softplus(a)
+#pragma unroll
+        for (int ib = 0; ib < NIBH; ++ib)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sc[ib][e] = -p.pro.decay_scale * softplus_f(sc[ib][e]);
+    }
+#pragma unroll
+    for (int ib = 0; ib < NIBH; ++ib)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sc[ib][e] = row_scan16(valid ? sc[ib][e] : 0.f);
+    if (rl == 15) {
+#pragma unroll
+        for (int ib = 0; ib < NIBH; ++ib) *(f32x4*)(&sm.tot[R][16 * (ibase + ib) + 4 * g]) = sc[ib];
+    }
+    lds_barrier();
+    for (int chn = tid; chn < DK; chn += NT) {
+        float refs[4], run = 0.f;
+#pragma unroll
+        for (int Rp = 0; Rp < 4; ++Rp) {
+            refs[Rp] = run;
+            run += sm.tot[Rp][chn];
+        }
+#pragma unroll
+        for (int Rp = 0; Rp < 4; ++Rp) {
+            sm.gRt[Rp][chn] = __expf(refs[Rp]);
+            sm.hRt[Rp][chn] = __expf(run - refs[Rp]);
+#pragma unroll
+            for (int S = 0; S < Rp; ++S) sm.ctab[Rp * (Rp - 1) / 2 + S][chn] = __expf(refs[Rp] - refs[S]);
+        }
     }
 
     // ---- fused prologue: the row norms of q and k (lanes 16g + rl of both channel halves)

@@ -47,11 +47,15 @@ template <typename OT> struct Raw4;
 template <> struct Raw4<float> {
     typedef f32x4 t;
     static __device__ __forceinline__ f32x4 widen(const t& x) { return x; }
+    static __device__ __forceinline__ t narrow(const f32x4& x) { return x; }
 };
 template <> struct Raw4<bf16> {
     typedef bf16x4 t;
     static __device__ __forceinline__ f32x4 widen(const t& x) {
         return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+    }
+    static __device__ __forceinline__ t narrow(const f32x4& x) {
+        return t{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
     }
 };
 __device__ __forceinline__ void store4(bf16* p, f32x4 v) {
