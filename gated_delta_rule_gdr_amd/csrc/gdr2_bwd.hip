@@ -602,8 +602,8 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
         } else {
 #pragma unroll
             for (int ks = 0; ks < NKF; ++ks) {
-                Yf[ks] = FFrag<OT>::fkc(Yc, DK, 16 * R, ks * KS);
-                Kf[ks] = FFrag<OT>::fkc(Kc, DK, 16 * R, ks * KS);
+                Yf[ks] = FFrag<OT>::fkc(Yc, DK, 16 * R, ks * KS, l);
+                Kf[ks] = FFrag<OT>::fkc(Kc, DK, 16 * R, ks * KS, l);
             }
         }
     }
@@ -758,19 +758,19 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
             for (int ks = 0; ks < NKS; ++ks) {
                 typename FR::t ay, ak;
                 if constexpr (YK_LDS) {
-                    ay = FR::kc(sm.u.j.Yt, PK, 16 * R, ks * KS);
-                    ak = FR::kc(sm.u.j.Kt, PK, 16 * R, ks * KS);
+                    ay = FR::kc(sm.u.j.Yt, PK, 16 * R, ks * KS, l);
+                    ak = FR::kc(sm.u.j.Kt, PK, 16 * R, ks * KS, l);
                 } else {
                     ay = Yf[ks < NKF ? ks : 0];
                     ak = Kf[ks < NKF ? ks : 0];
                 }
-                MM::mma(aD, ay, FR::kc(St, PK, 16 * jb, ks * KS));
-                MM::mma(adD, ak, FR::kc(dSt, PK, 16 * jb, ks * KS));
+                MM::mma(aD, ay, FR::kc(St, PK, 16 * jb, ks * KS, l));
+                MM::mma(adD, ak, FR::kc(dSt, PK, 16 * jb, ks * KS, l));
             }
             for (int k0 = kbeg; k0 < C; k0 += KS)
-                MM::mma(adD, FR::tr(sm.u.j.Pt, PC, k0, 16 * R), FR::tr(dOt, PH, k0, 16 * jb));
-            store_acc_T(sm.u.j.DlT, PC, 16 * jb, 16 * R, aD);
-            store_acc_T(sm.u.j.dDT, PC, 16 * jb, 16 * R, adD);
+                MM::mma(adD, FR::tr(sm.u.j.Pt, PC, k0, 16 * R, l), FR::tr(dOt, PH, k0, 16 * jb, l));
+            store_acc_T(sm.u.j.DlT, PC, 16 * jb, 16 * R, aD, l);
+            store_acc_T(sm.u.j.dDT, PC, 16 * jb, 16 * R, adD, l);
         }
         lds_barrier();
         // dX^T = dDelta^T T (lane: token r, columns 16 half + 4g .. +3); dv = dX . w, dw = dX . v
@@ -778,7 +778,7 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
             const int jb = half;
             f32x4 ax = {0.f, 0.f, 0.f, 0.f};
             for (int k0 = kbeg; k0 < C; k0 += KS)
-                MM::mma(ax, FR::kc(sm.u.j.dDT, PC, 16 * jb, k0), FR::tr(sm.u.j.Tt, PC, k0, 16 * R));
+                MM::mma(ax, FR::kc(sm.u.j.dDT, PC, 16 * jb, k0, l), FR::tr(sm.u.j.Tt, PC, k0, 16 * R, l));
             const int jc = 16 * jb + 4 * g;
             store4(sm.u.j.dXt + r * PH + jc, ax);
             f32x4 wg = RW::widen(cw), dwv = ax * RW::widen(cv);
@@ -803,14 +803,14 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
         // reductions over this block of value columns
 #pragma unroll
         for (int k0 = 0; k0 < DVH; k0 += KS) {
-            const typename FR::t bO = FR::kc(dOt, PH, 16 * R, k0);          // dO    (col r, k = j)
-            const typename FR::t bX = FR::kc(sm.u.j.dXt, PH, 16 * R, k0);   // dX    (col r, k = j)
-            const typename FR::t bD = FR::tr(sm.u.j.DlT, PC, k0, 16 * R);   // Delta (col r, k = j)
+            const typename FR::t bO = FR::kc(dOt, PH, 16 * R, k0, l);          // dO    (col r, k = j)
+            const typename FR::t bX = FR::kc(sm.u.j.dXt, PH, 16 * R, k0, l);   // dX    (col r, k = j)
+            const typename FR::t bD = FR::tr(sm.u.j.DlT, PC, k0, 16 * R, l);   // Delta (col r, k = j)
 #pragma unroll
             for (int ib = 0; ib < NIBH; ++ib) {
                 const int i0 = 16 * (ibase + ib);
-                const typename FR::t aS = FR::tr(St, PK, k0, i0);    // S   (row i, k = j)
-                const typename FR::t adS = FR::tr(dSt, PK, k0, i0);  // dS' (row i, k = j)
+                const typename FR::t aS = FR::tr(St, PK, k0, i0, l);    // S   (row i, k = j)
+                const typename FR::t adS = FR::tr(dSt, PK, k0, i0, l);  // dS' (row i, k = j)
                 MM::mma(A1[ib], aS, bO);
                 MM::mma(A2[ib], aS, bX);
                 MM::mma(A3[ib], adS, bD);
@@ -825,7 +825,7 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
             for (int u = 0; u < 2; ++u) {
                 const int S = 2 * half + u;
                 if (S <= R) {
-                    const typename FR::t bDs = FR::tr(sm.u.j.DlT, PC, k0, 16 * S);  // Delta (col s, k = j)
+                    const typename FR::t bDs = FR::tr(sm.u.j.DlT, PC, k0, 16 * S, l);  // Delta (col s, k = j)
                     MM::mma(R4[u], bO, bDs);
                     MM::mma(R5[u], bX, bDs);
                 }
@@ -894,10 +894,10 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
             sq += (q4[0] * q4[0] + q4[1] * q4[1]) + (q4[2] * q4[2] + q4[3] * q4[3]);
             sk += (k4[0] * k4[0] + k4[1] * k4[1]) + (k4[2] * k4[2] + k4[3] * k4[3]);
         }
-        sq += __shfl_xor(sq, 16);
-        sq += __shfl_xor(sq, 32);
-        sk += __shfl_xor(sk, 16);
-        sk += __shfl_xor(sk, 32);
+        sq += shfl_xor_l(sq, 16, l);
+        sq += shfl_xor_l(sq, 32, l);
+        sk += shfl_xor_l(sk, 16, l);
+        sk += shfl_xor_l(sk, 32, l);
         if (g == 0) {
             sm.nrm[half][r][0] = sq;
             sm.nrm[half][r][1] = sk;
@@ -944,13 +944,13 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
         if (S <= R) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int rr = 16 * R + acc_row(e), ss = 16 * S + acc_col();
+                const int rr = 16 * R + acc_row(e, l), ss = 16 * S + acc_col(l);
                 pm[e] = ss <= rr ? R4[u][e] : 0.f;
                 am[e] = ss < rr ? -R5[u][e] : 0.f;
             }
         }
-        store_acc_T(sm.u.g.dPT, PC, 16 * S, 16 * R, pm);
-        store_acc_T(sm.u.g.dAT, PC, 16 * S, 16 * R, am);
+        store_acc_T(sm.u.g.dPT, PC, 16 * S, 16 * R, pm, l);
+        store_acc_T(sm.u.g.dAT, PC, 16 * S, 16 * R, am, l);
     }
     lds_barrier();
     if (tid < DK) sm.r6[tid] = (sm.r6x[0][tid] + sm.r6x[1][tid]) + (sm.r6x[2][tid] + sm.r6x[3][tid]);
@@ -960,19 +960,19 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
     for (int ib = 0; ib < NIBH; ++ib) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const float gr = sm.gRt[R][16 * (ibase + ib) + acc_row(e)];
+            const float gr = sm.gRt[R][16 * (ibase + ib) + acc_row(e, l)];
             A1[ib][e] *= gr;
             A2[ib][e] *= -gr;
         }
     }
     for (int k0 = 0; k0 < 16 * R + 16; k0 += KS) {
-        const typename FR::t bP = FR::tr(sm.u.g.dPT, PC, k0, 16 * R);  // dP (col r, k = s)
-        const typename FR::t bA = FR::tr(sm.u.g.dAT, PC, k0, 16 * R);  // dA (col r, k = s)
+        const typename FR::t bP = FR::tr(sm.u.g.dPT, PC, k0, 16 * R, l);  // dP (col r, k = s)
+        const typename FR::t bA = FR::tr(sm.u.g.dAT, PC, k0, 16 * R, l);  // dA (col r, k = s)
         const int Sl = (k0 + KPL * g) / 16;                             // token block of this lane's k
 #pragma unroll
         for (int ib = 0; ib < NIBH; ++ib) {
             const int i0 = 16 * (ibase + ib);
-            typename FR::t a = FR::tr(sm.u.g.Kb, PK, k0, i0);            // Kbar^T (row i, k = s)
+            typename FR::t a = FR::tr(sm.u.g.Kb, PK, k0, i0, l);            // Kbar^T (row i, k = s)
             if (Sl < R) a = FR::scale(a, sm.ctab[R * (R - 1) / 2 + Sl][i0 + rl]);
             MM::mma(A1[ib], a, bP);
             MM::mma(A2[ib], a, bA);
@@ -982,14 +982,14 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
 #pragma unroll
     for (int ib = 0; ib < NIBH; ++ib) A4[ib] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int k0 = kbeg; k0 < C; k0 += KS) {
-        const typename FR::t bP = FR::kc(sm.u.g.dPT, PC, 16 * R, k0);  // dP (col s, k = r)
-        const typename FR::t bA = FR::kc(sm.u.g.dAT, PC, 16 * R, k0);  // dA (col s, k = r)
+        const typename FR::t bP = FR::kc(sm.u.g.dPT, PC, 16 * R, k0, l);  // dP (col s, k = r)
+        const typename FR::t bA = FR::kc(sm.u.g.dAT, PC, 16 * R, k0, l);  // dA (col s, k = r)
         const int Rl = (k0 + KPL * g) / 16;
 #pragma unroll
         for (int ib = 0; ib < NIBH; ++ib) {
             const int i0 = 16 * (ibase + ib);
-            typename FR::t aq = FR::tr(sm.u.g.Qb, PK, k0, i0);           // Qbar^T (row i, k = r)
-            typename FR::t ae = FR::tr(sm.u.g.Eb, PK, k0, i0);           // Ebar^T (row i, k = r)
+            typename FR::t aq = FR::tr(sm.u.g.Qb, PK, k0, i0, l);           // Qbar^T (row i, k = r)
+            typename FR::t ae = FR::tr(sm.u.g.Eb, PK, k0, i0, l);           // Ebar^T (row i, k = r)
             if (Rl > R) {
                 const float cs = sm.ctab[Rl * (Rl - 1) / 2 + R][i0 + rl];
                 aq = FR::scale(aq, cs);
@@ -1051,20 +1051,20 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
     // scalar gates: the gradient is the sum over this token's channels (lanes 16g + rl of both
     // channel halves)
     if (b_sc || w_sc) {
-        db_acc += __shfl_xor(db_acc, 16);
-        db_acc += __shfl_xor(db_acc, 32);
-        dw_acc += __shfl_xor(dw_acc, 16);
-        dw_acc += __shfl_xor(dw_acc, 32);
+        db_acc += shfl_xor_l(db_acc, 16, l);
+        db_acc += shfl_xor_l(db_acc, 32, l);
+        dw_acc += shfl_xor_l(dw_acc, 16, l);
+        dw_acc += shfl_xor_l(dw_acc, 32, l);
         if (g == 0) {
             sm.gred[half][r][0] = db_acc;
             sm.gred[half][r][1] = dw_acc;
         }
     }
     if (PRO) {
-        Dq += __shfl_xor(Dq, 16);
-        Dq += __shfl_xor(Dq, 32);
-        Dk += __shfl_xor(Dk, 16);
-        Dk += __shfl_xor(Dk, 32);
+        Dq += shfl_xor_l(Dq, 16, l);
+        Dq += shfl_xor_l(Dq, 32, l);
+        Dk += shfl_xor_l(Dk, 16, l);
+        Dk += shfl_xor_l(Dk, 32, l);
         if (g == 0) {
             sm.nrm[half][r][2] = Dq;
             sm.nrm[half][r][3] = Dk;
@@ -1107,8 +1107,8 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
         }
     }
     if (a_sc) {
-        dl_acc += __shfl_xor(dl_acc, 16);
-        dl_acc += __shfl_xor(dl_acc, 32);
+        dl_acc += shfl_xor_l(dl_acc, 16, l);
+        dl_acc += shfl_xor_l(dl_acc, 32, l);
         if (g == 0) sm.gred[half][r][2] = dl_acc;
         lds_barrier();
     }

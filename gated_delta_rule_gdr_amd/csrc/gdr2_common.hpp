@@ -127,21 +127,33 @@ __device__ __forceinline__ void mma32(f32x4& c, float a, float b) {
     c = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// Accumulator element (i) of the calling lane: row and column inside its 16x16 block.
-__device__ __forceinline__ int acc_row(int i) { return 4 * (lane_id() >> 4) + i; }
-__device__ __forceinline__ int acc_col() { return lane_id() & 15; }
+// Accumulator element (i) of the calling lane: row and column inside its 16x16 block.  The
+// helpers here also come with an explicit lane argument `l`, for kernels that keep the lane index
+// in a value of their own.
+__device__ __forceinline__ int acc_row(int i, int l) { return 4 * (l >> 4) + i; }
+__device__ __forceinline__ int acc_col(int l) { return l & 15; }
+__device__ __forceinline__ int acc_row(int i) { return acc_row(i, lane_id()); }
+__device__ __forceinline__ int acc_col() { return acc_col(lane_id()); }
 
 // Write a 16x16 accumulator block transposed into a k-contiguous tile: dst[n][m] (n = column of
 // the block, m = row); the four rows of a lane are contiguous in dst, one 8/16-byte store.
 template <typename OT>
-__device__ __forceinline__ void store_acc_T(OT* dst, int pitch, int n0, int m0, const f32x4& c) {
-    int l = lane_id();
+__device__ __forceinline__ void store_acc_T(OT* dst, int pitch, int n0, int m0, const f32x4& c, int l) {
     OT* p = dst + (n0 + (l & 15)) * pitch + m0 + 4 * (l >> 4);
     if constexpr (sizeof(OT) == 2) {
         *(bf16x4*)p = bf16x4{(bf16)c[0], (bf16)c[1], (bf16)c[2], (bf16)c[3]};
     } else {
         *(f32x4*)p = c;
     }
+}
+template <typename OT>
+__device__ __forceinline__ void store_acc_T(OT* dst, int pitch, int n0, int m0, const f32x4& c) {
+    store_acc_T(dst, pitch, n0, m0, c, lane_id());
+}
+
+// x of lane (l ^ m) through ds_bpermute, with the caller's lane index
+__device__ __forceinline__ float shfl_xor_l(float x, int m, int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((l ^ m) << 2, __builtin_bit_cast(int, x)));
 }
 
 __device__ __forceinline__ void wave_sync() {
@@ -166,10 +178,11 @@ namespace gdr2 {
 // loads in flight, so that next-chunk prefetches survive it.  The empty asm with a memory clobber
 // keeps the compiler from moving memory accesses across the barrier.
 __device__ __forceinline__ void lds_barrier() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // vmcnt = max, expcnt = max, lgkmcnt = 0
+    // workgroup fences limited to LDS: they order the LDS accesses around the barrier and wait
+    // for LDS only (lgkmcnt), so global loads stay in flight across it
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 }  // namespace gdr2
 
@@ -194,16 +207,17 @@ template <> struct Frag<bf16> {
     typedef bf16x8 t;
     static constexpr int N = 8;
     static __device__ __forceinline__ float at(const t& x, int e) { return (float)x[e]; }
-    static __device__ __forceinline__ t kc(const bf16* X, int pitch, int i0, int k0) {
-        const int l = lane_id();
+    static __device__ __forceinline__ t kc(const bf16* X, int pitch, int i0, int k0, int l) {
         return *(const bf16x8*)(X + (i0 + (l & 15)) * pitch + k0 + 8 * (l >> 4));
     }
-    static __device__ __forceinline__ t tr(const bf16* X, int pitch, int k0, int i0) {
-        const int l = lane_id(), p = l & 15, kb = k0 + 8 * (l >> 4) + (p >> 2);
+    static __device__ __forceinline__ t tr(const bf16* X, int pitch, int k0, int i0, int l) {
+        const int p = l & 15, kb = k0 + 8 * (l >> 4) + (p >> 2);
         const bf16* a = X + kb * pitch + i0 + 4 * (p & 3);
         bf16x4 lo = ds_read_tr4(a), hi = ds_read_tr4(a + 4 * pitch);
         return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
+    static __device__ __forceinline__ t kc(const bf16* X, int pitch, int i0, int k0) { return kc(X, pitch, i0, k0, lane_id()); }
+    static __device__ __forceinline__ t tr(const bf16* X, int pitch, int k0, int i0) { return tr(X, pitch, k0, i0, lane_id()); }
     // fragment straight from global memory, row-major [idx][k] with the given pitch
     static __device__ __forceinline__ t gkc(const bf16* X, long pitch, int i0, int k0) {
         const int l = lane_id();
@@ -231,14 +245,14 @@ template <> struct Frag<float> {
     typedef float t;
     static constexpr int N = 1;
     static __device__ __forceinline__ float at(const t& x, int) { return x; }
-    static __device__ __forceinline__ t kc(const float* X, int pitch, int i0, int k0) {
-        const int l = lane_id();
+    static __device__ __forceinline__ t kc(const float* X, int pitch, int i0, int k0, int l) {
         return X[(i0 + (l & 15)) * pitch + k0 + (l >> 4)];
     }
-    static __device__ __forceinline__ t tr(const float* X, int pitch, int k0, int i0) {
-        const int l = lane_id();
+    static __device__ __forceinline__ t tr(const float* X, int pitch, int k0, int i0, int l) {
         return X[(k0 + (l >> 4)) * pitch + i0 + (l & 15)];
     }
+    static __device__ __forceinline__ t kc(const float* X, int pitch, int i0, int k0) { return kc(X, pitch, i0, k0, lane_id()); }
+    static __device__ __forceinline__ t tr(const float* X, int pitch, int k0, int i0) { return tr(X, pitch, k0, i0, lane_id()); }
     static __device__ __forceinline__ t gkc(const float* X, long pitch, int i0, int k0) {
         const int l = lane_id();
         return X[(long)(i0 + (l & 15)) * pitch + k0 + (l >> 4)];
@@ -278,12 +292,13 @@ template <typename OT> struct FLay {
 template <typename OT> struct FFrag;
 template <> struct FFrag<bf16> {
     typedef bf16x8 t;
-    static __device__ __forceinline__ t fkc(const bf16* X, int cols, int i0, int k0) {
-        const int l = lane_id();
+    static __device__ __forceinline__ t fkc(const bf16* X, int cols, int i0, int k0, int l) {
         return *(const bf16x8*)(X + FLay<bf16>::off(i0 + (l & 15), k0 + 8 * (l >> 4), cols));
     }
-    static __device__ __forceinline__ t ftr(const bf16* X, int cols, int k0, int i0) {
-        const int l = lane_id(), p = l & 15, kb = k0 + 8 * (l >> 4) + (p >> 2);
+    static __device__ __forceinline__ t fkc(const bf16* X, int cols, int i0, int k0) { return fkc(X, cols, i0, k0, lane_id()); }
+    static __device__ __forceinline__ t ftr(const bf16* X, int cols, int k0, int i0) { return ftr(X, cols, k0, i0, lane_id()); }
+    static __device__ __forceinline__ t ftr(const bf16* X, int cols, int k0, int i0, int l) {
+        const int p = l & 15, kb = k0 + 8 * (l >> 4) + (p >> 2);
         const int c = i0 + 4 * (p & 3);
         bf16x4 lo = ds_read_tr4(X + FLay<bf16>::off(kb, c, cols));
         bf16x4 hi = ds_read_tr4(X + FLay<bf16>::off(kb + 4, c, cols));
@@ -292,14 +307,14 @@ template <> struct FFrag<bf16> {
 };
 template <> struct FFrag<float> {
     typedef float t;
-    static __device__ __forceinline__ t fkc(const float* X, int cols, int i0, int k0) {
-        const int l = lane_id();
+    static __device__ __forceinline__ t fkc(const float* X, int cols, int i0, int k0, int l) {
         return X[FLay<float>::off(i0 + (l & 15), k0 + (l >> 4), cols)];
     }
-    static __device__ __forceinline__ t ftr(const float* X, int cols, int k0, int i0) {
-        const int l = lane_id();
+    static __device__ __forceinline__ t ftr(const float* X, int cols, int k0, int i0, int l) {
         return X[FLay<float>::off(k0 + (l >> 4), i0 + (l & 15), cols)];
     }
+    static __device__ __forceinline__ t fkc(const float* X, int cols, int i0, int k0) { return fkc(X, cols, i0, k0, lane_id()); }
+    static __device__ __forceinline__ t ftr(const float* X, int cols, int k0, int i0) { return ftr(X, cols, k0, i0, lane_id()); }
 };
 
 // Activations of the fused prologue.
