@@ -199,7 +199,8 @@ def main():
     ap.add_argument("--profile-pass", action="store_true",
                     help="short run for hardware-counter passes: 1 warm-up + 1 step, one decode "
                          "step, then a 512 MiB device-to-device copy that calibrates FETCH_SIZE / "
-                         "WRITE_SIZE (no JSON line)")
+                         "WRITE_SIZE and a 4096^3 bf16 GEMM that calibrates the MFMA counters "
+                         "(no JSON line)")
     args = ap.parse_args()
     if args.profile_pass:
         args.warmup, args.steps, args.decode_steps = 1, 1, 1
@@ -292,8 +293,13 @@ def main():
         src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         dst.copy_(src)
+        # a bf16 GEMM of known size calibrates the MFMA instruction counters the same way
+        ga = torch.randn(4096, 4096, dtype=bf, device=dev)
+        gb = torch.randn(4096, 4096, dtype=bf, device=dev)
+        torch.mm(ga, gb)
         torch.cuda.synchronize()
-        print("profile pass done: 512 MiB copy issued for counter calibration", flush=True)
+        print("profile pass done: 512 MiB copy and 4096^3 bf16 GEMM issued for counter calibration",
+              flush=True)
         return
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
