@@ -552,8 +552,10 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
     const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(wave_id()), R = w & 3, half = w >> 2;
     const int l = lane_id(), rl = l & 15, g = l >> 4;
     const int NC = p.NC;
-    const int chain = blockIdx.x / NC, c = blockIdx.x % NC;
-    const int bb = chain / p.H, h = chain % p.H;
+    // heads fastest: workgroups that run at the same time read neighbouring 256-byte pieces of the
+    // same token rows of q, k, v, dO, ... ([B, T, H, D] layout) rather than rows 4 KB apart
+    const int h = blockIdx.x % p.H, c = (blockIdx.x / p.H) % NC, bb = blockIdx.x / (p.H * NC);
+    const int chain = bb * p.H + h;
     const long T = p.T, H = p.H;
     const long cix = (long)chain * NC + c;
     const int r = 16 * R + rl;

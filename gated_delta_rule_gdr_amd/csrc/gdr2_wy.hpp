@@ -182,9 +182,10 @@ struct WyChunk {
         gates = gates_;
         pro = pro_;
         (void)B;
-        chain = bid / NC;
-        c = bid % NC;
-        const int bb = chain / H_, h = chain % H_;
+        // heads fastest: concurrent workgroups share the token rows of the [B, T, H, D] inputs
+        const int h = bid % H_, bb = bid / (H_ * NC);
+        c = (bid / H_) % NC;
+        chain = bb * H_ + h;
         R = wave_id();
         l = lane_id();
         rl = l & 15;
