@@ -12,8 +12,9 @@
 //     dg_j = dy_j * o_j * rs * weight_j * silu'(g_j),  silu'(x) = s (1 + x (1 - s)), s = sigmoid(x)
 //     dweight_j = sum over rows of dy_j * o_j * rs * silu(g_j)
 //
-// One wave per row at a time, each lane holding d_v / 64 consecutive channels; the row sums are
-// wave reductions.  Both passes are pure streams.  The weight gradient is reduced without
+// Sixteen lanes per row (a lane holds d_v / 16 consecutive channels, one 16-byte load for bf16 at
+// d_v = 128), four rows per wave step and two steps' rows loaded together; the row sums are
+// 16-lane DPP reductions.  Both passes are pure streams.  The weight gradient is reduced without
 // atomics: every workgroup writes its partial sums (its waves combined in LDS), and a second
 // small kernel adds the partials in a fixed order, so the result is bitwise deterministic.
 #include "gdr2_common.hpp"
@@ -21,99 +22,158 @@
 
 namespace gdr2 {
 
-constexpr int kEpiRowsPerWave = 16;  // rows a wave handles
+constexpr int kEpiRowsPerWave = 32;  // rows a wave handles: 4 steps of 8 rows (2 per lane group)
 
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+// sum over the 16 lanes of the caller's DPP row, in every lane of the row
+__device__ __forceinline__ float row_sum16(float x) {
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xf, 0xf, false));   // quad_perm 1,0,3,2
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4E, 0xf, 0xf, false));   // quad_perm 2,3,0,1
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x141, 0xf, 0xf, false));  // row_half_mirror
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x140, 0xf, 0xf, false));  // row_mirror
     return x;
+}
+
+// N consecutive elements of a row to fp32 and back (one or two vector accesses)
+template <typename OT, int N>
+__device__ __forceinline__ void load_n(const OT* p, float* v) {
+    if constexpr (sizeof(OT) == 2 && N == 8) {
+        const bf16x8 x = *(const bf16x8*)p;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) v[c] = (float)x[c];
+    } else if constexpr (sizeof(OT) == 2 && N == 4) {
+        const bf16x4 x = *(const bf16x4*)p;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v[c] = (float)x[c];
+    } else {
+#pragma unroll
+        for (int c = 0; c < N; c += 4) {
+            const f32x4 x = *(const f32x4*)((const float*)p + c);
+            v[c] = x[0]; v[c + 1] = x[1]; v[c + 2] = x[2]; v[c + 3] = x[3];
+        }
+    }
+}
+template <typename OT, int N>
+__device__ __forceinline__ void store_n(OT* p, const float* v) {
+    if constexpr (sizeof(OT) == 2 && N == 8) {
+        bf16x8 x;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) x[c] = (bf16)v[c];
+        *(bf16x8*)p = x;
+    } else if constexpr (sizeof(OT) == 2 && N == 4) {
+        *(bf16x4*)p = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+    } else {
+#pragma unroll
+        for (int c = 0; c < N; c += 4) *(f32x4*)((float*)p + c) = f32x4{v[c], v[c + 1], v[c + 2], v[c + 3]};
+    }
 }
 
 template <typename OT, int DV>
 __global__ __launch_bounds__(kThreads) void gdr2_epi_fwd_kernel(EpiParams p) {
-    constexpr int CPL = DV / 64;  // channels per lane
-    const int l = lane_id();
+    constexpr int CPL = DV / 16;  // channels per lane
+    const int l = lane_id(), g = l >> 4, ch = (l & 15) * CPL;
     const long wave = (long)blockIdx.x * kWaves + wave_id();
-    const OT* o = (const OT*)p.o;
-    const OT* gt = (const OT*)p.g;
-    OT* y = (OT*)p.y;
+    const OT* __restrict__ o = (const OT*)p.o;
+    const OT* __restrict__ gt = (const OT*)p.g;
+    OT* __restrict__ y = (OT*)p.y;
     float wt[CPL];
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) wt[c] = p.weight[l * CPL + c];
-    for (int i = 0; i < kEpiRowsPerWave; ++i) {
-        const long row = wave * kEpiRowsPerWave + i;
-        if (row >= p.rows) break;
-        const long base = row * DV + l * CPL;
-        float ov[CPL], gv[CPL];
+    for (int c = 0; c < CPL; ++c) wt[c] = p.weight[ch + c];
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-            ov[c] = to_f(o[base + c]);
-            gv[c] = to_f(gt[base + c]);
+    for (int it = 0; it < kEpiRowsPerWave / 8; ++it) {
+        const long r0 = wave * kEpiRowsPerWave + it * 8 + g;  // rows r0 and r0 + 4 of this lane group
+        // loads from a row clamped into range (no branch, so all of them are in flight together);
+        // rows past the end are not stored
+        float ov[2][CPL], gv[2][CPL];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const long rl = r0 + 4 * u < p.rows ? r0 + 4 * u : p.rows - 1;
+            load_n<OT, CPL>(o + rl * DV + ch, ov[u]);
+            load_n<OT, CPL>(gt + rl * DV + ch, gv[u]);
         }
-        float ss = 0.f;
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) ss += ov[c] * ov[c];
-        ss = wave_sum(ss);
-        const float rs = rsqrtf(ss / DV + p.eps);
+        for (int u = 0; u < 2; ++u) {
+            const long row = r0 + 4 * u;
+            if (row < p.rows) {
+                float ss = 0.f;
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-            const float s = sigmoid_f(gv[c]);
-            y[base + c] = from_f<OT>(ov[c] * rs * wt[c] * gv[c] * s);
+                for (int c = 0; c < CPL; ++c) ss += ov[u][c] * ov[u][c];
+                const float rs = rsqrtf(row_sum16(ss) / DV + p.eps);
+                float yv[CPL];
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) yv[c] = ov[u][c] * rs * wt[c] * gv[u][c] * sigmoid_f(gv[u][c]);
+                store_n<OT, CPL>(y + row * DV + ch, yv);
+            }
         }
     }
 }
 
 template <typename OT, int DV>
 __global__ __launch_bounds__(kThreads) void gdr2_epi_bwd_kernel(EpiParams p) {
-    constexpr int CPL = DV / 64;
-    const int l = lane_id();
+    constexpr int CPL = DV / 16;
+    const int l = lane_id(), g = l >> 4, ch = (l & 15) * CPL;
     const long wave = (long)blockIdx.x * kWaves + wave_id();
-    const OT* o = (const OT*)p.o;
-    const OT* gt = (const OT*)p.g;
-    const OT* dy = (const OT*)p.dy;
-    OT* dox = (OT*)p.dox;
-    OT* dg = (OT*)p.dg;
+    const OT* __restrict__ o = (const OT*)p.o;
+    const OT* __restrict__ gt = (const OT*)p.g;
+    const OT* __restrict__ dy = (const OT*)p.dy;
+    OT* __restrict__ dox = (OT*)p.dox;
+    OT* __restrict__ dg = (OT*)p.dg;
     __shared__ float part[kWaves][DV];
     float wt[CPL], dwp[CPL];
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
-        wt[c] = p.weight[l * CPL + c];
+        wt[c] = p.weight[ch + c];
         dwp[c] = 0.f;
     }
-    for (int i = 0; i < kEpiRowsPerWave; ++i) {
-        const long row = wave * kEpiRowsPerWave + i;
-        if (row >= p.rows) break;
-        const long base = row * DV + l * CPL;
-        float ov[CPL], gv[CPL], dv_[CPL];
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-            ov[c] = to_f(o[base + c]);
-            gv[c] = to_f(gt[base + c]);
-            dv_[c] = to_f(dy[base + c]);
+    for (int it = 0; it < kEpiRowsPerWave / 8; ++it) {
+        const long r0 = wave * kEpiRowsPerWave + it * 8 + g;
+        float ov[2][CPL], gv[2][CPL], dv_[2][CPL];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const long rl = r0 + 4 * u < p.rows ? r0 + 4 * u : p.rows - 1;
+            load_n<OT, CPL>(o + rl * DV + ch, ov[u]);
+            load_n<OT, CPL>(gt + rl * DV + ch, gv[u]);
+            load_n<OT, CPL>(dy + rl * DV + ch, dv_[u]);
         }
-        float ss = 0.f;
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) ss += ov[c] * ov[c];
-        ss = wave_sum(ss);
-        const float rs = rsqrtf(ss / DV + p.eps);
-        float a[CPL], ao = 0.f;
+        for (int u = 0; u < 2; ++u) {
+            const long row = r0 + 4 * u;
+            if (row < p.rows) {
+                float ss = 0.f;
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-            const float s = sigmoid_f(gv[c]);
-            const float sl = gv[c] * s;
-            a[c] = dv_[c] * wt[c] * sl;
-            ao += a[c] * ov[c];
-            const float n = ov[c] * rs;
-            dwp[c] += dv_[c] * n * sl;
-            dg[base + c] = from_f<OT>(dv_[c] * n * wt[c] * s * (1.f + gv[c] * (1.f - s)));
+                for (int c = 0; c < CPL; ++c) ss += ov[u][c] * ov[u][c];
+                const float rs = rsqrtf(row_sum16(ss) / DV + p.eps);
+                float a[CPL], dgv[CPL], ao = 0.f;
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) {
+                    const float s = sigmoid_f(gv[u][c]);
+                    const float sl = gv[u][c] * s;
+                    a[c] = dv_[u][c] * wt[c] * sl;
+                    ao += a[c] * ov[u][c];
+                    const float n = ov[u][c] * rs;
+                    dwp[c] += dv_[u][c] * n * sl;
+                    dgv[c] = dv_[u][c] * n * wt[c] * s * (1.f + gv[u][c] * (1.f - s));
+                }
+                store_n<OT, CPL>(dg + row * DV + ch, dgv);
+                ao = row_sum16(ao) / DV;
+                float dov[CPL];
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) dov[c] = rs * (a[c] - ov[u][c] * rs * rs * ao);
+                store_n<OT, CPL>(dox + row * DV + ch, dov);
+            }
         }
-        ao = wave_sum(ao) / DV;
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) dox[base + c] = from_f<OT>(rs * (a[c] - ov[c] * rs * rs * ao));
     }
-    // this workgroup's weight-gradient partial: [workgroup][DV], its waves added in order
+    // this workgroup's weight-gradient partial: the four lane groups of a wave, then its waves,
+    // added in a fixed order
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) part[wave_id()][l * CPL + c] = dwp[c];
+    for (int c = 0; c < CPL; ++c) {
+        dwp[c] += __shfl_xor(dwp[c], 16);
+        dwp[c] += __shfl_xor(dwp[c], 32);
+    }
+    if (g == 0) {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) part[wave_id()][ch + c] = dwp[c];
+    }
     __syncthreads();
     for (int j = threadIdx.x; j < DV; j += kThreads) {
         float acc = 0.f;
