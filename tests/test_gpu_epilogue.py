@@ -79,3 +79,14 @@ def test_out_gate_deterministic():
     torch.cuda.synchronize()
     for n in ("do", "dg", "dweight"):
         assert torch.equal(a[n], b[n]), n
+
+
+def test_out_gate_empty_input():
+    """No rows (T = 0): the forward writes nothing and the weight gradient is exactly zero."""
+    o, g, w, dy = (t.to(DEV) for t in _inputs((1, 0, 2, 128), "bf16", seed=5))
+    announce("out gate empty input")
+    y = gdr2_out_gate_fwd(o, g, w)
+    gr = gdr2_out_gate_bwd(o, g, w, dy)
+    torch.cuda.synchronize()
+    assert y.shape == o.shape and gr["do"].shape == o.shape and gr["dg"].shape == g.shape
+    assert torch.equal(gr["dweight"].cpu(), torch.zeros(128))
