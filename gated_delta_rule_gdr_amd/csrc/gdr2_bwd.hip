@@ -467,8 +467,7 @@ hipError_t dstate_dispatch(int bf, int dk, int dvs, const BwdParams& p, hipStrea
 // --------------------------------------------------------------------------------------------
 // Chunk gradients: one workgroup (8 waves) per (chain, chunk), all chunks in parallel.  Given the
 // state S entering the chunk (forward checkpoint), the gradient dS' of the state leaving it (the
-// state-carry kernel above) and dO, it recomputes Delta = U - Y S (U = T Z rebuilt from the T tile
-// and z = w . v of the block, so the U factor is not read), dDelta and dX for DVH value columns at a
+// state-carry kernel above) and dO, it recomputes Delta, dDelta and dX for DVH value columns at a
 // time and reduces over the value columns in MFMA accumulators (held transposed, channel x token):
 //     R1 = S dO^T,  R2 = S dX^T,  R3 = dS' Delta^T,   R4 = dO Delta^T,  R5 = dX Delta^T,
 //     R6_i = sum_j dS'_ij S_ij.
@@ -513,7 +512,6 @@ struct alignas(16) BgSmem {
             OT St[Cf::NBUF][DVH * Cf::PK];      // S^T block   [j][i]  (16-bit: two buffers, the
             OT dSt[Cf::NBUF][DVH * Cf::PK];     // dS'^T block [j][i]   next block is staged
             OT dOt[Cf::NBUF][kChunk * Cf::PH];  // dO block    [r][j]   while this one is reduced)
-            OT Zt[Cf::NBUF][kChunk * Cf::PH];   // z = w . v   [r][j]  (U = T Z is rebuilt here)
             OT DlT[DVH * Cf::PC];      // Delta^T             [j][r]
             OT dDT[DVH * Cf::PC];      // dDelta^T            [j][r]
             OT dXt[kChunk * Cf::PH];   // dX block            [r][j]
@@ -567,7 +565,6 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
     const long tok0 = ((long)bb * T + (long)c * C) * H + h;  // token row of the chunk's first token
     const int ibase = NIBH * half;                            // this wave's first key-channel block
     const int kbeg = (16 * R / KS) * KS;                      // first k-step touching tokens >= 16R
-    const int kend = ((16 * R + 16 + KS - 1) / KS) * KS;      // k-steps covering tokens <= 16R + 15
 
     // ---- this lane's log alpha (token r, channels 16 (ibase+ib) + 4g + e); q, k, b come later
     typename RW::t qr[NIBH], kr[NIBH], br[NIBH];
@@ -619,7 +616,8 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
     // block's work), fp32 one
     constexpr int NS = Cf::NBUF;
     i32x4 pS[NS][SVEC], pdS[NS][SVEC], pO[NS][OVEC];
-    typename RW::t pv[NS], pw[NS];
+    typename RW::t pv[NS], pw[NS], pU[NS];
+    const OT* Uc = (const OT*)p.wy.U + cix * C * DV;
     auto fetch_block = [&](int jq, int st) __attribute__((always_inline)) {
         const int jb0 = jq * DVH;
 #pragma unroll
@@ -650,6 +648,7 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
         } else {
             pw[st] = *(const typename RW::t*)((const OT*)p.w + o);
         }
+        pU[st] = *(const typename RW::t*)(Uc + ((long)(R * (DV / 16) + jb0 / 16 + half) * 64 + l) * 4);
     };
     i32x4 pT[TVEC], pP[TVEC];
     {
@@ -699,7 +698,7 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
     // staging of a fetched value-column block into LDS buffer b, and the next fetch (block jn, or
     // after the last block the raw key inputs for the Gram phase and the epilogue)
     constexpr int NJ = DV / DVH;
-    typename RW::t cv, cw;
+    typename RW::t cv, cw, cU;
     auto stage = [&](int b, int st) __attribute__((always_inline)) {
 #pragma unroll
         for (int m = 0; m < SVEC; ++m) {
@@ -718,18 +717,7 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
         }
         cv = pv[st];
         cw = pw[st];
-        // z = w . v of (token r, columns 16 half + 4g .. +3), zero past the end, rounded to the
-        // operand type as the factor kernel rounds it
-        f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        if (valid) {
-            f32x4 wz = RW::widen(cw);
-            if (PRO) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) wz[e] = sigmoid_f(wz[e]);
-            }
-            z = RW::widen(cv) * wz;
-        }
-        store4(sm.u.j.Zt[b] + r * PH + 16 * half + 4 * g, z);
+        cU = pU[st];
     };
     auto fetch_next = [&](int jn, int st) __attribute__((always_inline)) {
         if (jn < NJ) {
@@ -766,11 +754,7 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
         // Delta = U - Y S, dDelta = Ktilde dS' + P^T dO: block (token R, columns 16 half)
         {
             const int jb = half;
-            // U = T Z (T lower triangular: key tokens s <= r), accumulated as the factor kernel
-            // does, then Delta = U - Y S
-            f32x4 aD = {0.f, 0.f, 0.f, 0.f};
-            for (int k0 = 0; k0 < kend; k0 += KS)
-                MM::mma(aD, FR::kc(sm.u.j.Tt, PC, 16 * R, k0, l), FR::tr(sm.u.j.Zt[bq], PH, k0, 16 * jb, l));
+            f32x4 aD = RW::widen(cU);
             f32x4 adD = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
