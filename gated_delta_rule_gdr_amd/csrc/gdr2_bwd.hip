@@ -855,11 +855,19 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
 
     // ---- in-block cumsum of log alpha (DPP over the 16 tokens), block totals, and the
     //      per-channel tables exp(ref_R), exp(G_C - ref_R), exp(ref_R - ref_S)
-    if (PRO) {  // log alpha = -decay_scale * softplus(a)
+    // fused prologue: log alpha = -decay_scale * softplus(a); the chain-rule factor
+    // -decay_scale * sigmoid(a) of dlog alpha comes from the same exponential
+    f32x4 dsa[PRO ? NIBH : 1];
+    if (PRO) {
 #pragma unroll
         for (int ib = 0; ib < NIBH; ++ib)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sc[ib][e] = -p.pro.decay_scale * softplus_f(sc[ib][e]);
+            for (int e = 0; e < 4; ++e) {
+                const float x = sc[ib][e], ex = __expf(x);
+                const float sp = x > 20.f ? x : 0.69314718f * __builtin_amdgcn_logf(1.f + ex);
+                dsa[PRO ? ib : 0][e] = -p.pro.decay_scale * (x > 20.f ? 1.f : ex * __builtin_amdgcn_rcpf(1.f + ex));
+                sc[ib][e] = -p.pro.decay_scale * sp;
+            }
     }
 #pragma unroll
     for (int ib = 0; ib < NIBH; ++ib)
@@ -908,16 +916,23 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
         rq = rsqrtf(sm.nrm[0][r][0] + sm.nrm[1][r][0] + p.pro.norm_eps);
         rk = rsqrtf(sm.nrm[0][r][1] + sm.nrm[1][r][1] + p.pro.norm_eps);
     }
-    // the activations the forward used: q, k normalised, b through the sigmoid
-    auto act = [&](int ib, f32x4& q4, f32x4& k4, f32x4& b4) __attribute__((always_inline)) {
+    // the activations the forward used: q, k normalised, b through the sigmoid (computed on the
+    // first use and kept, in fp32 as the forward used it)
+    f32x4 bsg[PRO ? NIBH : 1];
+    auto act = [&](int ib, f32x4& q4, f32x4& k4, f32x4& b4, bool first) __attribute__((always_inline)) {
         q4 = RW::widen(qr[ib]);
         k4 = RW::widen(kr[ib]);
         b4 = RW::widen(br[ib]);
         if (PRO) {
             q4 *= rq;
             k4 *= rk;
+            if (first) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) b4[e] = sigmoid_f(b4[e]);
+                for (int e = 0; e < 4; ++e) b4[e] = sigmoid_f(b4[e]);
+                bsg[PRO ? ib : 0] = b4;
+            } else {
+                b4 = bsg[PRO ? ib : 0];
+            }
         }
     };
 
@@ -926,7 +941,7 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
     for (int ib = 0; ib < NIBH; ++ib) {
         const int i0 = 16 * (ibase + ib) + 4 * g;
         f32x4 q4, k4, b4;
-        act(ib, q4, k4, b4);
+        act(ib, q4, k4, b4, true);
         f32x4 eb, qb, kb;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -1012,7 +1027,7 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
     for (int ib = 0; ib < NIBH; ++ib) {
         const int i0 = 16 * (ibase + ib) + 4 * g;
         f32x4 q4, k4, b4;
-        act(ib, q4, k4, b4);
+        act(ib, q4, k4, b4, false);
         if (!valid) q4 = k4 = b4 = f32x4{0.f, 0.f, 0.f, 0.f};
         const f32x4 hr = *(const f32x4*)(&sm.hRt[R][i0]);
         f32x4 dqv, dkv, dbv, kdk;
@@ -1079,7 +1094,7 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
         for (int ib = 0; ib < NIBH; ++ib) {
             const int i0 = 16 * (ibase + ib) + 4 * g;
             f32x4 q4, k4, b4;
-            act(ib, q4, k4, b4);
+            act(ib, q4, k4, b4, false);
             store4((OT*)p.dq + orow + i0, rq * (dqs[PRO ? ib : 0] - q4 * Dqt));
             store4((OT*)p.dk + orow + i0, rk * (dks[PRO ? ib : 0] - k4 * Dkt));
         }
@@ -1096,11 +1111,7 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
                 dl += *(const f32x4*)&sm.ktot[Rp][i0];
                 if (Rp > R) dl += *(const f32x4*)&sm.btot[Rp][i0];
             }
-            if (PRO && !a_sc) {  // log alpha = -c softplus(a): d a = d log alpha . (-c sigmoid(a))
-                const f32x4 a4 = *(const f32x4*)(p.la + orow + i0);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) dl[e] *= -p.pro.decay_scale * sigmoid_f(a4[e]);
-            }
+            if (PRO && !a_sc) dl *= dsa[PRO ? ib : 0];  // d a = d log alpha . (-c sigmoid(a))
             if (a_sc) {
                 dl_acc += (dl[0] + dl[1]) + (dl[2] + dl[3]);
             } else {
