@@ -4,7 +4,7 @@ import pytest
 import torch
 
 from gated_delta_rule_gdr_amd import gdr2_decode_step, gdr2_fwd_chunked
-from gated_delta_rule_gdr_amd.inputs import (config_inputs, decode_inputs, layer_inputs,
+from gated_delta_rule_gdr_amd.inputs import (DECODE, config_inputs, decode_inputs, layer_inputs,
                                              strong_decay_inputs, to_f64)
 from oracle import oracle as orc
 from tests._util import TOL, announce, assert_close, to_np
@@ -154,3 +154,32 @@ def test_decode_equals_chunked_forward():
     od = torch.stack(outs, dim=1)
     assert_close("decode vs chunked o", to_np(od), to_np(o), TOL["bf16"])
     assert_close("decode vs chunked S_T", to_np(S), to_np(ST), TOL["bf16"])
+
+
+def test_decode_full_workload_sampled_chains():
+    """The decode workload at full size (256 sequences x 16 heads, d = 128, 1024 steps, bf16
+    tokens, fp32 state updated in place in HBM, the launch the benchmark times): three sampled
+    (sequence, head) chains against the oracle's token recurrence at every step and at the end."""
+    N, H, dk, dv, steps = DECODE["N"], DECODE["H"], DECODE["dk"], DECODE["dv"], DECODE["steps"]
+    announce(f"decode full workload N={N} H={H} steps={steps}")
+    samples = [(0, 0), (137, 9), (255, 15)]
+    S = torch.zeros((N, H, dk, dv), dtype=torch.float32, device=DEV)
+    Sref = {c: None for c in samples}
+    worst = 0.0
+    for s in range(steps):
+        x = decode_inputs(s, N=N, H=H, dk=dk, dv=dv, device=DEV)
+        o, _ = gdr2_decode_step(x["q"], x["k"], x["v"], x["log_alpha"], x["b"], x["w"], S_in=S, S_out=S)
+        sub = {n: torch.stack([x[n][a, h] for a, h in samples]) for n in x}
+        osub = torch.stack([o[a, h] for a, h in samples]).float().cpu().numpy()
+        f = {n: t.to("cpu", torch.float64).numpy() for n, t in sub.items()}
+        for i, c in enumerate(samples):
+            ro, Sref[c] = orc.decode_step(*(f[n][i:i + 1, None] for n in ("q", "k", "v", "log_alpha", "b", "w")),
+                                          Sref[c])
+            if s % 128 == 127 or s == steps - 1:
+                worst = max(worst, assert_close(f"decode o step {s} chain {c}", osub[i:i + 1, None], ro,
+                                                TOL["bf16"]))
+    torch.cuda.synchronize()
+    for c in samples:
+        assert_close(f"decode S after {steps} steps chain {c}", to_np(S[c[0]:c[0] + 1, c[1]:c[1] + 1]),
+                     Sref[c], TOL["bf16"])
+    print(f"  full decode: worst sampled o error {worst:.2e}", flush=True)
