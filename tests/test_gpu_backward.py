@@ -189,3 +189,17 @@ def test_bwd_deterministic():
     _, _, g2 = _run(x)
     for n in GRADS:
         assert torch.equal(g1[n], g2[n]), n
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64)])
+def test_empty_sequence(dtype, d):
+    """T = 0: no token is processed, so the forward returns S_T = S0 and the backward passes the
+    state gradient straight through, dS0 = dS_T (both exactly); the token-shaped outputs are empty."""
+    x = layer_inputs(2, 0, 3, d, d, dtype=dtype, seed=31, s0_std=0.05, dST=True)
+    announce(f"empty sequence {dtype} d={d}")
+    o, ST, gr = _run(x)
+    assert o.shape == (2, 0, 3, d)
+    assert torch.equal(ST.cpu(), x["S0"].float())
+    assert torch.equal(gr["dS0"].cpu(), x["dST"].float())
+    for n in ("dq", "dk", "dv", "dlog_alpha", "db", "dw"):
+        assert gr[n].numel() == 0, n
