@@ -203,3 +203,18 @@ def test_empty_sequence(dtype, d):
     assert torch.equal(gr["dS0"].cpu(), x["dST"].float())
     for n in ("dq", "dk", "dv", "dlog_alpha", "db", "dw"):
         assert gr[n].numel() == 0, n
+
+
+@pytest.mark.parametrize("case", ["decay_only", "no_write", "full_erase"])
+def test_degenerate_gates(case):
+    """Degenerate gate settings from a random S0: pure decay (b = w = 0: the state only decays and
+    o_t = S_t^T q_t), erase without write (w = 0), and a full-strength erase (b = 1); forward and
+    backward against the oracle."""
+    x = layer_inputs(2, 100, 3, 64, 64, dtype="bf16", seed=41, s0_std=0.05, dST=True)
+    if case in ("decay_only", "no_write"):
+        x["w"] = torch.zeros_like(x["w"])
+    if case == "decay_only":
+        x["b"] = torch.zeros_like(x["b"])
+    if case == "full_erase":
+        x["b"] = torch.ones_like(x["b"])
+    _check(x, TOL["bf16"], f"degenerate gates {case}")
