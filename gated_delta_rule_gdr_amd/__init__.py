@@ -134,8 +134,15 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _stream():
-    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+def _stream(dev):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _run(fn_name, dev, fn, *args):
+    """Call a C entry point with dev current and its current stream appended; raise on error."""
+    with torch.cuda.device(dev):
+        st = fn(*args, _stream(dev))
+    _check(fn_name, st)
 
 
 def _check(fn, st):
@@ -164,6 +171,8 @@ def gate_bits(q, log_alpha, b, w):
     channel shape."""
     bits = 0
     for t, bit, name in ((b, ERASE_SCALAR, "b"), (w, WRITE_SCALAR, "w"), (log_alpha, DECAY_SCALAR, "log_alpha")):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a tensor")
         if tuple(t.shape) == tuple(q.shape[:-1]):
             bits |= bit
         elif t.dim() != q.dim() or tuple(t.shape[:-1]) != tuple(q.shape[:-1]):
@@ -172,10 +181,55 @@ def gate_bits(q, log_alpha, b, w):
     return bits
 
 
-def _contig(*ts):
-    for t in ts:
-        if t is not None and not t.is_contiguous():
-            raise ValueError("all tensors must be contiguous")
+# Tensor checks.  The C ABI receives raw pointers and cannot see shapes or dtypes, so a tensor of
+# the wrong shape or dtype would be read out of bounds: every tensor is checked against the layout
+# include/gdr2.h gives before any call.  Shape and dtype come first and the device last, so that a
+# consistent set of host tensors fails only on the device check.
+def _need(name, t, shape, dtype, dev, optional=False):
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}; expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}; expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device != dev:
+        raise ValueError(f"{name} is on {t.device}; expected {dev}")
+
+
+def _on_gpu(dev):
+    if dev.type != "cuda":
+        raise ValueError(f"tensors must be GPU tensors; got device {dev}")
+
+
+def _ws(name, t, dev):
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.uint8 or t.dim() != 1:
+        raise TypeError(f"{name} must be a 1-D uint8 tensor")
+    _need(name, t, t.shape, torch.uint8, dev)
+
+
+def _inputs(q, k, v, log_alpha, b, w, ndim):
+    """Checks the layer inputs ([B, T, H, d], or [N, H, d] for decode, ndim = 4 or 3) against q
+    and returns (device, gate bits)."""
+    for name, t in (("q", q), ("v", v)):
+        if not isinstance(t, torch.Tensor) or t.dim() != ndim:
+            raise ValueError(f"{name} must be a {ndim}-D tensor")
+    dt, dev = q.dtype, q.device
+    _dtype(q)
+    tok, dk, dv = tuple(q.shape[:-1]), q.shape[-1], v.shape[-1]
+    bits = gate_bits(q, log_alpha, b, w)
+    _need("q", q, q.shape, dt, dev)
+    _need("k", k, q.shape, dt, dev)
+    _need("v", v, tok + (dv,), dt, dev)
+    _need("log_alpha", log_alpha, tok if bits & DECAY_SCALAR else tok + (dk,), torch.float32, dev)
+    _need("b", b, tok if bits & ERASE_SCALAR else tok + (dk,), dt, dev)
+    _need("w", w, tok if bits & WRITE_SCALAR else tok + (dv,), dt, dev)
+    return dev, bits
 
 
 def gdr2_fwd_chunked(q, k, v, log_alpha, b, w, S0=None, want_final_state=True, workspace=None,
@@ -184,19 +238,21 @@ def gdr2_fwd_chunked(q, k, v, log_alpha, b, w, S0=None, want_final_state=True, w
     chunk-entry states that gdr2_bwd_chunked needs.  ``workspace`` may pass a preallocated uint8
     device tensor of at least the required size."""
     lib = load_library()
-    _contig(q, k, v, log_alpha, b, w, S0)
+    dev, bits = _inputs(q, k, v, log_alpha, b, w, 4)
     B, T, H, dk, dv = _shapes(q, v)
     dt = _dtype(q)
-    o = torch.empty((B, T, H, dv), dtype=q.dtype, device=q.device)
-    ST = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device) if want_final_state else None
+    _need("S0", S0, (B, H, dk, dv), torch.float32, dev, optional=True)
+    if workspace is not None:
+        _ws("workspace", workspace, dev)
+    _on_gpu(dev)
+    o = torch.empty((B, T, H, dv), dtype=q.dtype, device=dev)
+    ST = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev) if want_final_state else None
     need = lib.gdr2_fwd_workspace_bytes(B, T, H, dk, dv, dt)
     ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8,
-                                                             device=q.device)
-    st = lib.gdr2_fwd_chunked_ex(B, T, H, dk, dv, dt, gate_bits(q, log_alpha, b, w),
-                                 _pro(prologue), _ptr(q),
-                                 _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w), _ptr(S0),
-                                 _ptr(o), _ptr(ST), _ptr(ws), ws.numel(), _stream())
-    _check("gdr2_fwd_chunked", st)
+                                                             device=dev)
+    _run("gdr2_fwd_chunked", dev, lib.gdr2_fwd_chunked_ex, B, T, H, dk, dv, dt, bits,
+         _pro(prologue), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w), _ptr(S0),
+         _ptr(o), _ptr(ST), _ptr(ws), ws.numel())
     return o, ST, ws
 
 
@@ -206,10 +262,15 @@ def gdr2_bwd_chunked(q, k, v, log_alpha, b, w, dO, fwd_ws, dS_T=None, want_dS0=T
     Returns a dict dq, dk, dv, dlog_alpha, db, dw, dS0 (None if not wanted).  ``prologue`` must
     be the one the forward ran with."""
     lib = load_library()
-    _contig(q, k, v, log_alpha, b, w, dO, dS_T)
+    dev, bits = _inputs(q, k, v, log_alpha, b, w, 4)
     B, T, H, dk, dv = _shapes(q, v)
     dt = _dtype(q)
-    dev = q.device
+    _need("dO", dO, (B, T, H, dv), q.dtype, dev)
+    _need("dS_T", dS_T, (B, H, dk, dv), torch.float32, dev, optional=True)
+    _ws("fwd_ws", fwd_ws, dev)
+    if workspace is not None:
+        _ws("workspace", workspace, dev)
+    _on_gpu(dev)
     g = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
              dlog_alpha=torch.empty_like(log_alpha), db=torch.empty_like(b),
              dw=torch.empty_like(w),
@@ -217,113 +278,150 @@ def gdr2_bwd_chunked(q, k, v, log_alpha, b, w, dO, fwd_ws, dS_T=None, want_dS0=T
     need = lib.gdr2_bwd_workspace_bytes(B, T, H, dk, dv, dt)
     ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8,
                                                              device=dev)
-    st = lib.gdr2_bwd_chunked_ex(B, T, H, dk, dv, dt, gate_bits(q, log_alpha, b, w),
-                                 _pro(prologue), _ptr(q),
-                                 _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w),
-                                 _ptr(fwd_ws), fwd_ws.numel(), _ptr(dO), _ptr(dS_T),
-                                 _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]),
-                                 _ptr(g["dlog_alpha"]), _ptr(g["db"]), _ptr(g["dw"]),
-                                 _ptr(g["dS0"]), _ptr(ws), ws.numel(), _stream())
-    _check("gdr2_bwd_chunked", st)
+    _run("gdr2_bwd_chunked", dev, lib.gdr2_bwd_chunked_ex, B, T, H, dk, dv, dt, bits,
+         _pro(prologue), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w),
+         _ptr(fwd_ws), fwd_ws.numel(), _ptr(dO), _ptr(dS_T), _ptr(g["dq"]), _ptr(g["dk"]),
+         _ptr(g["dv"]), _ptr(g["dlog_alpha"]), _ptr(g["db"]), _ptr(g["dw"]), _ptr(g["dS0"]),
+         _ptr(ws), ws.numel())
     return g
 
 
+def _dt_code(dtype):
+    if dtype not in _DT:
+        raise TypeError(f"unsupported dtype {dtype}")
+    return _DT[dtype]
+
+
 def fwd_workspace_bytes(B, T, H, dk, dv, dtype):
-    return load_library().gdr2_fwd_workspace_bytes(B, T, H, dk, dv, _DT[dtype])
+    return load_library().gdr2_fwd_workspace_bytes(B, T, H, dk, dv, _dt_code(dtype))
 
 
 def bwd_workspace_bytes(B, T, H, dk, dv, dtype):
-    return load_library().gdr2_bwd_workspace_bytes(B, T, H, dk, dv, _DT[dtype])
+    return load_library().gdr2_bwd_workspace_bytes(B, T, H, dk, dv, _dt_code(dtype))
 
 
 def gdr2_fwd_factors(q, k, v, log_alpha, b, w, ws, prologue=None):
     """Stage 1 of the forward: per-chunk WY factors into ``ws`` (uint8 device tensor)."""
+    lib = load_library()
+    dev, bits = _inputs(q, k, v, log_alpha, b, w, 4)
     B, T, H, dk, dv = _shapes(q, v)
-    st = load_library().gdr2_fwd_factors_ex(B, T, H, dk, dv, _dtype(q),
-                                            gate_bits(q, log_alpha, b, w), _pro(prologue),
-                                            _ptr(q), _ptr(k),
-                                            _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w), _ptr(ws),
-                                            ws.numel(), _stream())
-    _check("gdr2_fwd_factors", st)
+    _ws("ws", ws, dev)
+    _on_gpu(dev)
+    _run("gdr2_fwd_factors", dev, lib.gdr2_fwd_factors_ex, B, T, H, dk, dv, _dtype(q), bits,
+         _pro(prologue), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w), _ptr(ws),
+         ws.numel())
 
 
 def gdr2_fwd_carry(B, T, H, dk, dv, dtype, ws, o, S0=None, S_T=None):
     """Stage 2 of the forward: o (and S_T) from the factors in ``ws``."""
-    st = load_library().gdr2_fwd_carry(B, T, H, dk, dv, _DT[dtype], _ptr(S0), _ptr(o), _ptr(S_T),
-                                       _ptr(ws), ws.numel(), _stream())
-    _check("gdr2_fwd_carry", st)
+    lib = load_library()
+    dt = _dt_code(dtype)
+    if not isinstance(o, torch.Tensor):
+        raise TypeError("o must be a tensor")
+    dev = o.device
+    _need("o", o, (B, T, H, dv), dtype, dev)
+    _need("S0", S0, (B, H, dk, dv), torch.float32, dev, optional=True)
+    _need("S_T", S_T, (B, H, dk, dv), torch.float32, dev, optional=True)
+    _ws("ws", ws, dev)
+    _on_gpu(dev)
+    _run("gdr2_fwd_carry", dev, lib.gdr2_fwd_carry, B, T, H, dk, dv, dt, _ptr(S0), _ptr(o),
+         _ptr(S_T), _ptr(ws), ws.numel())
 
 
 def gdr2_bwd_state(B, T, H, dk, dv, dtype, fwd_ws, dO, bws, dS_T=None, dS0=None):
     """Stage 1 of the backward: per-chunk state gradients into ``bws`` and dS0."""
-    st = load_library().gdr2_bwd_state(B, T, H, dk, dv, _DT[dtype], _ptr(fwd_ws), fwd_ws.numel(),
-                                       _ptr(dO), _ptr(dS_T), _ptr(dS0), _ptr(bws), bws.numel(),
-                                       _stream())
-    _check("gdr2_bwd_state", st)
+    lib = load_library()
+    dt = _dt_code(dtype)
+    if not isinstance(dO, torch.Tensor):
+        raise TypeError("dO must be a tensor")
+    dev = dO.device
+    _need("dO", dO, (B, T, H, dv), dtype, dev)
+    _need("dS_T", dS_T, (B, H, dk, dv), torch.float32, dev, optional=True)
+    _need("dS0", dS0, (B, H, dk, dv), torch.float32, dev, optional=True)
+    _ws("fwd_ws", fwd_ws, dev)
+    _ws("bws", bws, dev)
+    _on_gpu(dev)
+    _run("gdr2_bwd_state", dev, lib.gdr2_bwd_state, B, T, H, dk, dv, dt, _ptr(fwd_ws),
+         fwd_ws.numel(), _ptr(dO), _ptr(dS_T), _ptr(dS0), _ptr(bws), bws.numel())
 
 
 def gdr2_bwd_grads(q, k, v, log_alpha, b, w, fwd_ws, dO, bws, g, prologue=None):
     """Stage 2 of the backward: fills g["dq"], g["dk"], g["dv"], g["dlog_alpha"], g["db"],
-    g["dw"] (preallocated)."""
+    g["dw"] (preallocated, each in the shape and dtype of its input)."""
+    lib = load_library()
+    dev, bits = _inputs(q, k, v, log_alpha, b, w, 4)
     B, T, H, dk, dv = _shapes(q, v)
-    st = load_library().gdr2_bwd_grads_ex(B, T, H, dk, dv, _dtype(q),
-                                          gate_bits(q, log_alpha, b, w), _pro(prologue),
-                                          _ptr(q), _ptr(k),
-                                          _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w),
-                                          _ptr(fwd_ws), fwd_ws.numel(), _ptr(dO), _ptr(g["dq"]),
-                                          _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["dlog_alpha"]),
-                                          _ptr(g["db"]), _ptr(g["dw"]), _ptr(bws), bws.numel(),
-                                          _stream())
-    _check("gdr2_bwd_grads", st)
+    _need("dO", dO, (B, T, H, dv), q.dtype, dev)
+    for name, like in (("dq", q), ("dk", k), ("dv", v), ("dlog_alpha", log_alpha), ("db", b),
+                       ("dw", w)):
+        _need(name, g.get(name), like.shape, like.dtype, dev)
+    _ws("fwd_ws", fwd_ws, dev)
+    _ws("bws", bws, dev)
+    _on_gpu(dev)
+    _run("gdr2_bwd_grads", dev, lib.gdr2_bwd_grads_ex, B, T, H, dk, dv, _dtype(q), bits,
+         _pro(prologue), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w),
+         _ptr(fwd_ws), fwd_ws.numel(), _ptr(dO), _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]),
+         _ptr(g["dlog_alpha"]), _ptr(g["db"]), _ptr(g["dw"]), _ptr(bws), bws.numel())
 
 
 def gdr2_decode_step(q, k, v, log_alpha, b, w, S_in=None, S_out=None, prologue=None):
     """One decode token for [N, H] sequences-heads.  S_out defaults to S_in (in place) or a new
     buffer.  Returns (o, S_out)."""
     lib = load_library()
-    _contig(q, k, v, log_alpha, b, w, S_in, S_out)
+    dev, bits = _inputs(q, k, v, log_alpha, b, w, 3)
     N, H, dk = q.shape
     dv = v.shape[-1]
     dt = _dtype(q)
+    _need("S_in", S_in, (N, H, dk, dv), torch.float32, dev, optional=True)
+    _need("S_out", S_out, (N, H, dk, dv), torch.float32, dev, optional=True)
+    _on_gpu(dev)
     if S_out is None:
         S_out = S_in if S_in is not None else torch.empty((N, H, dk, dv), dtype=torch.float32,
-                                                          device=q.device)
-    o = torch.empty((N, H, dv), dtype=q.dtype, device=q.device)
-    st = lib.gdr2_decode_step_ex(N, H, dk, dv, dt, gate_bits(q, log_alpha, b, w),
-                                 _pro(prologue), _ptr(q),
-                                 _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w), _ptr(S_in),
-                                 _ptr(S_out), _ptr(o), _stream())
-    _check("gdr2_decode_step", st)
+                                                          device=dev)
+    o = torch.empty((N, H, dv), dtype=q.dtype, device=dev)
+    _run("gdr2_decode_step", dev, lib.gdr2_decode_step_ex, N, H, dk, dv, dt, bits, _pro(prologue),
+         _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w), _ptr(S_in), _ptr(S_out),
+         _ptr(o))
     return o, S_out
+
+
+def _gate_inputs(o, g, weight):
+    if not isinstance(o, torch.Tensor) or o.dim() < 1:
+        raise ValueError("o must be a tensor [..., dv]")
+    _dtype(o)
+    dev, dv = o.device, o.shape[-1]
+    _need("o", o, o.shape, o.dtype, dev)
+    _need("g", g, o.shape, o.dtype, dev)
+    _need("weight", weight, (dv,), torch.float32, dev)
+    return dev, (o.numel() // dv if dv else 0), dv
 
 
 def gdr2_out_gate_fwd(o, g, weight, eps=1e-6):
     """Output epilogue y = RMSNorm(o) * weight * silu(g) over the last (d_v) axis of o [..., dv];
     g has o's shape and dtype, weight is [dv] fp32.  Returns y."""
     lib = load_library()
-    _contig(o, g, weight)
-    dv = o.shape[-1]
-    rows = o.numel() // dv
+    dev, rows, dv = _gate_inputs(o, g, weight)
+    _on_gpu(dev)
     y = torch.empty_like(o)
-    st = lib.gdr2_out_gate_fwd(rows, dv, _dtype(o), _ptr(o), _ptr(g), _ptr(weight), float(eps),
-                               _ptr(y), _stream())
-    _check("gdr2_out_gate_fwd", st)
+    _run("gdr2_out_gate_fwd", dev, lib.gdr2_out_gate_fwd, rows, dv, _dtype(o), _ptr(o), _ptr(g),
+         _ptr(weight), float(eps), _ptr(y))
     return y
 
 
 def gdr2_out_gate_bwd(o, g, weight, dy, eps=1e-6, workspace=None):
     """Backward of gdr2_out_gate_fwd for the cotangent dy.  Returns dict do, dg, dweight."""
     lib = load_library()
-    _contig(o, g, weight, dy)
-    dv = o.shape[-1]
-    rows = o.numel() // dv
+    dev, rows, dv = _gate_inputs(o, g, weight)
+    _need("dy", dy, o.shape, o.dtype, dev)
+    if workspace is not None:
+        _ws("workspace", workspace, dev)
+    _on_gpu(dev)
     need = lib.gdr2_out_gate_bwd_workspace_bytes(rows, dv)
     ws = workspace if workspace is not None else torch.empty(max(need, 16), dtype=torch.uint8,
-                                                             device=o.device)
+                                                             device=dev)
     out = dict(do=torch.empty_like(o), dg=torch.empty_like(g),
-               dweight=torch.empty((dv,), dtype=torch.float32, device=o.device))
-    st = lib.gdr2_out_gate_bwd(rows, dv, _dtype(o), _ptr(o), _ptr(g), _ptr(weight), float(eps),
-                               _ptr(dy), _ptr(out["do"]), _ptr(out["dg"]), _ptr(out["dweight"]),
-                               _ptr(ws), ws.numel(), _stream())
-    _check("gdr2_out_gate_bwd", st)
+               dweight=torch.empty((dv,), dtype=torch.float32, device=dev))
+    _run("gdr2_out_gate_bwd", dev, lib.gdr2_out_gate_bwd, rows, dv, _dtype(o), _ptr(o), _ptr(g),
+         _ptr(weight), float(eps), _ptr(dy), _ptr(out["do"]), _ptr(out["dg"]),
+         _ptr(out["dweight"]), _ptr(ws), ws.numel())
     return out
