@@ -1017,7 +1017,14 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
         }
     }
 
-    // ---- epilogue: lane = token r, channels 16 (ibase + ib) + 4g + e
+    // ---- epilogue: lane = token r, channels 16 (ibase + ib) + 4g + e.  With the fused prologue,
+    //      dq and dk wait for their row dot products (a cross-wave exchange); rather than as a burst
+    //      of 4-element pieces at the end, they and db then go through the (now dead) Gram tiles in
+    //      LDS and reach HBM as whole token rows of 16-byte lane stores
+    if constexpr (PRO) lds_barrier();
+    OT* const stq = sm.u.g.Kb;  // prologue staging [r][i], pitch PK: dq, dk, db
+    OT* const stk = sm.u.g.Qb;
+    OT* const stb = sm.u.g.Eb;
     f32x4 dG[NIBH];
     const long orow = row * DK;
     float db_acc = 0.f;
@@ -1053,11 +1060,11 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
             Dk += (k4[0] * dkv[0] + k4[1] * dkv[1]) + (k4[2] * dkv[2] + k4[3] * dkv[3]);
         }
         if (b_sc) db_acc += (dbv[0] + dbv[1]) + (dbv[2] + dbv[3]);
-        if (valid) {
-            if (!PRO) {
-                store4((OT*)p.dq + orow + i0, dqv);
-                store4((OT*)p.dk + orow + i0, dkv);
-            }
+        if constexpr (PRO) {
+            if (!b_sc) store4(stb + r * PK + i0, dbv);
+        } else if (valid) {
+            store4((OT*)p.dq + orow + i0, dqv);
+            store4((OT*)p.dk + orow + i0, dkv);
             if (!b_sc) store4((OT*)p.db + orow + i0, dbv);
         }
         if (rl == 0) {
@@ -1088,15 +1095,15 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
         }
     }
     lds_barrier();
-    if (PRO && valid) {  // d q_pre = r_q (dq - qhat (qhat . dq)), the same for k
+    if (PRO) {  // d q_pre = r_q (dq - qhat (qhat . dq)), the same for k
         const float Dqt = sm.nrm[0][r][2] + sm.nrm[1][r][2], Dkt = sm.nrm[0][r][3] + sm.nrm[1][r][3];
 #pragma unroll
         for (int ib = 0; ib < NIBH; ++ib) {
             const int i0 = 16 * (ibase + ib) + 4 * g;
             f32x4 q4, k4, b4;
             act(ib, q4, k4, b4, false);
-            store4((OT*)p.dq + orow + i0, rq * (dqs[PRO ? ib : 0] - q4 * Dqt));
-            store4((OT*)p.dk + orow + i0, rk * (dks[PRO ? ib : 0] - k4 * Dkt));
+            store4(stq + r * PK + i0, rq * (dqs[PRO ? ib : 0] - q4 * Dqt));
+            store4(stk + r * PK + i0, rk * (dks[PRO ? ib : 0] - k4 * Dkt));
         }
     }
     float dl_acc = 0.f;
@@ -1131,6 +1138,21 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
         if (a_sc) {
             const float d = sm.gred[0][r][2] + sm.gred[1][r][2];
             p.dla[row] = PRO ? d * (-p.pro.decay_scale * sigmoid_f(p.la[row])) : d;
+        }
+    }
+    // ---- prologue: the staged dq, dk, db rows to HBM
+    if constexpr (PRO) {
+        lds_barrier();
+        constexpr int UPR = DK / VEC;  // 16-byte units per token row
+#pragma unroll
+        for (int m = 0; m < C * UPR / NT; ++m) {
+            const int x = tid + m * NT, rr = x / UPR, i = (x % UPR) * VEC;
+            if ((long)c * C + rr < T) {
+                const long o = (tok0 + (long)rr * H) * DK + i;
+                *(i32x4*)((OT*)p.dq + o) = *(const i32x4*)(stq + rr * PK + i);
+                *(i32x4*)((OT*)p.dk + o) = *(const i32x4*)(stk + rr * PK + i);
+                if (!b_sc) *(i32x4*)((OT*)p.db + o) = *(const i32x4*)(stb + rr * PK + i);
+            }
         }
     }
 }
