@@ -877,6 +877,25 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
 #pragma unroll
         for (int ib = 0; ib < NIBH; ++ib) *(f32x4*)(&sm.tot[R][16 * (ibase + ib) + 4 * g]) = sc[ib];
     }
+    // fused prologue: this wave's half of the squared row norms of q and k (lanes 16g + rl of both
+    // channel halves), exchanged through the same barrier as the block totals
+    if (PRO) {
+        float sq = 0.f, sk = 0.f;
+#pragma unroll
+        for (int ib = 0; ib < NIBH; ++ib) {
+            const f32x4 q4 = RW::widen(qr[ib]), k4 = RW::widen(kr[ib]);
+            sq += (q4[0] * q4[0] + q4[1] * q4[1]) + (q4[2] * q4[2] + q4[3] * q4[3]);
+            sk += (k4[0] * k4[0] + k4[1] * k4[1]) + (k4[2] * k4[2] + k4[3] * k4[3]);
+        }
+        sq += shfl_xor_l(sq, 16, l);
+        sq += shfl_xor_l(sq, 32, l);
+        sk += shfl_xor_l(sk, 16, l);
+        sk += shfl_xor_l(sk, 32, l);
+        if (g == 0) {
+            sm.nrm[half][r][0] = sq;
+            sm.nrm[half][r][1] = sk;
+        }
+    }
     lds_barrier();
     for (int chn = tid; chn < DK; chn += NT) {
         float refs[4], run = 0.f;
@@ -894,25 +913,9 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
         }
     }
 
-    // ---- fused prologue: the row norms of q and k (lanes 16g + rl of both channel halves)
+    // ---- fused prologue: the reciprocal row norms of q and k
     float rq = 1.f, rk = 1.f;
     if (PRO) {
-        float sq = 0.f, sk = 0.f;
-#pragma unroll
-        for (int ib = 0; ib < NIBH; ++ib) {
-            const f32x4 q4 = RW::widen(qr[ib]), k4 = RW::widen(kr[ib]);
-            sq += (q4[0] * q4[0] + q4[1] * q4[1]) + (q4[2] * q4[2] + q4[3] * q4[3]);
-            sk += (k4[0] * k4[0] + k4[1] * k4[1]) + (k4[2] * k4[2] + k4[3] * k4[3]);
-        }
-        sq += shfl_xor_l(sq, 16, l);
-        sq += shfl_xor_l(sq, 32, l);
-        sk += shfl_xor_l(sk, 16, l);
-        sk += shfl_xor_l(sk, 32, l);
-        if (g == 0) {
-            sm.nrm[half][r][0] = sq;
-            sm.nrm[half][r][1] = sk;
-        }
-        lds_barrier();
         rq = rsqrtf(sm.nrm[0][r][0] + sm.nrm[1][r][0] + p.pro.norm_eps);
         rk = rsqrtf(sm.nrm[0][r][1] + sm.nrm[1][r][1] + p.pro.norm_eps);
     }
