@@ -463,7 +463,8 @@ gdr2_status gdr2_decode_step(int64_t N, int64_t H, int64_t dk, int64_t dv, gdr2_
 // ------------------------------------------------------------------ output epilogue
 static gdr2_status check_epi(int64_t rows, int64_t dv, gdr2_dtype dt, float eps) {
     if (dt != GDR2_F32 && dt != GDR2_BF16) return GDR2_E_DTYPE;
-    if (rows < 0 || dv < 0 || rows > ((int64_t)1 << 40)) return GDR2_E_SHAPE;
+    // one workgroup per 128 rows, and a launch takes at most 2^31 - 1 workgroups
+    if (rows < 0 || dv < 0 || rows > ((int64_t)1 << 37)) return GDR2_E_SHAPE;
     if (!dims_ok(dv)) return GDR2_E_UNSUPPORTED;
     if (!(eps > 0.f) || !(eps < 1e30f)) return GDR2_E_VALUE;
     return GDR2_OK;

@@ -258,7 +258,8 @@ gdr2_status gdr2_decode_step_ex(int64_t N, int64_t H, int64_t dk, int64_t dv, gd
  *   eps             > 0, finite (else GDR2_E_VALUE)
  * The backward takes dy [rows][dv] and writes do_, dg [rows][dv] (dtype) and dweight [dv] (fp32,
  * the sum over all rows, reduced in a fixed order: bitwise deterministic); it needs a workspace
- * of gdr2_out_gate_bwd_workspace_bytes(rows, dv) bytes.  dv in {64, 128}.
+ * of gdr2_out_gate_bwd_workspace_bytes(rows, dv) bytes.  dv in {64, 128}; rows <= 2^37
+ * (GDR2_E_SHAPE above).
  */
 gdr2_status gdr2_out_gate_fwd(int64_t rows, int64_t dv, gdr2_dtype dtype, const void* o,
                               const void* g, const float* weight, float eps, void* y,

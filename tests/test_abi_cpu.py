@@ -183,6 +183,8 @@ def test_out_gate_rejects_before_launch():
     assert fwd(o=0x10008) == E_ALIGN
     assert fwd(y=0x30000) == E_ALIAS
     assert fwd(rows=0) == OK
+    # one workgroup per 128 rows: beyond 2^37 rows the grid would not fit a launch
+    assert fwd(rows=-1) == E_SHAPE and fwd(rows=(1 << 37) + 1) == E_SHAPE
     assert lib.gdr2_out_gate_bwd_workspace_bytes(1 << 18, 128) > 0
     bwd = lambda ws=0x400000, wsb=1 << 30, dw=0x200000: lib.gdr2_out_gate_bwd(
         64, 128, 1, P(0x10000), P(0x30000), P(0x50000), F(1e-6), P(0x60000), P(0x70000),
