@@ -206,7 +206,7 @@ def main():
         args.warmup, args.steps, args.decode_steps = 1, 1, 1
         args.no_cpu_baseline = True
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for "
+        print(f"bench.py runs on one GPU only: the library has no multi-GPU path (asked for "
               f"--gpus {args.gpus})", file=sys.stderr)
         sys.exit(2)
 
