@@ -85,3 +85,33 @@ def test_decode_on_offset_buffers_and_side_stream():
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     assert torch.equal(o, o_ref) and torch.equal(S, S_ref)
+
+
+@pytest.mark.parametrize("B,T,H,d,pro", [(4, 4096, 16, 128, False), (2, 200, 3, 64, False),
+                                         (2, 130, 4, 128, True)])
+def test_phase_entry_points_match_the_chunked_calls(B, T, H, d, pro):
+    """The four phase entry points in the sequence the benchmark times (factors, carry, state
+    gradient, chunk gradients) give bitwise the results of gdr2_fwd_chunked + gdr2_bwd_chunked,
+    at the full 1.3B-layer size too, so the timed path is the one the parity tests check."""
+    import gated_delta_rule_gdr_amd as g2
+    prologue = g2.Prologue(0.1, 1e-6) if pro else None
+    x = _gpu(layer_inputs(B, T, H, d, d, dtype="bf16", seed=64, s0_std=0.05, dST=True, raw=pro))
+    announce(f"phase entry points vs chunked calls B={B} T={T} H={H} d={d} prologue={pro}")
+    args = [x[n] for n in NAMES]
+    o, ST, fws = gdr2_fwd_chunked(*args, S0=x["S0"], prologue=prologue)
+    ref = gdr2_bwd_chunked(*args, x["dO"], fws, dS_T=x["dST"], prologue=prologue)
+    bf = torch.bfloat16
+    fws2 = torch.empty(g2.fwd_workspace_bytes(B, T, H, d, d, bf), dtype=torch.uint8, device=DEV)
+    bws2 = torch.empty(g2.bwd_workspace_bytes(B, T, H, d, d, bf), dtype=torch.uint8, device=DEV)
+    o2, ST2 = torch.empty_like(o), torch.empty_like(ST)
+    dS0 = torch.empty_like(ref["dS0"])
+    gr = {n: torch.empty_like(x[s]) for n, s in (("dq", "q"), ("dk", "k"), ("dv", "v"),
+                                                ("dlog_alpha", "log_alpha"), ("db", "b"), ("dw", "w"))}
+    g2.gdr2_fwd_factors(*args, fws2, prologue=prologue)
+    g2.gdr2_fwd_carry(B, T, H, d, d, bf, fws2, o2, S0=x["S0"], S_T=ST2)
+    g2.gdr2_bwd_state(B, T, H, d, d, bf, fws2, x["dO"], bws2, dS_T=x["dST"], dS0=dS0)
+    g2.gdr2_bwd_grads(*args, fws2, x["dO"], bws2, gr, prologue=prologue)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(ST, ST2) and torch.equal(ref["dS0"], dS0)
+    for n in GRADS[:-1]:
+        assert torch.equal(ref[n], gr[n]), n
