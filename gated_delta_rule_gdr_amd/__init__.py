@@ -8,6 +8,8 @@ fails to load, every call raises.
 Entry points (same names as the C ABI):
   gdr2_fwd_chunked(q, k, v, log_alpha, b, w, S0=None, want_final_state=True) -> (o, S_T, fwd_ws)
   gdr2_bwd_chunked(q, k, v, log_alpha, b, w, dO, fwd_ws, dS_T=None, want_dS0=True) -> grads
+  gdr2_fwd_infer(q, k, v, log_alpha, b, w, S0=None, want_final_state=True) -> (o, S_T)
+  gdr2_bwd_chunked_recompute(q, k, v, log_alpha, b, w, dO, S0=None, dS_T=None) -> grads
   gdr2_decode_step(q, k, v, log_alpha, b, w, S_in=None, S_out=None)
   gdr2_out_gate_fwd(o, g, weight, eps) / gdr2_out_gate_bwd(o, g, weight, dy, eps)
 Each of b, w and log_alpha may be channel-wise ([..., d]) or a scalar per head (the token shape of
@@ -25,6 +27,8 @@ import os
 import torch
 
 __all__ = ["gdr2_fwd_chunked", "gdr2_bwd_chunked", "gdr2_decode_step", "gdr2_fwd_factors",
+           "gdr2_fwd_infer", "gdr2_bwd_chunked_recompute", "fwd_infer_workspace_bytes",
+           "bwd_recompute_workspace_bytes",
            "gdr2_fwd_carry", "gdr2_bwd_state", "gdr2_bwd_grads", "fwd_workspace_bytes",
            "bwd_workspace_bytes", "library_path", "load_library", "Gdr2Error", "CHUNK", "gate_bits",
            "ERASE_SCALAR", "WRITE_SCALAR", "DECAY_SCALAR", "gdr2_out_gate_fwd", "gdr2_out_gate_bwd",
@@ -92,6 +96,19 @@ def load_library():
     lib.gdr2_bwd_grads.argtypes = ([I64] * 5 + [ctypes.c_int] + [P] * 7 + [SZ] + [P] * 8
                                    + [SZ, P])
     lib.gdr2_bwd_grads.restype = ctypes.c_int
+    lib.gdr2_fwd_infer_ex.argtypes = [I64] * 5 + [ctypes.c_int, ctypes.c_uint, P] + [P] * 10 + [SZ, P]
+    lib.gdr2_fwd_infer_ex.restype = ctypes.c_int
+    lib.gdr2_fwd_infer.argtypes = [I64] * 5 + [ctypes.c_int] + [P] * 10 + [SZ, P]
+    lib.gdr2_fwd_infer.restype = ctypes.c_int
+    lib.gdr2_bwd_chunked_recompute.argtypes = [I64] * 5 + [ctypes.c_int] + [P] * 17 + [SZ, P]
+    lib.gdr2_bwd_chunked_recompute.restype = ctypes.c_int
+    lib.gdr2_fwd_infer_workspace_bytes.argtypes = [I64] * 5 + [ctypes.c_int]
+    lib.gdr2_fwd_infer_workspace_bytes.restype = SZ
+    lib.gdr2_bwd_chunked_recompute_ex.argtypes = ([I64] * 5 + [ctypes.c_int, ctypes.c_uint, P]
+                                                  + [P] * 17 + [SZ, P])
+    lib.gdr2_bwd_chunked_recompute_ex.restype = ctypes.c_int
+    lib.gdr2_bwd_recompute_workspace_bytes.argtypes = [I64] * 5 + [ctypes.c_int]
+    lib.gdr2_bwd_recompute_workspace_bytes.restype = SZ
     lib.gdr2_decode_step.argtypes = [I64] * 4 + [ctypes.c_int] + [P] * 10
     lib.gdr2_decode_step.restype = ctypes.c_int
     U = ctypes.c_uint
@@ -286,6 +303,59 @@ def gdr2_bwd_chunked(q, k, v, log_alpha, b, w, dO, fwd_ws, dS_T=None, want_dS0=T
     return g
 
 
+def gdr2_fwd_infer(q, k, v, log_alpha, b, w, S0=None, want_final_state=True, workspace=None,
+                   prologue=None):
+    """Forward-only chunked forward (no backward follows): o and S_T bit for bit as
+    gdr2_fwd_chunked, without the chunk-entry states the backward would read.  Returns
+    (o, S_T or None).  ``workspace`` may pass a preallocated uint8 device tensor of at least
+    fwd_infer_workspace_bytes(...) bytes."""
+    lib = load_library()
+    dev, bits = _inputs(q, k, v, log_alpha, b, w, 4)
+    B, T, H, dk, dv = _shapes(q, v)
+    dt = _dtype(q)
+    _need("S0", S0, (B, H, dk, dv), torch.float32, dev, optional=True)
+    if workspace is not None:
+        _ws("workspace", workspace, dev)
+    _on_gpu(dev)
+    o = torch.empty((B, T, H, dv), dtype=q.dtype, device=dev)
+    ST = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev) if want_final_state else None
+    need = lib.gdr2_fwd_infer_workspace_bytes(B, T, H, dk, dv, dt)
+    ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8,
+                                                             device=dev)
+    _run("gdr2_fwd_infer", dev, lib.gdr2_fwd_infer_ex, B, T, H, dk, dv, dt, bits, _pro(prologue),
+         _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w), _ptr(S0), _ptr(o), _ptr(ST),
+         _ptr(ws), ws.numel())
+    return o, ST
+
+
+def gdr2_bwd_chunked_recompute(q, k, v, log_alpha, b, w, dO, S0=None, dS_T=None, want_dS0=True,
+                               workspace=None, prologue=None):
+    """Gate-aware backward without a forward workspace: the factors and chunk-entry states are
+    recomputed from the inputs and S0.  Returns the dict of gdr2_bwd_chunked (bitwise equal)."""
+    lib = load_library()
+    dev, bits = _inputs(q, k, v, log_alpha, b, w, 4)
+    B, T, H, dk, dv = _shapes(q, v)
+    dt = _dtype(q)
+    _need("dO", dO, (B, T, H, dv), q.dtype, dev)
+    _need("S0", S0, (B, H, dk, dv), torch.float32, dev, optional=True)
+    _need("dS_T", dS_T, (B, H, dk, dv), torch.float32, dev, optional=True)
+    if workspace is not None:
+        _ws("workspace", workspace, dev)
+    _on_gpu(dev)
+    g = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
+             dlog_alpha=torch.empty_like(log_alpha), db=torch.empty_like(b),
+             dw=torch.empty_like(w),
+             dS0=torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev) if want_dS0 else None)
+    need = lib.gdr2_bwd_recompute_workspace_bytes(B, T, H, dk, dv, dt)
+    ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8,
+                                                             device=dev)
+    _run("gdr2_bwd_chunked_recompute", dev, lib.gdr2_bwd_chunked_recompute_ex, B, T, H, dk, dv, dt,
+         bits, _pro(prologue), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w),
+         _ptr(S0), _ptr(dO), _ptr(dS_T), _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]),
+         _ptr(g["dlog_alpha"]), _ptr(g["db"]), _ptr(g["dw"]), _ptr(g["dS0"]), _ptr(ws), ws.numel())
+    return g
+
+
 def _dt_code(dtype):
     if dtype not in _DT:
         raise TypeError(f"unsupported dtype {dtype}")
@@ -298,6 +368,14 @@ def fwd_workspace_bytes(B, T, H, dk, dv, dtype):
 
 def bwd_workspace_bytes(B, T, H, dk, dv, dtype):
     return load_library().gdr2_bwd_workspace_bytes(B, T, H, dk, dv, _dt_code(dtype))
+
+
+def fwd_infer_workspace_bytes(B, T, H, dk, dv, dtype):
+    return load_library().gdr2_fwd_infer_workspace_bytes(B, T, H, dk, dv, _dt_code(dtype))
+
+
+def bwd_recompute_workspace_bytes(B, T, H, dk, dv, dtype):
+    return load_library().gdr2_bwd_recompute_workspace_bytes(B, T, H, dk, dv, _dt_code(dtype))
 
 
 def gdr2_fwd_factors(q, k, v, log_alpha, b, w, ws, prologue=None):

@@ -15,7 +15,7 @@ OBJ_DIR = os.path.join(PKG, "_build")
 SOURCES = ["gdr2_api.hip", "gdr2_fwd.hip", "gdr2_bwd.hip", "gdr2_decode.hip", "gdr2_epilogue.hip"]
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-I", INCLUDE, "-I", CSRC,
-         "-Wall", "-Wno-unused-function",
+         "-Wall", "-Wshadow", "-Wno-unused-function",
          # packed fp32 VALU forms are kept out of the device code
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 

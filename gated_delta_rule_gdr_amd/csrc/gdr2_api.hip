@@ -36,6 +36,9 @@ bool any_alias(const Range* outs, int no, const Range* ins, int ni) {
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// a * b <= lim for a, b >= 0, decided without forming a product that could overflow
+bool prod_le(int64_t a, int64_t b, int64_t lim) { return a == 0 || b <= lim / a; }
+
 bool gates_ok(unsigned gates) { return (gates & ~7u) == 0; }
 
 bool prologue_ok(const gdr2_prologue* pro) {
@@ -125,28 +128,44 @@ static gdr2::WyBufs wy_bufs(const FwdWs& L, void* base) {
     return w;
 }
 
-size_t gdr2_fwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
-                                gdr2_dtype dt) {
-    if (B < 0 || T < 0 || H < 0 || dk < 0 || dv < 0 || gdr2_dtype_size(dt) == 0) return 0;
-    return fwd_ws_layout(B, T, H, dk, dv, dt).total;
-}
-
-size_t gdr2_bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
-                                gdr2_dtype dt) {
-    if (B < 0 || T < 0 || H < 0 || dk < 0 || dv < 0 || gdr2_dtype_size(dt) == 0) return 0;
-    return round_up((size_t)B * H * gdr2_num_chunks(T) * dk * dv * gdr2_dtype_size(dt), 256);
-}
-
-// Shared shape / dtype checks of the two chunked passes.
+// Shared shape / dtype checks of the two chunked passes.  Each bound is tested before any product
+// that depends on it, so that no size arithmetic here or in the layouts below can overflow: after
+// it, B*H <= 2^30 chains, B*H*ceil(T/64) <= 2^30 chunk-heads, B*T*H <= 2^50 head-tokens.
 static gdr2_status check_chunked(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
                                  gdr2_dtype dt) {
     if (dt != GDR2_F32 && dt != GDR2_BF16) return GDR2_E_DTYPE;
     if (B < 0 || T < 0 || H < 0 || dk < 0 || dv < 0) return GDR2_E_SHAPE;
     if (!dims_ok(dk) || !dims_ok(dv)) return GDR2_E_UNSUPPORTED;
-    if (B * H * (dv / 16) > (int64_t)1 << 30) return GDR2_E_SHAPE;
-    if (B * H * gdr2_num_chunks(T) > (int64_t)1 << 30) return GDR2_E_SHAPE;
-    if (T > ((int64_t)1 << 40) || B * T * H > ((int64_t)1 << 50)) return GDR2_E_SHAPE;
+    if (T > ((int64_t)1 << 40) || !prod_le(B, H, (int64_t)1 << 30)) return GDR2_E_SHAPE;
+    const int64_t BH = B * H;
+    if (!prod_le(BH, dv / 16, (int64_t)1 << 30)) return GDR2_E_SHAPE;
+    if (!prod_le(BH, gdr2_num_chunks(T), (int64_t)1 << 30)) return GDR2_E_SHAPE;
+    if (!prod_le(BH, T, (int64_t)1 << 50)) return GDR2_E_SHAPE;
     return GDR2_OK;
+}
+
+size_t gdr2_fwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                                gdr2_dtype dt) {
+    if (check_chunked(B, T, H, dk, dv, dt) != GDR2_OK) return 0;
+    return fwd_ws_layout(B, T, H, dk, dv, dt).total;
+}
+
+size_t gdr2_fwd_infer_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                                      gdr2_dtype dt) {
+    if (check_chunked(B, T, H, dk, dv, dt) != GDR2_OK) return 0;
+    return fwd_ws_layout(B, T, H, dk, dv, dt).states;  // the factors: everything before the states
+}
+
+size_t gdr2_bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                                gdr2_dtype dt) {
+    if (check_chunked(B, T, H, dk, dv, dt) != GDR2_OK) return 0;
+    return round_up((size_t)B * H * gdr2_num_chunks(T) * dk * dv * gdr2_dtype_size(dt), 256);
+}
+
+size_t gdr2_bwd_recompute_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                                          gdr2_dtype dt) {
+    if (check_chunked(B, T, H, dk, dv, dt) != GDR2_OK) return 0;
+    return fwd_ws_layout(B, T, H, dk, dv, dt).total + gdr2_bwd_workspace_bytes(B, T, H, dk, dv, dt);
 }
 
 static gdr2::FwdParams fwd_params(int64_t B, int64_t T, int64_t H, int64_t dv, const void* q,
@@ -175,11 +194,13 @@ static gdr2::FwdParams fwd_params(int64_t B, int64_t T, int64_t H, int64_t dv, c
 
 // Validation shared by the forward phases.  `need_inputs` / `need_out` select which pointers a
 // phase requires; every pointer given must be aligned and every output disjoint from the inputs.
+// `with_states`: the workspace also holds the chunk-entry states (training); without them it holds
+// only the factors (forward-only calls).
 static gdr2_status check_fwd(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
                              gdr2_dtype dt, const void* q, const void* k, const void* v,
                              const float* la, const void* b, const void* w, const float* S0,
                              void* o, float* S_T, void* ws, size_t ws_bytes, bool need_inputs,
-                             bool need_out, unsigned gates = 0) {
+                             bool need_out, unsigned gates = 0, bool with_states = true) {
     gdr2_status st = check_chunked(B, T, H, dk, dv, dt);
     if (st != GDR2_OK) return st;
     if (!gates_ok(gates)) return GDR2_E_UNSUPPORTED;
@@ -190,14 +211,15 @@ static gdr2_status check_fwd(int64_t B, int64_t T, int64_t H, int64_t dk, int64_
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return GDR2_E_ALIGN;
     const FwdWs L = fwd_ws_layout(B, T, H, dk, dv, dt);
-    if (have_tokens && (!ws || ws_bytes < L.total)) return GDR2_E_WORKSPACE;
+    const size_t ws_need = with_states ? L.total : L.states;
+    if (have_tokens && (!ws || ws_bytes < ws_need)) return GDR2_E_WORKSPACE;
     const size_t es = gdr2_dtype_size(dt);
     const size_t nk = (size_t)B * T * H * dk, nv = (size_t)B * T * H * dv;
     const size_t ns = (size_t)B * H * dk * dv;
     const GateSizes gs = gate_sizes(gates, (size_t)B * T * H, dk, dv);
     const Range ins[] = {{q, nk * es}, {k, nk * es}, {v, nv * es}, {la, gs.na * 4},
                          {b, gs.nb * es}, {w, gs.nw * es}, {S0, ns * 4}};
-    const Range outs[] = {{o, nv * es}, {S_T, ns * 4}, {ws, have_tokens ? L.total : 0}};
+    const Range outs[] = {{o, nv * es}, {S_T, ns * 4}, {ws, have_tokens ? ws_need : 0}};
     if (any_alias(outs, 3, ins, 7)) return GDR2_E_ALIAS;
     return GDR2_OK;
 }
@@ -230,19 +252,60 @@ gdr2_status gdr2_fwd_factors(int64_t B, int64_t T, int64_t H, int64_t dk, int64_
                                workspace, workspace_bytes, stream);
 }
 
+// The state carry after validation: o (may be NULL), S_T (may be NULL) and, with `with_states`,
+// the chunk-entry states in the workspace's states region.
+static gdr2_status launch_carry(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                                gdr2_dtype dt, const float* S0, void* o, float* S_T,
+                                void* workspace, bool with_states, void* stream) {
+    const int bf = dt == GDR2_BF16;
+    const FwdWs L = fwd_ws_layout(B, T, H, dk, dv, dt);
+    const int dvs = gdr2::carry_slice_width(bf, (int)dk, (int)dv, B * H);
+    gdr2::FwdParams p = fwd_params(B, T, H, dv, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                   nullptr, S0, o, S_T, L, T > 0 ? workspace : nullptr, dvs);
+    if (!with_states) p.states = nullptr;
+    hipError_t e = gdr2::carry_fwd_dispatch(bf, (int)dk, dvs, p, (hipStream_t)stream);
+    return e == hipSuccess ? GDR2_OK : GDR2_E_HIP;
+}
+
 gdr2_status gdr2_fwd_carry(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
                            gdr2_dtype dt, const float* S0, void* o, float* S_T, void* workspace,
                            size_t workspace_bytes, void* stream) {
     gdr2_status st = check_fwd(B, T, H, dk, dv, dt, nullptr, nullptr, nullptr, nullptr, nullptr,
                                nullptr, S0, o, S_T, workspace, workspace_bytes, false, true);
     if (st != GDR2_OK || B == 0 || H == 0) return st;
-    const int bf = dt == GDR2_BF16;
-    const FwdWs L = fwd_ws_layout(B, T, H, dk, dv, dt);
-    const int dvs = gdr2::carry_slice_width(bf, (int)dk, (int)dv, B * H);
-    gdr2::FwdParams p = fwd_params(B, T, H, dv, nullptr, nullptr, nullptr, nullptr, nullptr,
-                                   nullptr, S0, o, S_T, L, T > 0 ? workspace : nullptr, dvs);
-    hipError_t e = gdr2::carry_fwd_dispatch(bf, (int)dk, dvs, p, (hipStream_t)stream);
-    return e == hipSuccess ? GDR2_OK : GDR2_E_HIP;
+    return launch_carry(B, T, H, dk, dv, dt, S0, o, S_T, workspace, true, stream);
+}
+
+gdr2_status gdr2_fwd_infer_ex(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                              gdr2_dtype dt, unsigned gates, const gdr2_prologue* pro,
+                              const void* q, const void* k, const void* v,
+                              const float* log_alpha, const void* b, const void* w,
+                              const float* S0, void* o, float* S_T, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+    gdr2_status st = check_fwd(B, T, H, dk, dv, dt, q, k, v, log_alpha, b, w, S0, o, S_T,
+                               workspace, workspace_bytes, true, true, gates, false);
+    if (st == GDR2_OK && !prologue_ok(pro)) st = GDR2_E_VALUE;
+    if (st != GDR2_OK || B == 0 || H == 0) return st;
+    if (T > 0) {
+        const FwdWs L = fwd_ws_layout(B, T, H, dk, dv, dt);
+        gdr2::FwdParams p = fwd_params(B, T, H, dv, q, k, v, log_alpha, b, w, nullptr, nullptr,
+                                       nullptr, L, workspace, 16, gates);
+        p.states = nullptr;
+        p.prologue = pro != nullptr;
+        p.pro = prologue_of(pro);
+        if (gdr2::wy_dispatch(dt == GDR2_BF16, (int)dk, (int)dv, p, (hipStream_t)stream) != hipSuccess)
+            return GDR2_E_HIP;
+    }
+    return launch_carry(B, T, H, dk, dv, dt, S0, o, S_T, workspace, false, stream);
+}
+
+gdr2_status gdr2_fwd_infer(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                           gdr2_dtype dt, const void* q, const void* k, const void* v,
+                           const float* log_alpha, const void* b, const void* w, const float* S0,
+                           void* o, float* S_T, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+    return gdr2_fwd_infer_ex(B, T, H, dk, dv, dt, 0u, nullptr, q, k, v, log_alpha, b, w, S0, o,
+                             S_T, workspace, workspace_bytes, stream);
 }
 
 gdr2_status gdr2_fwd_chunked_ex(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
@@ -416,6 +479,76 @@ gdr2_status gdr2_bwd_chunked(int64_t B, int64_t T, int64_t H, int64_t dk, int64_
                                dlog_alpha, db, dw, dS0, workspace, workspace_bytes, stream);
 }
 
+gdr2_status gdr2_bwd_chunked_recompute_ex(int64_t B, int64_t T, int64_t H, int64_t dk,
+                                          int64_t dv, gdr2_dtype dt, unsigned gates,
+                                          const gdr2_prologue* pro, const void* q, const void* k,
+                                          const void* v, const float* log_alpha, const void* b,
+                                          const void* w, const float* S0, const void* dO,
+                                          const float* dS_T, void* dq, void* dk_, void* dv_,
+                                          float* dlog_alpha, void* db, void* dw, float* dS0,
+                                          void* workspace, size_t workspace_bytes, void* stream) {
+    gdr2_status st = check_chunked(B, T, H, dk, dv, dt);
+    if (st != GDR2_OK) return st;
+    if (!gates_ok(gates)) return GDR2_E_UNSUPPORTED;
+    if (!prologue_ok(pro)) return GDR2_E_VALUE;
+    const bool have_tokens = B > 0 && H > 0 && T > 0;
+    if (have_tokens && (!q || !k || !v || !log_alpha || !b || !w || !dO)) return GDR2_E_NULL;
+    if (have_tokens && (!dq || !dk_ || !dv_ || !dlog_alpha || !db || !dw)) return GDR2_E_NULL;
+    const void* ptrs[] = {q, k, v, log_alpha, b, w, S0, dO, dS_T, dq, dk_, dv_, dlog_alpha, db, dw,
+                          dS0, workspace};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return GDR2_E_ALIGN;
+    const FwdWs L = fwd_ws_layout(B, T, H, dk, dv, dt);
+    const size_t need = gdr2_bwd_recompute_workspace_bytes(B, T, H, dk, dv, dt);
+    if (have_tokens && (!workspace || workspace_bytes < need)) return GDR2_E_WORKSPACE;
+    const size_t es = gdr2_dtype_size(dt);
+    const size_t nk = (size_t)B * T * H * dk, nv = (size_t)B * T * H * dv;
+    const size_t ns = (size_t)B * H * dk * dv;
+    const GateSizes gs = gate_sizes(gates, (size_t)B * T * H, dk, dv);
+    const Range ins[] = {{q, nk * es},      {k, nk * es},      {v, nv * es},
+                         {log_alpha, gs.na * 4}, {b, gs.nb * es}, {w, gs.nw * es},
+                         {S0, ns * 4},      {dO, nv * es},     {dS_T, ns * 4}};
+    const Range outs[] = {{dq, nk * es},     {dk_, nk * es},    {dv_, nv * es},
+                          {dlog_alpha, gs.na * 4}, {db, gs.nb * es}, {dw, gs.nw * es},
+                          {dS0, ns * 4},     {workspace, have_tokens ? need : 0}};
+    if (any_alias(outs, 8, ins, 9)) return GDR2_E_ALIAS;
+    if (B == 0 || H == 0) return GDR2_OK;
+    // the forward's factors and chunk-entry states into the first part of the workspace (o and
+    // S_T are not formed), then the backward with the rest of it
+    char* fws = (char*)workspace;
+    char* bws = have_tokens ? fws + L.total : nullptr;
+    const size_t bws_bytes = have_tokens ? workspace_bytes - L.total : 0;
+    if (T > 0) {
+        gdr2::FwdParams p = fwd_params(B, T, H, dv, q, k, v, log_alpha, b, w, nullptr, nullptr,
+                                       nullptr, L, fws, 16, gates);
+        p.prologue = pro != nullptr;
+        p.pro = prologue_of(pro);
+        if (gdr2::wy_dispatch(dt == GDR2_BF16, (int)dk, (int)dv, p, (hipStream_t)stream) != hipSuccess)
+            return GDR2_E_HIP;
+        st = launch_carry(B, T, H, dk, dv, dt, S0, nullptr, nullptr, fws, true, stream);
+        if (st != GDR2_OK) return st;
+    }
+    if (T == 0) {  // nothing to recompute: the state gradient passes straight through
+        return gdr2_bwd_state(B, T, H, dk, dv, dt, nullptr, 0, dO, dS_T, dS0, nullptr, 0, stream);
+    }
+    st = gdr2_bwd_state(B, T, H, dk, dv, dt, fws, L.total, dO, dS_T, dS0, bws, bws_bytes, stream);
+    if (st != GDR2_OK) return st;
+    return gdr2_bwd_grads_ex(B, T, H, dk, dv, dt, gates, pro, q, k, v, log_alpha, b, w, fws,
+                             L.total, dO, dq, dk_, dv_, dlog_alpha, db, dw, bws, bws_bytes, stream);
+}
+
+gdr2_status gdr2_bwd_chunked_recompute(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                                       gdr2_dtype dt, const void* q, const void* k, const void* v,
+                                       const float* log_alpha, const void* b, const void* w,
+                                       const float* S0, const void* dO, const float* dS_T,
+                                       void* dq, void* dk_, void* dv_, float* dlog_alpha,
+                                       void* db, void* dw, float* dS0, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+    return gdr2_bwd_chunked_recompute_ex(B, T, H, dk, dv, dt, 0u, nullptr, q, k, v, log_alpha, b,
+                                         w, S0, dO, dS_T, dq, dk_, dv_, dlog_alpha, db, dw, dS0,
+                                         workspace, workspace_bytes, stream);
+}
+
 gdr2_status gdr2_decode_step_ex(int64_t N, int64_t H, int64_t dk, int64_t dv, gdr2_dtype dt,
                                 unsigned gates, const gdr2_prologue* pro, const void* q,
                                 const void* k, const void* v,
@@ -425,7 +558,7 @@ gdr2_status gdr2_decode_step_ex(int64_t N, int64_t H, int64_t dk, int64_t dv, gd
     if (N < 0 || H < 0 || dk < 0 || dv < 0) return GDR2_E_SHAPE;
     if (!dims_ok(dk) || !dims_ok(dv) || !gates_ok(gates)) return GDR2_E_UNSUPPORTED;
     if (!prologue_ok(pro)) return GDR2_E_VALUE;
-    if (N * H > ((int64_t)1 << 31) - 1) return GDR2_E_SHAPE;
+    if (!prod_le(N, H, ((int64_t)1 << 31) - 1)) return GDR2_E_SHAPE;
     if (N == 0 || H == 0) return GDR2_OK;
     if (!q || !k || !v || !log_alpha || !b || !w || !S_out || !o) return GDR2_E_NULL;
     const void* ptrs[] = {q, k, v, log_alpha, b, w, S_in, S_out, o};

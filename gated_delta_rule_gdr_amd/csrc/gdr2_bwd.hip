@@ -528,6 +528,8 @@ struct alignas(16) BgSmem {
     float ctab[6][DK];
     float gRt[4][DK];
     float hRt[4][DK];
+    float hRl[4][DK];   // G_C - ref_R (deep-decay path)
+    int deep[8];        // per wave: its block decays by more than exp(-kDeepDecay) on a channel
     float r6[DK];
     float r6x[4][DK];  // R6 partials: [lane group l / 16][channel]
     float btot[4][DK];
@@ -873,6 +875,15 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
     for (int ib = 0; ib < NIBH; ++ib)
 #pragma unroll
         for (int e = 0; e < 4; ++e) sc[ib][e] = row_scan16(valid ? sc[ib][e] : 0.f);
+    {   // does this block decay past the fast path's range on one of this wave's channels?
+        float mn = 0.f;
+#pragma unroll
+        for (int ib = 0; ib < NIBH; ++ib)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) mn = fminf(mn, sc[ib][e]);
+        const unsigned long long dp = __ballot(rl == 15 && mn < -kDeepDecay);
+        if (l == 0) sm.deep[w] = dp != 0ull;
+    }
     if (rl == 15) {
 #pragma unroll
         for (int ib = 0; ib < NIBH; ++ib) *(f32x4*)(&sm.tot[R][16 * (ibase + ib) + 4 * g]) = sc[ib];
@@ -908,10 +919,18 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
         for (int Rp = 0; Rp < 4; ++Rp) {
             sm.gRt[Rp][chn] = __expf(refs[Rp]);
             sm.hRt[Rp][chn] = __expf(run - refs[Rp]);
+            sm.hRl[Rp][chn] = run - refs[Rp];
 #pragma unroll
             for (int S = 0; S < Rp; ++S) sm.ctab[Rp * (Rp - 1) / 2 + S][chn] = __expf(refs[Rp] - refs[S]);
         }
     }
+    // deep-decay path for the whole chunk (uniform over the workgroup): right Gram factors
+    // referenced to the end of their block and the diagonal blocks entry by entry, so that no
+    // factor exceeds one
+    bool deep = false;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) deep |= sm.deep[x] != 0;
+    deep = __builtin_amdgcn_readfirstlane(deep);
 
     // ---- fused prologue: the reciprocal row norms of q and k
     float rq = 1.f, rk = 1.f;
@@ -946,9 +965,11 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
         f32x4 q4, k4, b4;
         act(ib, q4, k4, b4, true);
         f32x4 eb, qb, kb;
+        const f32x4 tb = *(const f32x4*)(&sm.tot[R][i0]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const float x = valid ? __expf(sc[ib][e]) : 0.f, y = valid ? __expf(-sc[ib][e]) : 0.f;
+            const float x = valid ? __expf(sc[ib][e]) : 0.f;
+            const float y = valid ? __expf(deep ? tb[e] - sc[ib][e] : -sc[ib][e]) : 0.f;
             eb[e] = b4[e] * k4[e] * x;
             qb[e] = q4[e] * x;
             kb[e] = k4[e] * y;
@@ -989,11 +1010,15 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
         const typename FR::t bP = FR::tr(sm.u.g.dPT, PC, k0, 16 * R, l);  // dP (col r, k = s)
         const typename FR::t bA = FR::tr(sm.u.g.dAT, PC, k0, 16 * R, l);  // dA (col r, k = s)
         const int Sl = (k0 + KPL * g) / 16;                             // token block of this lane's k
+        // cross-block factor exp(ref_R - ref_S), or exp(ref_R - ref_{S+1}) on the deep-decay path
+        // (whose diagonal block is added entry by entry in the epilogue)
+        const int cS = deep ? Sl + 1 : Sl;
 #pragma unroll
         for (int ib = 0; ib < NIBH; ++ib) {
             const int i0 = 16 * (ibase + ib);
             typename FR::t a = FR::tr(sm.u.g.Kb, PK, k0, i0, l);            // Kbar^T (row i, k = s)
-            if (Sl < R) a = FR::scale(a, sm.ctab[R * (R - 1) / 2 + Sl][i0 + rl]);
+            if (deep && Sl == R) a = FR::scale(a, 0.f);
+            else if (cS < R) a = FR::scale(a, sm.ctab[R * (R - 1) / 2 + cS][i0 + rl]);
             MM::mma(A1[ib], a, bP);
             MM::mma(A2[ib], a, bA);
         }
@@ -1005,13 +1030,17 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
         const typename FR::t bP = FR::kc(sm.u.g.dPT, PC, 16 * R, k0, l);  // dP (col s, k = r)
         const typename FR::t bA = FR::kc(sm.u.g.dAT, PC, 16 * R, k0, l);  // dA (col s, k = r)
         const int Rl = (k0 + KPL * g) / 16;
+        const int cR = deep ? R + 1 : R;  // as above, with this wave's block on the right
 #pragma unroll
         for (int ib = 0; ib < NIBH; ++ib) {
             const int i0 = 16 * (ibase + ib);
             typename FR::t aq = FR::tr(sm.u.g.Qb, PK, k0, i0, l);           // Qbar^T (row i, k = r)
             typename FR::t ae = FR::tr(sm.u.g.Eb, PK, k0, i0, l);           // Ebar^T (row i, k = r)
-            if (Rl > R) {
-                const float cs = sm.ctab[Rl * (Rl - 1) / 2 + R][i0 + rl];
+            if (deep && Rl == R) {
+                aq = FR::scale(aq, 0.f);
+                ae = FR::scale(ae, 0.f);
+            } else if (Rl > cR) {
+                const float cs = sm.ctab[Rl * (Rl - 1) / 2 + cR][i0 + rl];
                 aq = FR::scale(aq, cs);
                 ae = FR::scale(ae, cs);
             }
@@ -1040,14 +1069,53 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
         act(ib, q4, k4, b4, false);
         if (!valid) q4 = k4 = b4 = f32x4{0.f, 0.f, 0.f, 0.f};
         const f32x4 hr = *(const f32x4*)(&sm.hRt[R][i0]);
+        // deep-decay path: the diagonal-block terms, each with exp(G_r - G_s) <= 1 (s <= r, same
+        // block), from lane 16 g + s%16 of this wave (same channels); right factors from single
+        // exponents
+        f32x4 xq = {0.f, 0.f, 0.f, 0.f}, xe = xq, xkb = xq, yd = xq, yt = xq;  // diagonal-block terms
+        if (deep) {
+            const f32x4 e4 = b4 * k4, l4 = sc[ib];
+            const OT* dPT = sm.u.g.dPT;
+            const OT* dAT = sm.u.g.dAT;
+#pragma unroll 1
+            for (int u = 0; u < 16; ++u) {
+                const int src = 16 * g + u, s_ = 16 * R + u;
+                const float pRT = to_f(dPT[s_ * PC + r]), aRT = to_f(dAT[s_ * PC + r]);  // dP_rs, dA_rs
+                const float pTR = to_f(dPT[r * PC + s_]), aTR = to_f(dAT[r * PC + s_]);  // dP_sr, dA_sr
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float ks_ = __shfl(k4[e], src), qs_ = __shfl(q4[e], src);
+                    const float es_ = __shfl(e4[e], src), ls_ = __shfl(l4[e], src);
+                    const float flo = __expf(fminf(l4[e] - ls_, 0.f)), fhi = __expf(fminf(ls_ - l4[e], 0.f));
+                    xq[e] += pRT * ks_ * flo;
+                    xe[e] += aRT * ks_ * flo;
+                    xkb[e] += (pTR * qs_ + aTR * es_) * fhi;
+                }
+            }
+            const f32x4 tb = *(const f32x4*)(&sm.tot[R][i0]), hl = *(const f32x4*)(&sm.hRl[R][i0]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                yd[e] = __expf(tb[e] - sc[ib][e]);
+                yt[e] = __expf(hl[e] - sc[ib][e]);
+            }
+        }
         f32x4 dqv, dkv, dbv, kdk;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const float x = __expf(sc[ib][e]), y = __expf(-sc[ib][e]);
-            const float dq = x * A1[ib][e];
-            const float de = x * A2[ib][e];
-            const float dkb = y * A4[ib][e];
-            const float dkt = hr[e] * y * A3[ib][e];
+            const float x = __expf(sc[ib][e]);
+            float dq, de, dkb, dkt;
+            if (deep) {
+                dq = x * A1[ib][e] + xq[e];
+                de = x * A2[ib][e] + xe[e];
+                dkb = yd[e] * A4[ib][e] + xkb[e];
+                dkt = yt[e] * A3[ib][e];
+            } else {
+                const float y = __expf(-sc[ib][e]);
+                dq = x * A1[ib][e];
+                de = x * A2[ib][e];
+                dkb = y * A4[ib][e];
+                dkt = hr[e] * y * A3[ib][e];
+            }
             dqv[e] = dq;
             dkv[e] = dkb + dkt + b4[e] * de;
             dbv[e] = k4[e] * de;

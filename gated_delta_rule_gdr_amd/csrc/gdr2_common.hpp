@@ -326,6 +326,34 @@ __device__ __forceinline__ float softplus_f(float x) {
     return x > 20.f ? x : 0.69314718f * __builtin_amdgcn_logf(1.f + __expf(x));
 }
 
+// ------------------------------------------------------------------ deep-decay support
+// The Gram products split exp(G_r - G_s) (r >= s, G = in-chunk cumsum of log alpha) into a left
+// factor exp(G_r - ref) <= 1 and a right factor exp(ref - G_s) >= 1 around one reference per
+// 16-token block.  The right factor is bounded by the decay across the block; when any channel of
+// a chunk decays by more than exp(-kDeepDecay) across one block, the kernels take a second path in
+// which every factor is <= 1 (right operands referenced to the end of their block, diagonal
+// blocks computed entry by entry).  exp(kDeepDecay) leaves a 1e12 margin below the fp32 range for
+// the products and sums the fast path forms from such factors.
+constexpr float kDeepDecay = 60.f;
+
+// Compile-time loop: f(IC<i>{}) for i = B .. E-1 (for builtins that need constant operands).
+template <int V> struct IC { static constexpr int value = V; };
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(IC<B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
+// Value of lane T of the caller's DPP row (lanes 16(l/16) .. +15): DPP row_newbcast.
+template <int T>
+__device__ __forceinline__ float row_bcast(float x) {
+    static_assert(T >= 0 && T < 16, "lane of a 16-lane row");
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x150 + T,
+                                                                 0xf, 0xf, false));
+}
+
 // Inclusive suffix sum over the 16 lanes of each DPP row: lane i gets the sum of lanes i..15.
 __device__ __forceinline__ float row_rscan16(float x) {
     int v = __builtin_bit_cast(int, x);

@@ -46,6 +46,8 @@ struct alignas(16) WySmem {
     float ctab[6][DK];           // exp(ref_R - ref_S), R > S
     float gRt[4][DK];            // exp(ref_R)
     float hRt[4][DK];            // exp(G_C - ref_R)
+    float hRl[4][DK];            // G_C - ref_R (deep-decay path)
+    int deep[4];                 // block R decays by more than exp(-kDeepDecay) on some channel
 };
 
 // Location of block T_RS of the inverse inside Af: diagonal blocks overwrite A_RR, off-diagonal
@@ -290,11 +292,20 @@ __device__ __forceinline__ void wy_factors(WySmem<OT, DK, DV>& sm, const WyChunk
     // in-block inclusive cumsum of log alpha (16 lanes = 16 rows) and the block totals
 #pragma unroll
     for (int n = 0; n < NCH; ++n) lv[n] = row_scan16(lv[n]);  // lv := G_r - ref_R
+    {   // does this block decay past the fast path's range on some channel?
+        float mn = 0.f;
+#pragma unroll
+        for (int n = 0; n < NCH; ++n) mn = fminf(mn, lv[n]);
+        const unsigned long long deep = __ballot(rl == 15 && mn < -kDeepDecay);
+        if (l == 0) sm.deep[R] = deep != 0ull;
+    }
     if (rl == 15) {
 #pragma unroll
         for (int n = 0; n < NCH; ++n) sm.tot[R][(n / KPL) * KS + KPL * g + n % KPL] = lv[n];
     }
     lds_barrier();
+    // deep-decay path for the whole chunk (uniform over the workgroup)
+    const bool deep = __builtin_amdgcn_readfirstlane((sm.deep[0] | sm.deep[1] | sm.deep[2] | sm.deep[3]) != 0);
 
     // per-channel tables from the block totals: ref_R = sum of earlier block totals,
     // exp(ref_R), exp(G_C - ref_R), exp(ref_R - ref_S) (R > S) and gamma = exp(G_C)
@@ -309,10 +320,50 @@ __device__ __forceinline__ void wy_factors(WySmem<OT, DK, DV>& sm, const WyChunk
         for (int Rp = 0; Rp < 4; ++Rp) {
             sm.gRt[Rp][chn] = __expf(refs[Rp]);
             sm.hRt[Rp][chn] = __expf(run - refs[Rp]);
+            sm.hRl[Rp][chn] = run - refs[Rp];
 #pragma unroll
             for (int S = 0; S < Rp; ++S) sm.ctab[Rp * (Rp - 1) / 2 + S][chn] = __expf(refs[Rp] - refs[S]);
         }
         wy.gam[cix * DK + chn] = __expf(run);
+    }
+    OT* const pt = (OT*)wy.P + cix * C * C;  // P tile, fragment order
+    if (deep) {
+        // Diagonal 16 x 16 blocks of A and P entry by entry, each term carrying
+        // exp(G_r - G_s) <= 1 (s <= r, same block): row s's k and G come from lane 16 g + s%16,
+        // which holds the same channels.  A rolled loop over s keeps the register footprint of
+        // this rare path small.
+        float myA[4] = {0.f, 0.f, 0.f, 0.f}, myP[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+        for (int t = 0; t < 16; ++t) {
+            const int src = 16 * g + t;
+            float a = 0.f, pp = 0.f;
+#pragma unroll
+            for (int n = 0; n < NCH; ++n) {
+                const float ks_ = __shfl(kv[n], src), ls_ = __shfl(lv[n], src);
+                const float f = ks_ * __expf(fminf(lv[n] - ls_, 0.f));
+                a += bv[n] * kv[n] * f;
+                pp += qv[n] * f;
+            }
+            a += __shfl_xor(a, 16);
+            a += __shfl_xor(a, 32);
+            pp += __shfl_xor(pp, 16);
+            pp += __shfl_xor(pp, 32);
+            const bool mine = (t >> 2) == g;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                myA[e] = (mine && (t & 3) == e) ? a : myA[e];
+                myP[e] = (mine && (t & 3) == e) ? pp : myP[e];
+            }
+        }
+        f32x4 am, pm;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int s_ = 16 * R + 4 * g + e;
+            am[e] = s_ < r ? myA[e] : 0.f;
+            pm[e] = s_ <= r ? myP[e] : 0.f;
+        }
+        *(f32x4*)(sm.Af + r * PAF + 16 * R + 4 * g) = am;
+        store4(pt + FLay<OT>::off(r, 16 * R + 4 * g, C), pm);
     }
     lds_barrier();
 
@@ -325,18 +376,38 @@ __device__ __forceinline__ void wy_factors(WySmem<OT, DK, DV>& sm, const WyChunk
     for (int ks = 0; ks < NKS; ++ks) {
         float ebk[KPL], qbk[KPL], kbk[KPL], qg[KPL], kt[KPL], gR[KPL], hR[KPL];
         load_lane_f32<OT>(sm.gRt[R], ks, g, gR);
-        load_lane_f32<OT>(sm.hRt[R], ks, g, hR);
+        if (deep) {
+            // right Gram operand referenced to the end of its block, exp(G_end - G_s) <= 1, and
+            // Ktilde = k exp(G_C - G_r) from one exponent
+            float tb[KPL], hl[KPL];
+            load_lane_f32<OT>(sm.tot[R], ks, g, tb);
+            load_lane_f32<OT>(sm.hRl[R], ks, g, hl);
 #pragma unroll
-        for (int j = 0; j < KPL; ++j) {
-            const int n = ks * KPL + j;
-            const float x = __expf(lv[n]), y = __expf(-lv[n]);
-            const float e = bv[n] * kv[n];
-            ebk[j] = e * x;
-            qbk[j] = qv[n] * x;
-            kbk[j] = kv[n] * y;
-            eg[n] = ebk[j] * gR[j];
-            qg[j] = qbk[j] * gR[j];
-            kt[j] = kbk[j] * hR[j];
+            for (int j = 0; j < KPL; ++j) {
+                const int n = ks * KPL + j;
+                const float x = __expf(lv[n]);
+                const float e = bv[n] * kv[n];
+                ebk[j] = e * x;
+                qbk[j] = qv[n] * x;
+                kbk[j] = kv[n] * __expf(tb[j] - lv[n]);
+                eg[n] = ebk[j] * gR[j];
+                qg[j] = qbk[j] * gR[j];
+                kt[j] = kv[n] * __expf(hl[j] - lv[n]);
+            }
+        } else {
+            load_lane_f32<OT>(sm.hRt[R], ks, g, hR);
+#pragma unroll
+            for (int j = 0; j < KPL; ++j) {
+                const int n = ks * KPL + j;
+                const float x = __expf(lv[n]), y = __expf(-lv[n]);
+                const float e = bv[n] * kv[n];
+                ebk[j] = e * x;
+                qbk[j] = qv[n] * x;
+                kbk[j] = kv[n] * y;
+                eg[n] = ebk[j] * gR[j];
+                qg[j] = qbk[j] * gR[j];
+                kt[j] = kbk[j] * hR[j];
+            }
         }
         Ef[ks] = FR::from_f32(ebk);
         Qf[ks] = FR::from_f32(qbk);
@@ -346,9 +417,11 @@ __device__ __forceinline__ void wy_factors(WySmem<OT, DK, DV>& sm, const WyChunk
     }
     lds_barrier();
 
-    // A^T and P^T blocks (S, R) for S <= R: rows s of block S, columns r of block R.
+    // A^T and P^T blocks (S, R) for S <= R: rows s of block S, columns r of block R.  The right
+    // operand of block S carries exp(ref_S - G_s) with the cross-block factor exp(ref_R - ref_S)
+    // -- on the deep-decay path exp(G_end(S) - G_s) with exp(ref_R - ref_{S+1}) (the diagonal
+    // blocks are done then).
     {
-        OT* pt = (OT*)wy.P + cix * C * C;  // fragment order
 #pragma unroll
         for (int S = 0; S < 4; ++S) {
             if (S > R) {
@@ -356,12 +429,14 @@ __device__ __forceinline__ void wy_factors(WySmem<OT, DK, DV>& sm, const WyChunk
                 store4(d, f32x4{0.f, 0.f, 0.f, 0.f});
                 continue;
             }
+            if (deep && S == R) continue;
             f32x4 aA = {0.f, 0.f, 0.f, 0.f}, aP = {0.f, 0.f, 0.f, 0.f};
-            const float* cs = S < R ? sm.ctab[R * (R - 1) / 2 + S] : nullptr;
+            const int cS = deep ? S + 1 : S;  // ctab column of the cross-block factor
+            const float* cs = cS < R ? sm.ctab[R * (R - 1) / 2 + cS] : nullptr;
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
                 typename FR::t a = FR::kc(sm.u.Kb, PK, 16 * S, ks * KS);
-                if (S < R) a = FR::scale(a, cs + ks * KS + KPL * g);
+                if (cS < R) a = FR::scale(a, cs + ks * KS + KPL * g);
                 MM::mma(aA, a, Ef[ks]);
                 MM::mma(aP, a, Qf[ks]);
             }

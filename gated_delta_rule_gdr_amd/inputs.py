@@ -133,15 +133,38 @@ def decode_inputs(step, N=DECODE["N"], H=DECODE["H"], dk=DECODE["dk"], dv=DECODE
 
 
 def strong_decay_inputs(B, T, H, dk, dv, dtype="bf16", seed=0, device="cpu", floor=-6.0):
-    """Layer inputs whose key channels decay fast: log alpha = floor * U(0.5, 1) on a random half of
-    the channels (e.g. alpha ~ 0.0025..0.05 per token at floor = -6), the usual recipe elsewhere.
-    Exercises the range of the chunked factorisation far beyond the default recipe."""
+    """Layer inputs whose key channels decay fast: log alpha = floor * U(0.5, 1) per token on a
+    random half of the channels (at floor = -5: log alpha in [-5, -2.5], alpha ~ 0.007..0.08 per
+    token), the usual recipe elsewhere."""
     x = layer_inputs(B, T, H, dk, dv, dtype=dtype, seed=seed, device=device)
     g = torch.Generator(device=device)
     g.manual_seed(int(seed) + 77)
     mask = torch.rand((B, 1, H, dk), generator=g, device=device) < 0.5
     fast = floor * (0.5 + 0.5 * torch.rand((B, T, H, dk), generator=g, device=device))
     x["log_alpha"] = torch.where(mask, fast, x["log_alpha"]).contiguous()
+    return x
+
+
+def deep_decay_inputs(B, T, H, dk, dv, dtype="bf16", seed=0, device="cpu", lo=-30.0, hi=-6.0,
+                      deep_chunk=1, s0_std=0.05, dST=True):
+    """Layer inputs with decays far past exp(-88) across a 16-token block.  Per (batch, head,
+    channel) a random half of the key channels draws log alpha ~ U(lo, hi) per token, a random
+    quarter has no decay at all (log alpha = 0 exactly) and the rest keep the usual recipe; every
+    channel of chunk ``deep_chunk`` (tokens 64 c .. 64 c + 63, if the sequence has them) decays by
+    log alpha = -20 per token.  alpha may be any value in (0, 1] (the decay is a per-channel
+    diagonal gate; ainews.random.gg article on Gated DeltaNet-2, section "Gated Delta Rule-2: two
+    gates instead of one"), so a trained decay branch can saturate like this."""
+    x = layer_inputs(B, T, H, dk, dv, dtype=dtype, seed=seed, device=device, s0_std=s0_std, dST=dST)
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed) + 91)
+    u = torch.rand((B, 1, H, dk), generator=g, device=device)
+    fast = lo + (hi - lo) * torch.rand((B, T, H, dk), generator=g, device=device)
+    la = torch.where(u < 0.5, fast, x["log_alpha"])
+    la = torch.where(u > 0.75, torch.zeros_like(la), la)
+    c0, c1 = 64 * deep_chunk, min(64 * deep_chunk + 64, T)
+    if c0 < T:
+        la[:, c0:c1] = -20.0
+    x["log_alpha"] = la.contiguous()
     return x
 
 

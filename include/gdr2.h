@@ -28,7 +28,15 @@
  *     surface at the caller's next synchronisation.  No C++ exception crosses this ABI.
  *   - Results are bitwise deterministic run to run (no floating-point atomics).
  *   - Supported sizes: d_k, d_v in {64, 128}.
- *     B, H >= 1 and T >= 0 (T = 0 produces no tokens; S_T then equals S0).
+ *     B, H >= 1 and T >= 0 (T = 0 produces no tokens; S_T then equals S0).  Larger problems are
+ *     rejected with GDR2_E_SHAPE before any size arithmetic could overflow: the chunked passes
+ *     accept T <= 2^40, B*H*ceil(T/64) <= 2^30 and B*T*H <= 2^50; decode accepts N*H < 2^31.
+ *   - Decay range: any finite log_alpha <= 0, i.e. any alpha in (0, 1] per channel and token (the
+ *     decay is a channel-wise diagonal gate: ainews.random.gg article, section "Gated Delta
+ *     Rule-2: two gates instead of one").  The chunked kernels fold the cumulative decay into
+ *     factors referenced to 16-token blocks; a chunk in which some channel decays by more than
+ *     exp(-60) across one block takes a second path whose factors are all <= 1, so no decay drives
+ *     a factor out of the fp32 range.
  */
 #ifndef GDR2_H
 #define GDR2_H
@@ -40,7 +48,7 @@
 extern "C" {
 #endif
 
-#define GDR2_ABI_VERSION 2
+#define GDR2_ABI_VERSION 3
 #define GDR2_CHUNK 64 /* tokens per chunk of the chunked passes */
 
 typedef enum gdr2_status {
@@ -126,9 +134,35 @@ gdr2_status gdr2_fwd_chunked(int64_t B, int64_t T, int64_t H, int64_t dk, int64_
                              size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace gdr2_fwd_chunked needs (per token and head about
- * (4*dk + 2*64 + dv) elements of dtype plus the chunk-entry states, dk*dv/64 elements). */
+ * (4*dk + 2*64 + dv) elements of dtype plus the chunk-entry states, dk*dv/64 elements); 0 for
+ * sizes the chunked passes reject. */
 size_t gdr2_fwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
                                 gdr2_dtype dtype);
+
+/*
+ * Forward-only chunked forward (inference prefill, where no backward follows): o and S_T exactly
+ * as gdr2_fwd_chunked computes them, bit for bit, without storing the chunk-entry states that only
+ * the backward reads (dk*dv/64 elements of dtype per token and head: 512 bytes at d = 128 in
+ * bf16).  Its workspace holds only the per-chunk factors -- gdr2_fwd_infer_workspace_bytes() bytes,
+ * device memory, no larger than the training forward's -- and cannot be passed to
+ * gdr2_bwd_chunked; gdr2_bwd_chunked_recompute is the backward that needs no forward workspace.
+ * Arguments and errors as gdr2_fwd_chunked(_ex).  Decoding can continue from S_T
+ * (gdr2_decode_step), constant-memory decoding after the prefill (forum summary on zhichai.net,
+ * section "The Memory Dilemma").
+ */
+size_t gdr2_fwd_infer_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                                      gdr2_dtype dtype);
+gdr2_status gdr2_fwd_infer(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                           gdr2_dtype dtype, const void* q, const void* k, const void* v,
+                           const float* log_alpha, const void* b, const void* w, const float* S0,
+                           void* o, float* S_T, void* workspace, size_t workspace_bytes,
+                           void* stream);
+gdr2_status gdr2_fwd_infer_ex(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                              gdr2_dtype dtype, unsigned gates, const gdr2_prologue* pro,
+                              const void* q, const void* k, const void* v,
+                              const float* log_alpha, const void* b, const void* w,
+                              const float* S0, void* o, float* S_T, void* workspace,
+                              size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace gdr2_bwd_chunked needs (the per-chunk state gradients). */
 size_t gdr2_bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
@@ -158,6 +192,34 @@ gdr2_status gdr2_bwd_chunked(int64_t B, int64_t T, int64_t H, int64_t dk, int64_
                              const void* dO, const float* dS_T, void* dq, void* dk_, void* dv_,
                              float* dlog_alpha, void* db, void* dw, float* dS0,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Gate-aware backward that needs no forward workspace: it recomputes the per-chunk factors and
+ * the chunk-entry states from the inputs and S0 (the chunked forward without o), then runs the
+ * backward of gdr2_bwd_chunked; the gradients equal gdr2_bwd_chunked's bit for bit.  For callers
+ * that ran gdr2_fwd_infer, or that do not keep the forward workspace between the passes.
+ *   S0              [B][H][dk][dv] fp32 or NULL (= 0): the initial state the forward used
+ *   workspace       device memory of at least gdr2_bwd_recompute_workspace_bytes() bytes (the
+ *                   training forward's workspace followed by the backward's)
+ * Every other argument and every error as in gdr2_bwd_chunked(_ex).
+ */
+size_t gdr2_bwd_recompute_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                                          gdr2_dtype dtype);
+gdr2_status gdr2_bwd_chunked_recompute(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                                       gdr2_dtype dtype, const void* q, const void* k,
+                                       const void* v, const float* log_alpha, const void* b,
+                                       const void* w, const float* S0, const void* dO,
+                                       const float* dS_T, void* dq, void* dk_, void* dv_,
+                                       float* dlog_alpha, void* db, void* dw, float* dS0,
+                                       void* workspace, size_t workspace_bytes, void* stream);
+gdr2_status gdr2_bwd_chunked_recompute_ex(int64_t B, int64_t T, int64_t H, int64_t dk,
+                                          int64_t dv, gdr2_dtype dtype, unsigned gates,
+                                          const gdr2_prologue* pro, const void* q, const void* k,
+                                          const void* v, const float* log_alpha, const void* b,
+                                          const void* w, const float* S0, const void* dO,
+                                          const float* dS_T, void* dq, void* dk_, void* dv_,
+                                          float* dlog_alpha, void* db, void* dw, float* dS0,
+                                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Phase entry points.  gdr2_fwd_chunked is gdr2_fwd_factors followed by gdr2_fwd_carry on the same

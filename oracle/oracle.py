@@ -121,15 +121,21 @@ def backward(q, k, v, log_alpha, b, w, dO, S0=None, dST=None):
     return out
 
 
-def decode_step(q, k, v, log_alpha, b, w, S_in=None):
+def decode_step(q, k, v, log_alpha, b, w, S_in=None, S_out=None):
     """One recurrent token for N sequences x H heads.
 
-    q, k, log_alpha, b: [N,H,dk]; v, w: [N,H,dv]; S_in: [N,H,dk,dv] or None (= 0).
+    q, k, log_alpha, b: [N,H,dk]; v, w: [N,H,dv]; S_in: [N,H,dk,dv] or None (= 0).  ``S_out``
+    (optional, C-contiguous float64) receives the new state; it may be S_in itself (in place).
     Returns (o [N,H,dv], S_out [N,H,dk,dv])."""
-    q, k, v, la, b, w, S_in = map(_f64, (q, k, v, log_alpha, b, w, S_in))
+    inplace = S_out is not None and S_in is S_out
+    q, k, v, la, b, w = map(_f64, (q, k, v, log_alpha, b, w))
     N, H, dk = q.shape
     dv = v.shape[-1]
-    S_out = np.zeros((N, H, dk, dv))
+    if S_out is None:
+        S_out = np.zeros((N, H, dk, dv))
+    if not (S_out.dtype == np.float64 and S_out.flags.c_contiguous and S_out.shape == (N, H, dk, dv)):
+        raise ValueError("S_out must be a C-contiguous float64 [N,H,dk,dv] array")
+    S_in = S_out if inplace else _f64(S_in)
     o = np.zeros((N, H, dv))
     _load().gdr2o_decode_step(N, H, dk, dv, *map(_ptr, (q, k, v, la, b, w, S_in, S_out, o)))
     return o, S_out

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_strings():
     lib = load_library()
-    assert lib.gdr2_abi_version() == 2
+    assert lib.gdr2_abi_version() == 3
     for s in range(10):
         assert lib.gdr2_status_string(s)
     assert lib.gdr2_dtype_size(0) == 4 and lib.gdr2_dtype_size(1) == 2 and lib.gdr2_dtype_size(7) == 0
@@ -52,6 +52,92 @@ def test_workspace_sizes():
     assert fws == expect
     assert lib.gdr2_bwd_workspace_bytes(B, T, H, dk, dv, 1) == per * dk * dv * 2
     assert lib.gdr2_fwd_workspace_bytes(1, 0, 1, 64, 64, 0) == 0
+
+
+def test_forward_only_and_recompute_workspace_sizes():
+    """The forward-only workspace is the training forward's without the chunk-entry states; the
+    recomputing backward needs the training forward's workspace followed by the backward's."""
+    lib = load_library()
+    for (B, T, H, dk, dv, dt) in [(4, 4096, 16, 128, 128, 1), (1, 100, 3, 64, 128, 0), (2, 1, 1, 64, 64, 1)]:
+        per = B * H * ((T + 63) // 64)
+        es = 2 if dt == 1 else 4
+        r = lambda n: (n + 255) // 256 * 256
+        fws = lib.gdr2_fwd_workspace_bytes(B, T, H, dk, dv, dt)
+        inf = lib.gdr2_fwd_infer_workspace_bytes(B, T, H, dk, dv, dt)
+        assert fws - inf == r(per * dv * dk * es)
+        assert lib.gdr2_bwd_recompute_workspace_bytes(B, T, H, dk, dv, dt) == fws + lib.gdr2_bwd_workspace_bytes(B, T, H, dk, dv, dt)
+
+
+def test_sizes_that_would_overflow_are_rejected():
+    """Shape products are bounded before they are formed: sizes whose products overflow 64 bits
+    get GDR2_E_SHAPE (and workspace queries 0) instead of wrapping around."""
+    lib = load_library()
+    P = lambda a: _fake(a)
+    big = 1 << 40
+    ins = [P(0x10000 + i * 0x8000) for i in range(6)]
+    for (B, T, H) in [(big, 8, big), (1 << 31, 8, 1 << 31), (1, 1 << 41, 1), (1 << 20, 1 << 30, 1),
+                      (big, big, big), ((1 << 62), 1, 4)]:
+        assert lib.gdr2_fwd_workspace_bytes(B, T, H, 128, 128, 1) == 0
+        assert lib.gdr2_fwd_infer_workspace_bytes(B, T, H, 128, 128, 1) == 0
+        assert lib.gdr2_bwd_workspace_bytes(B, T, H, 128, 128, 1) == 0
+        assert lib.gdr2_bwd_recompute_workspace_bytes(B, T, H, 128, 128, 1) == 0
+        assert lib.gdr2_fwd_chunked(B, T, H, 128, 128, 1, *ins, NULL, P(0x90000), NULL,
+                                    P(0x200000), 1 << 30, NULL) == E_SHAPE
+        assert lib.gdr2_fwd_infer(B, T, H, 128, 128, 1, *ins, NULL, P(0x90000), NULL,
+                                  P(0x200000), 1 << 30, NULL) == E_SHAPE
+        assert lib.gdr2_bwd_chunked_recompute(B, T, H, 128, 128, 1, *ins, NULL, P(0x300000), NULL,
+                                              *[P(0x400000 + i * 0x1000) for i in range(6)], NULL,
+                                              P(0x500000), 1 << 30, NULL) == E_SHAPE
+    assert lib.gdr2_decode_step(big, big, 64, 64, 1, *ins, NULL, P(0x100000), P(0x200000), NULL) == E_SHAPE
+    assert lib.gdr2_decode_step(1 << 16, 1 << 15, 64, 64, 1, *ins, NULL, P(0x100000), P(0x200000), NULL) == E_SHAPE
+
+
+def test_forward_only_rejects_before_launch():
+    lib = load_library()
+    P = lambda a: _fake(a)
+    B, T, H, dk, dv = 1, 8, 1, 64, 64
+    need = lib.gdr2_fwd_infer_workspace_bytes(B, T, H, dk, dv, 1)
+
+    def call(dt=1, q=0x10000, o=0x90000, ws=0x200000, wsb=1 << 30, gates=0):
+        ins = [P(q + i * 0x8000) if q else NULL for i in range(6)]
+        return lib.gdr2_fwd_infer_ex(B, T, H, dk, dv, dt, gates, NULL, *ins, NULL, P(o) if o else NULL,
+                                     NULL, P(ws) if ws else NULL, wsb, NULL)
+    assert call(dt=3) == E_DTYPE
+    assert call(gates=8) == E_UNSUP
+    assert call(q=0) == E_NULL
+    assert call(o=0) == E_NULL
+    assert call(ws=0) == E_WS
+    assert call(wsb=need - 1) == E_WS
+    assert call(o=0x10008) == E_ALIGN
+    assert call(o=0x18000) == E_ALIAS
+    # the overlap test covers the forward-only workspace's own extent: ending 64 bytes into w
+    assert call(ws=0x10000 + 5 * 0x8000 + 64 - need) == E_ALIAS
+
+
+def test_recompute_backward_rejects_before_launch():
+    from gated_delta_rule_gdr_amd import Prologue
+    lib = load_library()
+    P = lambda a: _fake(a)
+    B, T, H, dk, dv = 1, 8, 1, 64, 64
+    need = lib.gdr2_bwd_recompute_workspace_bytes(B, T, H, dk, dv, 1)
+    ins = [P(0x10000 + i * 0x8000) for i in range(6)]
+
+    def call(dt=1, S0=0, dO=0x300000, dq=0x400000, ws=0x900000, wsb=1 << 30, pro=None, gates=0):
+        grads = [P(dq + i * 0x8000) if dq else NULL for i in range(6)]
+        return lib.gdr2_bwd_chunked_recompute_ex(B, T, H, dk, dv, dt, gates, pro, *ins,
+                                                 P(S0) if S0 else NULL, P(dO) if dO else NULL, NULL,
+                                                 *grads, NULL, P(ws) if ws else NULL, wsb, NULL)
+    assert call(dt=7) == E_DTYPE
+    assert call(gates=16) == E_UNSUP
+    assert call(pro=ctypes.byref(Prologue(0.0, 1e-6))) == 9
+    assert call(dO=0) == E_NULL
+    assert call(dq=0) == E_NULL
+    assert call(ws=0) == E_WS
+    assert call(wsb=need - 1) == E_WS
+    assert call(S0=0x300008) == E_ALIGN
+    assert call(dq=0x10000) == E_ALIAS
+    assert call(ws=0x300000) == E_ALIAS      # workspace over dO
+    assert call(S0=0x400000) == E_ALIAS      # an input under the gradient outputs
 
 
 def _fake(addr):

@@ -6,7 +6,7 @@ import torch
 from gated_delta_rule_gdr_amd import gdr2_bwd_chunked, gdr2_fwd_chunked
 from gated_delta_rule_gdr_amd.inputs import config_inputs, layer_inputs, strong_decay_inputs, to_f64
 from oracle import oracle as orc
-from tests._util import TOL, announce, assert_close, to_np
+from tests._util import TOL, announce, assert_close, assert_close_chains, to_np
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -80,81 +80,66 @@ def test_bwd_strong_decay():
     _check(x, TOL["f32"], "bwd f32 strong decay")
 
 
-def test_bwd_layer_1p3b_sampled_chains():
-    """Model-shaped 1.3B layer (B=4, T=4096, H=16, d=128) in the launch configuration the bench
-    times; the oracle recomputes forward and backward of two whole (b, h) chains."""
-    x = config_inputs("layer_1p3b")
-    announce("layer_1p3b fwd+bwd full size")
-    o, ST, gr = _run(x)
-    f = to_f64(x)
-    for (b, h) in [(0, 0), (3, 15)]:
-        sub = {n: (None if a is None else a[b:b + 1, :, h:h + 1]) for n, a in f.items()
-               if n in ("q", "k", "v", "log_alpha", "b", "w", "dO")}
-        ro, _ = orc.forward(sub["q"], sub["k"], sub["v"], sub["log_alpha"], sub["b"], sub["w"])
-        rg = orc.backward(sub["q"], sub["k"], sub["v"], sub["log_alpha"], sub["b"], sub["w"],
-                          sub["dO"])
-        assert_close(f"o ({b},{h})", to_np(o[b:b + 1, :, h:h + 1]), ro, TOL["bf16"])
-        for n in ("dq", "dk", "dv", "dlog_alpha", "db", "dw"):
-            e = assert_close(f"{n} ({b},{h})", to_np(gr[n][b:b + 1, :, h:h + 1]), rg[n], TOL["bf16"])
-            print(f"  {n} ({b},{h}) {e:.2e}", flush=True)
-        assert_close(f"dS0 ({b},{h})", to_np(gr["dS0"][b:b + 1, h:h + 1]), rg["dS0"], TOL["bf16"])
-
-
-def test_bwd_long_context_sampled_chain():
-    """Long context (B=1, T=32768, H=16, d=128) with S0 ~ N(0, 0.02^2), returning the final state;
-    the oracle recomputes one whole chain."""
-    x = config_inputs("long_ctx")
-    announce("long_ctx fwd+bwd full size")
-    o, ST, gr = _run(x)
-    f = to_f64(x)
-    h = 5
-    sub = {n: (None if a is None else a[:, :, h:h + 1]) for n, a in f.items()
-           if n in ("q", "k", "v", "log_alpha", "b", "w", "dO")}
-    s0 = f["S0"][:, h:h + 1]
-    ro, rS = orc.forward(sub["q"], sub["k"], sub["v"], sub["log_alpha"], sub["b"], sub["w"], s0)
-    rg = orc.backward(sub["q"], sub["k"], sub["v"], sub["log_alpha"], sub["b"], sub["w"], sub["dO"],
-                      S0=s0)
-    assert_close("o", to_np(o[:, :, h:h + 1]), ro, TOL["bf16"])
-    assert_close("S_T", to_np(ST[:, h:h + 1]), rS, TOL["bf16"])
+def _check_chains(tag, o, ST, gr, ro, rS, rg, tol):
+    errs = {"o": assert_close_chains(f"{tag} o", to_np(o), ro, tol, "tok")}
+    if ST is not None:
+        errs["S_T"] = assert_close_chains(f"{tag} S_T", to_np(ST), rS, tol, "state")
     for n in ("dq", "dk", "dv", "dlog_alpha", "db", "dw"):
-        e = assert_close(n, to_np(gr[n][:, :, h:h + 1]), rg[n], TOL["bf16"])
-        print(f"  {n} {e:.2e}", flush=True)
-    assert_close("dS0", to_np(gr["dS0"][:, h:h + 1]), rg["dS0"], TOL["bf16"])
+        errs[n] = assert_close_chains(f"{tag} {n}", to_np(gr[n]), rg[n], tol, "tok")
+    errs["dS0"] = assert_close_chains(f"{tag} dS0", to_np(gr["dS0"]), rg["dS0"], tol, "state")
+    print("  " + tag + " worst chain: " + "  ".join(f"{k} {v:.1e}" for k, v in errs.items()), flush=True)
+
+
+def test_bwd_layer_1p3b_all_chains():
+    """Model-shaped 1.3B layer (B=4, T=4096, H=16, d=128) in the launch configuration the bench
+    times; the oracle recomputes forward and backward of all 64 (b, h) chains, each compared on
+    its own."""
+    x = config_inputs("layer_1p3b")
+    announce("layer_1p3b fwd+bwd full size, all chains")
+    o, ST, gr = _run(x)
+    ro, rS, rg = _oracle(x)
+    _check_chains("layer_1p3b", o, ST, gr, ro, rS, rg, TOL["bf16"])
+
+
+def test_bwd_long_context_all_heads():
+    """Long context (B=1, T=32768, H=16, d=128) with S0 ~ N(0, 0.02^2), returning the final state;
+    the oracle recomputes all 16 chains."""
+    x = config_inputs("long_ctx")
+    announce("long_ctx fwd+bwd full size, all heads")
+    o, ST, gr = _run(x)
+    ro, rS, rg = _oracle(x)
+    _check_chains("long_ctx", o, ST, gr, ro, rS, rg, TOL["bf16"])
 
 
 @pytest.mark.parametrize("variant", ["tied_kda", "tied_gdn", "tied_la"])
 def test_tied_gate_reductions(variant):
-    """Tied-gate sweep (B=2, T=2048, H=16, d=128): the forward must match the reduced rule's own
-    oracle (KDA, Gated DeltaNet, or the linear-attention closed form), and the gradients of the
-    tied parameters (sum of db and dw for beta; sum of dlog alpha for a scalar decay) must match
-    the main oracle's, on sampled chains."""
+    """Tied-gate sweep (B=2, T=2048, H=16, d=128), all 32 chains: the forward must match the
+    reduced rule's own oracle (KDA, Gated DeltaNet, or the linear-attention closed form), and the
+    gradients of the tied parameters (sum of db and dw for beta; sum of dlog alpha for a scalar
+    decay) must match the main oracle's."""
     x = config_inputs(variant)
     announce(variant)
     o, ST, gr = _run(x)
     f = to_f64(x)
-    for (b, h) in [(0, 3), (1, 12)]:
-        sub = {n: (None if a is None else a[b:b + 1, :, h:h + 1]) for n, a in f.items()
-               if n in ("q", "k", "v", "log_alpha", "b", "w", "dO")}
-        if variant == "tied_la":
-            ro, rS = orc.la_closed_form(sub["q"], sub["k"], sub["v"])
-        else:
-            beta = sub["b"][..., 0]
-            ro, rS = orc.kda_forward(sub["q"], sub["k"], sub["v"], sub["log_alpha"], beta,
-                                     scalar_decay=(variant == "tied_gdn"))
-        assert_close(f"{variant} o ({b},{h})", to_np(o[b:b + 1, :, h:h + 1]), ro, TOL["bf16"])
-        assert_close(f"{variant} S_T ({b},{h})", to_np(ST[b:b + 1, h:h + 1]), rS, TOL["bf16"])
-        rg = orc.backward(sub["q"], sub["k"], sub["v"], sub["log_alpha"], sub["b"], sub["w"],
-                          sub["dO"])
-        for n in ("dq", "dk", "dv"):
-            assert_close(f"{variant} {n}", to_np(gr[n][b:b + 1, :, h:h + 1]), rg[n], TOL["bf16"])
-        gb = to_np(gr["db"][b:b + 1, :, h:h + 1]).sum(-1) + to_np(gr["dw"][b:b + 1, :, h:h + 1]).sum(-1)
-        rb = rg["db"].sum(-1) + rg["dw"].sum(-1)
-        assert_close(f"{variant} dbeta", gb, rb, TOL["bf16"])
-        gl = to_np(gr["dlog_alpha"][b:b + 1, :, h:h + 1])
-        if variant == "tied_gdn":
-            assert_close(f"{variant} dlog_alpha (scalar)", gl.sum(-1), rg["dlog_alpha"].sum(-1), TOL["bf16"])
-        else:
-            assert_close(f"{variant} dlog_alpha", gl, rg["dlog_alpha"], TOL["bf16"])
+    if variant == "tied_la":
+        ro, rS = orc.la_closed_form(f["q"], f["k"], f["v"])
+    else:
+        ro, rS = orc.kda_forward(f["q"], f["k"], f["v"], f["log_alpha"], f["b"][..., 0],
+                                 scalar_decay=(variant == "tied_gdn"))
+    tol = TOL["bf16"]
+    assert_close_chains(f"{variant} o", to_np(o), ro, tol, "tok")
+    assert_close_chains(f"{variant} S_T", to_np(ST), rS, tol, "state")
+    rg = orc.backward(f["q"], f["k"], f["v"], f["log_alpha"], f["b"], f["w"], f["dO"])
+    for n in ("dq", "dk", "dv"):
+        assert_close_chains(f"{variant} {n}", to_np(gr[n]), rg[n], tol, "tok")
+    gb = to_np(gr["db"]).sum(-1) + to_np(gr["dw"]).sum(-1)
+    rb = rg["db"].sum(-1) + rg["dw"].sum(-1)
+    assert_close_chains(f"{variant} dbeta", gb, rb, tol, "tok")
+    gl = to_np(gr["dlog_alpha"])
+    if variant == "tied_gdn":
+        assert_close_chains(f"{variant} dlog_alpha (scalar)", gl.sum(-1), rg["dlog_alpha"].sum(-1), tol, "tok")
+    else:
+        assert_close_chains(f"{variant} dlog_alpha", gl, rg["dlog_alpha"], tol, "tok")
 
 
 def test_bwd_split_sequence_handoff():

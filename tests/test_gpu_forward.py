@@ -7,7 +7,7 @@ from gated_delta_rule_gdr_amd import gdr2_decode_step, gdr2_fwd_chunked
 from gated_delta_rule_gdr_amd.inputs import (DECODE, config_inputs, decode_inputs, layer_inputs,
                                              strong_decay_inputs, to_f64)
 from oracle import oracle as orc
-from tests._util import TOL, announce, assert_close, to_np
+from tests._util import TOL, announce, assert_close, assert_close_chains, to_np
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -76,8 +76,9 @@ def test_fwd_many_chains_slice_paths():
 
 
 def test_fwd_strong_decay():
-    """Channels decaying by up to e^-6 per token: far outside the naive e^{+-G} factor range of a
-    whole chunk (|G| up to 384), inside the per-16-token-block range the kernel guarantees."""
+    """Half the key channels decaying by log alpha in [-5, -2.5] per token: far outside the range
+    of one exp(+-G) factor over a whole chunk (|G| up to 320); the deeper decays are in
+    tests/test_gpu_deep_decay.py."""
     x = strong_decay_inputs(1, 256, 2, 128, 128, dtype="bf16", seed=3, floor=-5.0)
     _check_fwd(x, TOL["bf16"], "bf16 strong decay")
     x = strong_decay_inputs(1, 256, 2, 64, 64, dtype="f32", seed=4, floor=-5.0)
@@ -105,19 +106,17 @@ def test_fwd_chunk_states_checkpoint():
         assert_close(f"state entering chunk {c}", got, ref, TOL["bf16"])
 
 
-def test_fwd_layer_1p3b_sampled_chains():
+def test_fwd_layer_1p3b_all_chains():
     """Full model-shaped layer (B=4, T=4096, H=16, d=128) in the launch configuration the bench
-    times; the oracle recomputes two whole (b, h) chains."""
+    times; the oracle recomputes every (b, h) chain, each compared on its own."""
     x = config_inputs("layer_1p3b")
-    announce("layer_1p3b forward, full size")
+    announce("layer_1p3b forward, full size, all chains")
     o, ST, _ = _run_fwd(x)
     f = to_f64(x)
-    for (b, h) in [(0, 0), (3, 15)]:
-        sub = {n: (None if a is None else a[b:b + 1, :, h:h + 1]) for n, a in f.items()
-               if n in ("q", "k", "v", "log_alpha", "b", "w")}
-        ro, rS = orc.forward(sub["q"], sub["k"], sub["v"], sub["log_alpha"], sub["b"], sub["w"])
-        assert_close(f"o chain ({b},{h})", to_np(o[b:b + 1, :, h:h + 1]), ro, TOL["bf16"])
-        assert_close(f"S_T chain ({b},{h})", to_np(ST[b:b + 1, h:h + 1]), rS, TOL["bf16"])
+    ro, rS = orc.forward(f["q"], f["k"], f["v"], f["log_alpha"], f["b"], f["w"])
+    eo = assert_close_chains("o", to_np(o), ro, TOL["bf16"], "tok")
+    eS = assert_close_chains("S_T", to_np(ST), rS, TOL["bf16"], "state")
+    print(f"  worst chain: o {eo:.2e}  S_T {eS:.2e}", flush=True)
 
 
 @pytest.mark.parametrize("dt,dk,dv", [("bf16", 128, 128), ("f32", 64, 128), ("bf16", 64, 64),
@@ -133,7 +132,7 @@ def test_decode_steps_vs_oracle(dt, dk, dv):
         o, S = gdr2_decode_step(g["q"], g["k"], g["v"], g["log_alpha"], g["b"], g["w"], S_in=S)
         torch.cuda.synchronize()
         f = to_f64(x)
-        ro, Sref = orc.decode_step(f["q"], f["k"], f["v"], f["log_alpha"], f["b"], f["w"], Sref)
+        ro, Sref = orc.decode_step(f["q"], f["k"], f["v"], f["log_alpha"], f["b"], f["w"], Sref, S_out=Sref)
         assert_close(f"decode o step {s}", to_np(o), ro, TOL[dt])
         assert_close(f"decode S step {s}", to_np(S), Sref, TOL[dt])
 
@@ -156,30 +155,25 @@ def test_decode_equals_chunked_forward():
     assert_close("decode vs chunked S_T", to_np(S), to_np(ST), TOL["bf16"])
 
 
-def test_decode_full_workload_sampled_chains():
+@pytest.mark.timeout(900)
+def test_decode_full_workload_all_chains():
     """The decode workload at full size (256 sequences x 16 heads, d = 128, 1024 steps, bf16
-    tokens, fp32 state updated in place in HBM, the launch the benchmark times): three sampled
-    (sequence, head) chains against the oracle's token recurrence at every step and at the end."""
+    tokens, fp32 state updated in place in HBM, the launch the benchmark times): every chain
+    against the oracle's token recurrence, o at every step and the state at eight checkpoints."""
     N, H, dk, dv, steps = DECODE["N"], DECODE["H"], DECODE["dk"], DECODE["dv"], DECODE["steps"]
-    announce(f"decode full workload N={N} H={H} steps={steps}")
-    samples = [(0, 0), (137, 9), (255, 15)]
+    announce(f"decode full workload N={N} H={H} steps={steps}, all chains")
     S = torch.zeros((N, H, dk, dv), dtype=torch.float32, device=DEV)
-    Sref = {c: None for c in samples}
-    worst = 0.0
+    Sref = np.zeros((N, H, dk, dv))  # the oracle's state, updated in place
+    worst_o = worst_S = 0.0
     for s in range(steps):
         x = decode_inputs(s, N=N, H=H, dk=dk, dv=dv, device=DEV)
         o, _ = gdr2_decode_step(x["q"], x["k"], x["v"], x["log_alpha"], x["b"], x["w"], S_in=S, S_out=S)
-        sub = {n: torch.stack([x[n][a, h] for a, h in samples]) for n in x}
-        osub = torch.stack([o[a, h] for a, h in samples]).float().cpu().numpy()
-        f = {n: t.to("cpu", torch.float64).numpy() for n, t in sub.items()}
-        for i, c in enumerate(samples):
-            ro, Sref[c] = orc.decode_step(*(f[n][i:i + 1, None] for n in ("q", "k", "v", "log_alpha", "b", "w")),
-                                          Sref[c])
-            if s % 128 == 127 or s == steps - 1:
-                worst = max(worst, assert_close(f"decode o step {s} chain {c}", osub[i:i + 1, None], ro,
-                                                TOL["bf16"]))
-    torch.cuda.synchronize()
-    for c in samples:
-        assert_close(f"decode S after {steps} steps chain {c}", to_np(S[c[0]:c[0] + 1, c[1]:c[1] + 1]),
-                     Sref[c], TOL["bf16"])
-    print(f"  full decode: worst sampled o error {worst:.2e}", flush=True)
+        f = {n: t.to("cpu", torch.float64).numpy() for n, t in x.items()}
+        ro, Sref = orc.decode_step(f["q"], f["k"], f["v"], f["log_alpha"], f["b"], f["w"], Sref, S_out=Sref)
+        # o[n, h, :] is chain (n, h) at this step: a one-token [N, 1, H, dv] view
+        worst_o = max(worst_o, assert_close_chains(f"decode o step {s}", to_np(o)[:, None], ro[:, None],
+                                                   TOL["bf16"], "tok"))
+        if s % 128 == 127:
+            worst_S = max(worst_S, assert_close_chains(f"decode S step {s}", to_np(S), Sref, TOL["bf16"],
+                                                       "state"))
+            print(f"  step {s + 1}: worst chain o {worst_o:.2e}  S {worst_S:.2e}", flush=True)
