@@ -28,6 +28,7 @@ import torch
 
 __all__ = ["gdr2_fwd_chunked", "gdr2_bwd_chunked", "gdr2_decode_step", "gdr2_fwd_factors",
            "gdr2_fwd_infer", "gdr2_bwd_chunked_recompute", "fwd_infer_workspace_bytes",
+           "gdr2_fwd_infer_noalloc", "fwd_infer_noalloc_max_bytes",
            "bwd_recompute_workspace_bytes",
            "gdr2_fwd_carry", "gdr2_bwd_state", "gdr2_bwd_grads", "fwd_workspace_bytes",
            "bwd_workspace_bytes", "library_path", "load_library", "Gdr2Error", "CHUNK", "gate_bits",
@@ -41,7 +42,7 @@ _lib = None
 
 _STATUS = {0: "ok", 1: "GDR2_E_NULL", 2: "GDR2_E_SHAPE", 3: "GDR2_E_DTYPE",
            4: "GDR2_E_UNSUPPORTED", 5: "GDR2_E_ALIGN", 6: "GDR2_E_ALIAS", 7: "GDR2_E_WORKSPACE",
-           8: "GDR2_E_HIP", 9: "GDR2_E_VALUE"}
+           8: "GDR2_E_HIP", 9: "GDR2_E_VALUE", 10: "GDR2_E_TOO_LARGE"}
 _DT = {torch.float32: 0, torch.bfloat16: 1}
 
 
@@ -102,6 +103,10 @@ def load_library():
     lib.gdr2_fwd_infer.restype = ctypes.c_int
     lib.gdr2_bwd_chunked_recompute.argtypes = [I64] * 5 + [ctypes.c_int] + [P] * 17 + [SZ, P]
     lib.gdr2_bwd_chunked_recompute.restype = ctypes.c_int
+    lib.gdr2_fwd_infer_noalloc_ex.argtypes = [I64] * 5 + [ctypes.c_int, ctypes.c_uint, P] + [P] * 10
+    lib.gdr2_fwd_infer_noalloc_ex.restype = ctypes.c_int
+    lib.gdr2_fwd_infer_noalloc_max_bytes.argtypes = []
+    lib.gdr2_fwd_infer_noalloc_max_bytes.restype = SZ
     lib.gdr2_fwd_infer_workspace_bytes.argtypes = [I64] * 5 + [ctypes.c_int]
     lib.gdr2_fwd_infer_workspace_bytes.restype = SZ
     lib.gdr2_bwd_chunked_recompute_ex.argtypes = ([I64] * 5 + [ctypes.c_int, ctypes.c_uint, P]
@@ -326,6 +331,34 @@ def gdr2_fwd_infer(q, k, v, log_alpha, b, w, S0=None, want_final_state=True, wor
          _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w), _ptr(S0), _ptr(o), _ptr(ST),
          _ptr(ws), ws.numel())
     return o, ST
+
+
+def gdr2_fwd_infer_noalloc(q, k, v, log_alpha, b, w, S0=None, want_final_state=True, o=None,
+                           S_T=None, prologue=None):
+    """gdr2_fwd_infer through the no-allocation entry point: the library keeps the per-chunk
+    factors in its static device scratch (at most fwd_infer_noalloc_max_bytes() bytes of them).
+    ``o`` / ``S_T`` may pass preallocated outputs so that the call itself allocates nothing.
+    Returns (o, S_T or None)."""
+    lib = load_library()
+    dev, bits = _inputs(q, k, v, log_alpha, b, w, 4)
+    B, T, H, dk, dv = _shapes(q, v)
+    dt = _dtype(q)
+    _need("S0", S0, (B, H, dk, dv), torch.float32, dev, optional=True)
+    _need("o", o, (B, T, H, dv), q.dtype, dev, optional=True)
+    _need("S_T", S_T, (B, H, dk, dv), torch.float32, dev, optional=True)
+    _on_gpu(dev)
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=q.dtype, device=dev)
+    if S_T is None and want_final_state:
+        S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    _run("gdr2_fwd_infer_noalloc", dev, lib.gdr2_fwd_infer_noalloc_ex, B, T, H, dk, dv, dt, bits,
+         _pro(prologue), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w), _ptr(S0),
+         _ptr(o), _ptr(S_T))
+    return o, S_T
+
+
+def fwd_infer_noalloc_max_bytes():
+    return load_library().gdr2_fwd_infer_noalloc_max_bytes()
 
 
 def gdr2_bwd_chunked_recompute(q, k, v, log_alpha, b, w, dO, S0=None, dS_T=None, want_dS0=True,

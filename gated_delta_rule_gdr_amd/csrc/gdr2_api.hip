@@ -86,6 +86,7 @@ const char* gdr2_status_string(gdr2_status s) {
         case GDR2_E_WORKSPACE: return "workspace missing or too small";
         case GDR2_E_HIP: return "HIP launch failed";
         case GDR2_E_VALUE: return "invalid scalar argument";
+        case GDR2_E_TOO_LARGE: return "problem exceeds the no-allocation entry point's static scratch";
     }
     return "unknown status";
 }
@@ -195,12 +196,14 @@ static gdr2::FwdParams fwd_params(int64_t B, int64_t T, int64_t H, int64_t dv, c
 // Validation shared by the forward phases.  `need_inputs` / `need_out` select which pointers a
 // phase requires; every pointer given must be aligned and every output disjoint from the inputs.
 // `with_states`: the workspace also holds the chunk-entry states (training); without them it holds
-// only the factors (forward-only calls).
+// only the factors (forward-only calls).  `caller_ws` false: the factors go to the library's own
+// scratch, so no workspace argument is checked.
 static gdr2_status check_fwd(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
                              gdr2_dtype dt, const void* q, const void* k, const void* v,
                              const float* la, const void* b, const void* w, const float* S0,
                              void* o, float* S_T, void* ws, size_t ws_bytes, bool need_inputs,
-                             bool need_out, unsigned gates = 0, bool with_states = true) {
+                             bool need_out, unsigned gates = 0, bool with_states = true,
+                             bool caller_ws = true) {
     gdr2_status st = check_chunked(B, T, H, dk, dv, dt);
     if (st != GDR2_OK) return st;
     if (!gates_ok(gates)) return GDR2_E_UNSUPPORTED;
@@ -212,14 +215,14 @@ static gdr2_status check_fwd(int64_t B, int64_t T, int64_t H, int64_t dk, int64_
         if (p && !aligned16(p)) return GDR2_E_ALIGN;
     const FwdWs L = fwd_ws_layout(B, T, H, dk, dv, dt);
     const size_t ws_need = with_states ? L.total : L.states;
-    if (have_tokens && (!ws || ws_bytes < ws_need)) return GDR2_E_WORKSPACE;
+    if (caller_ws && have_tokens && (!ws || ws_bytes < ws_need)) return GDR2_E_WORKSPACE;
     const size_t es = gdr2_dtype_size(dt);
     const size_t nk = (size_t)B * T * H * dk, nv = (size_t)B * T * H * dv;
     const size_t ns = (size_t)B * H * dk * dv;
     const GateSizes gs = gate_sizes(gates, (size_t)B * T * H, dk, dv);
     const Range ins[] = {{q, nk * es}, {k, nk * es}, {v, nv * es}, {la, gs.na * 4},
                          {b, gs.nb * es}, {w, gs.nw * es}, {S0, ns * 4}};
-    const Range outs[] = {{o, nv * es}, {S_T, ns * 4}, {ws, have_tokens ? ws_need : 0}};
+    const Range outs[] = {{o, nv * es}, {S_T, ns * 4}, {ws, have_tokens && caller_ws ? ws_need : 0}};
     if (any_alias(outs, 3, ins, 7)) return GDR2_E_ALIAS;
     return GDR2_OK;
 }
@@ -297,6 +300,28 @@ gdr2_status gdr2_fwd_infer_ex(int64_t B, int64_t T, int64_t H, int64_t dk, int64
             return GDR2_E_HIP;
     }
     return launch_carry(B, T, H, dk, dv, dt, S0, o, S_T, workspace, false, stream);
+}
+
+size_t gdr2_fwd_infer_noalloc_max_bytes(void) { return gdr2::kNoAllocScratchBytes; }
+
+gdr2_status gdr2_fwd_infer_noalloc_ex(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                                      gdr2_dtype dt, unsigned gates, const gdr2_prologue* pro,
+                                      const void* q, const void* k, const void* v,
+                                      const float* log_alpha, const void* b, const void* w,
+                                      const float* S0, void* o, float* S_T, void* stream) {
+    gdr2_status st = check_fwd(B, T, H, dk, dv, dt, q, k, v, log_alpha, b, w, S0, o, S_T, nullptr,
+                               0, true, true, gates, false, false);
+    if (st == GDR2_OK && !prologue_ok(pro)) st = GDR2_E_VALUE;
+    if (st != GDR2_OK) return st;
+    const size_t need = fwd_ws_layout(B, T, H, dk, dv, dt).states;
+    if (need > gdr2::kNoAllocScratchBytes) return GDR2_E_TOO_LARGE;
+    if (B == 0 || H == 0) return GDR2_OK;
+    // the factors go to this device's static scratch (library memory: it cannot overlap the
+    // caller's buffers); the launches are those of gdr2_fwd_infer_ex
+    void* scr = nullptr;
+    if (gdr2::noalloc_scratch(&scr) != hipSuccess) return GDR2_E_HIP;
+    return gdr2_fwd_infer_ex(B, T, H, dk, dv, dt, gates, pro, q, k, v, log_alpha, b, w, S0, o, S_T,
+                             scr, need, stream);
 }
 
 gdr2_status gdr2_fwd_infer(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,

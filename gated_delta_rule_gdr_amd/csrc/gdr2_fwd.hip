@@ -29,11 +29,38 @@
 // exp(ref_S - G_s) (the inverse of the decay across at most 16 tokens) times exp(ref_R - ref_S)
 // <= 1.  The only factor above one stays finite in fp32 as long as the decay across one 16-token
 // block is above exp(-88) on every channel.
+#include <mutex>
+
 #include "gdr2_common.hpp"
 #include "gdr2_kernels.hpp"
 #include "gdr2_wy.hpp"
 
 namespace gdr2 {
+
+// Static device scratch of the no-allocation forward-only entry point: the per-chunk factors of
+// one call (the region a workspace argument brings in for the other entry points).  Every device
+// the library runs on holds its own copy until the process ends.  In host code `scratch` names a
+// host-side stand-in, not device memory: only the address from hipGetSymbolAddress is used.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+hipError_t noalloc_scratch(void** ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* per_device[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!per_device[dev]) {  // once per device, with that device current
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        per_device[dev] = p;
+    }
+    *ptr = per_device[dev];
+    return hipSuccess;
+}
 
 template <typename OT, int DK, int DV, int MODE>
 __global__ __launch_bounds__(kThreads, 2) void gdr2_wy_kernel(FwdParams p) {

@@ -90,6 +90,11 @@ struct EpiParams {
     float* dw_part;         // backward workspace [epi_blocks(rows)][DV] fp32
 };
 
+// No-allocation forward-only entry point: bytes of its static device scratch, and the scratch's
+// device address on the current device (looked up once per device).
+constexpr size_t kNoAllocScratchBytes = (size_t)128 << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 // forward: factor kernel (chunk-parallel) + state carry (sequential over chunks)
 hipError_t wy_dispatch(int dtype_bf16, int dk, int dv, const FwdParams& p, hipStream_t s);
 int carry_slice_width(int dtype_bf16, int dk, int dv, long chains);

@@ -61,7 +61,8 @@ typedef enum gdr2_status {
     GDR2_E_ALIAS = 6,       /* an output overlaps an input or another output */
     GDR2_E_WORKSPACE = 7,   /* workspace missing or smaller than the size its query returns */
     GDR2_E_HIP = 8,         /* the HIP runtime refused the launch */
-    GDR2_E_VALUE = 9        /* a scalar argument is out of range (e.g. eps <= 0) */
+    GDR2_E_VALUE = 9,       /* a scalar argument is out of range (e.g. eps <= 0) */
+    GDR2_E_TOO_LARGE = 10   /* the problem exceeds the no-allocation entry point's static scratch */
 } gdr2_status;
 
 typedef enum gdr2_dtype { GDR2_F32 = 0, GDR2_BF16 = 1 } gdr2_dtype;
@@ -192,6 +193,30 @@ gdr2_status gdr2_bwd_chunked(int64_t B, int64_t T, int64_t H, int64_t dk, int64_
                              const void* dO, const float* dS_T, void* dq, void* dk_, void* dv_,
                              float* dlog_alpha, void* db, void* dw, float* dS0,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * No-allocation variant of gdr2_fwd_infer_ex, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * per-chunk factors go to a static device array of the library instead of a workspace argument.
+ * The caller still passes every input and output.  The call allocates nothing and calls no
+ * allocating routine; on its first call on a device it looks up that device's copy of the array
+ * (hipGetSymbolAddress) and keeps the address.
+ *   - Limit: the problem's factors, gdr2_fwd_infer_workspace_bytes(B, T, H, dk, dv, dtype), must
+ *     fit gdr2_fwd_infer_noalloc_max_bytes() (128 MiB: e.g. B*H*ceil(T/64) <= 1,600 chunk-heads
+ *     at d = 128 in bf16); larger problems return GDR2_E_TOO_LARGE before any launch.
+ *   - Every call on one device shares that device's array, which keeps the last call's contents
+ *     (each call overwrites every byte it reads, so nothing needs clearing).  Calls that overlap
+ *     in time on one device -- on different streams, or from different threads without
+ *     synchronisation -- race on the array; order them on one stream.
+ *   - Each device the library runs on holds its array (128 MiB) until the process ends.
+ * Arguments, results (bit for bit) and every other error as gdr2_fwd_infer_ex.
+ */
+size_t gdr2_fwd_infer_noalloc_max_bytes(void);
+gdr2_status gdr2_fwd_infer_noalloc_ex(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                                      gdr2_dtype dtype, unsigned gates, const gdr2_prologue* pro,
+                                      const void* q, const void* k, const void* v,
+                                      const float* log_alpha, const void* b, const void* w,
+                                      const float* S0, void* o, float* S_T, void* stream);
 
 /*
  * Gate-aware backward that needs no forward workspace: it recomputes the per-chunk factors and

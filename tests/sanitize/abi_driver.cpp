@@ -25,6 +25,8 @@ hipError_t epi_dispatch(int, int, bool, const EpiParams&, hipStream_t) { ++g_lau
 // workgroups of the output epilogue); any positive answer exercises the same validation
 int carry_slice_width(int, int, int dv, long) { return dv >= 32 ? 32 : 16; }
 long epi_blocks(long rows) { return (rows + 127) / 128; }
+// stand-in address of the static scratch (never dereferenced: the launches are stand-ins too)
+hipError_t noalloc_scratch(void** ptr) { *ptr = (void*)(uintptr_t)0x7f0000000000ull; return hipSuccess; }
 }  // namespace gdr2
 
 static int g_fail = 0;
@@ -94,6 +96,16 @@ static void chunked_cases(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t d
         EXPECT(gdr2_fwd_chunked(B, T, H, dk, dv, dt, (char*)q.p + 8, k.p, v.p, la.f(), b.p, w.p, S0.f(), o.p,
                                 ST.f(), fws.p, fwb, nullptr), GDR2_E_ALIGN, false);
     }
+    // the no-allocation forward-only call: same validation, factors in the library's scratch
+    for (unsigned gates = 0; gates < 8; gates += 3)
+        EXPECT(gdr2_fwd_infer_noalloc_ex(B, T, H, dk, dv, dt, gates, &pro, q.p, k.p, v.p, la.f(), b.p, w.p,
+                                         S0.f(), o.p, ST.f(), nullptr), GDR2_OK, B * H > 0);
+    if (tok) {
+        EXPECT(gdr2_fwd_infer_noalloc_ex(B, T, H, dk, dv, dt, 0, nullptr, q.p, k.p, v.p, la.f(), b.p, w.p,
+                                         S0.f(), q.p, ST.f(), nullptr), GDR2_E_ALIAS, false);
+        EXPECT(gdr2_fwd_infer_noalloc_ex(B, T, H, dk, dv, dt, 0, nullptr, q.p, k.p, v.p, la.f(), b.p, w.p,
+                                         S0.f(), nullptr, ST.f(), nullptr), GDR2_E_NULL, false);
+    }
     // decode over the same buffers, one token per (sequence, head), in place
     if (tok) {
         EXPECT(gdr2_decode_step(B, H, dk, dv, dt, q.p, k.p, v.p, la.f(), b.p, w.p, S0.f(), S0.f(), o.p,
@@ -144,6 +156,12 @@ static void huge_cases() {
     }
     EXPECT(gdr2_out_gate_fwd(huge, 128, GDR2_BF16, P[0], P[1], (float*)P[2], 1e-6f, P[3], nullptr), GDR2_E_SHAPE,
            false);
+    // factors beyond the no-allocation scratch: a valid shape that needs more than 128 MiB
+    void* F[7];  // 4 GiB apart: the token tensors of this shape do not overlap
+    for (int i = 0; i < 7; ++i) F[i] = (void*)(uintptr_t)(((uintptr_t)1 << 32) * (i + 1));
+    EXPECT(gdr2_fwd_infer_noalloc_ex(1, 64 * 1700, 1, 128, 128, GDR2_BF16, 0, nullptr, F[0], F[1], F[2],
+                                     (float*)F[3], F[4], F[5], nullptr, F[6], nullptr, nullptr),
+           GDR2_E_TOO_LARGE, false);
     if (gdr2_out_gate_bwd_workspace_bytes(-5, 128) != 0) { std::printf("FAIL negative rows\n"); ++g_fail; }
 }
 

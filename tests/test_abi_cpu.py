@@ -34,8 +34,8 @@ def test_library_exports_every_declared_symbol():
 def test_version_and_strings():
     lib = load_library()
     assert lib.gdr2_abi_version() == 3
-    for s in range(10):
-        assert lib.gdr2_status_string(s)
+    for s in range(11):
+        assert lib.gdr2_status_string(s) and lib.gdr2_status_string(s) != b"unknown status"
     assert lib.gdr2_dtype_size(0) == 4 and lib.gdr2_dtype_size(1) == 2 and lib.gdr2_dtype_size(7) == 0
     assert lib.gdr2_num_chunks(0) == 0 and lib.gdr2_num_chunks(1) == 1 and lib.gdr2_num_chunks(64) == 1
     assert lib.gdr2_num_chunks(65) == 2
@@ -138,6 +138,40 @@ def test_recompute_backward_rejects_before_launch():
     assert call(dq=0x10000) == E_ALIAS
     assert call(ws=0x300000) == E_ALIAS      # workspace over dO
     assert call(S0=0x400000) == E_ALIAS      # an input under the gradient outputs
+
+
+def test_noalloc_entry_point_rejects_before_launch():
+    """The no-allocation forward-only call validates like gdr2_fwd_infer_ex (no workspace
+    argument) and rejects problems whose factors exceed its static scratch with GDR2_E_TOO_LARGE;
+    none of these calls reaches the device."""
+    lib = load_library()
+    P = lambda a: _fake(a)
+    cap = lib.gdr2_fwd_infer_noalloc_max_bytes()
+    assert cap == 128 << 20
+    ins = [P(0x10000 + i * 0x8000) for i in range(6)]
+
+    def call(B=1, T=8, H=1, dk=64, dv=64, dt=1, o=0x90000, gates=0, pro=None):
+        return lib.gdr2_fwd_infer_noalloc_ex(B, T, H, dk, dv, dt, gates, pro, *ins, NULL,
+                                             P(o) if o else NULL, NULL, NULL)
+    assert call(dt=2) == E_DTYPE
+    assert call(dk=32) == E_UNSUP
+    assert call(gates=9) == E_UNSUP
+    assert call(o=0) == E_NULL
+    assert call(o=0x90008) == E_ALIGN
+    assert call(o=0x10000) == E_ALIAS
+    from gated_delta_rule_gdr_amd import Prologue
+    assert call(pro=ctypes.byref(Prologue(1.0, 0.0))) == 9
+    # largest sequence whose factors fit, and the next chunk over the limit (B = H = 1, d = 128, bf16)
+    per_chunk = lib.gdr2_fwd_infer_workspace_bytes(1, 64, 1, 128, 128, 1)
+    n = cap // per_chunk
+    while lib.gdr2_fwd_infer_workspace_bytes(1, 64 * n, 1, 128, 128, 1) > cap:
+        n -= 1
+    assert lib.gdr2_fwd_infer_workspace_bytes(1, 64 * (n + 1), 1, 128, 128, 1) > cap
+    far = lambda T: lib.gdr2_fwd_infer_noalloc_ex(1, T, 1, 128, 128, 1, 0, NULL,
+                                                  *[P(0x100000000 * (i + 1)) for i in range(6)], NULL,
+                                                  P(0x1000000000), NULL, NULL)
+    assert far(64 * (n + 1)) == 10
+    assert far(64 * n + 65) == 10
 
 
 def _fake(addr):
