@@ -965,11 +965,12 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
         f32x4 q4, k4, b4;
         act(ib, q4, k4, b4, true);
         f32x4 eb, qb, kb;
-        const f32x4 tb = *(const f32x4*)(&sm.tot[R][i0]);
+        f32x4 tb = {0.f, 0.f, 0.f, 0.f};  // deep-decay path: right factor referenced to the block end
+        if (deep) tb = *(const f32x4*)(&sm.tot[R][i0]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const float x = valid ? __expf(sc[ib][e]) : 0.f;
-            const float y = valid ? __expf(deep ? tb[e] - sc[ib][e] : -sc[ib][e]) : 0.f;
+            const float y = valid ? __expf(tb[e] - sc[ib][e]) : 0.f;
             eb[e] = b4[e] * k4[e] * x;
             qb[e] = q4[e] * x;
             kb[e] = k4[e] * y;
@@ -1072,7 +1073,8 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
         // deep-decay path: the diagonal-block terms, each with exp(G_r - G_s) <= 1 (s <= r, same
         // block), from lane 16 g + s%16 of this wave (same channels); right factors from single
         // exponents
-        f32x4 xq = {0.f, 0.f, 0.f, 0.f}, xe = xq, xkb = xq, yd = xq, yt = xq;  // diagonal-block terms
+        f32x4 xq = {0.f, 0.f, 0.f, 0.f}, xe = xq, xkb = xq;  // diagonal-block terms (deep path)
+        f32x4 ykb, ykt;  // right factors of the dKbar and dKtilde sums
         if (deep) {
             const f32x4 e4 = b4 * k4, l4 = sc[ib];
             const OT* dPT = sm.u.g.dPT;
@@ -1095,27 +1097,24 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
             const f32x4 tb = *(const f32x4*)(&sm.tot[R][i0]), hl = *(const f32x4*)(&sm.hRl[R][i0]);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                yd[e] = __expf(tb[e] - sc[ib][e]);
-                yt[e] = __expf(hl[e] - sc[ib][e]);
+                ykb[e] = __expf(tb[e] - sc[ib][e]);
+                ykt[e] = __expf(hl[e] - sc[ib][e]);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                ykb[e] = __expf(-sc[ib][e]);
+                ykt[e] = hr[e] * ykb[e];
             }
         }
         f32x4 dqv, dkv, dbv, kdk;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const float x = __expf(sc[ib][e]);
-            float dq, de, dkb, dkt;
-            if (deep) {
-                dq = x * A1[ib][e] + xq[e];
-                de = x * A2[ib][e] + xe[e];
-                dkb = yd[e] * A4[ib][e] + xkb[e];
-                dkt = yt[e] * A3[ib][e];
-            } else {
-                const float y = __expf(-sc[ib][e]);
-                dq = x * A1[ib][e];
-                de = x * A2[ib][e];
-                dkb = y * A4[ib][e];
-                dkt = hr[e] * y * A3[ib][e];
-            }
+            const float dq = x * A1[ib][e] + xq[e];
+            const float de = x * A2[ib][e] + xe[e];
+            const float dkb = ykb[e] * A4[ib][e] + xkb[e];
+            const float dkt = ykt[e] * A3[ib][e];
             dqv[e] = dq;
             dkv[e] = dkb + dkt + b4[e] * de;
             dbv[e] = k4[e] * de;
@@ -1226,6 +1225,7 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
             }
         }
     }
+
 }
 
 template <typename OT, int DK, int DV>
