@@ -4,9 +4,13 @@ One step = one pass of the whole chunked hot path over one batch of the model-sh
 (B=4, T=4096, H=16, d_k=d_v=128, bf16 q/k/v/b/w, fp32 log-decay and state): the WY-factor
 kernel, the forward state carry (o), the backward state-gradient carry and the chunk-gradient
 kernel, in that order on one stream.  Inputs are synthetic (seeded), already resident in HBM when
-the timed region starts.  Prints one JSON line.
+the timed region starts.  Prints one JSON line; besides the step it reports the decode workload
+(256 sequences x 16 heads, 1024 steps), the gate-shape and fused-prologue variants of the step,
+the output epilogue, the other named workloads (long context, tied-gate reductions, the fp32
+reference shape) and the fp64 oracle on the host as a CPU baseline.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode]
+                  [--no-workloads] [--decode-steps N] [--profile-pass]
 """
 from __future__ import annotations
 
@@ -61,6 +65,23 @@ def measured_traffic(kernel):
     return int(m.group(1)) + int(m.group(2)) if m else None
 
 
+def host_cpu():
+    """The host's CPU model and logical CPU count (from /proc/cpuinfo and os.cpu_count)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    if model is None:
+        import platform
+        model = platform.processor() or platform.machine()
+    return model, os.cpu_count()
+
+
 def cpu_baseline():
     """The fp64 oracle (token recurrence + hand-derived backward) on the host cores, on the same
     synthetic batch as the GPU step (B=4, T=4096, H=16): its cost is bounded (about 1.2e11 fp64
@@ -73,28 +94,31 @@ def cpu_baseline():
     orc.forward(x["q"], x["k"], x["v"], x["log_alpha"], x["b"], x["w"])
     orc.backward(x["q"], x["k"], x["v"], x["log_alpha"], x["b"], x["w"], x["dO"])
     dt = time.perf_counter() - t0
+    model, ncpu = host_cpu()
     return {"value": round(B * T / dt / 1e6, 6), "unit": "Mtokens/s", "cores": orc.num_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": model, "host_logical_cpus": ncpu,
             "sample": f"fp64 oracle forward + backward over the full timed batch (B={B} T={T} "
                       f"H={H} d=128, one chain per OpenMP task), {dt:.1f} s wall"}
 
 
 def bench_decode(torch, lib_decode, steps):
     """Recurrent decode: 256 sequences x 16 heads, fp32 state in HBM updated in place, bf16
-    token inputs (a new token per step, pre-generated for 8 steps and cycled)."""
+    token inputs, a fresh token per step (all steps drawn before the timed region; the decode
+    workload is 1024 steps)."""
     from gated_delta_rule_gdr_amd.inputs import decode_inputs
     N = 256
     S = torch.zeros((N, H, DK, DV), dtype=torch.float32, device="cuda")
-    xs = [decode_inputs(s, N=N, H=H, dk=DK, dv=DV, device="cuda") for s in range(8)]
+    xs = [decode_inputs(s, N=N, H=H, dk=DK, dv=DV, device="cuda") for s in range(steps)]
     o = torch.empty((N, H, DV), dtype=torch.bfloat16, device="cuda")
     for s in range(3):
-        x = xs[s % 8]
+        x = xs[s]
         lib_decode(x["q"], x["k"], x["v"], x["log_alpha"], x["b"], x["w"], S_in=S, S_out=S)
+    S.zero_()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for s in range(steps):
-        x = xs[s % 8]
+        x = xs[s]
         lib_decode(x["q"], x["k"], x["v"], x["log_alpha"], x["b"], x["w"], S_in=S, S_out=S)
     e1.record()
     torch.cuda.synchronize()
@@ -107,6 +131,93 @@ def bench_decode(torch, lib_decode, steps):
             "steps": steps}
 
 
+def train_step_fn(torch, g2, x, B_, T_, H_, dk, dv, prologue=None, S0=None, want_ST=False):
+    """The four phase entry points of one forward + backward over the batch x (device tensors),
+    with every buffer allocated up front; returns step(ev=None) that records an event before each
+    phase and after the last when given a list of five."""
+    dt = x["q"].dtype
+    fws = torch.empty(g2.fwd_workspace_bytes(B_, T_, H_, dk, dv, dt), dtype=torch.uint8, device="cuda")
+    bws = torch.empty(g2.bwd_workspace_bytes(B_, T_, H_, dk, dv, dt), dtype=torch.uint8, device="cuda")
+    o = torch.empty((B_, T_, H_, dv), dtype=dt, device="cuda")
+    ST = torch.empty((B_, H_, dk, dv), dtype=torch.float32, device="cuda") if want_ST else None
+    dS0 = torch.empty((B_, H_, dk, dv), dtype=torch.float32, device="cuda")
+    gr = {n: torch.empty_like(x[s_]) for n, s_ in (("dq", "q"), ("dk", "k"), ("dv", "v"),
+                                                   ("dlog_alpha", "log_alpha"), ("db", "b"), ("dw", "w"))}
+    q, k, v, la, b, w, dO = (x[n] for n in ("q", "k", "v", "log_alpha", "b", "w", "dO"))
+
+    def step(ev=None):
+        if ev: ev[0].record()
+        g2.gdr2_fwd_factors(q, k, v, la, b, w, fws, prologue=prologue)
+        if ev: ev[1].record()
+        g2.gdr2_fwd_carry(B_, T_, H_, dk, dv, dt, fws, o, S0=S0, S_T=ST)
+        if ev: ev[2].record()
+        g2.gdr2_bwd_state(B_, T_, H_, dk, dv, dt, fws, dO, bws, dS0=dS0)
+        if ev: ev[3].record()
+        g2.gdr2_bwd_grads(q, k, v, la, b, w, fws, dO, bws, gr, prologue=prologue)
+        if ev: ev[4].record()
+    return step
+
+
+def time_steps(torch, step, steps, warm=2):
+    for _ in range(warm):
+        step()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def bench_workloads(torch, g2, steps):
+    """The other named workloads, each timed on its own: the long-context layer (B=1, T=32768,
+    H=16, d=128, S0 ~ N(0, 0.02^2), forward returning S_T, plus backward), the three tied-gate
+    reductions (B=2, T=2048, H=16, d=128; materialised gate tensors, so the same algorithmic bytes
+    as the plain layer) and the fp32 reference shape (B=1, H=1, T=256, d=64, forward only:
+    launch latency)."""
+    from gated_delta_rule_gdr_amd.inputs import CONFIGS, config_inputs
+    out = {}
+    for name in ("long_ctx", "tied_kda", "tied_gdn", "tied_la"):
+        c = CONFIGS[name]
+        x = config_inputs(name, device="cuda")
+        step = train_step_fn(torch, g2, x, c["B"], c["T"], c["H"], c["dk"], c["dv"], S0=x["S0"],
+                             want_ST=True)
+        ms = time_steps(torch, step, steps)
+        ht = c["B"] * c["T"] * c["H"]
+        alg = (16 * c["dk"] + 30 * c["dk"]) * ht
+        out[name] = {"B": c["B"], "T": c["T"], "H": c["H"], "ms_per_step": round(ms, 4),
+                     "Mtokens_per_s": round(c["B"] * c["T"] / ms / 1e3, 3),
+                     "hbm_frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        del x, step
+    c = CONFIGS["pr1_fp32"]
+    x = config_inputs("pr1_fp32", device="cuda")
+    ws = torch.empty(g2.fwd_infer_workspace_bytes(c["B"], c["T"], c["H"], c["dk"], c["dv"], torch.float32),
+                     dtype=torch.uint8, device="cuda")
+
+    def fwd():
+        g2.gdr2_fwd_infer(x["q"], x["k"], x["v"], x["log_alpha"], x["b"], x["w"], workspace=ws)
+    ms = time_steps(torch, fwd, 200, warm=5)
+    out["pr1_fp32"] = {"B": 1, "T": 256, "H": 1, "d": 64, "pass": "forward (forward-only entry point)",
+                       "us_per_call": round(ms * 1e3, 2), "Mtokens_per_s": round(256 / ms / 1e3, 3)}
+    return out
+
+
+def step_traffic(ht):
+    """Whole-step HBM traffic from the committed counter summary (sum of the four kernels' scaled
+    FETCH_SIZE + WRITE_SIZE), or None when any kernel source changed since it was taken."""
+    tot = 0
+    for k in KERNELS:
+        t = measured_traffic(k)
+        if t is None:
+            return None
+        tot += t
+    alg = (16 * DK + 30 * DK)
+    return {"bytes": tot, "B_per_head_token": round(tot / ht, 1), "alg_B_per_head_token": alg,
+            "ratio_to_alg": round(tot / ht / alg, 3)}
+
+
 def bench_gate_variants(torch, g2, steps):
     """The same fwd+bwd step with scalar-per-head gates (one value per token and head instead of
     one per channel): erase and write gates ("bw"), and additionally the decay ("bwa").  Each
@@ -114,36 +225,12 @@ def bench_gate_variants(torch, g2, steps):
     over as pre-activations, the kernels applying the q/k normalisation, the sigmoid gates and the
     softplus decay themselves (same bytes as the plain step)."""
     from gated_delta_rule_gdr_amd.inputs import layer_inputs
-    bf = torch.bfloat16
     out = {}
     for name, scalar, pro in (("scalar_bw", "bw", None), ("scalar_bwa", "bwa", None),
                               ("prologue", "", g2.Prologue(0.1, 1e-6))):
         x = layer_inputs(B, T, H, DK, DV, dtype="bf16", seed=1001, device="cuda", scalar=scalar,
                          raw=pro is not None)
-        fws = torch.empty(g2.fwd_workspace_bytes(B, T, H, DK, DV, bf), dtype=torch.uint8, device="cuda")
-        bws = torch.empty(g2.bwd_workspace_bytes(B, T, H, DK, DV, bf), dtype=torch.uint8, device="cuda")
-        o = torch.empty((B, T, H, DV), dtype=bf, device="cuda")
-        gr = {n: torch.empty_like(x[s_]) for n, s_ in (("dq", "q"), ("dk", "k"), ("dv", "v"),
-                                                       ("dlog_alpha", "log_alpha"), ("db", "b"),
-                                                       ("dw", "w"))}
-        q, k, v, la, b, w, dO = (x[n] for n in ("q", "k", "v", "log_alpha", "b", "w", "dO"))
-
-        def step():
-            g2.gdr2_fwd_factors(q, k, v, la, b, w, fws, prologue=pro)
-            g2.gdr2_fwd_carry(B, T, H, DK, DV, bf, fws, o)
-            g2.gdr2_bwd_state(B, T, H, DK, DV, bf, fws, dO, bws)
-            g2.gdr2_bwd_grads(q, k, v, la, b, w, fws, dO, bws, gr, prologue=pro)
-
-        for _ in range(2):
-            step()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(steps):
-            step()
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / steps
+        ms = time_steps(torch, train_step_fn(torch, g2, x, B, T, H, DK, DV, prologue=pro), steps)
         # algorithmic bytes per head-token: a scalar bf16 gate moves 2 B instead of 2 d, a scalar
         # decay 4 B instead of 4 d (read in both passes; its gradient written once)
         fwd, bwd = 16 * DK, 30 * DK
@@ -152,10 +239,9 @@ def bench_gate_variants(torch, g2, steps):
             fwd -= wide * (2 * DK - 2)
             bwd -= wide * (4 * DK - 4)
         out[name] = {"ms_per_step": round(ms, 4),
-                                   "Mtokens_per_s": round(B * T / ms / 1e3, 3),
-                                   "alg_bytes_per_head_token": fwd + bwd,
-                                   "hbm_frac": round((fwd + bwd) * B * T * H / (ms * 1e-3) / 1e9
-                                                     / HBM_PEAK_GBS, 4)}
+                     "Mtokens_per_s": round(B * T / ms / 1e3, 3),
+                     "alg_bytes_per_head_token": fwd + bwd,
+                     "hbm_frac": round((fwd + bwd) * B * T * H / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     return out
 
 
@@ -195,7 +281,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--decode-steps", type=int, default=256)
+    ap.add_argument("--decode-steps", type=int, default=1024)
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the long-context, tied-gate and fp32-reference lines")
     ap.add_argument("--profile-pass", action="store_true",
                     help="short run for hardware-counter passes: 1 warm-up + 1 step, one decode "
                          "step, then a 512 MiB device-to-device copy that calibrates FETCH_SIZE / "
@@ -216,26 +304,7 @@ def main():
 
     dev = "cuda"
     x = layer_inputs(B, T, H, DK, DV, dtype="bf16", seed=1001, device=dev)
-    bf = torch.bfloat16
-    fws = torch.empty(g2.fwd_workspace_bytes(B, T, H, DK, DV, bf), dtype=torch.uint8, device=dev)
-    bws = torch.empty(g2.bwd_workspace_bytes(B, T, H, DK, DV, bf), dtype=torch.uint8, device=dev)
-    o = torch.empty((B, T, H, DV), dtype=bf, device=dev)
-    grads = dict(dq=torch.empty_like(x["q"]), dk=torch.empty_like(x["k"]), dv=torch.empty_like(x["v"]),
-                 dlog_alpha=torch.empty_like(x["log_alpha"]), db=torch.empty_like(x["b"]),
-                 dw=torch.empty_like(x["w"]))
-    dS0 = torch.empty((B, H, DK, DV), dtype=torch.float32, device=dev)
-    q, k, v, la, b, w, dO = (x[n] for n in ("q", "k", "v", "log_alpha", "b", "w", "dO"))
-
-    def step(ev=None):
-        if ev: ev[0].record()
-        g2.gdr2_fwd_factors(q, k, v, la, b, w, fws)
-        if ev: ev[1].record()
-        g2.gdr2_fwd_carry(B, T, H, DK, DV, bf, fws, o)
-        if ev: ev[2].record()
-        g2.gdr2_bwd_state(B, T, H, DK, DV, bf, fws, dO, bws, dS0=dS0)
-        if ev: ev[3].record()
-        g2.gdr2_bwd_grads(q, k, v, la, b, w, fws, dO, bws, grads)
-        if ev: ev[4].record()
+    step = train_step_fn(torch, g2, x, B, T, H, DK, DV)
 
     for _ in range(args.warmup):
         step()
@@ -283,19 +352,22 @@ def main():
                           "mfma_frac": round(flops / (ms_step * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
                           "roofline_Mtokens_per_s": round(tokens / (step_alg_bytes / (HBM_PEAK_GBS * 1e9)) / 1e6, 2)},
         "kernel_us": {kn: round(t_, 2) for kn, t_ in kern_us.items()},
+        "step_traffic": step_traffic(ht),
     }
     if not args.no_decode:
         out["decode"] = bench_decode(torch, g2.gdr2_decode_step, args.decode_steps)
     if not args.profile_pass:
         out["gate_variants"] = bench_gate_variants(torch, g2, 5)
         out["out_gate"] = bench_out_gate(torch, g2, 10)
+        if not args.no_workloads:
+            out["workloads"] = bench_workloads(torch, g2, 5)
     if args.profile_pass:
         src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         dst.copy_(src)
         # a bf16 GEMM of known size calibrates the MFMA instruction counters the same way
-        ga = torch.randn(4096, 4096, dtype=bf, device=dev)
-        gb = torch.randn(4096, 4096, dtype=bf, device=dev)
+        ga = torch.randn(4096, 4096, dtype=torch.bfloat16, device=dev)
+        gb = torch.randn(4096, 4096, dtype=torch.bfloat16, device=dev)
         torch.mm(ga, gb)
         torch.cuda.synchronize()
         print("profile pass done: 512 MiB copy and 4096^3 bf16 GEMM issued for counter calibration",

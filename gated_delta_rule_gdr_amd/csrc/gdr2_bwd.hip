@@ -363,6 +363,12 @@ __global__ __launch_bounds__(2 * kThreads, 1) void gdr2_dstate_lds_kernel(BwdPar
         const bf16* Ks = sm.slot[sl] + Cf::OK;
         const bf16* Ps = sm.slot[sl] + Cf::OP;
         const bf16* Os = sm.slot[sl] + Cf::OO;
+        // dO as a B operand (k = tokens) per (k-step, value block): read once, used by both phases
+        bf16x8 ob[NCK][NJB];
+#pragma unroll
+        for (int kk = 0; kk < NCK; ++kk)
+#pragma unroll
+            for (int jb = 0; jb < NJB; ++jb) ob[kk][jb] = FR::tr(Os, PO, kk * KS, 16 * jb);
         // ---- dDelta = Ktilde dS' + P^T dO   (wave R: token block R)
         {
             f32x4 aD[NJB];
@@ -379,24 +385,45 @@ __global__ __launch_bounds__(2 * kThreads, 1) void gdr2_dstate_lds_kernel(BwdPar
                 if (kk * KS + KS > 16 * R) {  // P^T is upper triangular: s >= r
                     const bf16x8 a = FF::ftr(Ps, C, kk * KS, 16 * R);
 #pragma unroll
-                    for (int jb = 0; jb < NJB; ++jb) MM::mma(aD[jb], a, FR::tr(Os, PO, kk * KS, 16 * jb));
+                    for (int jb = 0; jb < NJB; ++jb) MM::mma(aD[jb], a, ob[kk][jb]);
                 }
             }
 #pragma unroll
             for (int jb = 0; jb < NJB; ++jb) store_acc_T(sm.dDT, PC, 16 * jb, 16 * R, aD[jb]);
         }
         lds_barrier();
-        // ---- dS <- Diag(gamma) dS' + Qbar^T dO + (-Y)^T dDelta
+        // ---- dS <- Diag(gamma) dS' + Qbar^T dO + (-Y)^T dDelta: dDelta^T fragments per (k-step,
+        // value block) and Qbar^T, -Y^T per (key block, k-step) read once (this wave's state blocks
+        // come in groups of NJB sharing one key block)
+        bf16x8 ddf[NCK][NJB];
+#pragma unroll
+        for (int kk = 0; kk < NCK; ++kk)
+#pragma unroll
+            for (int jb = 0; jb < NJB; ++jb) ddf[kk][jb] = FR::kc(sm.dDT, PC, 16 * jb, kk * KS);
+#pragma unroll
+        for (int v = 0; v < BPW / NJB; ++v) {
+            const int ib = R * BPW / NJB + v;
+            const f32x4 gm = *(const f32x4*)(sm.gam[sl] + 16 * ib + 4 * (l >> 4));
+            bf16x8 qf[NCK], yf[NCK];
+#pragma unroll
+            for (int kk = 0; kk < NCK; ++kk) {
+                qf[kk] = FF::ftr(Qs, DK, kk * KS, 16 * ib);
+                yf[kk] = FF::ftr(Ys, DK, kk * KS, 16 * ib);
+            }
+#pragma unroll
+            for (int jb = 0; jb < NJB; ++jb) {
+                f32x4& acc = dS[v * NJB + jb];
+                acc *= gm;
+#pragma unroll
+                for (int kk = 0; kk < NCK; ++kk) {
+                    MM::mma(acc, qf[kk], ob[kk][jb]);
+                    MM::mma(acc, yf[kk], ddf[kk][jb]);
+                }
+            }
+        }
 #pragma unroll
         for (int u = 0; u < BPW; ++u) {
             const int bi = R * BPW + u, ib = bi / NJB, jb = bi % NJB;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) dS[u][e] *= sm.gam[sl][16 * ib + acc_row(e)];
-#pragma unroll
-            for (int kk = 0; kk < NCK; ++kk) {
-                MM::mma(dS[u], FF::ftr(Qs, DK, kk * KS, 16 * ib), FR::tr(Os, PO, kk * KS, 16 * jb));
-                MM::mma(dS[u], FF::ftr(Ys, DK, kk * KS, 16 * ib), FR::kc(sm.dDT, PC, 16 * jb, kk * KS));
-            }
             store_acc_T(sm.dST, PK, 16 * jb, 16 * ib, dS[u]);
         }
         lds_barrier();

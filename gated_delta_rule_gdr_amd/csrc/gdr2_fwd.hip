@@ -435,13 +435,20 @@ __global__ __launch_bounds__(2 * kThreads, 1) void gdr2_carry_lds_kernel(FwdPara
 #pragma unroll
         for (int jb = 0; jb < NJB; ++jb) store_acc_T(sm.DT, PC, 16 * jb, 16 * R, aD[jb]);
         lds_barrier();
-        // ---- O += P Delta, S' = Diag(gamma) S + Ktilde^T Delta
+        // ---- O += P Delta, S' = Diag(gamma) S + Ktilde^T Delta.  Every operand fragment is read
+        // from LDS once: Delta^T per (k-step, value block), Ktilde^T per (key block, k-step) -- this
+        // wave's state blocks come in groups of NJB that share one key block.
+        bf16x8 dtf[NCK][NJB];
+#pragma unroll
+        for (int kk = 0; kk < NCK; ++kk)
+#pragma unroll
+            for (int jb = 0; jb < NJB; ++jb) dtf[kk][jb] = FR::kc(sm.DT, PC, 16 * jb, kk * KS);
 #pragma unroll
         for (int kk = 0; kk < NCK; ++kk) {
             if (kk * KS < 16 * R + 16) {
                 const bf16x8 ap = FF::fkc(Ps, C, 16 * R, kk * KS);
 #pragma unroll
-                for (int jb = 0; jb < NJB; ++jb) MM::mma(aO[jb], ap, FR::kc(sm.DT, PC, 16 * jb, kk * KS));
+                for (int jb = 0; jb < NJB; ++jb) MM::mma(aO[jb], ap, dtf[kk][jb]);
             }
         }
 #pragma unroll
@@ -450,13 +457,23 @@ __global__ __launch_bounds__(2 * kThreads, 1) void gdr2_carry_lds_kernel(FwdPara
             for (int e = 0; e < 4; ++e)
                 sm.Ost[(16 * R + acc_row(e)) * PO + 16 * jb + acc_col()] = (bf16)aO[jb][e];
 #pragma unroll
+        for (int v = 0; v < BPW / NJB; ++v) {
+            const int ib = R * BPW / NJB + v;
+            const f32x4 gm = *(const f32x4*)(sm.gam[sl] + 16 * ib + 4 * (l >> 4));
+            bf16x8 kf[NCK];
+#pragma unroll
+            for (int kk = 0; kk < NCK; ++kk) kf[kk] = FF::ftr(Ks, DK, kk * KS, 16 * ib);
+#pragma unroll
+            for (int jb = 0; jb < NJB; ++jb) {
+                f32x4& acc = Sacc[v * NJB + jb];
+                acc *= gm;
+#pragma unroll
+                for (int kk = 0; kk < NCK; ++kk) MM::mma(acc, kf[kk], dtf[kk][jb]);
+            }
+        }
+#pragma unroll
         for (int u = 0; u < BPW; ++u) {
             const int bi = R * BPW + u, ib = bi / NJB, jb = bi % NJB;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) Sacc[u][e] *= sm.gam[sl][16 * ib + acc_row(e)];
-#pragma unroll
-            for (int kk = 0; kk < NCK; ++kk)
-                MM::mma(Sacc[u], FF::ftr(Ks, DK, kk * KS, 16 * ib), FR::kc(sm.DT, PC, 16 * jb, kk * KS));
             store_acc_T(sm.ST, PK, 16 * jb, 16 * ib, Sacc[u]);
         }
         lds_barrier();
