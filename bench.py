@@ -111,7 +111,7 @@ def bench_decode(torch, lib_decode, steps):
     xs = [decode_inputs(s, N=N, H=H, dk=DK, dv=DV, device="cuda") for s in range(steps)]
     o = torch.empty((N, H, DV), dtype=torch.bfloat16, device="cuda")
     for s in range(3):
-        x = xs[s]
+        x = xs[s % steps]
         lib_decode(x["q"], x["k"], x["v"], x["log_alpha"], x["b"], x["w"], S_in=S, S_out=S)
     S.zero_()
     torch.cuda.synchronize()
