@@ -354,7 +354,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void gdr2_dstate_lds_kernel(BwdPar
                 const int x = x0 + tid;
                 if (NSV % kThreads == 0 || x < NSV) {
                     const int j = (x * 8) / DK, i = (x * 8) % DK;
-                    *(i32x4*)(dst + (long)j * DK + i) = *(const i32x4*)(sm.dST + j * PK + i);
+                    store_stream((i32x4*)(dst + (long)j * DK + i), *(const i32x4*)(sm.dST + j * PK + i));
                 }
             }
         }

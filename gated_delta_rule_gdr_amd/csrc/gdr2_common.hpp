@@ -62,6 +62,17 @@ __device__ __forceinline__ void store4(bf16* p, f32x4 v) {
     *(bf16x4*)p = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
 }
 
+// Streaming (nontemporal) stores for outputs that a later kernel reads back, written by whole
+// cache lines per wave instruction: they go past the L2 instead of sitting in it as dirty lines
+// that the next kernel then has to write back while it runs.  (Partial-line pieces are not
+// streamed: written past the L2 they become many small memory writes.)
+template <typename T>
+__device__ __forceinline__ void store_stream(T* p, const T& v) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ void store4_stream(bf16* p, f32x4 v) {
+    store_stream((bf16x4*)p, bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]});
+}
+__device__ __forceinline__ void store4_stream(float* p, f32x4 v) { store_stream((f32x4*)p, v); }
+
 // ------------------------------------------------------------------ MFMA wrappers
 template <typename OT> struct Mfma;
 

@@ -395,7 +395,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void gdr2_carry_lds_kernel(FwdPara
                 const int x = x0 + tid;
                 if (NSV % kThreads == 0 || x < NSV) {
                     const int j = (x * 8) / DK, i = (x * 8) % DK;
-                    *(i32x4*)(dst + (long)j * DK + i) = *(const i32x4*)(sm.ST + j * PK + i);
+                    store_stream((i32x4*)(dst + (long)j * DK + i), *(const i32x4*)(sm.ST + j * PK + i));
                 }
             }
         }

@@ -154,7 +154,7 @@ __device__ __forceinline__ void store_lane(OT* row, int ks, int g, const float* 
 template <typename OT>
 __device__ __forceinline__ void store_lane_F(OT* tile, int cols, int r, int ks, int g, const float* v) {
     if constexpr (sizeof(OT) == 2) {
-        *(bf16x8*)(tile + FLay<OT>::off(r, ks * 32 + 8 * g, cols)) = Frag<bf16>::from_f32(v);
+        store_stream((bf16x8*)(tile + FLay<OT>::off(r, ks * 32 + 8 * g, cols)), Frag<bf16>::from_f32(v));
     } else {
         tile[FLay<OT>::off(r, ks * 4 + g, cols)] = v[0];
     }
@@ -464,7 +464,7 @@ __device__ __forceinline__ void wy_factors(WySmem<OT, DK, DV>& sm, const WyChunk
         constexpr int VEC = 16 / (int)sizeof(OT);
         for (int x = threadIdx.x; x < C * C / VEC; x += kThreads) {  // fragment order
             const int rr = FLay<OT>::unit_row(x, C), ss = FLay<OT>::unit_col(x, C);
-            *(i32x4*)(tg + (long)x * VEC) = *(const i32x4*)(sm.Tm + rr * PC + ss);
+            store_stream((i32x4*)(tg + (long)x * VEC), *(const i32x4*)(sm.Tm + rr * PC + ss));
         }
     }
     lds_barrier();
@@ -478,7 +478,7 @@ __device__ __forceinline__ void wy_factors(WySmem<OT, DK, DV>& sm, const WyChunk
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             for (int k0 = 0; k0 < kend; k0 += KS)
                 MM::mma(acc, FR::tr(sm.u.e.Eg, PK, k0, 16 * ib), FR::kc(sm.Tm, PC, 16 * R, k0));
-            store4(yt + FLay<OT>::off(r, 16 * ib + 4 * g, DK), f32x4{-acc[0], -acc[1], -acc[2], -acc[3]});
+            store4_stream(yt + FLay<OT>::off(r, 16 * ib + 4 * g, DK), f32x4{-acc[0], -acc[1], -acc[2], -acc[3]});
         }
     }
     {
@@ -488,7 +488,7 @@ __device__ __forceinline__ void wy_factors(WySmem<OT, DK, DV>& sm, const WyChunk
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             for (int k0 = 0; k0 < kend; k0 += KS)
                 MM::mma(acc, FR::kc(sm.Tm, PC, 16 * R, k0), FR::tr(sm.u.e.Z, PV, k0, 16 * jb));
-            store4(ub + ((long)(R * (DV / 16) + jb) * 64 + l) * 4, acc);
+            store4_stream(ub + ((long)(R * (DV / 16) + jb) * 64 + l) * 4, acc);
         }
     }
 }
