@@ -190,6 +190,7 @@ static gdr2::FwdParams fwd_params(int64_t B, int64_t T, int64_t H, int64_t dv, c
     p.ST = S_T;
     p.states = ws ? (char*)ws + L.states : nullptr;
     p.wy = wy_bufs(L, ws);
+    p.stream = L.states >= gdr2::kStreamFactorBytes;  // L.states = bytes of the factor tiles
     return p;
 }
 

@@ -62,12 +62,12 @@ hipError_t noalloc_scratch(void** ptr) {
     return hipSuccess;
 }
 
-template <typename OT, int DK, int DV, int MODE>
+template <typename OT, int DK, int DV, int MODE, bool STREAM>
 __global__ __launch_bounds__(kThreads, 2) void gdr2_wy_kernel(FwdParams p) {
     __shared__ WySmem<OT, DK, DV> sm;
     WyChunk<OT, DK, DV> ch(p.B, p.H, p.T, p.DV, p.NC, p.gates, p.pro, blockIdx.x, p.q, p.k, p.b,
                            p.la, p.v, p.w);
-    wy_factors<OT, DK, DV, MODE>(sm, ch, p.wy);
+    wy_factors<OT, DK, DV, MODE, STREAM>(sm, ch, p.wy);
 }
 
 template <typename OT, int DK, int DVS>
@@ -523,16 +523,22 @@ __global__ __launch_bounds__(2 * kThreads, 1) void gdr2_carry_lds_kernel(FwdPara
     }
 }
 
+template <typename OT, int DK, int DV, bool STREAM>
+static void launch_wy_mode(const FwdParams& p, long nblk, hipStream_t s) {
+    if (p.prologue)
+        hipLaunchKernelGGL((gdr2_wy_kernel<OT, DK, DV, kModePrologue, STREAM>), dim3(nblk), dim3(kThreads), 0, s, p);
+    else if (p.gates)
+        hipLaunchKernelGGL((gdr2_wy_kernel<OT, DK, DV, kModeGates, STREAM>), dim3(nblk), dim3(kThreads), 0, s, p);
+    else
+        hipLaunchKernelGGL((gdr2_wy_kernel<OT, DK, DV, kModePlain, STREAM>), dim3(nblk), dim3(kThreads), 0, s, p);
+}
 template <typename OT, int DK, int DV>
 static hipError_t launch_wy(const FwdParams& p, hipStream_t s) {
     const long nblk = (long)p.B * p.H * p.NC;
     if (nblk == 0) return hipSuccess;
-    if (p.prologue)
-        hipLaunchKernelGGL((gdr2_wy_kernel<OT, DK, DV, kModePrologue>), dim3(nblk), dim3(kThreads), 0, s, p);
-    else if (p.gates)
-        hipLaunchKernelGGL((gdr2_wy_kernel<OT, DK, DV, kModeGates>), dim3(nblk), dim3(kThreads), 0, s, p);
-    else
-        hipLaunchKernelGGL((gdr2_wy_kernel<OT, DK, DV, kModePlain>), dim3(nblk), dim3(kThreads), 0, s, p);
+    // streaming instances for the 16-bit path only (the fp32 path is the precision path)
+    if (sizeof(OT) == 2 && p.stream) launch_wy_mode<OT, DK, DV, sizeof(OT) == 2>(p, nblk, s);
+    else launch_wy_mode<OT, DK, DV, false>(p, nblk, s);
     return hipGetLastError();
 }
 

@@ -47,7 +47,15 @@ struct FwdParams {
     float* ST;          // [B,H,DK,DV] fp32 or null
     void* states;       // [B*H][NC][DV][DK] input dtype (chunk-entry states, transposed)
     WyBufs wy;
+    int stream;         // write the factor tiles past the L2 (see kStreamFactorBytes)
 };
+
+// Factor tiles are streamed past the caches (nontemporal stores) when they take at least this
+// many bytes: then they do not fit the 256 MB memory-side cache and the carry reads them from HBM
+// anyway, and streaming spares the next kernel the write-back of their dirty L2 lines (carry 135
+// -> 121 us at B=4 T=4096 H=16 d=128, 335 MB of factors).  Smaller sets stay cached for the carry
+// (at B=2 T=2048, 84 MB, the carry takes 42 us with cached factors and 58 us with streamed ones).
+constexpr size_t kStreamFactorBytes = (size_t)256 << 20;
 
 struct DecodeParams {
     long N, H;

@@ -151,10 +151,12 @@ __device__ __forceinline__ void store_lane(OT* row, int ks, int g, const float* 
     }
 }
 // The same KPL values stored into a fragment-order tile of `cols` columns (row r).
-template <typename OT>
+template <typename OT, bool STREAM>
 __device__ __forceinline__ void store_lane_F(OT* tile, int cols, int r, int ks, int g, const float* v) {
     if constexpr (sizeof(OT) == 2) {
-        store_stream((bf16x8*)(tile + FLay<OT>::off(r, ks * 32 + 8 * g, cols)), Frag<bf16>::from_f32(v));
+        bf16x8* d = (bf16x8*)(tile + FLay<OT>::off(r, ks * 32 + 8 * g, cols));
+        if constexpr (STREAM) store_stream(d, Frag<bf16>::from_f32(v));
+        else *d = Frag<bf16>::from_f32(v);
     } else {
         tile[FLay<OT>::off(r, ks * 4 + g, cols)] = v[0];
     }
@@ -213,8 +215,10 @@ struct WyChunk {
 // Compute and store the WY factors of one chunk (see the file comment); every thread of the
 // workgroup calls it.  MODE (kModePlain / kModeGates / kModePrologue): the plain instance has no
 // gate branches, so its loads issue back to back; the others read the gate bits (and apply the
-// fused prologue) at run time.
-template <typename OT, int DK, int DV, int MODE>
+// fused prologue) at run time.  STREAM: write the factor tiles with streaming stores (a
+// separate instance: a run-time choice between the two store kinds is folded into one plain
+// store by the compiler).
+template <typename OT, int DK, int DV, int MODE, bool STREAM>
 __device__ __forceinline__ void wy_factors(WySmem<OT, DK, DV>& sm, const WyChunk<OT, DK, DV>& ch, const WyBufs& wy) {
     using Cf = WyCfg<OT, DK, DV>;
     using MM = Mfma<OT>;
@@ -412,8 +416,8 @@ __device__ __forceinline__ void wy_factors(WySmem<OT, DK, DV>& sm, const WyChunk
         Ef[ks] = FR::from_f32(ebk);
         Qf[ks] = FR::from_f32(qbk);
         store_lane<OT>(sm.u.Kb + r * PK, ks, g, kbk);
-        store_lane_F<OT>(qg_out, DK, r, ks, g, qg);
-        store_lane_F<OT>(kt_out, DK, r, ks, g, kt);
+        store_lane_F<OT, STREAM>(qg_out, DK, r, ks, g, qg);
+        store_lane_F<OT, STREAM>(kt_out, DK, r, ks, g, kt);
     }
     lds_barrier();
 
@@ -464,7 +468,9 @@ __device__ __forceinline__ void wy_factors(WySmem<OT, DK, DV>& sm, const WyChunk
         constexpr int VEC = 16 / (int)sizeof(OT);
         for (int x = threadIdx.x; x < C * C / VEC; x += kThreads) {  // fragment order
             const int rr = FLay<OT>::unit_row(x, C), ss = FLay<OT>::unit_col(x, C);
-            store_stream((i32x4*)(tg + (long)x * VEC), *(const i32x4*)(sm.Tm + rr * PC + ss));
+            i32x4* d = (i32x4*)(tg + (long)x * VEC);
+            if constexpr (STREAM) store_stream(d, *(const i32x4*)(sm.Tm + rr * PC + ss));
+            else *d = *(const i32x4*)(sm.Tm + rr * PC + ss);
         }
     }
     lds_barrier();
@@ -478,7 +484,9 @@ __device__ __forceinline__ void wy_factors(WySmem<OT, DK, DV>& sm, const WyChunk
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             for (int k0 = 0; k0 < kend; k0 += KS)
                 MM::mma(acc, FR::tr(sm.u.e.Eg, PK, k0, 16 * ib), FR::kc(sm.Tm, PC, 16 * R, k0));
-            store4_stream(yt + FLay<OT>::off(r, 16 * ib + 4 * g, DK), f32x4{-acc[0], -acc[1], -acc[2], -acc[3]});
+            OT* d = yt + FLay<OT>::off(r, 16 * ib + 4 * g, DK);
+            if constexpr (STREAM) store4_stream(d, f32x4{-acc[0], -acc[1], -acc[2], -acc[3]});
+            else store4(d, f32x4{-acc[0], -acc[1], -acc[2], -acc[3]});
         }
     }
     {
@@ -488,7 +496,9 @@ __device__ __forceinline__ void wy_factors(WySmem<OT, DK, DV>& sm, const WyChunk
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             for (int k0 = 0; k0 < kend; k0 += KS)
                 MM::mma(acc, FR::kc(sm.Tm, PC, 16 * R, k0), FR::tr(sm.u.e.Z, PV, k0, 16 * jb));
-            store4_stream(ub + ((long)(R * (DV / 16) + jb) * 64 + l) * 4, acc);
+            OT* d = ub + ((long)(R * (DV / 16) + jb) * 64 + l) * 4;
+            if constexpr (STREAM) store4_stream(d, acc);
+            else store4(d, acc);
         }
     }
 }
