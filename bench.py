@@ -40,7 +40,7 @@ ALG_BYTES_PER_HT = {"gdr2_wy_kernel": 14 * DK, "gdr2_carry_lds_kernel": 2 * DV,
 ALG_FLOPS_PER_HT = {"forward": 6 * DK * DK + 5 * 64 * DK + 64 * 64 / 3,
                     "backward": 14 * DK * DK + 14 * 64 * DK + 64 * 64}
 KERNELS = ["gdr2_wy_kernel", "gdr2_carry_lds_kernel", "gdr2_dstate_lds_kernel", "gdr2_bgrad_kernel"]
-SOURCES = ["gdr2_common.hpp", "gdr2_wy.hpp", "gdr2_fwd.hip", "gdr2_bwd.hip"]
+SOURCES = ["gdr2_common.hpp", "gdr2_kernels.hpp", "gdr2_wy.hpp", "gdr2_fwd.hip", "gdr2_bwd.hip"]
 
 
 def source_hash():
