@@ -6,7 +6,7 @@ import torch
 from gated_delta_rule_gdr_amd import gdr2_bwd_chunked, gdr2_fwd_chunked
 from gated_delta_rule_gdr_amd.inputs import config_inputs, layer_inputs, strong_decay_inputs, to_f64
 from oracle import oracle as orc
-from tests._util import TOL, announce, assert_close, assert_close_chains, to_np
+from tests._util import TOL, announce, assert_close, assert_close_chains, assert_close_rows, to_np
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -38,11 +38,19 @@ def _check(x, tol, tag):
     announce(tag)
     o, ST, gr = _run(x)
     ro, rS, rg = _oracle(x)
-    errs = {"o": assert_close(f"{tag} o", to_np(o), ro, tol),
-            "S_T": assert_close(f"{tag} S_T", to_np(ST), rS, tol)}
+    errs = {"o": assert_close_chains(f"{tag} o", to_np(o), ro, tol, "tok"),
+            "S_T": assert_close_chains(f"{tag} S_T", to_np(ST), rS, tol, "state")}
     for n in GRADS:
-        errs[n] = assert_close(f"{tag} {n}", to_np(gr[n]), rg[n], tol)
+        errs[n] = assert_close_chains(f"{tag} {n}", to_np(gr[n]), rg[n], tol,
+                                      "state" if n == "dS0" else "tok")
     print("  " + tag + ": " + "  ".join(f"{k} {v:.1e}" for k, v in errs.items()), flush=True)
+    if tol <= TOL["f32"]:  # fp32: every row on its own as well
+        rows = {"o": assert_close_rows(f"{tag} o rows", to_np(o), ro, tol, "tok"),
+                "S_T": assert_close_rows(f"{tag} S_T rows", to_np(ST), rS, tol, "state")}
+        for n in GRADS:
+            rows[n] = assert_close_rows(f"{tag} {n} rows", to_np(gr[n]), rg[n], tol,
+                                        "state" if n == "dS0" else "tok")
+        print("  " + tag + " rows: " + "  ".join(f"{k} {v:.1e}" for k, v in rows.items()), flush=True)
 
 
 @pytest.mark.parametrize("T", [1, 37, 64, 65, 130])

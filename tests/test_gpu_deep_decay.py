@@ -14,7 +14,7 @@ import torch
 from gated_delta_rule_gdr_amd import Prologue, gdr2_bwd_chunked, gdr2_decode_step, gdr2_fwd_chunked
 from gated_delta_rule_gdr_amd.inputs import deep_decay_inputs, layer_inputs, to_f64
 from oracle import oracle as orc
-from tests._util import TOL, announce, assert_close_chains, to_np
+from tests._util import TOL, announce, assert_close_chains, assert_close_rows, to_np
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -42,6 +42,13 @@ def _check_all(tag, o, ST, gr, ro, rS, rg, tol):
         errs[n] = assert_close_chains(f"{tag} {n}", to_np(gr[n]), rg[n], tol, "tok")
     errs["dS0"] = assert_close_chains(f"{tag} dS0", to_np(gr["dS0"]), rg["dS0"], tol, "state")
     print("  " + tag + ": " + "  ".join(f"{k} {v:.1e}" for k, v in errs.items()), flush=True)
+    if tol <= TOL["f32"]:  # fp32: every row on its own as well
+        rows = {"o": assert_close_rows(f"{tag} o rows", to_np(o), ro, tol, "tok"),
+                "S_T": assert_close_rows(f"{tag} S_T rows", to_np(ST), rS, tol, "state"),
+                "dS0": assert_close_rows(f"{tag} dS0 rows", to_np(gr["dS0"]), rg["dS0"], tol, "state")}
+        for n in GRADS:
+            rows[n] = assert_close_rows(f"{tag} {n} rows", to_np(gr[n]), rg[n], tol, "tok")
+        print("  " + tag + " rows: " + "  ".join(f"{k} {v:.1e}" for k, v in rows.items()), flush=True)
 
 
 def _check(x, tol, tag):

@@ -7,7 +7,7 @@ from gated_delta_rule_gdr_amd import gdr2_decode_step, gdr2_fwd_chunked
 from gated_delta_rule_gdr_amd.inputs import (DECODE, config_inputs, decode_inputs, layer_inputs,
                                              strong_decay_inputs, to_f64)
 from oracle import oracle as orc
-from tests._util import TOL, announce, assert_close, assert_close_chains, to_np
+from tests._util import TOL, announce, assert_close, assert_close_chains, assert_close_rows, to_np
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -43,9 +43,14 @@ def _check_fwd(x, tol, tag):
     o, ST, _ = _run_fwd(x)
     f = to_f64(x)
     ro, rS = orc.forward(f["q"], f["k"], f["v"], f["log_alpha"], f["b"], f["w"], f["S0"])
-    eo = assert_close(f"{tag} o", to_np(o), ro, tol)
-    eS = assert_close(f"{tag} S_T", to_np(ST), rS, tol)
-    print(f"  {tag}: o {eo:.2e}  S_T {eS:.2e}", flush=True)
+    eo = assert_close_chains(f"{tag} o", to_np(o), ro, tol, "tok")
+    eS = assert_close_chains(f"{tag} S_T", to_np(ST), rS, tol, "state")
+    msg = f"  {tag}: o {eo:.2e}  S_T {eS:.2e}"
+    if tol <= TOL["f32"]:  # fp32: every row on its own as well
+        ro_ = assert_close_rows(f"{tag} o rows", to_np(o), ro, tol, "tok")
+        rS_ = assert_close_rows(f"{tag} S_T rows", to_np(ST), rS, tol, "state")
+        msg += f"  (rows: o {ro_:.2e}  S_T {rS_:.2e})"
+    print(msg, flush=True)
 
 
 def test_fwd_pr1_fp32():
