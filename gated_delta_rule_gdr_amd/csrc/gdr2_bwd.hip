@@ -512,7 +512,10 @@ struct BgCfg {
     static constexpr int KS = Mfma<OT>::KS, KPL = Mfma<OT>::KPL;
     static constexpr int ES = (int)sizeof(OT);
     static constexpr int PAD = 16 / ES;
-    static constexpr int PK = DK + PAD, PC = C + PAD, PH = DVH + PAD;
+    // key-indexed tiles (-Y, Ktilde, S, dS' and the Gram-phase tiles) padded by 32 bytes per row in
+    // the 16-bit path: their transposed 8-byte reads conflict less in the LDS banks than with 16
+    // bytes (bgrad 436 -> 426 us at B=4 T=4096 H=16 d=128; 48 or more bytes were slower again)
+    static constexpr int PK = DK + (ES == 2 ? 2 : 1) * PAD, PC = C + PAD, PH = DVH + PAD;
     static constexpr int NKS = DK / KS, NIB = DK / 16, NIBH = NIB / 2, NJH = DVH / 16;
     static constexpr int VEC = 16 / ES;
     static constexpr int NSV = DVH * DK / VEC;   // [DVH][DK] tile, 16-byte vectors
