@@ -171,19 +171,30 @@ def time_steps(torch, step, steps, warm=2):
     return e0.elapsed_time(e1) / steps
 
 
+def chunked_step_fn(g2, x, S0=None):
+    """One forward + backward through the composed calls gdr2_fwd_chunked + gdr2_bwd_chunked (what
+    a training loop calls; for long sequences at a small batch they pipeline their chunk ranges
+    over a second stream), returning S_T."""
+    q, k, v, la, b, w, dO = (x[n] for n in ("q", "k", "v", "log_alpha", "b", "w", "dO"))
+
+    def step():
+        o, ST, ws = g2.gdr2_fwd_chunked(q, k, v, la, b, w, S0=S0)
+        g2.gdr2_bwd_chunked(q, k, v, la, b, w, dO, ws)
+    return step
+
+
 def bench_workloads(torch, g2, steps):
-    """The other named workloads, each timed on its own: the long-context layer (B=1, T=32768,
-    H=16, d=128, S0 ~ N(0, 0.02^2), forward returning S_T, plus backward), the three tied-gate
-    reductions (B=2, T=2048, H=16, d=128; materialised gate tensors, so the same algorithmic bytes
-    as the plain layer) and the fp32 reference shape (B=1, H=1, T=256, d=64, forward only:
-    launch latency)."""
+    """The other named workloads, each timed on its own through the composed calls: the
+    long-context layer (B=1, T=32768, H=16, d=128, S0 ~ N(0, 0.02^2), forward returning S_T, plus
+    backward), the three tied-gate reductions (B=2, T=2048, H=16, d=128; materialised gate tensors,
+    so the same algorithmic bytes as the plain layer) and the fp32 reference shape (B=1, H=1,
+    T=256, d=64, forward only: launch latency)."""
     from gated_delta_rule_gdr_amd.inputs import CONFIGS, config_inputs
     out = {}
     for name in ("long_ctx", "tied_kda", "tied_gdn", "tied_la"):
         c = CONFIGS[name]
         x = config_inputs(name, device="cuda")
-        step = train_step_fn(torch, g2, x, c["B"], c["T"], c["H"], c["dk"], c["dv"], S0=x["S0"],
-                             want_ST=True)
+        step = chunked_step_fn(g2, x, S0=x["S0"])
         ms = time_steps(torch, step, steps)
         ht = c["B"] * c["T"] * c["H"]
         alg = (16 * c["dk"] + 30 * c["dk"]) * ht

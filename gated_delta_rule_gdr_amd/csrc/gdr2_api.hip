@@ -4,6 +4,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "gdr2_kernels.hpp"
 
 namespace {
@@ -93,10 +95,78 @@ const char* gdr2_status_string(gdr2_status s) {
 
 int gdr2_abi_version(void) { return GDR2_ABI_VERSION; }
 
-// Layout of the forward workspace: per-chunk WY factors, then the chunk-entry states.
+// ------------------------------------------------------------------ pipelined long sequences
+// When the 16-bit state carries occupy at most half of the compute units (few chains: a long
+// sequence at a small batch), the composed calls split the chunks into ranges and run the
+// chunk-parallel kernel of the later ranges on a second stream, on the idle compute units, while
+// the carry walks the earlier ones on the caller's stream: the factor kernel beside the forward
+// carry, the chunk-gradient kernel beside the backward state carry.  The carry hands its fp32
+// state from one range to the next through a buffer at the end of the workspace, so the results
+// are bitwise those of the unsplit calls.  The decision depends on the shapes only (the size
+// queries need no device): at most kPipeMaxCarryWGs carry workgroups (half of MI355X's 256
+// compute units), and at least two ranges of kPipeRangeChunks chunks and kPipeRangeChunkHeads
+// chunk-heads each, so that every chunk-parallel launch still fills the other half of the chip
+// and every range of the carry is long enough to pay for the switch between ranges.  More or
+// shorter ranges cost more than they overlap: each new range of the carry has to win its compute
+// units back from the chunk-parallel kernel queued beside it (fwd+bwd at B=1 T=32768 H=16: 2374
+// us unsplit, 2277 / 2194 / 2236 us with 2 / 4 / 8 ranges, 2156 us once the side stream also waits
+// for the first range's factors; at B=1 T=8192 H=16: 593 us unsplit, 633 / 605 us with four
+// ranges of 32 / two of 64 chunks).
+constexpr int64_t kPipeMaxCarryWGs = 128;
+constexpr int64_t kPipeRangeChunks = 128;
+constexpr int64_t kPipeRangeChunkHeads = 512;
+constexpr int kPipeMaxPieces = 4;
+
+static int pipe_pieces(int64_t chains, int64_t NC) {
+    int64_t n = chains * NC / kPipeRangeChunkHeads;
+    if (NC / kPipeRangeChunks < n) n = NC / kPipeRangeChunks;
+    return (int)(n < kPipeMaxPieces ? n : kPipeMaxPieces);
+}
+static bool pipelined(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, gdr2_dtype dt) {
+    if (dt != GDR2_BF16 || B <= 0 || H <= 0) return false;
+    const int64_t chains = B * H;
+    if (chains > kPipeMaxCarryWGs) return false;
+    const int dvs = gdr2::carry_slice_width(1, (int)dk, (int)dv, chains);
+    return chains * (dv / dvs) <= kPipeMaxCarryWGs && pipe_pieces(chains, gdr2_num_chunks(T)) >= 2;
+}
+static int pipe_bound(int64_t NC, int np, int k) { return (int)(NC * k / np); }  // chunk of range k
+
+// The second stream and its events, one set per device, created on first use and kept until the
+// process ends.  Calls that pipeline hold the device's lock while they enqueue, so that two host
+// threads never interleave their records and waits on the shared events.
+struct Pipe {
+    hipStream_t side = nullptr;
+    hipEvent_t ev[kPipeMaxPieces + 2] = {};
+    std::mutex mu;
+    bool tried = false, ok = false;
+};
+static Pipe* pipe_of_device() {
+    static std::mutex mu;
+    static Pipe per_device[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    std::lock_guard<std::mutex> g(mu);
+    Pipe& P = per_device[dev];
+    if (!P.tried) {
+        P.tried = true;
+        bool ok = hipStreamCreateWithFlags(&P.side, hipStreamNonBlocking) == hipSuccess;
+        for (hipEvent_t& e : P.ev)
+            ok = ok && hipEventCreateWithFlags(&e, hipEventDisableTiming) == hipSuccess;
+        P.ok = ok;
+    }
+    return P.ok ? &P : nullptr;
+}
+
+// Layout of the forward workspace: per-chunk WY factors, then the chunk-entry states, then (for
+// pipelined shapes) the fp32 state hand-off buffer.  A forward-only workspace holds the factors and
+// the hand-off buffer right after them.
 struct FwdWs {
     size_t yh, qg, kt, p, tm, u, gam, states, total;
+    size_t pipe_bytes;   // hand-off buffer (0: shape not pipelined)
+    size_t infer_total;  // forward-only workspace
 };
+static size_t pipe_train_off(const FwdWs& L) { return L.total - L.pipe_bytes; }
+static size_t pipe_infer_off(const FwdWs& L) { return L.states; }
 static FwdWs fwd_ws_layout(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, gdr2_dtype dt) {
     const size_t es = gdr2_dtype_size(dt);
     const size_t ncc = (size_t)B * H * gdr2_num_chunks(T);
@@ -112,7 +182,9 @@ static FwdWs fwd_ws_layout(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t 
     w.u = take(ncc * C * dv * es);
     w.gam = take(ncc * dk * 4);
     w.states = take(ncc * dv * dk * es);
-    w.total = off;
+    w.pipe_bytes = pipelined(B, T, H, dk, dv, dt) ? round_up((size_t)B * H * dk * dv * 4, 256) : 0;
+    w.total = off + w.pipe_bytes;
+    w.infer_total = w.states + w.pipe_bytes;
     return w;
 }
 
@@ -154,13 +226,19 @@ size_t gdr2_fwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int
 size_t gdr2_fwd_infer_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
                                       gdr2_dtype dt) {
     if (check_chunked(B, T, H, dk, dv, dt) != GDR2_OK) return 0;
-    return fwd_ws_layout(B, T, H, dk, dv, dt).states;  // the factors: everything before the states
+    return fwd_ws_layout(B, T, H, dk, dv, dt).infer_total;  // the factors (+ hand-off buffer)
 }
 
+// Backward workspace: the per-chunk exit-state gradients, then (pipelined shapes) the fp32
+// hand-off buffer of the state-gradient carry.
+static size_t bwd_dsx_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, gdr2_dtype dt) {
+    return round_up((size_t)B * H * gdr2_num_chunks(T) * dk * dv * gdr2_dtype_size(dt), 256);
+}
 size_t gdr2_bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
                                 gdr2_dtype dt) {
     if (check_chunked(B, T, H, dk, dv, dt) != GDR2_OK) return 0;
-    return round_up((size_t)B * H * gdr2_num_chunks(T) * dk * dv * gdr2_dtype_size(dt), 256);
+    const size_t pipe = pipelined(B, T, H, dk, dv, dt) ? round_up((size_t)B * H * dk * dv * 4, 256) : 0;
+    return bwd_dsx_bytes(B, T, H, dk, dv, dt) + pipe;
 }
 
 size_t gdr2_bwd_recompute_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
@@ -181,6 +259,8 @@ static gdr2::FwdParams fwd_params(int64_t B, int64_t T, int64_t H, int64_t dv, c
     p.H = (int)H;
     p.NS = (int)(dv / dvs);
     p.NC = (int)gdr2_num_chunks(T);
+    p.c0 = 0;          // every chunk (a pipelined call narrows the range per launch)
+    p.ncr = p.NC;
     p.T = T;
     p.DV = dv;
     p.q = q; p.k = k; p.v = v; p.b = b; p.w = w;
@@ -215,7 +295,7 @@ static gdr2_status check_fwd(int64_t B, int64_t T, int64_t H, int64_t dk, int64_
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return GDR2_E_ALIGN;
     const FwdWs L = fwd_ws_layout(B, T, H, dk, dv, dt);
-    const size_t ws_need = with_states ? L.total : L.states;
+    const size_t ws_need = with_states ? L.total : L.infer_total;
     if (caller_ws && have_tokens && (!ws || ws_bytes < ws_need)) return GDR2_E_WORKSPACE;
     const size_t es = gdr2_dtype_size(dt);
     const size_t nk = (size_t)B * T * H * dk, nv = (size_t)B * T * H * dv;
@@ -280,6 +360,60 @@ gdr2_status gdr2_fwd_carry(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t 
     return launch_carry(B, T, H, dk, dv, dt, S0, o, S_T, workspace, true, stream);
 }
 
+// Factor kernel and state carry of a validated forward (B, H > 0).  `with_states`: training
+// workspace (chunk-entry states kept) or forward-only workspace.  `allow_pipe`: the chunk ranges
+// may be pipelined over a second stream (not for the no-allocation entry point).
+static gdr2_status fwd_launch(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                              gdr2_dtype dt, unsigned gates, const gdr2_prologue* pro,
+                              const void* q, const void* k, const void* v, const float* la,
+                              const void* b, const void* w, const float* S0, void* o, float* S_T,
+                              void* ws, bool with_states, bool allow_pipe, void* stream) {
+    if (T == 0) return launch_carry(B, T, H, dk, dv, dt, S0, o, S_T, ws, with_states, stream);
+    const int bf = dt == GDR2_BF16;
+    const FwdWs L = fwd_ws_layout(B, T, H, dk, dv, dt);
+    hipStream_t m = (hipStream_t)stream;
+    gdr2::FwdParams pw = fwd_params(B, T, H, dv, q, k, v, la, b, w, nullptr, nullptr, nullptr, L,
+                                    ws, 16, gates);
+    pw.prologue = pro != nullptr;
+    pw.pro = prologue_of(pro);
+    Pipe* P = (allow_pipe && L.pipe_bytes) ? pipe_of_device() : nullptr;
+    if (!P) {
+        if (gdr2::wy_dispatch(bf, (int)dk, (int)dv, pw, m) != hipSuccess) return GDR2_E_HIP;
+        return launch_carry(B, T, H, dk, dv, dt, S0, o, S_T, ws, with_states, stream);
+    }
+    std::lock_guard<std::mutex> g(P->mu);
+    hipStream_t s = P->side;
+    const int64_t NC = gdr2_num_chunks(T);
+    const int np = pipe_pieces(B * H, NC);
+    float* hand = (float*)((char*)ws + (with_states ? pipe_train_off(L) : pipe_infer_off(L)));
+    const int dvs = gdr2::carry_slice_width(bf, (int)dk, (int)dv, B * H);
+    gdr2::FwdParams pc = fwd_params(B, T, H, dv, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                    nullptr, S0, o, S_T, L, ws, dvs);
+    if (!with_states) pc.states = nullptr;
+    // factors of range 0 on the caller's stream (the whole chip); the side stream starts after
+    // them, so that the factors of ranges 1.. share the chip only with the carry, each announced
+    // by an event
+    bool ok = true;
+    for (int r = 0; ok && r < np; ++r) {
+        pw.c0 = pipe_bound(NC, np, r);
+        pw.ncr = pipe_bound(NC, np, r + 1) - pw.c0;
+        ok = gdr2::wy_dispatch(bf, (int)dk, (int)dv, pw, r == 0 ? m : s) == hipSuccess;
+        if (ok && r == 0)
+            ok = hipEventRecord(P->ev[0], m) == hipSuccess && hipStreamWaitEvent(s, P->ev[0], 0) == hipSuccess;
+        if (ok && r > 0) ok = hipEventRecord(P->ev[r], s) == hipSuccess;
+    }
+    // the carry walks the ranges on the caller's stream, its fp32 state handed over in `hand`
+    for (int r = 0; ok && r < np; ++r) {
+        if (r > 0) ok = hipStreamWaitEvent(m, P->ev[r], 0) == hipSuccess;
+        pc.c0 = pipe_bound(NC, np, r);
+        pc.ncr = pipe_bound(NC, np, r + 1) - pc.c0;
+        pc.S0 = r == 0 ? S0 : hand;
+        pc.ST = r == np - 1 ? S_T : hand;
+        if (ok) ok = gdr2::carry_fwd_dispatch(bf, (int)dk, dvs, pc, m) == hipSuccess;
+    }
+    return ok ? GDR2_OK : GDR2_E_HIP;
+}
+
 gdr2_status gdr2_fwd_infer_ex(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
                               gdr2_dtype dt, unsigned gates, const gdr2_prologue* pro,
                               const void* q, const void* k, const void* v,
@@ -290,17 +424,8 @@ gdr2_status gdr2_fwd_infer_ex(int64_t B, int64_t T, int64_t H, int64_t dk, int64
                                workspace, workspace_bytes, true, true, gates, false);
     if (st == GDR2_OK && !prologue_ok(pro)) st = GDR2_E_VALUE;
     if (st != GDR2_OK || B == 0 || H == 0) return st;
-    if (T > 0) {
-        const FwdWs L = fwd_ws_layout(B, T, H, dk, dv, dt);
-        gdr2::FwdParams p = fwd_params(B, T, H, dv, q, k, v, log_alpha, b, w, nullptr, nullptr,
-                                       nullptr, L, workspace, 16, gates);
-        p.states = nullptr;
-        p.prologue = pro != nullptr;
-        p.pro = prologue_of(pro);
-        if (gdr2::wy_dispatch(dt == GDR2_BF16, (int)dk, (int)dv, p, (hipStream_t)stream) != hipSuccess)
-            return GDR2_E_HIP;
-    }
-    return launch_carry(B, T, H, dk, dv, dt, S0, o, S_T, workspace, false, stream);
+    return fwd_launch(B, T, H, dk, dv, dt, gates, pro, q, k, v, log_alpha, b, w, S0, o, S_T,
+                      workspace, false, true, stream);
 }
 
 size_t gdr2_fwd_infer_noalloc_max_bytes(void) { return gdr2::kNoAllocScratchBytes; }
@@ -318,11 +443,12 @@ gdr2_status gdr2_fwd_infer_noalloc_ex(int64_t B, int64_t T, int64_t H, int64_t d
     if (need > gdr2::kNoAllocScratchBytes) return GDR2_E_TOO_LARGE;
     if (B == 0 || H == 0) return GDR2_OK;
     // the factors go to this device's static scratch (library memory: it cannot overlap the
-    // caller's buffers); the launches are those of gdr2_fwd_infer_ex
+    // caller's buffers); the launches are those of gdr2_fwd_infer_ex, never pipelined (that would
+    // create the second stream and need the hand-off buffer)
     void* scr = nullptr;
     if (gdr2::noalloc_scratch(&scr) != hipSuccess) return GDR2_E_HIP;
-    return gdr2_fwd_infer_ex(B, T, H, dk, dv, dt, gates, pro, q, k, v, log_alpha, b, w, S0, o, S_T,
-                             scr, need, stream);
+    return fwd_launch(B, T, H, dk, dv, dt, gates, pro, q, k, v, log_alpha, b, w, S0, o, S_T, scr,
+                      false, false, stream);
 }
 
 gdr2_status gdr2_fwd_infer(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
@@ -344,12 +470,8 @@ gdr2_status gdr2_fwd_chunked_ex(int64_t B, int64_t T, int64_t H, int64_t dk, int
                                workspace, workspace_bytes, true, true, gates);
     if (st == GDR2_OK && !prologue_ok(pro)) st = GDR2_E_VALUE;
     if (st != GDR2_OK || B == 0 || H == 0) return st;
-    if (T > 0) {
-        st = gdr2_fwd_factors_ex(B, T, H, dk, dv, dt, gates, pro, q, k, v, log_alpha, b, w,
-                                 workspace, workspace_bytes, stream);
-        if (st != GDR2_OK) return st;
-    }
-    return gdr2_fwd_carry(B, T, H, dk, dv, dt, S0, o, S_T, workspace, workspace_bytes, stream);
+    return fwd_launch(B, T, H, dk, dv, dt, gates, pro, q, k, v, log_alpha, b, w, S0, o, S_T,
+                      workspace, true, true, stream);
 }
 
 gdr2_status gdr2_fwd_chunked(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
@@ -410,6 +532,8 @@ static gdr2::BwdParams bwd_params(int64_t B, int64_t T, int64_t H, int64_t dk, i
     p.prologue = 0;
     p.pro = prologue_of(nullptr);
     p.B = (int)B; p.H = (int)H; p.NC = (int)gdr2_num_chunks(T); p.T = T; p.DV = dv;
+    p.c0 = 0;
+    p.ncr = p.NC;
     p.NS = (int)(dv / gdr2::carry_slice_width(bf, (int)dk, (int)dv, B * H));
     p.q = q; p.k = k; p.v = v; p.b = b; p.w = w; p.la = la;
     void* f = const_cast<void*>(fws);
@@ -418,6 +542,56 @@ static gdr2::BwdParams bwd_params(int64_t B, int64_t T, int64_t H, int64_t dk, i
     p.dO = dO; p.dST = dS_T; p.dSx = const_cast<void*>(ws); p.dS0 = dS0;
     p.dq = dq; p.dk = dk_; p.dv = dv_; p.db = db; p.dw = dw; p.dla = dla;
     return p;
+}
+
+// State-gradient carry and chunk gradients of a validated backward (B, H > 0; for T = 0 only the
+// pass-through of the state gradient).  Pipelined shapes run the chunk-gradient kernel of each
+// chunk range on the second stream as soon as the state-gradient carry, walking the ranges
+// backwards on the caller's stream, has produced that range's dS'.
+static gdr2_status bwd_launch(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                              gdr2_dtype dt, unsigned gates, const gdr2_prologue* pro,
+                              const void* q, const void* k, const void* v, const float* la,
+                              const void* b, const void* w, const void* fws, const void* dO,
+                              const float* dS_T, void* dq, void* dk_, void* dv_, float* dla,
+                              void* db, void* dw, float* dS0, void* bws, bool allow_pipe,
+                              void* stream) {
+    const int bf = dt == GDR2_BF16;
+    hipStream_t m = (hipStream_t)stream;
+    gdr2::BwdParams pd = bwd_params(B, T, H, dk, dv, dt, nullptr, nullptr, nullptr, nullptr,
+                                    nullptr, nullptr, fws, dO, dS_T, nullptr, nullptr, nullptr,
+                                    nullptr, nullptr, nullptr, dS0, bws);
+    const int dvs = (int)(dv / pd.NS);
+    if (T == 0)
+        return gdr2::dstate_dispatch(bf, (int)dk, dvs, pd, m) == hipSuccess ? GDR2_OK : GDR2_E_HIP;
+    gdr2::BwdParams pg = bwd_params(B, T, H, dk, dv, dt, q, k, v, la, b, w, fws, dO, nullptr, dq,
+                                    dk_, dv_, dla, db, dw, nullptr, bws, gates);
+    pg.prologue = pro != nullptr;
+    pg.pro = prologue_of(pro);
+    Pipe* P = (allow_pipe && pipelined(B, T, H, dk, dv, dt)) ? pipe_of_device() : nullptr;
+    if (!P) {
+        if (gdr2::dstate_dispatch(bf, (int)dk, dvs, pd, m) != hipSuccess) return GDR2_E_HIP;
+        return gdr2::bgrad_dispatch(bf, (int)dk, (int)dv, pg, m) == hipSuccess ? GDR2_OK : GDR2_E_HIP;
+    }
+    std::lock_guard<std::mutex> g(P->mu);
+    hipStream_t s = P->side;
+    const int64_t NC = gdr2_num_chunks(T);
+    const int np = pipe_pieces(B * H, NC);
+    float* hand = (float*)((char*)bws + bwd_dsx_bytes(B, T, H, dk, dv, dt));
+    bool ok = hipEventRecord(P->ev[0], m) == hipSuccess && hipStreamWaitEvent(s, P->ev[0], 0) == hipSuccess;
+    for (int r = np - 1; ok && r >= 0; --r) {
+        const int c0 = pipe_bound(NC, np, r), ncr = pipe_bound(NC, np, r + 1) - c0;
+        pd.c0 = pg.c0 = c0;
+        pd.ncr = pg.ncr = ncr;
+        pd.dST = r == np - 1 ? dS_T : hand;  // the fp32 state gradient handed between ranges
+        pd.dS0 = r == 0 ? dS0 : hand;
+        ok = gdr2::dstate_dispatch(bf, (int)dk, dvs, pd, m) == hipSuccess &&
+             hipEventRecord(P->ev[1 + r], m) == hipSuccess &&
+             hipStreamWaitEvent(s, P->ev[1 + r], 0) == hipSuccess &&
+             gdr2::bgrad_dispatch(bf, (int)dk, (int)dv, pg, s) == hipSuccess;
+    }
+    // the caller's stream continues once the side stream's chunk gradients are done
+    if (ok) ok = hipEventRecord(P->ev[np + 1], s) == hipSuccess && hipStreamWaitEvent(m, P->ev[np + 1], 0) == hipSuccess;
+    return ok ? GDR2_OK : GDR2_E_HIP;
 }
 
 gdr2_status gdr2_bwd_state(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
@@ -485,12 +659,8 @@ gdr2_status gdr2_bwd_chunked_ex(int64_t B, int64_t T, int64_t H, int64_t dk, int
                                dS0, workspace, workspace_bytes, true, true, gates);
     if (st == GDR2_OK && !prologue_ok(pro)) st = GDR2_E_VALUE;
     if (st != GDR2_OK || B == 0 || H == 0) return st;
-    st = gdr2_bwd_state(B, T, H, dk, dv, dt, fwd_workspace, fwd_workspace_bytes, dO, dS_T, dS0,
-                        workspace, workspace_bytes, stream);
-    if (st != GDR2_OK || T == 0) return st;
-    return gdr2_bwd_grads_ex(B, T, H, dk, dv, dt, gates, pro, q, k, v, log_alpha, b, w,
-                             fwd_workspace, fwd_workspace_bytes, dO, dq, dk_, dv_, dlog_alpha, db,
-                             dw, workspace, workspace_bytes, stream);
+    return bwd_launch(B, T, H, dk, dv, dt, gates, pro, q, k, v, log_alpha, b, w, fwd_workspace,
+                      dO, dS_T, dq, dk_, dv_, dlog_alpha, db, dw, dS0, workspace, true, stream);
 }
 
 gdr2_status gdr2_bwd_chunked(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
@@ -543,24 +713,14 @@ gdr2_status gdr2_bwd_chunked_recompute_ex(int64_t B, int64_t T, int64_t H, int64
     // S_T are not formed), then the backward with the rest of it
     char* fws = (char*)workspace;
     char* bws = have_tokens ? fws + L.total : nullptr;
-    const size_t bws_bytes = have_tokens ? workspace_bytes - L.total : 0;
-    if (T > 0) {
-        gdr2::FwdParams p = fwd_params(B, T, H, dv, q, k, v, log_alpha, b, w, nullptr, nullptr,
-                                       nullptr, L, fws, 16, gates);
-        p.prologue = pro != nullptr;
-        p.pro = prologue_of(pro);
-        if (gdr2::wy_dispatch(dt == GDR2_BF16, (int)dk, (int)dv, p, (hipStream_t)stream) != hipSuccess)
-            return GDR2_E_HIP;
-        st = launch_carry(B, T, H, dk, dv, dt, S0, nullptr, nullptr, fws, true, stream);
-        if (st != GDR2_OK) return st;
-    }
     if (T == 0) {  // nothing to recompute: the state gradient passes straight through
         return gdr2_bwd_state(B, T, H, dk, dv, dt, nullptr, 0, dO, dS_T, dS0, nullptr, 0, stream);
     }
-    st = gdr2_bwd_state(B, T, H, dk, dv, dt, fws, L.total, dO, dS_T, dS0, bws, bws_bytes, stream);
+    st = fwd_launch(B, T, H, dk, dv, dt, gates, pro, q, k, v, log_alpha, b, w, S0, nullptr, nullptr,
+                    fws, true, true, stream);
     if (st != GDR2_OK) return st;
-    return gdr2_bwd_grads_ex(B, T, H, dk, dv, dt, gates, pro, q, k, v, log_alpha, b, w, fws,
-                             L.total, dO, dq, dk_, dv_, dlog_alpha, db, dw, bws, bws_bytes, stream);
+    return bwd_launch(B, T, H, dk, dv, dt, gates, pro, q, k, v, log_alpha, b, w, fws, dO, dS_T, dq,
+                      dk_, dv_, dlog_alpha, db, dw, dS0, bws, true, stream);
 }
 
 gdr2_status gdr2_bwd_chunked_recompute(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,

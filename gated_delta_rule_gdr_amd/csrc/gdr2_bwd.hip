@@ -261,7 +261,8 @@ __global__ __launch_bounds__(2 * kThreads, 1) void gdr2_dstate_lds_kernel(BwdPar
     const int bb = chain / p.H, h = chain % p.H;
     const int j0 = slice * DVS;
     const long T = p.T, H = p.H, DV = p.DV;
-    const int NC = p.NC;
+    const int NC = p.NC, c0 = p.c0, NR = p.ncr;  // chunks [c0, c0 + NR) of NC, walked backwards
+    const int cl = c0 + NR - 1;                   // from the range's last chunk
     const bf16* dO = (const bf16*)p.dO + ((long)bb * T * H + h) * DV + j0;
 
     // ---- loader units of chunk cc (the region of unit lt + kThreads * m depends on m only)
@@ -302,7 +303,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void gdr2_dstate_lds_kernel(BwdPar
         x -= Cf::UO;
         *(i32x4*)(sm.gam[sl] + 4 * x) = v;
     };
-    i32x4 lbA[LPT], lbB[LPT];  // loader registers; step s handles chunk NC - 1 - s
+    i32x4 lbA[LPT], lbB[LPT];  // loader registers; step s handles chunk cl - s
 
     f32x4 dS[BPW];
     if (!loader) {
@@ -317,27 +318,27 @@ __global__ __launch_bounds__(2 * kThreads, 1) void gdr2_dstate_lds_kernel(BwdPar
             }
             store_acc_T(sm.dST, PK, 16 * jb, 16 * ib, dS[u]);
         }
-    } else if (NC > 0) {
-        const int c0 = NC - 1, c1 = NC > 1 ? NC - 2 : 0, c2 = NC > 2 ? NC - 3 : 0;
+    } else if (NR > 0) {
+        const int a1 = NR > 1 ? cl - 1 : c0, a2 = NR > 2 ? cl - 2 : c0;
 #pragma unroll
-        for (int m = 0; m < LPT; ++m) lbB[m] = *src_unit(c0, m);
+        for (int m = 0; m < LPT; ++m) lbB[m] = *src_unit(cl, m);
 #pragma unroll
-        for (int m = 0; m < LPT; ++m) put_unit(0, c0, m, lbB[m]);
+        for (int m = 0; m < LPT; ++m) put_unit(0, cl, m, lbB[m]);
 #pragma unroll
-        for (int m = 0; m < LPT; ++m) lbA[m] = *src_unit(c1, m);
+        for (int m = 0; m < LPT; ++m) lbA[m] = *src_unit(a1, m);
 #pragma unroll
-        for (int m = 0; m < LPT; ++m) lbB[m] = *src_unit(c2, m);
+        for (int m = 0; m < LPT; ++m) lbB[m] = *src_unit(a2, m);
     }
     lds_barrier();
 
     // loader step st: the chunk of step st + 1 (registers `cur`) into slot (st + 1) & 1, then the
-    // loads of the chunk of step st + 3 (clamped) into the same registers
+    // loads of the chunk of step st + 3 (clamped to the range) into the same registers
     auto loader_step = [&](int st, i32x4* cur) __attribute__((always_inline)) {
-        if (st + 1 < NC) {
+        if (st + 1 < NR) {
 #pragma unroll
-            for (int m = 0; m < LPT; ++m) put_unit((st + 1) & 1, NC - 2 - st, m, cur[m]);
+            for (int m = 0; m < LPT; ++m) put_unit((st + 1) & 1, cl - 1 - st, m, cur[m]);
         }
-        const int c3 = st + 3 < NC ? NC - 4 - st : 0;
+        const int c3 = st + 3 < NR ? cl - 3 - st : c0;
 #pragma unroll
         for (int m = 0; m < LPT / 2; ++m) cur[m] = *src_unit(c3, m);
         lds_barrier();
@@ -429,7 +430,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void gdr2_dstate_lds_kernel(BwdPar
         lds_barrier();
     };
 
-    const int NCR = (NC + 1) / 2 * 2;
+    const int NCR = (NR + 1) / 2 * 2;
     if (loader) {
         for (int st = 0; st < NCR; st += 2) {
             loader_step(st, lbA);
@@ -439,8 +440,8 @@ __global__ __launch_bounds__(2 * kThreads, 1) void gdr2_dstate_lds_kernel(BwdPar
         for (int st = 0; st < NCR; st += 2) {
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
-                if (st + u < NC) {
-                    compute_step(NC - 1 - st - u, (st + u) & 1);
+                if (st + u < NR) {
+                    compute_step(cl - st - u, (st + u) & 1);
                 } else {
                     lds_barrier();
                     lds_barrier();
@@ -586,7 +587,8 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
     const int NC = p.NC;
     // heads fastest: workgroups that run at the same time read neighbouring 256-byte pieces of the
     // same token rows of q, k, v, dO, ... ([B, T, H, D] layout) rather than rows 4 KB apart
-    const int h = blockIdx.x % p.H, c = (blockIdx.x / p.H) % NC, bb = blockIdx.x / (p.H * NC);
+    // (chunks [c0, c0 + ncr) of the sequence: one launch may cover a part of it)
+    const int h = blockIdx.x % p.H, c = p.c0 + (blockIdx.x / p.H) % p.ncr, bb = blockIdx.x / (p.H * p.ncr);
     const int chain = bb * p.H + h;
     const long T = p.T, H = p.H;
     const long cix = (long)chain * NC + c;
@@ -1260,7 +1262,7 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
 
 template <typename OT, int DK, int DV>
 static hipError_t launch_bgrad(const BwdParams& p, hipStream_t s) {
-    const long nblk = (long)p.B * p.H * p.NC;
+    const long nblk = (long)p.B * p.H * p.ncr;
     if (nblk == 0) return hipSuccess;
     if (p.prologue)
         hipLaunchKernelGGL((gdr2_bgrad_kernel<OT, DK, DV, 32, kModePrologue>), dim3(nblk), dim3(kBgThreads), 0, s, p);

@@ -65,8 +65,8 @@ hipError_t noalloc_scratch(void** ptr) {
 template <typename OT, int DK, int DV, int MODE, bool STREAM>
 __global__ __launch_bounds__(kThreads, 2) void gdr2_wy_kernel(FwdParams p) {
     __shared__ WySmem<OT, DK, DV> sm;
-    WyChunk<OT, DK, DV> ch(p.B, p.H, p.T, p.DV, p.NC, p.gates, p.pro, blockIdx.x, p.q, p.k, p.b,
-                           p.la, p.v, p.w);
+    WyChunk<OT, DK, DV> ch(p.B, p.H, p.T, p.DV, p.NC, p.c0, p.ncr, p.gates, p.pro, blockIdx.x, p.q,
+                           p.k, p.b, p.la, p.v, p.w);
     wy_factors<OT, DK, DV, MODE, STREAM>(sm, ch, p.wy);
 }
 
@@ -307,7 +307,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void gdr2_carry_lds_kernel(FwdPara
     const int bb = chain / p.H, h = chain % p.H;
     const int j0 = slice * DVS;
     const long T = p.T, H = p.H, DV = p.DV;
-    const int NC = p.NC;
+    const int NC = p.NC, c0 = p.c0, NR = p.ncr;  // chunks [c0, c0 + NR) of NC
     bf16* o = p.o ? (bf16*)p.o + ((long)bb * T * H + h) * DV + j0 : nullptr;
 
     // ---- loader: unit x = lt + kThreads * m of chunk cc (the region of x depends on m only)
@@ -355,28 +355,30 @@ __global__ __launch_bounds__(2 * kThreads, 1) void gdr2_carry_lds_kernel(FwdPara
             }
             store_acc_T(sm.ST, PK, 16 * jb, 16 * ib, Sacc[u]);
         }
-    } else if (NC > 0) {
-        // chunk 0 into slot 0 (through lbB), then chunks 1 and 2 into the registers (clamped)
+    } else if (NR > 0) {
+        // chunk c0 into slot 0 (through lbB), then chunks c0 + 1 and c0 + 2 into the registers
+        // (clamped to the range)
 #pragma unroll
-        for (int m = 0; m < LPT; ++m) lbB[m] = *src_unit(0, m);
+        for (int m = 0; m < LPT; ++m) lbB[m] = *src_unit(c0, m);
 #pragma unroll
         for (int m = 0; m < LPT; ++m) put_unit(0, m, lbB[m]);
 #pragma unroll
-        for (int m = 0; m < LPT; ++m) lbA[m] = *src_unit(NC > 1 ? 1 : NC - 1, m);
+        for (int m = 0; m < LPT; ++m) lbA[m] = *src_unit(c0 + (NR > 1 ? 1 : NR - 1), m);
 #pragma unroll
-        for (int m = 0; m < LPT; ++m) lbB[m] = *src_unit(NC > 2 ? 2 : NC - 1, m);
+        for (int m = 0; m < LPT; ++m) lbB[m] = *src_unit(c0 + (NR > 2 ? 2 : NR - 1), m);
     }
     lds_barrier();
 
-    // loader step cc: chunk cc + 1 (registers `cur`) into slot (cc + 1) & 1, then the loads of
-    // chunk cc + 3 into the same registers (clamped to the last chunk, so that every step issues
-    // the same loads and the waits stay exact), half before and half after the mid-step barrier
+    // loader step cc (counted from c0): chunk cc + 1 (registers `cur`) into slot (cc + 1) & 1,
+    // then the loads of chunk cc + 3 into the same registers (clamped to the range's last chunk,
+    // so that every step issues the same loads and the waits stay exact, and nothing outside the
+    // range is read), half before and half after the mid-step barrier
     auto loader_step = [&](int cc, i32x4* cur) __attribute__((always_inline)) {
-        if (cc + 1 < NC) {
+        if (cc + 1 < NR) {
 #pragma unroll
             for (int m = 0; m < LPT; ++m) put_unit((cc + 1) & 1, m, cur[m]);
         }
-        const int c3 = cc + 3 < NC ? cc + 3 : NC - 1;
+        const int c3 = c0 + (cc + 3 < NR ? cc + 3 : NR - 1);
 #pragma unroll
         for (int m = 0; m < LPT / 2; ++m) cur[m] = *src_unit(c3, m);
         lds_barrier();
@@ -387,6 +389,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void gdr2_carry_lds_kernel(FwdPara
     auto compute_step = [&](int c, int sl) __attribute__((always_inline)) {
         const long t0 = (long)c * C;
         // outputs of the previous step: checkpoint of the state entering chunk c, O of chunk c-1
+        // (of this launch's range)
         if (p.states) {
             bf16* dst = (bf16*)p.states + (((long)chain * NC + c) * DV + j0) * DK;
             constexpr int NSV = DVS * DK / 8;
@@ -399,7 +402,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void gdr2_carry_lds_kernel(FwdPara
                 }
             }
         }
-        if (o && c > 0) {
+        if (o && c > c0) {
             constexpr int NV = C * DVS / 8;
 #pragma unroll
             for (int x0 = 0; x0 < NV; x0 += kThreads) {
@@ -479,9 +482,9 @@ __global__ __launch_bounds__(2 * kThreads, 1) void gdr2_carry_lds_kernel(FwdPara
         lds_barrier();
     };
 
-    // Steps run in pairs (the register alternation); a step past the last chunk only keeps the
-    // barrier count of the two roles equal.
-    const int NCR = (NC + 1) / 2 * 2;
+    // Steps run in pairs (the register alternation); a step past the range's last chunk only keeps
+    // the barrier count of the two roles equal.
+    const int NCR = (NR + 1) / 2 * 2;
     if (loader) {
         for (int c = 0; c < NCR; c += 2) {
             loader_step(c, lbA);
@@ -491,16 +494,16 @@ __global__ __launch_bounds__(2 * kThreads, 1) void gdr2_carry_lds_kernel(FwdPara
         for (int c = 0; c < NCR; c += 2) {
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
-                if (c + u < NC) {
-                    compute_step(c + u, (c + u) & 1);
+                if (c + u < NR) {
+                    compute_step(c0 + c + u, (c + u) & 1);
                 } else {
                     lds_barrier();
                     lds_barrier();
                 }
             }
         }
-        if (o && NC > 0) {  // output tile of the last chunk
-            const long t0 = (long)(NC - 1) * C;
+        if (o && NR > 0) {  // output tile of the range's last chunk
+            const long t0 = (long)(c0 + NR - 1) * C;
             constexpr int NV = C * DVS / 8;
 #pragma unroll
             for (int x0 = 0; x0 < NV; x0 += kThreads) {
@@ -534,7 +537,7 @@ static void launch_wy_mode(const FwdParams& p, long nblk, hipStream_t s) {
 }
 template <typename OT, int DK, int DV>
 static hipError_t launch_wy(const FwdParams& p, hipStream_t s) {
-    const long nblk = (long)p.B * p.H * p.NC;
+    const long nblk = (long)p.B * p.H * p.ncr;
     if (nblk == 0) return hipSuccess;
     // streaming instances for the 16-bit path only (the fp32 path is the precision path)
     if (sizeof(OT) == 2 && p.stream) launch_wy_mode<OT, DK, DV, sizeof(OT) == 2>(p, nblk, s);

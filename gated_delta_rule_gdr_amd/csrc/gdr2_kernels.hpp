@@ -36,6 +36,8 @@ struct WyBufs {
 
 struct FwdParams {
     int B, H, NS, NC;   // batch, heads, value slices per chain, chunks
+    int c0, ncr;        // chunks this launch covers: [c0, c0 + ncr) (the factor kernel, the 16-bit
+                        // carry); the fp32 carry always covers all NC
     int gates;          // gate shapes (kEraseScalar | kWriteScalar | kDecayScalar)
     int prologue;       // inputs are pre-activations (see Prologue)
     Prologue pro;
@@ -70,6 +72,8 @@ struct DecodeParams {
 
 struct BwdParams {
     int B, H, NS, NC;
+    int c0, ncr;          // chunks this launch covers: [c0, c0 + ncr) (the 16-bit state-gradient
+                          // carry, the chunk-gradient kernel); the fp32 carry always covers all NC
     int gates, prologue;
     Prologue pro;
     long T, DV;

@@ -180,15 +180,16 @@ struct WyChunk {
     const float* la;
     int gates;
     Prologue pro;
-    __device__ WyChunk(int B, int H_, long T_, long DV_, int NC, int gates_, Prologue pro_, int bid, const void* q_,
-                       const void* k_, const void* b_, const float* la_, const void* v_,
+    // chunks [c0, c0 + ncr) of the NC of the sequence, one workgroup each
+    __device__ WyChunk(int B, int H_, long T_, long DV_, int NC, int c0, int ncr, int gates_, Prologue pro_, int bid,
+                       const void* q_, const void* k_, const void* b_, const float* la_, const void* v_,
                        const void* w_) {
         gates = gates_;
         pro = pro_;
         (void)B;
         // heads fastest: concurrent workgroups share the token rows of the [B, T, H, D] inputs
-        const int h = bid % H_, bb = bid / (H_ * NC);
-        c = (bid / H_) % NC;
+        const int h = bid % H_, bb = bid / (H_ * ncr);
+        c = c0 + (bid / H_) % ncr;
         chain = bb * H_ + h;
         R = wave_id();
         l = lane_id();

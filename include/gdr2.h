@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define GDR2_ABI_VERSION 3
+#define GDR2_ABI_VERSION 4
 #define GDR2_CHUNK 64 /* tokens per chunk of the chunked passes */
 
 typedef enum gdr2_status {

@@ -29,6 +29,23 @@ long epi_blocks(long rows) { return (rows + 127) / 128; }
 hipError_t noalloc_scratch(void** ptr) { *ptr = (void*)(uintptr_t)0x7f0000000000ull; return hipSuccess; }
 }  // namespace gdr2
 
+// stand-ins for the runtime calls of the pipelined long-sequence path (second stream, events):
+// handles that are never dereferenced
+extern "C" {
+hipError_t hipGetDevice(int* dev) { *dev = 0; return hipSuccess; }
+hipError_t hipStreamCreateWithFlags(hipStream_t* s, unsigned int) {
+    *s = (hipStream_t)(uintptr_t)0x5100;
+    return hipSuccess;
+}
+hipError_t hipEventCreateWithFlags(hipEvent_t* e, unsigned) {
+    static uintptr_t next = 0x6100;
+    *e = (hipEvent_t)(next += 0x10);
+    return hipSuccess;
+}
+hipError_t hipEventRecord(hipEvent_t, hipStream_t) { return hipSuccess; }
+hipError_t hipStreamWaitEvent(hipStream_t, hipEvent_t, unsigned int) { return hipSuccess; }
+}
+
 static int g_fail = 0;
 #define EXPECT(call, want, launch)                                                              \
     do {                                                                                        \
@@ -171,6 +188,7 @@ int main() {
         chunked_cases(2, 70, 3, 128, 64, dt);
         chunked_cases(1, 1, 2, 64, 128, dt);
         chunked_cases(2, 0, 2, 64, 64, dt);
+        chunked_cases(1, 64 * 256 + 6, 4, 64, 64, dt);  // bf16: the pipelined long-sequence path
     }
     huge_cases();
     std::printf("%s: %d failures, %ld launches\n", g_fail ? "FAIL" : "ok", g_fail, gdr2::g_launches);

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_strings():
     lib = load_library()
-    assert lib.gdr2_abi_version() == 3
+    assert lib.gdr2_abi_version() == 4
     for s in range(11):
         assert lib.gdr2_status_string(s) and lib.gdr2_status_string(s) != b"unknown status"
     assert lib.gdr2_dtype_size(0) == 4 and lib.gdr2_dtype_size(1) == 2 and lib.gdr2_dtype_size(7) == 0
@@ -161,17 +161,26 @@ def test_noalloc_entry_point_rejects_before_launch():
     assert call(o=0x10000) == E_ALIAS
     from gated_delta_rule_gdr_amd import Prologue
     assert call(pro=ctypes.byref(Prologue(1.0, 0.0))) == 9
-    # largest sequence whose factors fit, and the next chunk over the limit (B = H = 1, d = 128, bf16)
-    per_chunk = lib.gdr2_fwd_infer_workspace_bytes(1, 64, 1, 128, 128, 1)
+    # largest sequence whose factors fit, and the next chunk over the limit (B = 1, H = 32, d = 128,
+    # bf16: enough chains that the forward is not pipelined, so the forward-only workspace is
+    # exactly the factors)
+    per_chunk = lib.gdr2_fwd_infer_workspace_bytes(1, 64, 32, 128, 128, 1)
     n = cap // per_chunk
-    while lib.gdr2_fwd_infer_workspace_bytes(1, 64 * n, 1, 128, 128, 1) > cap:
+    while lib.gdr2_fwd_infer_workspace_bytes(1, 64 * n, 32, 128, 128, 1) > cap:
         n -= 1
-    assert lib.gdr2_fwd_infer_workspace_bytes(1, 64 * (n + 1), 1, 128, 128, 1) > cap
-    far = lambda T: lib.gdr2_fwd_infer_noalloc_ex(1, T, 1, 128, 128, 1, 0, NULL,
-                                                  *[P(0x100000000 * (i + 1)) for i in range(6)], NULL,
-                                                  P(0x1000000000), NULL, NULL)
+    assert lib.gdr2_fwd_infer_workspace_bytes(1, 64 * (n + 1), 32, 128, 128, 1) > cap
+    far = lambda T, H=32: lib.gdr2_fwd_infer_noalloc_ex(1, T, H, 128, 128, 1, 0, NULL,
+                                                        *[P(0x100000000 * (i + 1)) for i in range(6)],
+                                                        NULL, P(0x1000000000), NULL, NULL)
     assert far(64 * (n + 1)) == 10
     assert far(64 * n + 65) == 10
+    # a pipelined shape (one chain, many chunks): the limit is on the factors alone, not on the
+    # forward-only workspace, which also holds the fp32 hand-off buffer of one d x d state
+    per_chunk1 = lib.gdr2_fwd_infer_workspace_bytes(1, 64, 1, 128, 128, 1)  # one chunk: not pipelined
+    m = cap // per_chunk1
+    assert lib.gdr2_fwd_infer_workspace_bytes(1, 64 * m, 1, 128, 128, 1) == m * per_chunk1 + 128 * 128 * 4
+    assert far(64 * (m + 1), H=1) == 10
+    assert far(64 * m, H=1) != 10
 
 
 def _fake(addr):

@@ -34,6 +34,8 @@ def _gpu(x):
     ("bf16", 64, 128, 65, "bwa", None),
     ("bf16", 128, 128, 150, "", (0.1, 1e-6)),
     ("f32", 128, 64, 1, "b", None),
+    ("bf16", 128, 128, 64 * 256 + 17, "", None),     # pipelined chunk ranges (few chains)
+    ("bf16", 64, 64, 64 * 257, "bw", (0.1, 1e-6)),
 ])
 def test_forward_only_equals_training_forward(dtype, dk, dv, T, scalar, pro):
     """o and S_T of the forward-only call equal the training forward's bit for bit, and the

@@ -87,16 +87,22 @@ def test_decode_on_offset_buffers_and_side_stream():
     assert torch.equal(o, o_ref) and torch.equal(S, S_ref)
 
 
-@pytest.mark.parametrize("B,T,H,d,pro", [(4, 4096, 16, 128, False), (2, 200, 3, 64, False),
-                                         (2, 130, 4, 128, True)])
-def test_phase_entry_points_match_the_chunked_calls(B, T, H, d, pro):
+@pytest.mark.parametrize("B,T,H,d,pro,scalar", [
+    (4, 4096, 16, 128, False, ""), (2, 200, 3, 64, False, ""), (2, 130, 4, 128, True, ""),
+    # few chains and many chunks: the chunked calls pipeline their chunk ranges over two streams
+    (1, 64 * 256 + 17, 8, 128, False, ""), (1, 64 * 256 + 17, 8, 64, False, "bwa"),
+    (1, 64 * 257, 8, 128, True, ""), (1, 32768, 16, 128, False, "")])
+def test_phase_entry_points_match_the_chunked_calls(B, T, H, d, pro, scalar):
     """The four phase entry points in the sequence the benchmark times (factors, carry, state
     gradient, chunk gradients) give bitwise the results of gdr2_fwd_chunked + gdr2_bwd_chunked,
-    at the full 1.3B-layer size too, so the timed path is the one the parity tests check."""
+    at the full 1.3B-layer size too, so the timed path is the one the parity tests check.  For
+    long sequences at a small batch the chunked calls split the chunks into ranges over a second
+    stream, handing the carries' fp32 states from range to range: bitwise the same again."""
     import gated_delta_rule_gdr_amd as g2
     prologue = g2.Prologue(0.1, 1e-6) if pro else None
-    x = _gpu(layer_inputs(B, T, H, d, d, dtype="bf16", seed=64, s0_std=0.05, dST=True, raw=pro))
-    announce(f"phase entry points vs chunked calls B={B} T={T} H={H} d={d} prologue={pro}")
+    x = _gpu(layer_inputs(B, T, H, d, d, dtype="bf16", seed=64, s0_std=0.05, dST=True, raw=pro,
+                          scalar=scalar))
+    announce(f"phase entry points vs chunked calls B={B} T={T} H={H} d={d} prologue={pro} scalar={scalar}")
     args = [x[n] for n in NAMES]
     o, ST, fws = gdr2_fwd_chunked(*args, S0=x["S0"], prologue=prologue)
     ref = gdr2_bwd_chunked(*args, x["dO"], fws, dS_T=x["dST"], prologue=prologue)
