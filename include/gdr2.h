@@ -37,6 +37,16 @@
  *     factors referenced to 16-token blocks; a chunk in which some channel decays by more than
  *     exp(-60) across one block takes a second path whose factors are all <= 1, so no decay drives
  *     a factor out of the fp32 range.
+ *   - Long sequences at a small batch (bf16; at most 128 state-carry workgroups, i.e. B*H <= 16 at
+ *     d_v = 128; at least two ranges of 128 chunks and 512 chunk-heads): gdr2_fwd_chunked(_ex),
+ *     gdr2_fwd_infer(_ex), gdr2_bwd_chunked(_ex) and gdr2_bwd_chunked_recompute(_ex) split the
+ *     chunks into up to four ranges and run the chunk-parallel kernel of the later ranges on a
+ *     second stream (one per device, created by the library on first use, default priority)
+ *     beside the sequential state carry, joined back into `stream` with events before the call's
+ *     work ends; the results are bitwise those of the unsplit phase entry points.  For these
+ *     shapes the workspace queries include an fp32 B*H*d_k*d_v buffer through which the carry
+ *     hands its state from range to range.  Calls that split serialise their enqueueing per
+ *     device (a lock), so they may be made from several host threads.
  */
 #ifndef GDR2_H
 #define GDR2_H
@@ -135,8 +145,9 @@ gdr2_status gdr2_fwd_chunked(int64_t B, int64_t T, int64_t H, int64_t dk, int64_
                              size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace gdr2_fwd_chunked needs (per token and head about
- * (4*dk + 2*64 + dv) elements of dtype plus the chunk-entry states, dk*dv/64 elements); 0 for
- * sizes the chunked passes reject. */
+ * (4*dk + 2*64 + dv) elements of dtype plus the chunk-entry states, dk*dv/64 elements; plus the
+ * fp32 hand-off buffer for the split long-sequence shapes above); 0 for sizes the chunked passes
+ * reject. */
 size_t gdr2_fwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
                                 gdr2_dtype dtype);
 
@@ -165,7 +176,8 @@ gdr2_status gdr2_fwd_infer_ex(int64_t B, int64_t T, int64_t H, int64_t dk, int64
                               const float* S0, void* o, float* S_T, void* workspace,
                               size_t workspace_bytes, void* stream);
 
-/* Bytes of device workspace gdr2_bwd_chunked needs (the per-chunk state gradients). */
+/* Bytes of device workspace gdr2_bwd_chunked needs (the per-chunk state gradients; plus the fp32
+ * hand-off buffer for the split long-sequence shapes). */
 size_t gdr2_bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
                                 gdr2_dtype dtype);
 
@@ -201,9 +213,11 @@ gdr2_status gdr2_bwd_chunked(int64_t B, int64_t T, int64_t H, int64_t dk, int64_
  * The caller still passes every input and output.  The call allocates nothing and calls no
  * allocating routine; on its first call on a device it looks up that device's copy of the array
  * (hipGetSymbolAddress) and keeps the address.
- *   - Limit: the problem's factors, gdr2_fwd_infer_workspace_bytes(B, T, H, dk, dv, dtype), must
- *     fit gdr2_fwd_infer_noalloc_max_bytes() (128 MiB: e.g. B*H*ceil(T/64) <= 1,600 chunk-heads
- *     at d = 128 in bf16); larger problems return GDR2_E_TOO_LARGE before any launch.
+ *   - Limit: the problem's factors -- gdr2_fwd_infer_workspace_bytes(B, T, H, dk, dv, dtype), less
+ *     the hand-off buffer of the split long-sequence shapes, which this entry point never splits
+ *     (that would create the second stream) -- must fit gdr2_fwd_infer_noalloc_max_bytes()
+ *     (128 MiB: e.g. B*H*ceil(T/64) <= 1,600 chunk-heads at d = 128 in bf16); larger problems
+ *     return GDR2_E_TOO_LARGE before any launch.
  *   - Every call on one device shares that device's array, which keeps the last call's contents
  *     (each call overwrites every byte it reads, so nothing needs clearing).  Calls that overlap
  *     in time on one device -- on different streams, or from different threads without
