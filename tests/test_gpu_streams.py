@@ -121,3 +121,36 @@ def test_phase_entry_points_match_the_chunked_calls(B, T, H, d, pro, scalar):
     assert torch.equal(o, o2) and torch.equal(ST, ST2) and torch.equal(ref["dS0"], dS0)
     for n in GRADS[:-1]:
         assert torch.equal(ref[n], gr[n]), n
+
+
+def test_split_long_sequences_from_two_host_threads():
+    """Two host threads, each on its own stream, run the split (two-stream) long-sequence path at
+    the same time; the library serialises their use of its shared second stream and events, so
+    each thread's results equal those of the same call made alone."""
+    import threading
+    xs = [_gpu(layer_inputs(1, 64 * 256 + 9, 8, 128, 128, dtype="bf16", seed=70 + i, s0_std=0.05,
+                            dST=True)) for i in range(2)]
+    announce("split long-sequence path from two host threads")
+    ref = [_layer(x) for x in xs]
+    torch.cuda.synchronize()
+    out, errs = [None, None], []
+
+    def run(i):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                for _ in range(3):
+                    out[i] = _layer(xs[i])
+            s.synchronize()
+        except Exception as e:  # reported by the main thread
+            errs.append(e)
+
+    th = [threading.Thread(target=run, args=(i,)) for i in range(2)]
+    for t in th:
+        t.start()
+    for t in th:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errs, errs
+    for i in range(2):
+        _same(out[i], ref[i])
