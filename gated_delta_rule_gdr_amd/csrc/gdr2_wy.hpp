@@ -57,22 +57,70 @@ __device__ __forceinline__ float* tblk(float* Af, int R, int S) {
     return R == S ? Af + 16 * R * PAF + 16 * R : Af + 16 * S * PAF + 16 * R;
 }
 
-// T = (I + A)^-1 for the strictly lower 64 x 64 A held in Af (fp32), 16 x 16 blocked:
-// diagonal blocks by forward substitution (wave R, lane = column), then
-// T_RS = -T_RR sum_{S <= K < R} A_RK T_KS level by level with fp32 MFMA.  T is also written, in
-// operand precision, to Tm (row-major, zero above the diagonal).  Ends with a barrier.
-template <typename OT, int PAF, int PC>
-__device__ __forceinline__ void solve_unit_lower_64(float* Af, float (*Mf)[16 * 17], OT* Tm) {
-    const int w = wave_id(), l = lane_id();
-    for (int x = threadIdx.x; x < 6 * 256; x += kThreads) {
-        const int blk = x >> 8, e = x & 255;
+// fp32 16x16 block products on the 16x16x4 MFMA with the k order 4g + j (g = lane / 16, j = the
+// MFMA step): lane (i = lane % 16, g) supplies X[i][4g + j] of the left block -- a 16-byte read of
+// its row -- and Y[4g + j][i] of the right one, which is element j of the accumulator that holds
+// Y in the calling wave.  A product therefore feeds the next one from registers.
+__device__ __forceinline__ f32x4 lhs4_f32(const float* X, int p, int l) {
+    return *(const f32x4*)(X + (l & 15) * p + 4 * (l >> 4));
+}
+__device__ __forceinline__ f32x4 rhs4_f32(const float* Y, int p, int l) {
+    const float* y = Y + 4 * (l >> 4) * p + (l & 15);
+    return f32x4{y[0], y[p], y[2 * p], y[3 * p]};
+}
+__device__ __forceinline__ void mm16_f32(f32x4& c, const f32x4& a, const f32x4& b) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) mma32(c, a[j], b[j]);
+}
+
+// Zero the blocks of Tm above the diagonal (T is lower triangular).  Nothing else touches Tm
+// before the solve, so this runs at the start of the workgroup, off the solve's path.
+template <typename OT, int PC>
+__device__ __forceinline__ void zero_upper_T(OT* Tm) {
+    constexpr int V = 16 / (int)sizeof(OT), PER_ROW = 16 / V;  // 16-byte stores per block row
+    for (int x = threadIdx.x; x < 6 * 16 * PER_ROW; x += kThreads) {
+        const int blk = x / (16 * PER_ROW), e = x % (16 * PER_ROW);
         const int R = blk < 3 ? 0 : blk < 5 ? 1 : 2;
         const int S = blk < 3 ? blk + 1 : blk < 5 ? blk - 1 : 3;
-        Tm[(16 * R + (e >> 4)) * PC + 16 * S + (e & 15)] = from_f<OT>(0.f);
+        *(i32x4*)(Tm + (16 * R + e / PER_ROW) * PC + 16 * S + (e % PER_ROW) * V) = i32x4{0, 0, 0, 0};
     }
+}
+
+// T = (I + A)^-1 for the strictly lower 64 x 64 A held in Af (fp32), 16 x 16 blocked; the upper
+// blocks of Tm must already be zero (zero_upper_T).  Diagonal blocks by forward substitution
+// (wave R, lane = column), then the off-diagonal blocks from T_RS = -T_RR sum_{S <= K < R} A_RK T_KS
+// in three barrier-separated steps that keep all four waves busy:
+//     1: T10 = -T11 (A10 T00), T32 = -T33 (A32 T22), M21 = A21 T11, M31 = A31 T11,
+//        and the first terms of M20 = A20 T00 + A21 T10, M30 = A30 T00 + A31 T10;
+//     2: M20, M30 completed, T21 = -T22 M21, T31 = -(T32 M21 + T33 M31);
+//     3: T20 = -T22 M20, T30 = -(T32 M20 + T33 M30).
+// T is written in operand precision to Tm (row-major); the fp32 copies in Af are kept only for the
+// blocks a later step reads (the diagonal, T10, T32).  Ends with a barrier.
+template <typename OT, int PAF, int PC>
+__device__ __forceinline__ void solve_unit_lower_64(float* Af, float (*Mf)[16 * 17], OT* Tm) {
+    const int w = wave_id(), l = lane_id(), g = l >> 4, c = l & 15;
+    const auto A = [&](int R, int S) { return Af + 16 * R * PAF + 16 * S; };  // A_RS, R > S
+    const auto T = [&](int R, int S) { return tblk<PAF>(Af, R, S); };
+    const auto put_T = [&](int R, int S, const f32x4& v, bool keep_f32) {
+        float* t = T(R, S);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if (keep_f32) t[acc_row(e, l) * PAF + acc_col(l)] = v[e];
+            Tm[(16 * R + acc_row(e, l)) * PC + 16 * S + acc_col(l)] = from_f<OT>(v[e]);
+        }
+    };
+    const auto put_M = [&](float* M, const f32x4& v) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) M[acc_row(e, l) * 17 + acc_col(l)] = v[e];
+    };
+    const auto neg = [](const f32x4& v) { return f32x4{-v[0], -v[1], -v[2], -v[3]}; };
+    constexpr f32x4 Z4 = {0.f, 0.f, 0.f, 0.f};
+
+    // diagonal block T_ww, column c (the four lane groups compute it alike; group g keeps rows
+    // 4g .. 4g+3, which is T_ww in accumulator layout)
+    f32x4 tw;
     {
-        float* Ab = Af + 16 * w * PAF + 16 * w;
-        const int c = l & 15;
+        const float* Ab = A(w, w);
         float x[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -81,44 +129,63 @@ __device__ __forceinline__ void solve_unit_lower_64(float* Af, float (*Mf)[16 * 
             for (int s = 0; s < r; ++s) acc -= Ab[r * PAF + s] * x[s];
             x[r] = acc;
         }
-        wave_sync();
-        if (l < 16) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                Ab[r * PAF + c] = x[r];
-                Tm[(16 * w + r) * PC + 16 * w + c] = from_f<OT>(x[r]);
-            }
-        }
+        for (int i = 0; i < 4; ++i) tw[i] = g == 0 ? x[i] : g == 1 ? x[4 + i] : g == 2 ? x[8 + i] : x[12 + i];
+    }
+    wave_sync();  // A_ww is read in full before T_ww overwrites it
+    put_T(w, w, tw, true);
+    lds_barrier();
+
+    f32x4 m0 = Z4, m1 = Z4;
+    if (w == 0) {
+        mm16_f32(m0, lhs4_f32(A(1, 0), PAF, l), tw);
+        mm16_f32(m1, lhs4_f32(T(1, 1), PAF, l), m0);
+        put_T(1, 0, neg(m1), true);
+    } else if (w == 1) {
+        mm16_f32(m0, lhs4_f32(A(2, 1), PAF, l), tw);
+        mm16_f32(m1, lhs4_f32(A(3, 1), PAF, l), tw);
+        put_M(Mf[2], m0);
+        put_M(Mf[3], m1);
+    } else if (w == 2) {
+        mm16_f32(m0, lhs4_f32(A(3, 2), PAF, l), tw);
+        mm16_f32(m1, lhs4_f32(T(3, 3), PAF, l), m0);
+        put_T(3, 2, neg(m1), true);
+    } else {
+        const f32x4 t00 = rhs4_f32(T(0, 0), PAF, l);
+        mm16_f32(m0, lhs4_f32(A(2, 0), PAF, l), t00);
+        mm16_f32(m1, lhs4_f32(A(3, 0), PAF, l), t00);
     }
     lds_barrier();
-#pragma unroll
-    for (int d = 1; d <= 3; ++d) {
-        if (w < 4 - d) {
-            const int S = w, R = w + d;
-            f32x4 m = {0.f, 0.f, 0.f, 0.f};
-            for (int K = S; K < R; ++K) {
-                const float* tks = tblk<PAF>(Af, K, S);
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk)
-                    mma32(m, fa32(Af, PAF, 16 * R, 16 * K + 4 * kk), fb32(tks, PAF, 4 * kk, 0));
-            }
-            float* M = Mf[w];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) M[acc_row(e) * 17 + acc_col()] = m[e];
-            wave_sync();
-            f32x4 n = {0.f, 0.f, 0.f, 0.f};
-            const float* trr = tblk<PAF>(Af, R, R);
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) mma32(n, fa32(trr, PAF, 0, 4 * kk), fb32(M, 17, 4 * kk, 0));
-            float* trs = tblk<PAF>(Af, R, S);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                trs[acc_row(e) * PAF + acc_col()] = -n[e];
-                Tm[(16 * R + acc_row(e)) * PC + 16 * S + acc_col()] = from_f<OT>(-n[e]);
-            }
-        }
-        lds_barrier();
+
+    if (w == 3) {
+        const f32x4 t10 = rhs4_f32(T(1, 0), PAF, l);
+        mm16_f32(m0, lhs4_f32(A(2, 1), PAF, l), t10);
+        mm16_f32(m1, lhs4_f32(A(3, 1), PAF, l), t10);
+        put_M(Mf[0], m0);
+        put_M(Mf[1], m1);
+    } else if (w == 0) {
+        f32x4 n = Z4;
+        mm16_f32(n, lhs4_f32(T(2, 2), PAF, l), rhs4_f32(Mf[2], 17, l));
+        put_T(2, 1, neg(n), false);
+    } else if (w == 1) {
+        f32x4 n = Z4;
+        mm16_f32(n, lhs4_f32(T(3, 2), PAF, l), rhs4_f32(Mf[2], 17, l));
+        mm16_f32(n, lhs4_f32(T(3, 3), PAF, l), rhs4_f32(Mf[3], 17, l));
+        put_T(3, 1, neg(n), false);
     }
+    lds_barrier();
+
+    if (w == 0) {
+        f32x4 n = Z4;
+        mm16_f32(n, lhs4_f32(T(2, 2), PAF, l), rhs4_f32(Mf[0], 17, l));
+        put_T(2, 0, neg(n), false);
+    } else if (w == 1) {
+        f32x4 n = Z4;
+        mm16_f32(n, lhs4_f32(T(3, 2), PAF, l), rhs4_f32(Mf[0], 17, l));
+        mm16_f32(n, lhs4_f32(T(3, 3), PAF, l), rhs4_f32(Mf[1], 17, l));
+        put_T(3, 0, neg(n), false);
+    }
+    lds_barrier();
 }
 
 // The KPL values of k-step ks that lane group g owns in a row: channels ks*KS + KPL*g + j.
@@ -231,6 +298,7 @@ __device__ __forceinline__ void wy_factors(WySmem<OT, DK, DV>& sm, const WyChunk
     const long cix = ch.cix, DVl = ch.DVl;
     constexpr bool GS = MODE != kModePlain, PRO = MODE == kModePrologue;
 
+    zero_upper_T<OT, PC>(sm.Tm);
     float qv[NCH], kv[NCH], bv[NCH], lv[NCH], zv[NCV];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
