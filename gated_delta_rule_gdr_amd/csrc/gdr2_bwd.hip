@@ -606,8 +606,8 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
     constexpr bool GS = MODE != kModePlain, PRO = MODE == kModePrologue;
     const bool b_sc = GS && (p.gates & kEraseScalar), w_sc = GS && (p.gates & kWriteScalar);
     const bool a_sc = GS && (p.gates & kDecayScalar);
-    // log alpha, then G_r - ref_R: not needed before the Gram phase, so it is loaded with the last
-    // value-column block (off the start-up path)
+    // log alpha, then G_r - ref_R (loaded ahead of the value-column blocks or with the last one,
+    // see scan_la)
     f32x4 sc[NIBH];
     auto load_la = [&]() __attribute__((always_inline)) {
         if (a_sc) {
@@ -617,6 +617,63 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
         } else {
 #pragma unroll
             for (int ib = 0; ib < NIBH; ++ib) sc[ib] = *(const f32x4*)(p.la + row * DK + 16 * (ibase + ib) + 4 * g);
+        }
+    };
+    // in-block cumsum of log alpha (DPP over the 16 tokens), the block totals and the deep-decay
+    // ballot; then the per-channel tables exp(ref_R), exp(G_C - ref_R), exp(ref_R - ref_S) from
+    // the totals.  Without the fused prologue this runs at the start, while the first value-column
+    // blocks are in flight (log alpha is loaded ahead of them; its registers then stay live across
+    // the value-column loop); with it, after the loop, where the prologue's q, k arrive.
+    // fused prologue: log alpha = -decay_scale * softplus(a); the chain-rule factor
+    // -decay_scale * sigmoid(a) of dlog alpha comes from the same exponential
+    constexpr bool EARLY = !PRO;
+    f32x4 dsa[PRO ? NIBH : 1];
+    auto scan_la = [&]() __attribute__((always_inline)) {
+        if (PRO) {
+#pragma unroll
+            for (int ib = 0; ib < NIBH; ++ib)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float x = sc[ib][e], ex = __expf(x);
+                    const float sp = x > 20.f ? x : 0.69314718f * __builtin_amdgcn_logf(1.f + ex);
+                    dsa[PRO ? ib : 0][e] = -p.pro.decay_scale * (x > 20.f ? 1.f : ex * __builtin_amdgcn_rcpf(1.f + ex));
+                    sc[ib][e] = -p.pro.decay_scale * sp;
+                }
+        }
+#pragma unroll
+        for (int ib = 0; ib < NIBH; ++ib)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sc[ib][e] = row_scan16(valid ? sc[ib][e] : 0.f);
+        {   // does this block decay past the fast path's range on one of this wave's channels?
+            float mn = 0.f;
+#pragma unroll
+            for (int ib = 0; ib < NIBH; ++ib)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) mn = fminf(mn, sc[ib][e]);
+            const unsigned long long dp = __ballot(rl == 15 && mn < -kDeepDecay);
+            if (l == 0) sm.deep[w] = dp != 0ull;
+        }
+        if (rl == 15) {
+#pragma unroll
+            for (int ib = 0; ib < NIBH; ++ib) *(f32x4*)(&sm.tot[R][16 * (ibase + ib) + 4 * g]) = sc[ib];
+        }
+    };
+    auto decay_tables = [&]() __attribute__((always_inline)) {
+        for (int chn = tid; chn < DK; chn += NT) {
+            float refs[4], run = 0.f;
+#pragma unroll
+            for (int Rp = 0; Rp < 4; ++Rp) {
+                refs[Rp] = run;
+                run += sm.tot[Rp][chn];
+            }
+#pragma unroll
+            for (int Rp = 0; Rp < 4; ++Rp) {
+                sm.gRt[Rp][chn] = __expf(refs[Rp]);
+                sm.hRt[Rp][chn] = __expf(run - refs[Rp]);
+                sm.hRl[Rp][chn] = run - refs[Rp];
+#pragma unroll
+                for (int S = 0; S < Rp; ++S) sm.ctab[Rp * (Rp - 1) / 2 + S][chn] = __expf(refs[Rp] - refs[S]);
+            }
         }
     };
     // ---- the chunk's -Y and Ktilde: staged into LDS with T and P below (16-bit operands), or
@@ -697,6 +754,7 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
             }
         }
     }
+    if constexpr (EARLY) load_la();
     fetch_block(0, 0);
     if (NS == 2 && DV / DVH > 1) fetch_block(1, 1);
 #pragma unroll
@@ -757,7 +815,7 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
         if (jn < NJ) {
             fetch_block(jn, st);
         } else if (jn == NJ) {
-            load_la();
+            if constexpr (!EARLY) load_la();
 #pragma unroll
             for (int ib = 0; ib < NIBH; ++ib) {
                 const int i0 = 16 * (ibase + ib) + 4 * g;
@@ -772,9 +830,11 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
             }
         }
     };
+    if constexpr (EARLY) scan_la();
     stage(0, 0);
     fetch_next(NS, 0);
     lds_barrier();
+    if constexpr (EARLY) decay_tables();  // read from the Gram phase on, after several barriers
 
     constexpr int JUNROLL = NS == 2 ? NJ : 1;  // two register sets: unrolled, set indices static
     typename RW::t dvk[NS == 2 ? NJ : 1], dwk[NS == 2 ? NJ : 1];  // dv, dw of every block
@@ -887,39 +947,7 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
         }
     }
 
-    // ---- in-block cumsum of log alpha (DPP over the 16 tokens), block totals, and the
-    //      per-channel tables exp(ref_R), exp(G_C - ref_R), exp(ref_R - ref_S)
-    // fused prologue: log alpha = -decay_scale * softplus(a); the chain-rule factor
-    // -decay_scale * sigmoid(a) of dlog alpha comes from the same exponential
-    f32x4 dsa[PRO ? NIBH : 1];
-    if (PRO) {
-#pragma unroll
-        for (int ib = 0; ib < NIBH; ++ib)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float x = sc[ib][e], ex = __expf(x);
-                const float sp = x > 20.f ? x : 0.69314718f * __builtin_amdgcn_logf(1.f + ex);
-                dsa[PRO ? ib : 0][e] = -p.pro.decay_scale * (x > 20.f ? 1.f : ex * __builtin_amdgcn_rcpf(1.f + ex));
-                sc[ib][e] = -p.pro.decay_scale * sp;
-            }
-    }
-#pragma unroll
-    for (int ib = 0; ib < NIBH; ++ib)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sc[ib][e] = row_scan16(valid ? sc[ib][e] : 0.f);
-    {   // does this block decay past the fast path's range on one of this wave's channels?
-        float mn = 0.f;
-#pragma unroll
-        for (int ib = 0; ib < NIBH; ++ib)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) mn = fminf(mn, sc[ib][e]);
-        const unsigned long long dp = __ballot(rl == 15 && mn < -kDeepDecay);
-        if (l == 0) sm.deep[w] = dp != 0ull;
-    }
-    if (rl == 15) {
-#pragma unroll
-        for (int ib = 0; ib < NIBH; ++ib) *(f32x4*)(&sm.tot[R][16 * (ibase + ib) + 4 * g]) = sc[ib];
-    }
+    if constexpr (!EARLY) scan_la();
     // fused prologue: this wave's half of the squared row norms of q and k (lanes 16g + rl of both
     // channel halves), exchanged through the same barrier as the block totals
     if (PRO) {
@@ -939,22 +967,9 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
             sm.nrm[half][r][1] = sk;
         }
     }
-    lds_barrier();
-    for (int chn = tid; chn < DK; chn += NT) {
-        float refs[4], run = 0.f;
-#pragma unroll
-        for (int Rp = 0; Rp < 4; ++Rp) {
-            refs[Rp] = run;
-            run += sm.tot[Rp][chn];
-        }
-#pragma unroll
-        for (int Rp = 0; Rp < 4; ++Rp) {
-            sm.gRt[Rp][chn] = __expf(refs[Rp]);
-            sm.hRt[Rp][chn] = __expf(run - refs[Rp]);
-            sm.hRl[Rp][chn] = run - refs[Rp];
-#pragma unroll
-            for (int S = 0; S < Rp; ++S) sm.ctab[Rp * (Rp - 1) / 2 + S][chn] = __expf(refs[Rp] - refs[S]);
-        }
+    if constexpr (!EARLY) {  // publishes the block totals (and the prologue's row norms)
+        lds_barrier();
+        decay_tables();
     }
     // deep-decay path for the whole chunk (uniform over the workgroup): right Gram factors
     // referenced to the end of their block and the diagonal blocks entry by entry, so that no
