@@ -603,9 +603,10 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
     // ---- this lane's log alpha (token r, channels 16 (ibase+ib) + 4g + e); q, k, b come later
     typename RW::t qr[NIBH], kr[NIBH], br[NIBH];
     // scalar gates and the fused prologue (the plain instance carries no gate branches)
-    constexpr bool GS = MODE != kModePlain, PRO = MODE == kModePrologue;
-    const bool b_sc = GS && (p.gates & kEraseScalar), w_sc = GS && (p.gates & kWriteScalar);
-    const bool a_sc = GS && (p.gates & kDecayScalar);
+    constexpr bool GS = MODE != kModePlain, PRO = mode_prologue(MODE);
+    const int gm = gate_bits<MODE>(p.gates);
+    const bool b_sc = GS && (gm & kEraseScalar), w_sc = GS && (gm & kWriteScalar);
+    const bool a_sc = GS && (gm & kDecayScalar);
     // log alpha, then G_r - ref_R (loaded ahead of the value-column blocks or with the last one,
     // see scan_la)
     f32x4 sc[NIBH];
@@ -1279,12 +1280,26 @@ template <typename OT, int DK, int DV>
 static hipError_t launch_bgrad(const BwdParams& p, hipStream_t s) {
     const long nblk = (long)p.B * p.H * p.ncr;
     if (nblk == 0) return hipSuccess;
-    if (p.prologue)
-        hipLaunchKernelGGL((gdr2_bgrad_kernel<OT, DK, DV, 32, kModePrologue>), dim3(nblk), dim3(kBgThreads), 0, s, p);
-    else if (p.gates)
-        hipLaunchKernelGGL((gdr2_bgrad_kernel<OT, DK, DV, 32, kModeGates>), dim3(nblk), dim3(kBgThreads), 0, s, p);
-    else
-        hipLaunchKernelGGL((gdr2_bgrad_kernel<OT, DK, DV, 32, kModePlain>), dim3(nblk), dim3(kBgThreads), 0, s, p);
+    auto go = [&](auto mode) {
+        hipLaunchKernelGGL((gdr2_bgrad_kernel<OT, DK, DV, 32, decltype(mode)::value>), dim3(nblk), dim3(kBgThreads), 0, s, p);
+    };
+    bool fixed = false;
+    if constexpr (sizeof(OT) == 2) {  // gate bits as compile-time constants (the fp32 path reads them)
+        if (!p.prologue) {
+            fixed = with_fixed_gates(p.gates, go);
+        } else if (p.gates == 0) {
+            go(std::integral_constant<int, kModePrologueChannel>{});
+            fixed = true;
+        }
+    }
+    if (fixed) {
+    } else if (p.prologue) {
+        go(std::integral_constant<int, kModePrologue>{});
+    } else if (p.gates) {
+        go(std::integral_constant<int, kModeGates>{});
+    } else {
+        go(std::integral_constant<int, kModePlain>{});
+    }
     return hipGetLastError();
 }
 

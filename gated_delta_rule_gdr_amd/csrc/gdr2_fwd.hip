@@ -65,7 +65,7 @@ hipError_t noalloc_scratch(void** ptr) {
 template <typename OT, int DK, int DV, int MODE, bool STREAM>
 __global__ __launch_bounds__(kThreads, 2) void gdr2_wy_kernel(FwdParams p) {
     __shared__ WySmem<OT, DK, DV> sm;
-    WyChunk<OT, DK, DV> ch(p.B, p.H, p.T, p.DV, p.NC, p.c0, p.ncr, p.gates, p.pro, blockIdx.x, p.q,
+    WyChunk<OT, DK, DV> ch(p.B, p.H, p.T, p.DV, p.NC, p.c0, p.ncr, gate_bits<MODE>(p.gates), p.pro, blockIdx.x, p.q,
                            p.k, p.b, p.la, p.v, p.w);
     wy_factors<OT, DK, DV, MODE, STREAM>(sm, ch, p.wy);
 }
@@ -528,12 +528,26 @@ __global__ __launch_bounds__(2 * kThreads, 1) void gdr2_carry_lds_kernel(FwdPara
 
 template <typename OT, int DK, int DV, bool STREAM>
 static void launch_wy_mode(const FwdParams& p, long nblk, hipStream_t s) {
-    if (p.prologue)
-        hipLaunchKernelGGL((gdr2_wy_kernel<OT, DK, DV, kModePrologue, STREAM>), dim3(nblk), dim3(kThreads), 0, s, p);
-    else if (p.gates)
-        hipLaunchKernelGGL((gdr2_wy_kernel<OT, DK, DV, kModeGates, STREAM>), dim3(nblk), dim3(kThreads), 0, s, p);
-    else
-        hipLaunchKernelGGL((gdr2_wy_kernel<OT, DK, DV, kModePlain, STREAM>), dim3(nblk), dim3(kThreads), 0, s, p);
+    auto go = [&](auto mode) {
+        hipLaunchKernelGGL((gdr2_wy_kernel<OT, DK, DV, decltype(mode)::value, STREAM>), dim3(nblk), dim3(kThreads), 0, s, p);
+    };
+    bool fixed = false;
+    if constexpr (sizeof(OT) == 2) {  // gate bits as compile-time constants (the fp32 path reads them)
+        if (!p.prologue) {
+            fixed = with_fixed_gates(p.gates, go);
+        } else if (p.gates == 0) {
+            go(std::integral_constant<int, kModePrologueChannel>{});
+            fixed = true;
+        }
+    }
+    if (fixed) {
+    } else if (p.prologue) {
+        go(std::integral_constant<int, kModePrologue>{});
+    } else if (p.gates) {
+        go(std::integral_constant<int, kModeGates>{});
+    } else {
+        go(std::integral_constant<int, kModePlain>{});
+    }
 }
 template <typename OT, int DK, int DV>
 static hipError_t launch_wy(const FwdParams& p, hipStream_t s) {

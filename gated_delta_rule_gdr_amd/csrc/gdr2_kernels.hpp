@@ -1,6 +1,7 @@
 // gdr2_kernels.hpp -- host-side launch interface between the C ABI and the HIP kernels.
 #pragma once
 #include <hip/hip_runtime.h>
+#include <type_traits>
 
 namespace gdr2 {
 
@@ -10,9 +11,41 @@ constexpr int kEraseScalar = 1;   // b
 constexpr int kWriteScalar = 2;   // w
 constexpr int kDecayScalar = 4;   // log alpha
 
-// Kernel instances: plain (every gate channel-wise, post-activation inputs), scalar gates (the
-// gates bits read at run time), fused prologue (pre-activation inputs, gate bits at run time).
-constexpr int kModePlain = 0, kModeGates = 1, kModePrologue = 2;
+// Kernel instances: plain (every gate channel-wise, post-activation inputs), scalar gates with the
+// gate bits read at run time (kModeGates), fused prologue (pre-activation inputs, gate bits at run
+// time), and, for the 16-bit path of the factor and chunk-gradient kernels, whose run-time gate
+// branches cost them about a fifth of their time: scalar gates with the bits fixed at compile
+// time (kModeFixedGates + bits) and the fused prologue with every gate channel-wise
+// (kModePrologueChannel).
+constexpr int kModePlain = 0, kModeGates = 1, kModePrologue = 2, kModePrologueChannel = 3;
+constexpr int kModeFixedGates = 8;
+
+__host__ __device__ constexpr bool mode_prologue(int mode) {
+    return mode == kModePrologue || mode == kModePrologueChannel;
+}
+// The gate bits an instance works with: none for the plain and channel-wise prologue instances,
+// its own for a fixed-gates instance, the run-time ones otherwise.
+template <int MODE>
+__host__ __device__ constexpr int gate_bits(int run_time) {
+    return MODE == kModePlain || MODE == kModePrologueChannel ? 0
+           : MODE >= kModeFixedGates                          ? MODE - kModeFixedGates
+                                                              : run_time;
+}
+
+// f(std::integral_constant<int, kModeFixedGates + gates>{}) for gate bits 1..7; false otherwise.
+template <typename F>
+inline bool with_fixed_gates(int gates, F&& f) {
+    switch (gates) {
+    case 1: f(std::integral_constant<int, kModeFixedGates + 1>{}); return true;
+    case 2: f(std::integral_constant<int, kModeFixedGates + 2>{}); return true;
+    case 3: f(std::integral_constant<int, kModeFixedGates + 3>{}); return true;
+    case 4: f(std::integral_constant<int, kModeFixedGates + 4>{}); return true;
+    case 5: f(std::integral_constant<int, kModeFixedGates + 5>{}); return true;
+    case 6: f(std::integral_constant<int, kModeFixedGates + 6>{}); return true;
+    case 7: f(std::integral_constant<int, kModeFixedGates + 7>{}); return true;
+    default: return false;
+    }
+}
 
 // Fused prologue parameters: q, k scaled by (sum of squares + norm_eps)^-1/2, b = sigmoid(b),
 // w = sigmoid(w), log alpha = -decay_scale * softplus(a).

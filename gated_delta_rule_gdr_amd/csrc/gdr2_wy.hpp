@@ -281,9 +281,10 @@ struct WyChunk {
 };
 
 // Compute and store the WY factors of one chunk (see the file comment); every thread of the
-// workgroup calls it.  MODE (kModePlain / kModeGates / kModePrologue): the plain instance has no
-// gate branches, so its loads issue back to back; the others read the gate bits (and apply the
-// fused prologue) at run time.  STREAM: write the factor tiles with streaming stores (a
+// workgroup calls it.  MODE (kModePlain / kModeGates / kModePrologue / kModePrologueChannel /
+// kModeFixedGates + bits): the plain, fixed-gates and channel-wise prologue instances have no gate
+// branches, so their loads issue back to back; the others read the gate bits at run time.  STREAM: write the
+// factor tiles with streaming stores (a
 // separate instance: a run-time choice between the two store kinds is folded into one plain
 // store by the compiler).
 template <typename OT, int DK, int DV, int MODE, bool STREAM>
@@ -296,7 +297,7 @@ __device__ __forceinline__ void wy_factors(WySmem<OT, DK, DV>& sm, const WyChunk
     constexpr int NCV = Cf::NCV;
     const int R = ch.R, l = ch.l, rl = ch.rl, g = ch.g, r = ch.r;
     const long cix = ch.cix, DVl = ch.DVl;
-    constexpr bool GS = MODE != kModePlain, PRO = MODE == kModePrologue;
+    constexpr bool GS = MODE != kModePlain, PRO = mode_prologue(MODE);
 
     zero_upper_T<OT, PC>(sm.Tm);
     float qv[NCH], kv[NCH], bv[NCH], lv[NCH], zv[NCV];
@@ -304,14 +305,14 @@ __device__ __forceinline__ void wy_factors(WySmem<OT, DK, DV>& sm, const WyChunk
     for (int ks = 0; ks < NKS; ++ks) {
         load_lane<OT>(ch.q, ks, g, qv + ks * KPL);
         load_lane<OT>(ch.k, ks, g, kv + ks * KPL);
-        if (GS && (ch.gates & kEraseScalar)) {
+        if (GS && (gate_bits<MODE>(ch.gates) & kEraseScalar)) {
             const float bs = to_f(ch.b[0]);
 #pragma unroll
             for (int j = 0; j < KPL; ++j) bv[ks * KPL + j] = bs;
         } else {
             load_lane<OT>(ch.b, ks, g, bv + ks * KPL);
         }
-        if (GS && (ch.gates & kDecayScalar)) {
+        if (GS && (gate_bits<MODE>(ch.gates) & kDecayScalar)) {
             const float ls = ch.la[0];
 #pragma unroll
             for (int j = 0; j < KPL; ++j) lv[ks * KPL + j] = ls;
@@ -323,7 +324,7 @@ __device__ __forceinline__ void wy_factors(WySmem<OT, DK, DV>& sm, const WyChunk
     for (int ks = 0; ks < NVS; ++ks) {
         float vv[KPL], wv[KPL];
         load_lane<OT>(ch.v, ks, g, vv);
-        if (GS && (ch.gates & kWriteScalar)) {
+        if (GS && (gate_bits<MODE>(ch.gates) & kWriteScalar)) {
             const float ws = to_f(ch.w[0]);
 #pragma unroll
             for (int j = 0; j < KPL; ++j) wv[j] = ws;

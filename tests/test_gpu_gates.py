@@ -37,7 +37,7 @@ def _reduce(name, ref, gpu_shape):
     return ref.sum(-1) if len(gpu_shape) == ref.ndim - 1 else ref
 
 
-@pytest.mark.parametrize("scalar", ["b", "w", "a", "bw", "bwa"])
+@pytest.mark.parametrize("scalar", ["b", "w", "a", "bw", "ba", "wa", "bwa"])
 @pytest.mark.parametrize("dtype,dk,dv,T", [("bf16", 128, 128, 130), ("f32", 64, 64, 100),
                                            ("bf16", 64, 128, 65)])
 def test_scalar_gates_fwd_bwd(scalar, dtype, dk, dv, T):
