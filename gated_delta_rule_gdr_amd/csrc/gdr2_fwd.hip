@@ -531,23 +531,7 @@ static void launch_wy_mode(const FwdParams& p, long nblk, hipStream_t s) {
     auto go = [&](auto mode) {
         hipLaunchKernelGGL((gdr2_wy_kernel<OT, DK, DV, decltype(mode)::value, STREAM>), dim3(nblk), dim3(kThreads), 0, s, p);
     };
-    bool fixed = false;
-    if constexpr (sizeof(OT) == 2) {  // gate bits as compile-time constants (the fp32 path reads them)
-        if (!p.prologue) {
-            fixed = with_fixed_gates(p.gates, go);
-        } else if (p.gates == 0) {
-            go(std::integral_constant<int, kModePrologueChannel>{});
-            fixed = true;
-        }
-    }
-    if (fixed) {
-    } else if (p.prologue) {
-        go(std::integral_constant<int, kModePrologue>{});
-    } else if (p.gates) {
-        go(std::integral_constant<int, kModeGates>{});
-    } else {
-        go(std::integral_constant<int, kModePlain>{});
-    }
+    with_mode<sizeof(OT) == 2>(p.prologue, p.gates, go);  // the fp32 path reads the gate bits
 }
 template <typename OT, int DK, int DV>
 static hipError_t launch_wy(const FwdParams& p, hipStream_t s) {

@@ -32,19 +32,28 @@ __host__ __device__ constexpr int gate_bits(int run_time) {
                                                               : run_time;
 }
 
-// f(std::integral_constant<int, kModeFixedGates + gates>{}) for gate bits 1..7; false otherwise.
-template <typename F>
-inline bool with_fixed_gates(int gates, F&& f) {
-    switch (gates) {
-    case 1: f(std::integral_constant<int, kModeFixedGates + 1>{}); return true;
-    case 2: f(std::integral_constant<int, kModeFixedGates + 2>{}); return true;
-    case 3: f(std::integral_constant<int, kModeFixedGates + 3>{}); return true;
-    case 4: f(std::integral_constant<int, kModeFixedGates + 4>{}); return true;
-    case 5: f(std::integral_constant<int, kModeFixedGates + 5>{}); return true;
-    case 6: f(std::integral_constant<int, kModeFixedGates + 6>{}); return true;
-    case 7: f(std::integral_constant<int, kModeFixedGates + 7>{}); return true;
-    default: return false;
+// Calls f(std::integral_constant<int, MODE>{}) with the instance MODE that serves a call with the
+// given fused-prologue flag and gate bits (validated: bits 0..2 only): with FIXED (the 16-bit
+// path) the gate bits of a scalar-gate call and of a channel-wise prologue call are template
+// constants; without, they are read at run time.
+template <bool FIXED, typename F>
+inline void with_mode(int prologue, int gates, F&& f) {
+    if constexpr (FIXED) {
+        switch (prologue ? (gates == 0 ? 8 : -1) : gates) {
+        case 1: f(std::integral_constant<int, kModeFixedGates + 1>{}); return;
+        case 2: f(std::integral_constant<int, kModeFixedGates + 2>{}); return;
+        case 3: f(std::integral_constant<int, kModeFixedGates + 3>{}); return;
+        case 4: f(std::integral_constant<int, kModeFixedGates + 4>{}); return;
+        case 5: f(std::integral_constant<int, kModeFixedGates + 5>{}); return;
+        case 6: f(std::integral_constant<int, kModeFixedGates + 6>{}); return;
+        case 7: f(std::integral_constant<int, kModeFixedGates + 7>{}); return;
+        case 8: f(std::integral_constant<int, kModePrologueChannel>{}); return;
+        default: break;  // no gates without the prologue, or the prologue with scalar gates
+        }
     }
+    if (prologue) f(std::integral_constant<int, kModePrologue>{});
+    else if (!FIXED && gates) f(std::integral_constant<int, FIXED ? kModePlain : kModeGates>{});
+    else f(std::integral_constant<int, kModePlain>{});
 }
 
 // Fused prologue parameters: q, k scaled by (sum of squares + norm_eps)^-1/2, b = sigmoid(b),
