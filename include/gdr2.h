@@ -14,8 +14,11 @@
  * The decay is passed as log(alpha_t), natural log, one value per key channel.
  *
  * Conventions shared by every entry point
- *   - Tensors are dense, row-major, and live in DEVICE memory owned by the caller.  The library
- *     allocates nothing, keeps no state between calls and never frees caller memory.
+ *   - Tensors are dense, row-major, and live in DEVICE memory owned by the caller.  No call
+ *     allocates or frees device memory, and caller memory is never freed.  Kept between calls,
+ *     per device: the second stream and its events of the long-sequence split below (created on
+ *     first use) and the static scratch of gdr2_fwd_infer_noalloc_ex.  No result depends on an
+ *     earlier call.
  *   - Token tensors: q, k, log_alpha, b : [B][T][H][d_k];  v, w, o, dO : [B][T][H][d_v].
  *     States: [B][H][d_k][d_v], fp32.
  *   - dtype selects the element type of q, k, v, b, w, o and of dq, dk, dv, db, dw:
