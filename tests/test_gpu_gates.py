@@ -39,7 +39,8 @@ def _reduce(name, ref, gpu_shape):
 
 @pytest.mark.parametrize("scalar", ["b", "w", "a", "bw", "ba", "wa", "bwa"])
 @pytest.mark.parametrize("dtype,dk,dv,T", [("bf16", 128, 128, 130), ("f32", 64, 64, 100),
-                                           ("bf16", 64, 128, 65)])
+                                           ("bf16", 64, 128, 65), ("bf16", 128, 64, 70),
+                                           ("bf16", 64, 64, 100)])
 def test_scalar_gates_fwd_bwd(scalar, dtype, dk, dv, T):
     x = layer_inputs(2, T, 3, dk, dv, dtype=dtype, seed=500 + T + len(scalar), s0_std=0.05,
                      dST=True, scalar=scalar)
