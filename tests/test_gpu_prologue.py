@@ -54,6 +54,8 @@ def _oracle(f, c, eps, want_bwd=True):
     ("bf16", 128, 128, 200, "b", 0.5),
     ("f32", 128, 64, 150, "a", 0.1),
     ("bf16", 128, 64, 1, "", 0.1),
+    ("bf16", 64, 64, 90, "", 0.3),
+    ("bf16", 64, 128, 66, "", 0.1),
 ])
 def test_prologue_fwd_bwd(dtype, dk, dv, T, scalar, c):
     eps = 1e-6
