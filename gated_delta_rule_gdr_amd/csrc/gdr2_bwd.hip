@@ -528,12 +528,27 @@ struct BgCfg {
     static_assert((C * DK / VEC) % kBgThreads == 0, "Y / Ktilde staging");
     static constexpr bool YK_LDS = ES == 2;
     static constexpr int NBUF = ES == 2 ? 2 : 1;  // value-column block buffers (fp32: LDS-bound)
+    // The gradients leave through LDS as whole token rows (dv, dw and dlog alpha on the 16-bit
+    // path, dq, dk and db on every path), written with streaming stores: whole cache lines per
+    // instruction go past the L2, so the kernels that follow do not write back this kernel's
+    // dirty lines (at B=4 T=4096 H=16 d=128 the next factor kernel runs 4-7 us faster; this
+    // kernel is unchanged).  The lanes' own 8-byte pieces could not be streamed: the L2 has to
+    // combine them into lines.
+    static constexpr bool STG = ES == 2;
+    static constexpr int PV = DV + PAD, PL = DK + 4;
     static_assert(NJH == 2, "one 16-column block per wave half");
 };
 
 template <typename OT, int DK, int DV, int DVH>
 struct alignas(16) BgSmem {
     using Cf = BgCfg<OT, DK, DV, DVH>;
+    struct alignas(16) Gram {  // Gram-gradient phase
+        OT Kb[kChunk * Cf::PK];    // k . exp(ref_S - G)  [s][i]
+        OT Qb[kChunk * Cf::PK];    // q . exp(G - ref_R)  [r][i]
+        OT Eb[kChunk * Cf::PK];    // e . exp(G - ref_R)  [r][i]
+        OT dPT[kChunk * Cf::PC];   // dP^T                [s][r]
+        OT dAT[kChunk * Cf::PC];   // dA^T                [s][r]
+    };
     union {
         struct {  // value-column phase
             OT Yt[Cf::YK_LDS ? kChunk * Cf::PK : 1];  // -Y      [r][i] (16-bit operands)
@@ -547,13 +562,18 @@ struct alignas(16) BgSmem {
             OT dDT[DVH * Cf::PC];      // dDelta^T            [j][r]
             OT dXt[kChunk * Cf::PH];   // dX block            [r][j]
         } j;
-        struct {  // Gram-gradient phase
-            OT Kb[kChunk * Cf::PK];    // k . exp(ref_S - G)  [s][i]
-            OT Qb[kChunk * Cf::PK];    // q . exp(G - ref_R)  [r][i]
-            OT Eb[kChunk * Cf::PK];    // e . exp(G - ref_R)  [r][i]
-            OT dPT[kChunk * Cf::PC];   // dP^T                [s][r]
-            OT dAT[kChunk * Cf::PC];   // dA^T                [s][r]
-        } g;
+        Gram g;
+        struct {  // token-row staging of the gradients behind the Gram tiles, which are still
+                  // read while dv and dw leave and hold dq, dk, db at the end
+            Gram keep;
+            union {
+                struct {
+                    OT dV[Cf::STG ? kChunk * Cf::PV : 1];  // dv  [r][j]
+                    OT dW[Cf::STG ? kChunk * Cf::PV : 1];  // dw  [r][j]
+                } vw;
+                float dL[Cf::STG ? kChunk * Cf::PL : 1];  // dlog alpha [r][i]
+            } x;
+        } s;
     } u;
     float tot[4][DK];
     float ctab[6][DK];
@@ -579,6 +599,8 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
     constexpr int NKS = Cf::NKS, NIBH = Cf::NIBH, VEC = Cf::VEC;
     constexpr int NSV = Cf::NSV, SVEC = Cf::SVEC, NOV = Cf::NOV, OVEC = Cf::OVEC;
     constexpr int NTV = Cf::NTV, TVEC = Cf::TVEC, NT = kBgThreads;
+    constexpr bool STG = Cf::STG;
+    constexpr int PV = Cf::PV, PL = Cf::PL;
     __shared__ BgSmem<OT, DK, DV, DVH> sm;
 
     // wave index made wave-uniform, so that branches on R and half are scalar branches
@@ -938,7 +960,14 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
         lds_barrier();
     }
     if constexpr (NS == 2) {
-        if (valid) {
+        if constexpr (STG) {  // the value tiles are dead (the loop ends with a barrier)
+#pragma unroll
+            for (int jq = 0; jq < NJ; ++jq) {
+                const int jc = jq * DVH + 16 * half + 4 * g;
+                *(typename RW::t*)(sm.u.s.x.vw.dV + r * PV + jc) = dvk[jq];
+                if (!w_sc) *(typename RW::t*)(sm.u.s.x.vw.dW + r * PV + jc) = dwk[jq];
+            }
+        } else if (valid) {
 #pragma unroll
             for (int jq = 0; jq < NJ; ++jq) {
                 const long o = (tok0 + (long)r * H) * DV + jq * DVH + 16 * half + 4 * g;
@@ -971,6 +1000,20 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
     if constexpr (!EARLY) {  // publishes the block totals (and the prologue's row norms)
         lds_barrier();
         decay_tables();
+    } else if constexpr (STG && NS == 2) {
+        lds_barrier();
+    }
+    if constexpr (STG && NS == 2) {  // dv, dw as whole token rows; they drain during the Gram phase
+        constexpr int UPV = DV / VEC;
+#pragma unroll
+        for (int m = 0; m < C * UPV / NT; ++m) {
+            const int x = tid + m * NT, rr = x / UPV, j = (x % UPV) * VEC;
+            if ((long)c * C + rr < T) {
+                const long o = (tok0 + (long)rr * H) * DV + j;
+                store_stream((i32x4*)((OT*)p.dv + o), *(const i32x4*)(sm.u.s.x.vw.dV + rr * PV + j));
+                if (!w_sc) store_stream((i32x4*)((OT*)p.dw + o), *(const i32x4*)(sm.u.s.x.vw.dW + rr * PV + j));
+            }
+        }
     }
     // deep-decay path for the whole chunk (uniform over the workgroup): right Gram factors
     // referenced to the end of their block and the diagonal blocks entry by entry, so that no
@@ -1098,12 +1141,12 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
         }
     }
 
-    // ---- epilogue: lane = token r, channels 16 (ibase + ib) + 4g + e.  With the fused prologue,
-    //      dq and dk wait for their row dot products (a cross-wave exchange); rather than as a burst
-    //      of 4-element pieces at the end, they and db then go through the (now dead) Gram tiles in
-    //      LDS and reach HBM as whole token rows of 16-byte lane stores
-    if constexpr (PRO) lds_barrier();
-    OT* const stq = sm.u.g.Kb;  // prologue staging [r][i], pitch PK: dq, dk, db
+    // ---- epilogue: lane = token r, channels 16 (ibase + ib) + 4g + e.  dq, dk and db go through
+    //      the Gram tiles in LDS (dead once every wave is past the products) and reach HBM as
+    //      whole token rows; with the fused prologue dq and dk also wait there for their row dot
+    //      products (a cross-wave exchange)
+    lds_barrier();
+    OT* const stq = sm.u.g.Kb;  // staging [r][i], pitch PK: dq, dk, db
     OT* const stk = sm.u.g.Qb;
     OT* const stb = sm.u.g.Eb;
     f32x4 dG[NIBH];
@@ -1178,13 +1221,11 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
             Dk += (k4[0] * dkv[0] + k4[1] * dkv[1]) + (k4[2] * dkv[2] + k4[3] * dkv[3]);
         }
         if (b_sc) db_acc += (dbv[0] + dbv[1]) + (dbv[2] + dbv[3]);
-        if constexpr (PRO) {
-            if (!b_sc) store4(stb + r * PK + i0, dbv);
-        } else if (valid) {
-            store4((OT*)p.dq + orow + i0, dqv);
-            store4((OT*)p.dk + orow + i0, dkv);
-            if (!b_sc) store4((OT*)p.db + orow + i0, dbv);
+        if (!PRO) {
+            store4(stq + r * PK + i0, dqv);
+            store4(stk + r * PK + i0, dkv);
         }
+        if (!b_sc) store4(stb + r * PK + i0, dbv);
         if (rl == 0) {
             *(f32x4*)(&sm.btot[R][i0]) = dG[ib];
             *(f32x4*)(&sm.ktot[R][i0]) = kdk;
@@ -1239,6 +1280,8 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
             if (PRO && !a_sc) dl *= dsa[PRO ? ib : 0];  // d a = d log alpha . (-c sigmoid(a))
             if (a_sc) {
                 dl_acc += (dl[0] + dl[1]) + (dl[2] + dl[3]);
+            } else if constexpr (STG) {  // dv, dw have left the staging tiles (barriers since)
+                *(f32x4*)(sm.u.s.x.dL + r * PL + i0) = dl;
             } else {
                 *(f32x4*)(p.dla + orow + i0) = dl;
             }
@@ -1258,18 +1301,29 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
             p.dla[row] = PRO ? d * (-p.pro.decay_scale * sigmoid_f(p.la[row])) : d;
         }
     }
-    // ---- prologue: the staged dq, dk, db rows to HBM
-    if constexpr (PRO) {
-        lds_barrier();
+    // ---- the staged dq, dk, db (and dlog alpha) rows to HBM
+    lds_barrier();
+    {
         constexpr int UPR = DK / VEC;  // 16-byte units per token row
 #pragma unroll
         for (int m = 0; m < C * UPR / NT; ++m) {
             const int x = tid + m * NT, rr = x / UPR, i = (x % UPR) * VEC;
             if ((long)c * C + rr < T) {
                 const long o = (tok0 + (long)rr * H) * DK + i;
-                *(i32x4*)((OT*)p.dq + o) = *(const i32x4*)(stq + rr * PK + i);
-                *(i32x4*)((OT*)p.dk + o) = *(const i32x4*)(stk + rr * PK + i);
-                if (!b_sc) *(i32x4*)((OT*)p.db + o) = *(const i32x4*)(stb + rr * PK + i);
+                store_stream((i32x4*)((OT*)p.dq + o), *(const i32x4*)(stq + rr * PK + i));
+                store_stream((i32x4*)((OT*)p.dk + o), *(const i32x4*)(stk + rr * PK + i));
+                if (!b_sc) store_stream((i32x4*)((OT*)p.db + o), *(const i32x4*)(stb + rr * PK + i));
+            }
+        }
+    }
+    if constexpr (STG) {
+        if (!a_sc) {
+            constexpr int UPL = DK / 4;  // 16-byte units per fp32 row
+#pragma unroll
+            for (int m = 0; m < C * UPL / NT; ++m) {
+                const int x = tid + m * NT, rr = x / UPL, i = (x % UPL) * 4;
+                if ((long)c * C + rr < T)
+                    store_stream((f32x4*)(p.dla + (tok0 + (long)rr * H) * DK + i), *(const f32x4*)(sm.u.s.x.dL + rr * PL + i));
             }
         }
     }
