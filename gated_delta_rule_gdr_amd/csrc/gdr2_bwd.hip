@@ -535,6 +535,11 @@ struct BgCfg {
     // kernel is unchanged).  The lanes' own 8-byte pieces could not be streamed: the L2 has to
     // combine them into lines.
     static constexpr bool STG = ES == 2;
+    // 16-bit path: v and w of a value-column block arrive like dO (16-byte pieces of token rows by
+    // consecutive threads) and are staged beside it; each lane then reads its own four columns
+    // from LDS (the lanes' own 8-byte pieces of 16 token rows cost the kernel about 19 us at
+    // B=4 T=4096 H=16 d=128)
+    static constexpr bool VW_LDS = ES == 2;
     static constexpr int PV = DV + PAD, PL = DK + 4;
     static_assert(NJH == 2, "one 16-column block per wave half");
 };
@@ -558,6 +563,8 @@ struct alignas(16) BgSmem {
             OT St[Cf::NBUF][DVH * Cf::PK];      // S^T block   [j][i]  (16-bit: two buffers, the
             OT dSt[Cf::NBUF][DVH * Cf::PK];     // dS'^T block [j][i]   next block is staged
             OT dOt[Cf::NBUF][kChunk * Cf::PH];  // dO block    [r][j]   while this one is reduced)
+            OT vt[Cf::NBUF][Cf::VW_LDS ? kChunk * Cf::PH : 1];  // v block [r][j]
+            OT wt[Cf::NBUF][Cf::VW_LDS ? kChunk * Cf::PH : 1];  // w block [r][j]
             OT DlT[DVH * Cf::PC];      // Delta^T             [j][r]
             OT dDT[DVH * Cf::PC];      // dDelta^T            [j][r]
             OT dXt[kChunk * Cf::PH];   // dX block            [r][j]
@@ -730,7 +737,9 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
     // block's work), fp32 one
     constexpr int NS = Cf::NBUF;
     i32x4 pS[NS][SVEC], pdS[NS][SVEC], pO[NS][OVEC];
+    constexpr bool VW_LDS = Cf::VW_LDS;
     typename RW::t pv[NS], pw[NS], pU[NS];
+    i32x4 pV[NS][VW_LDS ? OVEC : 1], pW[NS][VW_LDS ? OVEC : 1];
     const OT* Uc = (const OT*)p.wy.U + cix * C * DV;
     auto fetch_block = [&](int jq, int st) __attribute__((always_inline)) {
         const int jb0 = jq * DVH;
@@ -747,19 +756,29 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
         for (int m = 0; m < OVEC; ++m) {
             const int x = tid + m * NT;
             const int rr = (x * VEC) / DVH, jj = (x * VEC) % DVH;
-            i32x4 z = {0, 0, 0, 0};
-            if ((NOV % NT == 0 || x < NOV) && (long)c * C + rr < T)
-                z = *(const i32x4*)((const OT*)p.dO + (tok0 + (long)rr * H) * DV + jb0 + jj);
+            i32x4 z = {0, 0, 0, 0}, zv = z, zw = z;
+            if ((NOV % NT == 0 || x < NOV) && (long)c * C + rr < T) {
+                const long o = (tok0 + (long)rr * H) * DV + jb0 + jj;
+                z = *(const i32x4*)((const OT*)p.dO + o);
+                if constexpr (VW_LDS) {
+                    zv = *(const i32x4*)((const OT*)p.v + o);
+                    if (!w_sc) zw = *(const i32x4*)((const OT*)p.w + o);
+                }
+            }
             pO[st][m] = z;
+            if constexpr (VW_LDS) {
+                pV[st][m] = zv;
+                pW[st][m] = zw;
+            }
         }
         // v, w of (token r, columns jb0 + 16 half + 4g .. +3) for dv, dw
         const long trow = valid ? (tok0 + (long)r * H) : row;
         const long o = trow * DV + jb0 + 16 * half + 4 * g;
-        pv[st] = *(const typename RW::t*)((const OT*)p.v + o);
+        if constexpr (!VW_LDS) pv[st] = *(const typename RW::t*)((const OT*)p.v + o);
         if (w_sc) {
             const OT x = ((const OT*)p.w)[trow];
             pw[st] = typename RW::t{x, x, x, x};
-        } else {
+        } else if constexpr (!VW_LDS) {
             pw[st] = *(const typename RW::t*)((const OT*)p.w + o);
         }
         pU[st] = *(const typename RW::t*)(Uc + ((long)(R * (DV / 16) + jb0 / 16 + half) * 64 + l) * 4);
@@ -827,11 +846,17 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
 #pragma unroll
         for (int m = 0; m < OVEC; ++m) {
             const int x = tid + m * NT;
-            if (NOV % NT == 0 || x < NOV)
-                *(i32x4*)(sm.u.j.dOt[b] + ((x * VEC) / DVH) * PH + (x * VEC) % DVH) = pO[st][m];
+            if (NOV % NT == 0 || x < NOV) {
+                const int o = ((x * VEC) / DVH) * PH + (x * VEC) % DVH;
+                *(i32x4*)(sm.u.j.dOt[b] + o) = pO[st][m];
+                if constexpr (VW_LDS) {
+                    *(i32x4*)(sm.u.j.vt[b] + o) = pV[st][m];
+                    if (!w_sc) *(i32x4*)(sm.u.j.wt[b] + o) = pW[st][m];
+                }
+            }
         }
-        cv = pv[st];
-        cw = pw[st];
+        if constexpr (!VW_LDS) cv = pv[st];
+        if (!VW_LDS || w_sc) cw = pw[st];
         cU = pU[st];
     };
     auto fetch_next = [&](int jn, int st) __attribute__((always_inline)) {
@@ -900,6 +925,10 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
                 MM::mma(ax, FR::kc(sm.u.j.dDT, PC, 16 * jb, k0, l), FR::tr(sm.u.j.Tt, PC, k0, 16 * R, l));
             const int jc = 16 * jb + 4 * g;
             store4(sm.u.j.dXt + r * PH + jc, ax);
+            if constexpr (VW_LDS) {  // this lane's columns of the staged v, w block
+                cv = *(const typename RW::t*)(sm.u.j.vt[bq] + r * PH + jc);
+                if (!w_sc) cw = *(const typename RW::t*)(sm.u.j.wt[bq] + r * PH + jc);
+            }
             f32x4 wg = RW::widen(cw), dwv = ax * RW::widen(cv);
             if (PRO) {  // w = sigmoid(w pre-activation): dw_pre = dw . w (1 - w)
 #pragma unroll
