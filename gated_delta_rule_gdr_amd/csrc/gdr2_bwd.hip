@@ -540,6 +540,12 @@ struct BgCfg {
     // from LDS (the lanes' own 8-byte pieces of 16 token rows cost the kernel about 19 us at
     // B=4 T=4096 H=16 d=128)
     static constexpr bool VW_LDS = ES == 2;
+    // 16-bit path: q, k and b of the chunk are loaded the same way with the last value-column
+    // block and put into the Gram tiles' places after the loop, where each lane reads back the
+    // elements it later overwrites with the decay-absorbed tiles (the lanes' own 8-byte pieces
+    // cost about 15 us)
+    static constexpr bool QKB_LDS = ES == 2;
+    static constexpr int QVEC = C * DK / VEC / kBgThreads;
     static constexpr int PV = DV + PAD, PL = DK + 4;
     static_assert(NJH == 2, "one 16-column block per wave half");
 };
@@ -631,6 +637,9 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
 
     // ---- this lane's log alpha (token r, channels 16 (ibase+ib) + 4g + e); q, k, b come later
     typename RW::t qr[NIBH], kr[NIBH], br[NIBH];
+    constexpr bool QKB_LDS = Cf::QKB_LDS;
+    constexpr int QVEC = QKB_LDS ? Cf::QVEC : 1;
+    i32x4 rQ[QVEC], rK[QVEC], rB[QVEC];  // raw q, k, b rows (16-byte pieces) on their way to LDS
     // scalar gates and the fused prologue (the plain instance carries no gate branches)
     constexpr bool GS = MODE != kModePlain, PRO = mode_prologue(MODE);
     const int gm = gate_bits<MODE>(p.gates);
@@ -864,15 +873,28 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
             fetch_block(jn, st);
         } else if (jn == NJ) {
             if constexpr (!EARLY) load_la();
+            if constexpr (QKB_LDS) {  // rows past T read row T - 1: finite values, zeroed later
+#pragma unroll
+                for (int m = 0; m < QVEC; ++m) {
+                    const int x = tid + m * NT, rr = x / (DK / VEC), i = (x % (DK / VEC)) * VEC;
+                    const long tc = (long)c * C + rr < T ? (long)c * C + rr : T - 1;
+                    const long o = (((long)bb * T + tc) * H + h) * DK + i;
+                    rQ[m] = *(const i32x4*)((const OT*)p.q + o);
+                    rK[m] = *(const i32x4*)((const OT*)p.k + o);
+                    if (!b_sc) rB[m] = *(const i32x4*)((const OT*)p.b + o);
+                }
+            }
 #pragma unroll
             for (int ib = 0; ib < NIBH; ++ib) {
                 const int i0 = 16 * (ibase + ib) + 4 * g;
-                qr[ib] = *(const typename RW::t*)((const OT*)p.q + row * DK + i0);
-                kr[ib] = *(const typename RW::t*)((const OT*)p.k + row * DK + i0);
+                if constexpr (!QKB_LDS) {
+                    qr[ib] = *(const typename RW::t*)((const OT*)p.q + row * DK + i0);
+                    kr[ib] = *(const typename RW::t*)((const OT*)p.k + row * DK + i0);
+                }
                 if (b_sc) {
                     const OT x = ((const OT*)p.b)[row];
                     br[ib] = typename RW::t{x, x, x, x};
-                } else {
+                } else if constexpr (!QKB_LDS) {
                     br[ib] = *(const typename RW::t*)((const OT*)p.b + row * DK + i0);
                 }
             }
@@ -1005,6 +1027,23 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
             }
         }
     }
+    if constexpr (QKB_LDS) {  // raw q, k, b rows into the places of Qbar, Kbar, Ebar (same layout)
+#pragma unroll
+        for (int m = 0; m < QVEC; ++m) {
+            const int x = tid + m * NT, rr = x / (DK / VEC), i = (x % (DK / VEC)) * VEC;
+            *(i32x4*)(sm.u.g.Qb + rr * PK + i) = rQ[m];
+            *(i32x4*)(sm.u.g.Kb + rr * PK + i) = rK[m];
+            if (!b_sc) *(i32x4*)(sm.u.g.Eb + rr * PK + i) = rB[m];
+        }
+        lds_barrier();  // (also publishes the dv, dw staging)
+#pragma unroll
+        for (int ib = 0; ib < NIBH; ++ib) {
+            const int i0 = 16 * (ibase + ib) + 4 * g;
+            qr[ib] = *(const typename RW::t*)(sm.u.g.Qb + r * PK + i0);
+            kr[ib] = *(const typename RW::t*)(sm.u.g.Kb + r * PK + i0);
+            if (!b_sc) br[ib] = *(const typename RW::t*)(sm.u.g.Eb + r * PK + i0);
+        }
+    }
 
     if constexpr (!EARLY) scan_la();
     // fused prologue: this wave's half of the squared row norms of q and k (lanes 16g + rl of both
@@ -1029,7 +1068,7 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
     if constexpr (!EARLY) {  // publishes the block totals (and the prologue's row norms)
         lds_barrier();
         decay_tables();
-    } else if constexpr (STG && NS == 2) {
+    } else if constexpr (STG && NS == 2 && !QKB_LDS) {
         lds_barrier();
     }
     if constexpr (STG && NS == 2) {  // dv, dw as whole token rows; they drain during the Gram phase
