@@ -637,7 +637,9 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
 
     // ---- this lane's log alpha (token r, channels 16 (ibase+ib) + 4g + e); q, k, b come later
     typename RW::t qr[NIBH], kr[NIBH], br[NIBH];
-    constexpr bool QKB_LDS = Cf::QKB_LDS;
+    // (a fixed scalar b or w leaves too little of q, k, b or v, w to move for the staging to pay)
+    constexpr int FGM = MODE >= kModeFixedGates ? MODE - kModeFixedGates : 0;
+    constexpr bool QKB_LDS = Cf::QKB_LDS && !(FGM & kEraseScalar);
     constexpr int QVEC = QKB_LDS ? Cf::QVEC : 1;
     i32x4 rQ[QVEC], rK[QVEC], rB[QVEC];  // raw q, k, b rows (16-byte pieces) on their way to LDS
     // scalar gates and the fused prologue (the plain instance carries no gate branches)
@@ -746,7 +748,7 @@ __global__ __launch_bounds__(kBgThreads, 1) void gdr2_bgrad_kernel(BwdParams p) 
     // block's work), fp32 one
     constexpr int NS = Cf::NBUF;
     i32x4 pS[NS][SVEC], pdS[NS][SVEC], pO[NS][OVEC];
-    constexpr bool VW_LDS = Cf::VW_LDS;
+    constexpr bool VW_LDS = Cf::VW_LDS && !(FGM & kWriteScalar);
     typename RW::t pv[NS], pw[NS], pU[NS];
     i32x4 pV[NS][VW_LDS ? OVEC : 1], pW[NS][VW_LDS ? OVEC : 1];
     const OT* Uc = (const OT*)p.wy.U + cix * C * DV;
