@@ -215,9 +215,31 @@ def bench_workloads(torch, g2, steps):
     return out
 
 
-def step_traffic(ht):
+def copy_rate_gbs(torch):
+    """The device-to-device copy rate of this GPU (1 GiB read + 1 GiB written by torch's copy,
+    averaged over 10 copies with HIP events): the practical rate for a stream that reads and writes
+    in equal parts, against which the measured step traffic is also set."""
+    a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(2):
+        b.copy_(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(10):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    rate = 2 * (1 << 30) * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del a, b
+    return rate
+
+
+def step_traffic(ht, ms_step=None, copy_gbs=None):
     """Whole-step HBM traffic from the committed counter summary (sum of the four kernels' scaled
-    FETCH_SIZE + WRITE_SIZE), or None when any kernel source changed since it was taken."""
+    FETCH_SIZE + WRITE_SIZE), or None when any kernel source changed since it was taken; with the
+    step time and the copy rate, also the rate the step moves that traffic at and its fraction of
+    the copy rate."""
     tot = 0
     for k in KERNELS:
         t = measured_traffic(k)
@@ -225,8 +247,13 @@ def step_traffic(ht):
             return None
         tot += t
     alg = (16 * DK + 30 * DK)
-    return {"bytes": tot, "B_per_head_token": round(tot / ht, 1), "alg_B_per_head_token": alg,
-            "ratio_to_alg": round(tot / ht / alg, 3)}
+    out = {"bytes": tot, "B_per_head_token": round(tot / ht, 1), "alg_B_per_head_token": alg,
+           "ratio_to_alg": round(tot / ht / alg, 3)}
+    if ms_step and copy_gbs:
+        gbs = tot / (ms_step * 1e-3) / 1e9
+        out.update({"achieved_GBs": round(gbs, 1), "copy_rate_GBs": round(copy_gbs, 1),
+                    "frac_of_copy_rate": round(gbs / copy_gbs, 4)})
+    return out
 
 
 def bench_gate_variants(torch, g2, steps):
@@ -369,7 +396,7 @@ def main():
                           "mfma_frac": round(flops / (ms_step * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
                           "roofline_Mtokens_per_s": round(tokens / (step_alg_bytes / (HBM_PEAK_GBS * 1e9)) / 1e6, 2)},
         "kernel_us": {kn: round(t_, 2) for kn, t_ in kern_us.items()},
-        "step_traffic": step_traffic(ht),
+        "step_traffic": step_traffic(ht, ms_step, None if args.profile_pass else copy_rate_gbs(torch)),
     }
     if not args.no_decode:
         out["decode"] = bench_decode(torch, g2.gdr2_decode_step, args.decode_steps)
