@@ -8,7 +8,11 @@ structure of the method fixes:
     Rule-2: two gates instead of one"), so permuting the key channels of q, k, b, log alpha (and
     the value channels of v, w, dO) permutes every output and gradient the same way;
   * chain isolation: each (batch, head) chain has its own state, so a NaN planted in one chain's
-    inputs leaves every other chain's outputs and gradients bitwise unchanged.
+    inputs leaves every other chain's outputs and gradients bitwise unchanged;
+  * the write gate and the value enter only through their product w . v (same section), so
+    (w, v) -> (c w, v / c) leaves the forward unchanged and scales dv by c and dw by 1 / c;
+  * for fixed q, k, b, w and decay the recurrence is linear in (v, S0) (the update equation,
+    same section), and the backward is linear in the incoming gradients (dO, dS_T).
 """
 import pytest
 import torch
@@ -16,7 +20,7 @@ import torch
 from gated_delta_rule_gdr_amd import (Prologue, gdr2_bwd_chunked, gdr2_bwd_chunked_recompute,
                                       gdr2_fwd_chunked, gdr2_fwd_infer)
 from gated_delta_rule_gdr_amd.inputs import config_inputs, layer_inputs
-from tests._util import TOL, announce, assert_close, to_np
+from tests._util import TOL, announce, assert_close, assert_close_chains, to_np
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -135,3 +139,66 @@ def test_nan_isolated_to_its_chain():
         assert torch.equal(gr[n].permute(0, 2, 1, 3)[keep], gr2[n].permute(0, 2, 1, 3)[keep]), n
     assert torch.equal(gr["dS0"][keep], gr2["dS0"][keep])
     assert torch.isnan(o2[bb, t:, hh]).any() and torch.isnan(ST2[bb, hh]).any()
+
+
+@pytest.mark.parametrize("dtype,dk,dv,T", [("bf16", 128, 128, 200), ("f32", 64, 128, 130)])
+def test_write_gate_value_rescaling(dtype, dk, dv, T):
+    """(w, v) -> (4 w, v / 4): a power-of-two scale is exact in both dtypes and commutes with
+    every rounding the kernels do on w . v, dX . w and dX . v, so the forward is bitwise the same
+    and dv, dw come back scaled by exactly 4 and 1/4; the other gradients are bitwise the same."""
+    x = layer_inputs(2, T, 3, dk, dv, dtype=dtype, seed=1300 + dk, s0_std=0.05, dST=True)
+    y = dict(x)
+    y["w"] = x["w"] * 4
+    y["v"] = x["v"] / 4
+    announce(f"write-gate rescaling {dtype} dk={dk} dv={dv} T={T}")
+    res = []
+    for z in (x, y):
+        g = _gpu(z)
+        o, ST, ws = gdr2_fwd_chunked(*(g[n] for n in NAMES), S0=g["S0"])
+        gr = gdr2_bwd_chunked(*(g[n] for n in NAMES), g["dO"], ws, dS_T=g["dST"])
+        res.append((o, ST, gr))
+    torch.cuda.synchronize()
+    (o, ST, gr), (o2, ST2, gr2) = res
+    assert torch.equal(o, o2) and torch.equal(ST, ST2)
+    for n in ("dq", "dk", "db", "dlog_alpha", "dS0"):
+        assert torch.equal(gr[n], gr2[n]), n
+    assert torch.equal(gr2["dv"], gr["dv"] * 4)
+    assert torch.equal(gr2["dw"], gr["dw"] / 4)
+
+
+@pytest.mark.parametrize("dtype,dk,dv,T", [("f32", 128, 128, 200), ("bf16", 64, 128, 130)])
+def test_linearity_in_values_state_and_gradients(dtype, dk, dv, T):
+    """Forward: (v, S0) -> (o, S_T) is linear for fixed q, k, b, w and decay.  Backward: every
+    gradient is linear in (dO, dS_T) for fixed forward inputs.  The two summands live on disjoint
+    halves of the sequence (values and dO) and of the key rows (S0 and dS_T), so their sums are
+    exact inputs in both dtypes; the results agree within the dtype's tolerance, chain by chain."""
+    x = layer_inputs(2, T, 3, dk, dv, dtype=dtype, seed=1400 + dk, s0_std=0.05, dST=True)
+    half, kh = T // 2, dk // 2
+    a, b_ = dict(x), dict(x)
+    a["v"] = x["v"].clone(); a["v"][:, half:] = 0
+    b_["v"] = x["v"].clone(); b_["v"][:, :half] = 0
+    a["S0"] = x["S0"].clone(); a["S0"][:, :, kh:] = 0
+    b_["S0"] = x["S0"].clone(); b_["S0"][:, :, :kh] = 0
+    a["dO"] = x["dO"].clone(); a["dO"][:, :half] = 0
+    b_["dO"] = x["dO"].clone(); b_["dO"][:, half:] = 0
+    a["dST"] = x["dST"].clone(); a["dST"][:, :, :kh] = 0
+    b_["dST"] = x["dST"].clone(); b_["dST"][:, :, kh:] = 0
+    announce(f"linearity {dtype} dk={dk} dv={dv} T={T}")
+    fwd, bwd = [], []
+    for z in (x, a, b_):
+        g = _gpu(z)
+        o, ST, _ = gdr2_fwd_chunked(*(g[n] for n in NAMES), S0=g["S0"])
+        fwd.append((o.double(), ST.double()))
+    gx = _gpu(x)
+    _, _, ws = gdr2_fwd_chunked(*(gx[n] for n in NAMES), S0=gx["S0"])
+    for z in (x, a, b_):
+        gz = _gpu(z)
+        gr = gdr2_bwd_chunked(*(gx[n] for n in NAMES), gz["dO"], ws, dS_T=gz["dST"])
+        bwd.append({n: gr[n].double() for n in GRADS})
+    torch.cuda.synchronize()
+    tol = TOL[dtype]
+    assert_close_chains("o", to_np(fwd[1][0] + fwd[2][0]), to_np(fwd[0][0]), tol, "tok")
+    assert_close_chains("S_T", to_np(fwd[1][1] + fwd[2][1]), to_np(fwd[0][1]), tol, "state")
+    for n in GRADS:
+        lay = "state" if n == "dS0" else "tok"
+        assert_close_chains(n, to_np(bwd[1][n] + bwd[2][n]), to_np(bwd[0][n]), tol, lay)
