@@ -40,13 +40,14 @@ ALG_BYTES_PER_HT = {"gdr2_wy_kernel": 14 * DK, "gdr2_carry_lds_kernel": 2 * DV,
 ALG_FLOPS_PER_HT = {"forward": 6 * DK * DK + 5 * 64 * DK + 64 * 64 / 3,
                     "backward": 14 * DK * DK + 14 * 64 * DK + 64 * 64}
 KERNELS = ["gdr2_wy_kernel", "gdr2_carry_lds_kernel", "gdr2_dstate_lds_kernel", "gdr2_bgrad_kernel"]
-SOURCES = ["gdr2_common.hpp", "gdr2_kernels.hpp", "gdr2_wy.hpp", "gdr2_fwd.hip", "gdr2_bwd.hip"]
+SOURCES = ["csrc/gdr2_common.hpp", "csrc/gdr2_kernels.hpp", "csrc/gdr2_wy.hpp", "csrc/gdr2_wy.hip",
+           "csrc/gdr2_fwd.hip", "csrc/gdr2_bwd.hip", "build.py"]  # build.py: the compile flags
 
 
 def source_hash():
     h = hashlib.sha256()
     for s in SOURCES:
-        with open(os.path.join(ROOT, "gated_delta_rule_gdr_amd", "csrc", s), "rb") as f:
+        with open(os.path.join(ROOT, "gated_delta_rule_gdr_amd", s), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
