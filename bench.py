@@ -159,7 +159,7 @@ def train_step_fn(torch, g2, x, B_, T_, H_, dk, dv, prologue=None, S0=None, want
     return step
 
 
-def time_steps(torch, step, steps, warm=2):
+def time_steps(torch, step, steps, warm=5):
     for _ in range(warm):
         step()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -402,7 +402,7 @@ def main():
     if not args.no_decode:
         out["decode"] = bench_decode(torch, g2.gdr2_decode_step, args.decode_steps)
     if not args.profile_pass:
-        out["gate_variants"] = bench_gate_variants(torch, g2, 5)
+        out["gate_variants"] = bench_gate_variants(torch, g2, 20)
         out["out_gate"] = bench_out_gate(torch, g2, 10)
         if not args.no_workloads:
             out["workloads"] = bench_workloads(torch, g2, 5)
