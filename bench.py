@@ -347,6 +347,15 @@ def main():
 
     for _ in range(args.warmup):
         step()
+    # per-kernel breakdown: the same number of steps, with HIP events around each phase on the
+    # stream the kernels run on (event records add their own gaps, so they stay out of `wall`).
+    # Run between the warm-up steps (which take the first-launch costs) and the timed steps, it
+    # also brings the GPU's clocks up from idle, which a short warm-up does not (20 timed steps
+    # after 5 warm-up steps read 3 % slow with this pass run after them).
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
     # the timed region: exactly `steps` steps, no instrumentation inside
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -354,12 +363,6 @@ def main():
         step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    # per-kernel breakdown: the same number of steps again, with HIP events around each phase on
-    # the stream the kernels run on (event records add their own gaps, so they stay out of `wall`)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-    for s in range(args.steps):
-        step(evs[s])
-    torch.cuda.synchronize()
 
     ms_step = wall * 1e3 / args.steps
     tokens = B * T
