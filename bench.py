@@ -147,15 +147,15 @@ def train_step_fn(torch, g2, x, B_, T_, H_, dk, dv, prologue=None, S0=None, want
     q, k, v, la, b, w, dO = (x[n] for n in ("q", "k", "v", "log_alpha", "b", "w", "dO"))
 
     def step(ev=None):
-        if ev: ev[0].record()
+        if ev and ev[0] is not None: ev[0].record()
         g2.gdr2_fwd_factors(q, k, v, la, b, w, fws, prologue=prologue)
-        if ev: ev[1].record()
+        if ev and ev[1] is not None: ev[1].record()
         g2.gdr2_fwd_carry(B_, T_, H_, dk, dv, dt, fws, o, S0=S0, S_T=ST)
-        if ev: ev[2].record()
+        if ev and ev[2] is not None: ev[2].record()
         g2.gdr2_bwd_state(B_, T_, H_, dk, dv, dt, fws, dO, bws, dS0=dS0)
-        if ev: ev[3].record()
+        if ev and ev[3] is not None: ev[3].record()
         g2.gdr2_bwd_grads(q, k, v, la, b, w, fws, dO, bws, gr, prologue=prologue)
-        if ev: ev[4].record()
+        if ev and ev[4] is not None: ev[4].record()
     return step
 
 
@@ -347,31 +347,34 @@ def main():
 
     for _ in range(args.warmup):
         step()
-    # per-kernel breakdown: the same number of steps, with HIP events around each phase on the
-    # stream the kernels run on (event records add their own gaps, so they stay out of `wall`).
-    # Run between the warm-up steps (which take the first-launch costs) and the timed steps, it
-    # also brings the GPU's clocks up from idle, which a short warm-up does not (20 timed steps
-    # after 5 warm-up steps read 3 % slow with this pass run after them).
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-    for s in range(args.steps):
+    # per-kernel breakdown: HIP events around every phase on the stream the kernels run on, over
+    # 2K steps; the first K bring the GPU from idle to its steady state (20 steps right after 5
+    # warm-up steps run about 5 % slow), the averages are taken over the last K
+    Ev = lambda: torch.cuda.Event(enable_timing=True)
+    evs = [[Ev() for _ in range(5)] for _ in range(2 * args.steps)]
+    for s in range(2 * args.steps):
         step(evs[s])
     torch.cuda.synchronize()
-    # the timed region: exactly `steps` steps, no instrumentation inside
+    kern_us = {kname: sum(e[i].elapsed_time(e[i + 1]) for e in evs[args.steps:]) * 1e3 / args.steps
+               for i, kname in enumerate(KERNELS)}
+    dom = max(kern_us, key=kern_us.get)
+    di = KERNELS.index(dom)
+    # the timed region: exactly `steps` steps; the only instrumentation is a pair of HIP events
+    # around the dominant kernel in every step, whose average duration gives the roofline figure
+    dev = [[Ev() if i in (di, di + 1) else None for i in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
-        step()
+        step(dev[s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    dom_us = sum(e[di].elapsed_time(e[di + 1]) for e in dev) * 1e3 / args.steps
 
     ms_step = wall * 1e3 / args.steps
     tokens = B * T
     value = tokens * args.steps / wall / 1e6
     ht = B * T * H
-    kern_us = {kname: sum(e[i].elapsed_time(e[i + 1]) for e in evs) * 1e3 / args.steps
-               for i, kname in enumerate(KERNELS)}
-    dom = max(kern_us, key=kern_us.get)
-    ach = ALG_BYTES_PER_HT[dom] * ht / (kern_us[dom] * 1e-6) / 1e9
+    ach = ALG_BYTES_PER_HT[dom] * ht / (dom_us * 1e-6) / 1e9
     traffic = measured_traffic(dom)
     flops = (ALG_FLOPS_PER_HT["forward"] + ALG_FLOPS_PER_HT["backward"]) * ht
     step_alg_bytes = (16 * DK + 30 * DK) * ht
@@ -392,7 +395,7 @@ def main():
         "config": {"workload": "GDR-2 layer fwd+bwd, model-shaped 1.3B layer", "B": B, "T": T,
                    "H": H, "d_k": DK, "d_v": DV, "chunk": 64,
                    "inputs": "bf16 q,k,v,b,w; fp32 log-decay and state"},
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1),
+        "roofline": {"bound": "hbm", "kernel": dom, "kernel_us": round(dom_us, 2), "achieved": round(ach, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
                      "traffic": traffic},
         "step_roofline": {"alg_bytes": step_alg_bytes, "alg_flops": flops,
