@@ -361,14 +361,14 @@ def main():
     di = KERNELS.index(dom)
     # the timed region: exactly `steps` steps; the only instrumentation is a pair of HIP events
     # around the dominant kernel in every step, whose average duration gives the roofline figure
-    dev = [[Ev() if i in (di, di + 1) else None for i in range(5)] for _ in range(args.steps)]
+    tev = [[Ev() if i in (di, di + 1) else None for i in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
-        step(dev[s])
+        step(tev[s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    dom_us = sum(e[di].elapsed_time(e[di + 1]) for e in dev) * 1e3 / args.steps
+    dom_us = sum(e[di].elapsed_time(e[di + 1]) for e in tev) * 1e3 / args.steps
 
     ms_step = wall * 1e3 / args.steps
     tokens = B * T
